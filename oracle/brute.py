@@ -1,0 +1,123 @@
+"""Independent scalar float64 implementation of the layer, token by token (test infrastructure only).
+
+Written separately from ``oracle.moe`` and ``oracle.nvfp4`` (it imports neither)
+so that it can pin them: plain Python loops, a literal E2M1 value table, an
+E4M3 decode written with ``math.ldexp``, and a per-token routing by sorting.
+Only for tiny layers (seconds at H=256, I=128).
+
+Definitions used (same sources as ``oracle.moe``):
+  * E2M1 magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}, top bit of the nibble = sign;
+    element 2j in the low nibble of byte j ("vLLM on the NVIDIA DGX Spark: A
+    Complete Technical Guide", section 6.1);
+  * E4M3 block scale per 16 elements along K; value = element * block scale *
+    global scale (same section);
+  * top-k on router logits (ties -> lower expert index), softmax renormalised
+    over the selected experts; SiLU(gate)*up; down projection; top-k-weighted
+    sum; shared expert added with weight 1 (same readings as ``oracle.moe``).
+"""
+
+from __future__ import annotations
+
+import math
+import struct
+
+E2M1_TABLE = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def bf16(bits: int) -> float:
+    return struct.unpack("<f", struct.pack("<I", (int(bits) & 0xFFFF) << 16))[0]
+
+
+def fp4(row_bytes, k: int) -> float:
+    byte = int(row_bytes[k // 2])
+    nib = (byte >> 4) if (k % 2) else (byte & 0xF)
+    mag = E2M1_TABLE[nib & 7]
+    return -mag if nib & 8 else mag
+
+
+def fp8_e4m3(byte: int) -> float:
+    byte = int(byte)
+    sign = -1.0 if byte & 0x80 else 1.0
+    e = (byte >> 3) & 0xF
+    m = byte & 7
+    if e == 15 and m == 7:
+        return math.nan
+    if e == 0:
+        return sign * math.ldexp(m, -9)          # m/8 * 2^-6
+    return sign * math.ldexp(8 + m, e - 10)      # (1 + m/8) * 2^(e-7)
+
+
+def weight(packed, scales, gscale: float, n: int, k: int) -> float:
+    return fp4(packed[n], k) * fp8_e4m3(scales[n][k // 16]) * float(gscale)
+
+
+def dequant_expert(ew):
+    """(Wg, Wu, Wd) as lists of float rows, decoded element by element."""
+    inter = len(ew.w13) // 2
+    hdim = 2 * len(ew.w13[0])
+    wg = [[weight(ew.w13, ew.w13_scale, ew.w13_gscale[0], i, h) for h in range(hdim)] for i in range(inter)]
+    wu = [[weight(ew.w13, ew.w13_scale, ew.w13_gscale[1], inter + i, h) for h in range(hdim)] for i in range(inter)]
+    wd = [[weight(ew.w2, ew.w2_scale, ew.w2_gscale, h, i) for i in range(inter)] for h in range(hdim)]
+    return wg, wu, wd
+
+
+def expert_out(xv, mats) -> list:
+    """y = Wd (silu(Wg x) * (Wu x)) for one token, scalar loops."""
+    wg, wu, wd = mats
+    hvec = []
+    for grow, urow in zip(wg, wu):
+        g = 0.0
+        u = 0.0
+        for xh, a, b in zip(xv, grow, urow):
+            g += xh * a
+            u += xh * b
+        act = g / (1.0 + math.exp(-g)) if g > -700.0 else 0.0
+        hvec.append(act * u)
+    y = []
+    for drow in wd:
+        acc = 0.0
+        for hv, c in zip(hvec, drow):
+            acc += hv * c
+        y.append(acc)
+    return y
+
+
+def forward(x_bits, layer, tokens=None):
+    """Per-token results [(ids, weights, out row, logits)] for the given token indices."""
+    cache = {}
+
+    def mats(bank, e):
+        key = (id(bank), e)
+        if key not in cache:
+            cache[key] = dequant_expert(bank[e])
+        return cache[key]
+
+    results = []
+    rows = range(len(x_bits)) if tokens is None else tokens
+    for t in rows:
+        xv = [bf16(b) for b in x_bits[t]]
+        e_count = len(layer.routed)
+        logits = []
+        for e in range(e_count):
+            acc = 0.0
+            for xh, wb in zip(xv, layer.w_router[e]):
+                acc += xh * bf16(wb)
+            if layer.router_bias is not None:
+                acc += float(layer.router_bias[e])
+            logits.append(acc)
+        chosen = sorted(range(e_count), key=lambda e: (-logits[e], e))[: layer.top_k]
+        top = max(logits[e] for e in chosen)
+        z = [math.exp(logits[e] - top) for e in chosen]
+        total = sum(z)
+        wts = [v / total for v in z]
+        out = [0.0] * len(xv)
+        for e, w in zip(chosen, wts):
+            y = expert_out(xv, mats(layer.routed, e))
+            for h in range(len(xv)):
+                out[h] += w * y[h]
+        if layer.shared is not None:
+            y = expert_out(xv, mats(layer.shared, 0))
+            for h in range(len(xv)):
+                out[h] += y[h]
+        results.append((chosen, wts, out, logits))
+    return results
