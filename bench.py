@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Throughput of the weight-only NVFP4 fused MoE layer on one MI355X.
+
+A step is one pass of the whole layer (router, top-k, permute, gate/up GEMM + SiLU*up, down
+GEMM, combine, shared expert) over one batch of synthetic tokens already resident in HBM.
+The default workload is the decode-shaped layer (T=8, H=4096, I=1536, E=320 top-8 + 1 shared).
+Prints one JSON line with the layer tokens/s, the roofline of the dominant kernel (timed live
+with HIP events recorded by the library at the stage boundaries of every timed step) and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+NVFP4_BYTES_PER_WEIGHT = 0.5625
+
+_DEFAULTS = {  # steps, warmup, weight copies cycled through (decode: defeat the 256 MB last-level cache)
+    "tiny": (200, 20, 1), "decode": (200, 20, 4), "prefill": (20, 3, 1), "skewed": (20, 3, 1),
+    "long_prefill": (5, 2, 1),
+}
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them on the stream it launches on)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def create(self) -> int:
+        ev = ctypes.c_void_p()
+        if self.lib.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        self.made.append(ev.value)
+        return ev.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        out = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+    def destroy_all(self):
+        for ev in self.made:
+            self.lib.hipEventDestroy(ctypes.c_void_p(ev))
+        self.made = []
+
+
+def clone_layer(layer, ops):
+    def bank(b):
+        return ops.NvFp4Experts(*(t.clone() for t in (b.w13, b.w13_scale, b.w13_gscale, b.w2, b.w2_scale,
+                                                     b.w2_gscale)))
+    return ops.NvFp4MoELayer(layer.w_router.clone(), None if layer.router_bias is None else layer.router_bias.clone(),
+                             bank(layer.routed), bank(layer.shared) if layer.shared is not None else None, layer.top_k)
+
+
+def cpu_baseline(wl, x_bits, ids, n_tokens, synth):
+    """The oracle as it stands, single-threaded, on the first ``n_tokens`` tokens of the workload."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    from oracle import moe as omoe
+    from oracle import nvfp4 as onv
+
+    def oracle_expert(bank, e):
+        w13, w2 = synth.expert_fp32(wl, bank, e, "cuda")
+        gs = synth.checkpoint_global_scales(synth.expert_amax(w13, w2), wl.gscale_convention)
+        d = onv.gscale_from_quant_scale(gs) if wl.gscale_convention == "compressed_tensors" else gs
+        w13, w2 = w13.cpu().numpy(), w2.cpu().numpy()
+        i = w13.shape[0] // 2
+        (pg, sg), (pu, su), (pd, sd) = onv.quantize(w13[:i], d[0]), onv.quantize(w13[i:], d[1]), onv.quantize(w2, d[2])
+        return omoe.ExpertWeights(np.concatenate([pg, pu]), np.concatenate([sg, su]), np.array(d[:2], np.float32),
+                                  pd, sd, float(d[2]))
+
+    used = sorted({int(e) for e in np.unique(ids[:n_tokens])})
+    with ThreadPoolExecutor(max_workers=8) as ex:   # input preparation, not timed
+        experts = dict(zip(used, ex.map(lambda e: oracle_expert("routed", e), used)))
+        shared = [oracle_expert("shared", 0)] if wl.I_shared > 0 else None
+
+    class Bank:
+        def __len__(self):
+            return wl.E
+
+        def __getitem__(self, e):
+            return experts[e]
+
+    layer = omoe.Layer(w_router=x_bits["router"], router_bias=synth.router_bias(wl), routed=Bank(), shared=shared,
+                       top_k=wl.k)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        omoe.forward(x_bits["x"][:n_tokens], layer)
+        dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n_tokens} of {wl.T} tokens of the {wl.name} workload ({len(used)} routed experts + "
+                      f"shared): float64 numpy oracle forward, one thread, {dt:.1f} s; weight quantization "
+                      f"untimed"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode", choices=sorted(_DEFAULTS))
+    ap.add_argument("--copies", type=int, default=None, help="weight copies cycled through")
+    ap.add_argument("--cpu-tokens", type=int, default=1, help="tokens in the CPU oracle sample (0: skip)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the layer on one GPU only: each layer runs whole on one MI355X "
+              "(no expert or tensor sharding, no collectives); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    from nvfp4_weight_quantized_amd import _lib, build_layer, ops, synth
+
+    _lib.lib()  # fail loudly now if the HIP library is missing
+    wl = synth.WORKLOADS[args.workload]
+    steps, warmup, copies = _DEFAULTS[args.workload]
+    steps = args.steps if args.steps is not None else steps
+    warmup = args.warmup if args.warmup is not None else warmup
+    copies = args.copies if args.copies is not None else copies
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    print(f"[bench] building {wl.name} layer ({copies} weight copies)", file=sys.stderr, flush=True)
+    layer = build_layer(wl, dev)
+    layers = [layer] + [clone_layer(layer, ops) for _ in range(copies - 1)]
+    x = synth.activations(wl, dev)
+    ws = ops.workspace_for(layer, wl.T, dev)
+    out = torch.empty_like(x)
+    _, aux = ops.forward(layer, x, ws, out, return_aux=True)
+    counts = aux["expert_counts"].cpu().numpy()
+    ids = aux["topk_ids"].cpu().numpy()
+    touched = int((counts > 0).sum())
+
+    for i in range(warmup):
+        ops.forward(layers[i % copies], x, ws, out)
+    torch.cuda.synchronize()
+
+    hip = HipEvents()
+    evs = [[hip.create() for _ in range(3)] for _ in range(steps)]   # after S3, after S4, after S5
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {steps} steps", file=sys.stderr, flush=True)
+    start.record()
+    for i in range(steps):
+        e = evs[i]
+        ops.forward(layers[i % copies], x, ws, out, stage_events=[None, None, e[0], e[1], e[2], None])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    gate_up_ms = float(np.mean([hip.elapsed_ms(e[0], e[1]) for e in evs]))
+    down_ms = float(np.mean([hip.elapsed_ms(e[1], e[2]) for e in evs]))
+    hip.destroy_all()
+
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
+    S = T * k
+    ms_per_step = total_ms / steps
+    value = T * steps / (total_ms / 1e3)
+    # roofline of the gate/up GEMM, the dominant kernel (2/3 of the weight bytes and flops)
+    n_banks = touched + (1 if wl.I_shared > 0 else 0)
+    gu_weight_bytes = n_banks * 2 * I * H * NVFP4_BYTES_PER_WEIGHT
+    gu_bytes = gu_weight_bytes + T * H * 2 + (S + T) * I * 2
+    gu_flops = 2.0 * (S + T) * H * 2 * I
+    if wl.name in ("tiny", "decode"):
+        roof = {"bound": "hbm", "achieved": gu_bytes / (gate_up_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": gu_flops / (gate_up_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "grouped_gemm_kernel gate/up (S4)"
+    roof["kernel_us"] = gate_up_ms * 1e3
+
+    cpu = None
+    if args.cpu_tokens > 0:
+        print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
+
+        def bits(t):
+            return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+        cpu = cpu_baseline(wl, {"x": bits(x), "router": bits(layer.w_router)}, ids, args.cpu_tokens, synth)
+    line = {
+        "metric": "NVFP4 MoE layer tokens/s; decode HBM GB/s %peak, prefill MFMA %peak",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{wl.name}: T={T} H={H} I={I} E={E} top-{k} + 1 shared (I={wl.I_shared}), "
+                               f"NVFP4 W4A16", "tokens": T, "hidden": H, "inter": I, "experts": E, "top_k": k,
+                   "weight_copies": copies, "experts_touched": touched},
+        "roofline": roof,
+        "stages_us": {"gate_up": gate_up_ms * 1e3, "down": down_ms * 1e3},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,215 @@
+/*
+ * moe_nvfp4.h -- C ABI of the weight-only NVFP4 fused MoE layer for AMD MI355X (gfx950).
+ *
+ * The layer (one pass per call of moe_nvfp4_forward):
+ *   S1  router logits   logits[t][e] = sum_h x[t][h] * Wr[e][h] (+ bias[e])        (fp32)
+ *   S2  top-k           the k largest logits per token, descending, equal logits -> lower
+ *                       expert index; weights = softmax over all E renormalised over the
+ *                       k selected, i.e. exp(l_j - l_max) / sum_selected exp(l_i - l_max)
+ *   S3  permute         group the T*k slots (slot = t*k + j) by expert, stable in slot order
+ *   S4  gate/up GEMM    per expert e and row r of its group:
+ *                       g = d_g * (x_t . Qg^T), u = d_u * (x_t . Qu^T), h = silu(g) * u
+ *   S5  down GEMM       y_r = d_d * (h_r . Qd^T)
+ *   S6  combine         out[t] = sum_j w[t][j] * y[row of slot t*k+j] + y_shared[t]
+ * plus one always-on shared expert (weight 1, no gate) computed on every token.
+ *
+ * Sources (web pages; section names as printed there):
+ *   - "vLLM on the NVIDIA DGX Spark: A Complete Technical Guide", section 6.1 "NVFP4 format":
+ *     E2M1 elements (2-bit exponent, 1-bit mantissa, max 6.0) packed two per byte, one FP8 E4M3
+ *     block scale per 16 contiguous elements along K, one fp32 global scale per tensor; an
+ *     element's value is element * block scale * global scale.
+ *   - same page, section 7.1: the modular fused-MoE stages Router -> Quantize-Dispatch ->
+ *     Permute-Experts-Unpermute -> Combine; section 4 (b12x fused MoE): token dispatch, two
+ *     GEMMs, SwiGLU and the top-k-weight reduction; section 5 (Marlin): weight-only W4A16,
+ *     16-bit activations, weights dequantized to 16-bit inside the GEMM.
+ *   - "Serving Solar Open 2 on DGX Spark": 320 routed experts + 1 shared expert, top-8
+ *     ("Solar Open 2 in brief"); a shared module-level workspace pool instead of per-layer
+ *     scratch, and fused gate/up projection ordering ("The fix" / "Supporting real NVFP4
+ *     checkpoints").
+ *   - "GLM-5.3-Flash-NVFP4 deployment blocked on SM121" (discussion): weight-only NVFP4 is
+ *     selected by the absence of input quantization; a missing activation scale must never
+ *     turn an expert's alpha into zero (MoE fault analysis); ModelOpt stores the dequant global
+ *     scale amax/(448*6), compressed-tensors the quant scale (448*6)/amax (follow-up reply).
+ *
+ * Layout conventions (readings of the pages where they are silent):
+ *   - bf16 values travel as uint16_t bit patterns.
+ *   - A packed NVFP4 tensor [N][K] is N rows of K/2 bytes; element 2j of a row is the low nibble
+ *     of byte j, element 2j+1 the high nibble; the nibble's top bit is the sign.
+ *   - Its block scales are [N][K/16] E4M3FN bytes (bias 7, max 448, no infinities).
+ *   - Fused gate/up weights w13 are [2I][H]: rows 0..I-1 gate, rows I..2I-1 up, each half with its
+ *     own dequant global scale.
+ *   - There is no activation-scale argument anywhere (W4A16): nothing can zero an expert.
+ *
+ * Conventions of every entry point:
+ *   - Pointers are DEVICE pointers unless marked (host).  All buffers are owned by the caller; the
+ *     library never allocates, frees or keeps a pointer after the call returns.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is only enqueued: no host
+ *     synchronisation, no device-to-host copy, so calls can be captured in a HIP graph.
+ *   - Arguments are validated on the host before anything is enqueued; on error nothing is
+ *     enqueued and a status != MOE_OK is returned.  A device that is not gfx950 gives
+ *     MOE_ERR_UNSUPPORTED_DEVICE.  Launch failures give MOE_ERR_HIP.  Device faults surface at
+ *     the caller's next synchronisation.  T == 0 is a valid no-op.
+ *   - Results are deterministic: no floating-point atomics; repeated calls are bitwise equal.
+ *   - Non-finite inputs are not checked and propagate.
+ *   - Calls on one stream are ordered; calls that overlap in time must use distinct outputs and
+ *     workspaces.
+ *
+ * Size limits: 1 <= k <= min(E, 64), E <= 1024; H and I multiples of 128 (the format needs 16;
+ * the kernels' K-chunk is 128); T*k < 2^31.
+ */
+#ifndef MOE_NVFP4_H
+#define MOE_NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,
+  MOE_ERR_UNSUPPORTED_DEVICE = 2,
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4
+} moe_status_t;
+
+/* Static, human-readable name of a status code (host). */
+const char* moe_status_string(moe_status_t s);
+
+/* One bank of NVFP4 experts (routed: num_experts = E; shared: num_experts = 1), device pointers. */
+typedef struct {
+  int32_t num_experts;
+  int32_t hidden;            /* H */
+  int32_t inter;             /* I */
+  const uint8_t* w13;        /* [E][2I][H/2]  packed E2M1, gate rows then up rows */
+  const uint8_t* w13_scale;  /* [E][2I][H/16] E4M3FN block scales */
+  const float* w13_gscale;   /* [E][2] dequant global scales (gate, up) */
+  const uint8_t* w2;         /* [E][H][I/2] */
+  const uint8_t* w2_scale;   /* [E][H][I/16] */
+  const float* w2_gscale;    /* [E] */
+} moe_nvfp4_experts_t;
+
+/* The whole layer: router + routed bank + optional shared bank (shared.num_experts == 0: none). */
+typedef struct {
+  int32_t hidden;            /* H */
+  int32_t num_experts;       /* E (routed) */
+  int32_t top_k;             /* k */
+  const uint16_t* w_router;  /* [E][H] bf16 */
+  const float* router_bias;  /* [E] fp32 added to the logits, or NULL */
+  moe_nvfp4_experts_t routed;
+  moe_nvfp4_experts_t shared;
+} moe_nvfp4_layer_t;
+
+/* ---------------------------------------------------------------- S1 + S2: route
+ * x [T][H] bf16, w_router [E][H] bf16, router_bias [E] fp32 or NULL.
+ * Writes logits [T][E] fp32 (the router GEMM output, fp32 accumulation of exact bf16 products),
+ * topk_ids [T][k] int32 (descending logit; equal logits -> lower index) and topk_w [T][k] fp32.
+ * flags & MOE_ROUTE_LOGITS_GIVEN: skip the GEMM and select from the logits the caller passes in
+ * `logits` (x, w_router and router_bias are then ignored and may be NULL).
+ * Source: modular fused-MoE stages ("vLLM on the NVIDIA DGX Spark", section 7.1); top-8 of 320
+ * ("Serving Solar Open 2 on DGX Spark", "Solar Open 2 in brief"). */
+#define MOE_ROUTE_LOGITS_GIVEN 1u
+moe_status_t moe_route(const uint16_t* x, const uint16_t* w_router, const float* router_bias,
+                       int32_t T, int32_t H, int32_t E, int32_t k, uint32_t flags,
+                       float* logits, int32_t* topk_ids, float* topk_w, void* stream);
+
+/* ---------------------------------------------------------------- S3: permute
+ * topk_ids [T][k] int32 in [0, E).  Writes expert_counts [E], expert_offsets [E+1] (exclusive
+ * prefix sum; offsets[E] = T*k), sorted_slot [T*k] (slot ids t*k+j grouped by expert, ascending
+ * inside a group) and slot_to_row [T*k] (inverse permutation).  Bit-exact and atomic-order free.
+ * Needs moe_permute_workspace_size(T, k, E) bytes of workspace.  ids outside [0, E) are not
+ * checked (the route stage never produces them).
+ * Source: "Permute-Experts-Unpermute" ("vLLM on the NVIDIA DGX Spark", section 7.1). */
+size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E);
+moe_status_t moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                         int32_t* expert_counts, int32_t* expert_offsets,
+                         int32_t* sorted_slot, int32_t* slot_to_row,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- S4 / S5: grouped NVFP4 GEMM
+ * Rows [expert_offsets[e], expert_offsets[e+1]) of the M_total output rows use expert e of `w`
+ * (expert_offsets: device [w->num_experts + 1], with expert_offsets[E] == M_total).
+ *   MOE_GEMM_GATE_UP: A row r = a[row_index[r] / row_divisor] (or a[r] when row_index == NULL),
+ *                     a has H columns; out[r] = bf16(silu(d_g * A_r.Qg^T) * (d_u * A_r.Qu^T)),
+ *                     out is [M_total][I] bf16.
+ *   MOE_GEMM_DOWN:    A row r = a[r] (row_index must be NULL), a has I columns;
+ *                     out[r] = bf16(d_d * A_r.Qd^T), out is [M_total][H] bf16.
+ * Weights are dequantized to bf16 (element * block scale is exact in bf16) and multiplied on the
+ * bf16 matrix cores with fp32 accumulation; the fp32 global scale is applied to the accumulator.
+ * Source: W4A16 "dequantize to 16-bit inside the GEMM" ("vLLM on the NVIDIA DGX Spark", section 5);
+ * SiLU(gate)*up between the GEMMs (section 4, fused MoE); NVFP4 format (section 6.1). */
+#define MOE_GEMM_GATE_UP 0
+#define MOE_GEMM_DOWN 1
+moe_status_t moe_nvfp4_grouped_gemm(int32_t stage, const moe_nvfp4_experts_t* w /* host */,
+                                    const uint16_t* a, const int32_t* row_index, int32_t row_divisor,
+                                    const int32_t* expert_offsets, int32_t M_total,
+                                    uint16_t* out, void* stream);
+
+/* ---------------------------------------------------------------- S6: combine
+ * out[t][:] = bf16( sum_j topk_w[t][j] * y_rows[slot_to_row[t*k+j]][:] + y_shared[t][:] ),
+ * accumulated in fp32 in the order j = 0..k-1, then the shared row.  y_shared may be NULL.
+ * Source: top-k-weight reduction of the fused MoE ("vLLM on the NVIDIA DGX Spark", section 4);
+ * the shared expert is added with weight 1 ("Serving Solar Open 2 on DGX Spark": one shared
+ * expert that every token uses). */
+moe_status_t moe_combine(const uint16_t* y_rows, const int32_t* slot_to_row, const float* topk_w,
+                         const uint16_t* y_shared, int32_t T, int32_t k, int32_t H,
+                         uint16_t* out, void* stream);
+
+/* ---------------------------------------------------------------- whole layer
+ * Optional extra outputs of moe_nvfp4_forward (each may be NULL): the router logits [T][E],
+ * the selection topk_ids [T][k], topk_w [T][k], and expert_counts [E] (device pointers).
+ * stage_events (host array of MOE_NUM_STAGE_EVENTS hipEvent_t handles, or NULL): when given,
+ * event i is recorded on the stream at stage boundary i -- 0 before S1, 1 after S2, 2 after S3,
+ * 3 after S4, 4 after S5, 5 after S6 -- so callers can time each stage; NULL entries are skipped.
+ * The events are created and owned by the caller. */
+#define MOE_NUM_STAGE_EVENTS 6
+typedef struct {
+  float* logits;
+  int32_t* topk_ids;
+  float* topk_w;
+  int32_t* expert_counts;
+  void* const* stage_events;
+} moe_forward_aux_t;
+
+/* Workspace bytes moe_nvfp4_forward needs for T tokens (I_shared = 0: no shared expert). */
+size_t moe_nvfp4_forward_workspace_size(int32_t T, int32_t H, int32_t I, int32_t I_shared,
+                                        int32_t E, int32_t k);
+
+/* S1..S6 for x [T][H] bf16 -> out [T][H] bf16.  `layer` and `aux` are host pointers to structs
+ * holding device pointers.  The workspace may be shared by every layer of a model that runs on
+ * the same stream (one pool instead of per-layer scratch). */
+moe_status_t moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int32_t T,
+                               uint16_t* out, void* workspace, size_t workspace_bytes,
+                               const moe_forward_aux_t* aux, void* stream);
+
+/* Pure-host validation used by moe_nvfp4_forward; needs no GPU when gfx_arch is given
+ * (e.g. "gfx950"; NULL = query the current device). */
+moe_status_t moe_validate_forward(const moe_nvfp4_layer_t* layer, int32_t T, size_t workspace_bytes,
+                                  const char* gfx_arch);
+
+/* ---------------------------------------------------------------- weight preparation
+ * Load-time conversion of compressed-tensors global scales (host memory): the checkpoint stores
+ * the quant scale q = (448*6)/amax, the kernels take the dequant scale d = fp32(1/q).
+ * Source: the reciprocal between ModelOpt and compressed-tensors global scales ("GLM-5.3-Flash-
+ * NVFP4" discussion, compressed-tensors follow-up).  Fails on q == 0 or non-finite q. */
+moe_status_t moe_gscale_from_quant_scale(const float* q_host, float* d_host, int32_t n);
+
+/* On-device NVFP4 quantization of fp32 weights (the on-the-fly quantization path a checkpoint
+ * without pre-quantized weights needs).  w: num_tensors tensors of [rows][cols] fp32, contiguous;
+ * gscale: device [num_tensors] dequant global scales d.  Per 16-group along cols, in fp32:
+ *   s = E4M3_RNE(min(amax_group / (6*d), 448)),  code = E2M1_RNE(w / (s*d)) (saturating at 6;
+ *   all codes 0 when s == 0; the sign bit is set for negative w).
+ * Writes packed [num_tensors][rows][cols/2] and scales [num_tensors][rows][cols/16].
+ * cols must be a multiple of 16.
+ * Source: the recipe g16 / symmetric / tensor-group / FP8-E4M3 block scales ("GLM-5.3-Flash-NVFP4"
+ * discussion); block scales clamped to 448 ("Serving Solar Open 2 on DGX Spark"). */
+moe_status_t moe_nvfp4_quantize(const float* w, int32_t num_tensors, int32_t rows, int32_t cols,
+                                const float* gscale, uint8_t* packed, uint8_t* scales, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_NVFP4_H */

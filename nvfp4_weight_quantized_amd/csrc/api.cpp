@@ -1,0 +1,333 @@
+// C ABI of libmoe_nvfp4: host-side validation, workspace carving and launch sequencing.
+// Every entry point validates on the host before enqueuing anything (loud failure instead of
+// silently wrong output -- the failure mode the DGX Spark pages keep warning about), never
+// synchronises and never allocates.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+
+#include "common.h"
+
+namespace {
+
+using moe::GemmBank;
+using moe::GemmProblem;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+// gfx950 check, cached per device (the value never changes for a device).
+int g_arch_ok[64];  // 0 unknown, 1 ok, 2 not gfx950
+
+moe_status_t check_arch(const char* arch) {
+  if (arch) return std::strncmp(arch, "gfx950", 6) == 0 ? MOE_OK : MOE_ERR_UNSUPPORTED_DEVICE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev >= 0 && dev < 64 && g_arch_ok[dev]) return g_arch_ok[dev] == 1 ? MOE_OK : MOE_ERR_UNSUPPORTED_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_HIP;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev >= 0 && dev < 64) g_arch_ok[dev] = ok ? 1 : 2;
+  return ok ? MOE_OK : MOE_ERR_UNSUPPORTED_DEVICE;
+}
+
+bool valid_bank(const moe_nvfp4_experts_t& b, int32_t H, int32_t expected_experts) {
+  if (b.num_experts != expected_experts || b.hidden != H) return false;
+  if (b.inter <= 0 || b.inter % 128 != 0) return false;
+  return b.w13 && b.w13_scale && b.w13_gscale && b.w2 && b.w2_scale && b.w2_gscale;
+}
+
+bool valid_route_dims(int32_t T, int32_t H, int32_t E, int32_t k) {
+  if (T < 0 || E < 1 || E > 1024 || k < 1 || k > E || k > 64) return false;
+  if (H <= 0 || H % 128 != 0) return false;
+  return (int64_t)T * k < (int64_t)0x7FFFFFFF;
+}
+
+GemmBank bank_w13(const moe_nvfp4_experts_t& b) { return GemmBank{b.w13, b.w13_scale, b.w13_gscale, 2}; }
+GemmBank bank_w2(const moe_nvfp4_experts_t& b) { return GemmBank{b.w2, b.w2_scale, b.w2_gscale, 1}; }
+
+struct ForwardLayout {
+  size_t logits, ids, w, counts, offsets, sorted_slot, slot_to_row, block_hist, h, h_shared, y;
+  size_t total;
+};
+
+ForwardLayout forward_layout(int32_t T, int32_t H, int32_t I, int32_t I_shared, int32_t E, int32_t k) {
+  ForwardLayout L{};
+  const size_t S = (size_t)T * k;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  L.logits = take((size_t)T * E * 4);
+  L.ids = take(S * 4);
+  L.w = take(S * 4);
+  L.counts = take((size_t)E * 4);
+  L.offsets = take((size_t)(E + 1) * 4);
+  L.sorted_slot = take(S * 4);
+  L.slot_to_row = take(S * 4);
+  L.block_hist = take(S > (size_t)moe::kPermuteChunk ? (size_t)moe::permute_blocks((int64_t)S) * E * 4 : 0);
+  L.h = take(S * I * 2);
+  L.h_shared = take((size_t)T * I_shared * 2);
+  L.y = take((S + (I_shared > 0 ? (size_t)T : 0)) * H * 2);
+  L.total = off;
+  return L;
+}
+
+template <typename P>
+P* at(void* base, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(base) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED_DEVICE: return "MOE_ERR_UNSUPPORTED_DEVICE (gfx950 required)";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "unknown moe_status_t";
+}
+
+moe_status_t moe_route(const uint16_t* x, const uint16_t* w_router, const float* router_bias, int32_t T,
+                       int32_t H, int32_t E, int32_t k, uint32_t flags, float* logits, int32_t* topk_ids,
+                       float* topk_w, void* stream) {
+  const bool given = (flags & MOE_ROUTE_LOGITS_GIVEN) != 0;
+  if ((flags & ~MOE_ROUTE_LOGITS_GIVEN) != 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (T < 0 || E < 1 || E > 1024 || k < 1 || k > E || k > 64) return MOE_ERR_INVALID_ARGUMENT;
+  if (!given && !valid_route_dims(T, H, E, k)) return MOE_ERR_INVALID_ARGUMENT;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARGUMENT;
+  if (!given && (!x || !w_router)) return MOE_ERR_INVALID_ARGUMENT;
+  if (moe_status_t st = check_arch(nullptr)) return st;
+  return moe::launch_route(x, w_router, router_bias, T, H, E, k, given, logits, topk_ids, topk_w,
+                           static_cast<hipStream_t>(stream));
+}
+
+size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E) {
+  if (T < 0 || k < 1 || E < 1) return 0;
+  const int64_t S = (int64_t)T * k;
+  if (S <= moe::kPermuteChunk) return 0;
+  return align_up((size_t)moe::permute_blocks(S) * E * 4);
+}
+
+moe_status_t moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* expert_counts,
+                         int32_t* expert_offsets, int32_t* sorted_slot, int32_t* slot_to_row, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (T < 0 || E < 1 || E > 1024 || k < 1 || k > E || (int64_t)T * k >= (int64_t)0x7FFFFFFF)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!expert_counts || !expert_offsets) return MOE_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!topk_ids || !sorted_slot || !slot_to_row)) return MOE_ERR_INVALID_ARGUMENT;
+  const size_t need = moe_permute_workspace_size(T, k, E);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (moe_status_t st = check_arch(nullptr)) return st;
+  // T == 0 still defines counts = 0 and offsets = 0 (S = 0 runs the single-workgroup path)
+  return moe::launch_permute(topk_ids, T, k, E, expert_counts, expert_offsets, sorted_slot, slot_to_row,
+                             static_cast<int32_t*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_nvfp4_grouped_gemm(int32_t stage, const moe_nvfp4_experts_t* w, const uint16_t* a,
+                                    const int32_t* row_index, int32_t row_divisor, const int32_t* expert_offsets,
+                                    int32_t M_total, uint16_t* out, void* stream) {
+  if (!w || (stage != MOE_GEMM_GATE_UP && stage != MOE_GEMM_DOWN)) return MOE_ERR_INVALID_ARGUMENT;
+  if (w->num_experts < 1 || w->num_experts > 1024) return MOE_ERR_INVALID_ARGUMENT;
+  if (!valid_bank(*w, w->hidden, w->num_experts) || w->hidden <= 0 || w->hidden % 128 != 0)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (M_total < 0 || row_divisor < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (stage == MOE_GEMM_DOWN && row_index) return MOE_ERR_INVALID_ARGUMENT;
+  if (M_total == 0) return MOE_OK;
+  if (!a || !expert_offsets || !out) return MOE_ERR_INVALID_ARGUMENT;
+  if (moe_status_t st = check_arch(nullptr)) return st;
+  GemmProblem p{};
+  p.stage = stage;
+  const bool gu = stage == MOE_GEMM_GATE_UP;
+  p.N = gu ? w->inter : w->hidden;
+  p.K = gu ? w->hidden : w->inter;
+  p.bank = gu ? bank_w13(*w) : bank_w2(*w);
+  p.offsets = expert_offsets;
+  p.G = w->num_experts;
+  p.M = M_total;
+  p.a = a;
+  p.row_index = row_index;
+  p.row_divisor = row_divisor;
+  p.out = out;
+  p.has_extra = 0;
+  return moe::launch_grouped_gemm(p, static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_combine(const uint16_t* y_rows, const int32_t* slot_to_row, const float* topk_w,
+                         const uint16_t* y_shared, int32_t T, int32_t k, int32_t H, uint16_t* out, void* stream) {
+  if (T < 0 || k < 1 || k > 1024 || H <= 0 || H % 8 != 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (T == 0) return MOE_OK;
+  if (!y_rows || !slot_to_row || !topk_w || !out) return MOE_ERR_INVALID_ARGUMENT;
+  if (moe_status_t st = check_arch(nullptr)) return st;
+  return moe::launch_combine(y_rows, slot_to_row, topk_w, y_shared, T, k, H, out, static_cast<hipStream_t>(stream));
+}
+
+size_t moe_nvfp4_forward_workspace_size(int32_t T, int32_t H, int32_t I, int32_t I_shared, int32_t E, int32_t k) {
+  if (T < 0 || H <= 0 || I <= 0 || I_shared < 0 || E < 1 || k < 1) return 0;
+  return forward_layout(T, H, I, I_shared, E, k).total;
+}
+
+moe_status_t moe_validate_forward(const moe_nvfp4_layer_t* layer, int32_t T, size_t workspace_bytes,
+                                  const char* gfx_arch) {
+  if (!layer) return MOE_ERR_INVALID_ARGUMENT;
+  const int32_t H = layer->hidden, E = layer->num_experts, k = layer->top_k;
+  if (!valid_route_dims(T, H, E, k)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!layer->w_router) return MOE_ERR_INVALID_ARGUMENT;
+  if (!valid_bank(layer->routed, H, E)) return MOE_ERR_INVALID_ARGUMENT;
+  const bool has_shared = layer->shared.num_experts != 0;
+  if (has_shared && !valid_bank(layer->shared, H, 1)) return MOE_ERR_INVALID_ARGUMENT;
+  const int32_t I = layer->routed.inter, Is = has_shared ? layer->shared.inter : 0;
+  if (T > 0 && workspace_bytes < moe_nvfp4_forward_workspace_size(T, H, I, Is, E, k))
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return check_arch(gfx_arch);
+}
+
+moe_status_t moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int32_t T, uint16_t* out,
+                               void* workspace, size_t workspace_bytes, const moe_forward_aux_t* aux,
+                               void* stream_) {
+  if (moe_status_t st = moe_validate_forward(layer, T, workspace_bytes, nullptr)) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !out || !workspace) return MOE_ERR_INVALID_ARGUMENT;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const int32_t H = layer->hidden, E = layer->num_experts, k = layer->top_k;
+  const bool has_shared = layer->shared.num_experts != 0;
+  const int32_t I = layer->routed.inter, Is = has_shared ? layer->shared.inter : 0;
+  const int32_t S = T * k;
+  const ForwardLayout L = forward_layout(T, H, I, Is, E, k);
+
+  float* logits = (aux && aux->logits) ? aux->logits : at<float>(workspace, L.logits);
+  int32_t* ids = (aux && aux->topk_ids) ? aux->topk_ids : at<int32_t>(workspace, L.ids);
+  float* w = (aux && aux->topk_w) ? aux->topk_w : at<float>(workspace, L.w);
+  int32_t* counts = (aux && aux->expert_counts) ? aux->expert_counts : at<int32_t>(workspace, L.counts);
+  int32_t* offsets = at<int32_t>(workspace, L.offsets);
+  int32_t* sorted_slot = at<int32_t>(workspace, L.sorted_slot);
+  int32_t* slot_to_row = at<int32_t>(workspace, L.slot_to_row);
+  int32_t* block_hist = at<int32_t>(workspace, L.block_hist);
+  uint16_t* h = at<uint16_t>(workspace, L.h);
+  uint16_t* h_shared = at<uint16_t>(workspace, L.h_shared);
+  uint16_t* y = at<uint16_t>(workspace, L.y);
+
+  void* const* events = aux ? aux->stage_events : nullptr;
+  auto mark = [&](int i) -> moe_status_t {
+    if (!events || !events[i]) return MOE_OK;
+    return hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  };
+
+  moe_status_t st = mark(0);
+  if (st) return st;
+  st = moe::launch_route(x, layer->w_router, layer->router_bias, T, H, E, k, false, logits, ids, w, stream);
+  if (st || (st = mark(1))) return st;
+  st = moe::launch_permute(ids, T, k, E, counts, offsets, sorted_slot, slot_to_row, block_hist, stream);
+  if (st || (st = mark(2))) return st;
+
+  // S4: routed rows gathered through sorted_slot; the shared expert rides in the same launch when
+  // its width matches, otherwise it gets a launch of its own.
+  const bool fuse_shared = has_shared && Is == I;
+  GemmProblem gu{};
+  gu.stage = MOE_GEMM_GATE_UP;
+  gu.N = I;
+  gu.K = H;
+  gu.bank = bank_w13(layer->routed);
+  gu.offsets = offsets;
+  gu.G = E;
+  gu.M = S;
+  gu.a = x;
+  gu.row_index = sorted_slot;
+  gu.row_divisor = k;
+  gu.out = h;
+  if (fuse_shared) {
+    // h_shared directly follows h: rows S..S+T-1 of one [S+T][I] matrix
+    gu.has_extra = 1;
+    gu.extra = bank_w13(layer->shared);
+    gu.M_extra = T;
+    gu.a_extra = x;
+  }
+  if ((st = moe::launch_grouped_gemm(gu, stream))) return st;
+  if (has_shared && !fuse_shared) {
+    GemmProblem gs{};
+    gs.stage = MOE_GEMM_GATE_UP;
+    gs.N = Is;
+    gs.K = H;
+    gs.bank = bank_w13(layer->shared);
+    gs.G = 0;
+    gs.M = 0;
+    gs.out = h_shared;
+    gs.has_extra = 1;
+    gs.extra = gs.bank;
+    gs.M_extra = T;
+    gs.a_extra = x;
+    if ((st = moe::launch_grouped_gemm(gs, stream))) return st;
+  }
+  if ((st = mark(3))) return st;
+
+  // S5
+  GemmProblem dn{};
+  dn.stage = MOE_GEMM_DOWN;
+  dn.N = H;
+  dn.K = I;
+  dn.bank = bank_w2(layer->routed);
+  dn.offsets = offsets;
+  dn.G = E;
+  dn.M = S;
+  dn.a = h;
+  dn.row_index = nullptr;
+  dn.row_divisor = 1;
+  dn.out = y;
+  if (fuse_shared) {
+    dn.has_extra = 1;
+    dn.extra = bank_w2(layer->shared);
+    dn.M_extra = T;
+    dn.a_extra = h + (size_t)S * I;
+  }
+  if ((st = moe::launch_grouped_gemm(dn, stream))) return st;
+  if (has_shared && !fuse_shared) {
+    GemmProblem ds{};
+    ds.stage = MOE_GEMM_DOWN;
+    ds.N = H;
+    ds.K = Is;
+    ds.bank = bank_w2(layer->shared);
+    ds.G = 0;
+    ds.M = S;  // output rows start after the routed rows
+    ds.out = y;
+    ds.has_extra = 1;
+    ds.extra = ds.bank;
+    ds.M_extra = T;
+    ds.a_extra = h_shared;
+    if ((st = moe::launch_grouped_gemm(ds, stream))) return st;
+  }
+  if ((st = mark(4))) return st;
+
+  // S6
+  st = moe::launch_combine(y, slot_to_row, w, has_shared ? y + (size_t)S * H : nullptr, T, k, H, out, stream);
+  if (st) return st;
+  return mark(5);
+}
+
+moe_status_t moe_gscale_from_quant_scale(const float* q_host, float* d_host, int32_t n) {
+  if (n < 0 || (n > 0 && (!q_host || !d_host))) return MOE_ERR_INVALID_ARGUMENT;
+  for (int32_t i = 0; i < n; ++i)
+    if (!(std::isfinite(q_host[i])) || q_host[i] == 0.0f) return MOE_ERR_INVALID_ARGUMENT;
+  for (int32_t i = 0; i < n; ++i) d_host[i] = 1.0f / q_host[i];
+  return MOE_OK;
+}
+
+moe_status_t moe_nvfp4_quantize(const float* w, int32_t num_tensors, int32_t rows, int32_t cols, const float* gscale,
+                                uint8_t* packed, uint8_t* scales, void* stream) {
+  if (num_tensors < 0 || rows < 0 || cols < 0 || cols % 16 != 0) return MOE_ERR_INVALID_ARGUMENT;
+  if ((int64_t)num_tensors * rows * cols == 0) return MOE_OK;
+  if (!w || !gscale || !packed || !scales) return MOE_ERR_INVALID_ARGUMENT;
+  if (moe_status_t st = check_arch(nullptr)) return st;
+  return moe::launch_quantize(w, num_tensors, rows, cols, gscale, packed, scales, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

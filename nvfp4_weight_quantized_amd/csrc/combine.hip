@@ -1,0 +1,66 @@
+// Combine (S6) of the NVFP4 MoE layer, gfx950: the top-k-weighted reduction of the expert rows of
+// each token plus the shared expert's row ("vLLM on the NVIDIA DGX Spark: A Complete Technical
+// Guide", section 4: fused MoE with top-k-weight reduction; "Serving Solar Open 2 on DGX Spark":
+// one shared expert used by every token, added here with weight 1).
+//
+// out[t][h] = bf16( sum_{j<k} w[t][j] * y[slot_to_row[t*k+j]][h]  +  y_shared[t][h] ),
+// accumulated in fp32 in that order.  A gather-add: each thread owns 8 consecutive columns and
+// reads 16-byte pieces of the k+1 source rows; no atomics, so the result is deterministic.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kCombineThreads = 256;
+constexpr int kCols = kCombineThreads * 8;  // columns per workgroup
+
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t* __restrict__ y,
+                                                                  const int32_t* __restrict__ slot_to_row,
+                                                                  const float* __restrict__ w,
+                                                                  const uint16_t* __restrict__ y_shared, int k,
+                                                                  int H, uint16_t* __restrict__ out) {
+  const int t = blockIdx.y;
+  const int h0 = blockIdx.x * kCols + threadIdx.x * 8;
+  if (h0 >= H) return;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[(size_t)t * k + j];
+    const int row = slot_to_row[(size_t)t * k + j];
+    const uint4 v = *reinterpret_cast<const uint4*>(y + (size_t)row * H + h0);
+    const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = fmaf(wj, __uint_as_float(q[i] << 16), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(wj, __uint_as_float(q[i] & 0xFFFF0000u), acc[2 * i + 1]);
+    }
+  }
+  if (y_shared) {
+    const uint4 v = *reinterpret_cast<const uint4*>(y_shared + (size_t)t * H + h0);
+    const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += __uint_as_float(q[i] << 16);
+      acc[2 * i + 1] += __uint_as_float(q[i] & 0xFFFF0000u);
+    }
+  }
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = (uint32_t)f32_to_bf16(acc[2 * i]) | ((uint32_t)f32_to_bf16(acc[2 * i + 1]) << 16);
+  *reinterpret_cast<uint4*>(out + (size_t)t * H + h0) = uint4{o[0], o[1], o[2], o[3]};
+}
+
+}  // namespace
+
+moe_status_t launch_combine(const uint16_t* y_rows, const int32_t* slot_to_row, const float* w,
+                            const uint16_t* y_shared, int32_t T, int32_t k, int32_t H, uint16_t* out,
+                            hipStream_t stream) {
+  if (T == 0) return MOE_OK;
+  hipLaunchKernelGGL(combine_kernel, dim3((H + kCols - 1) / kCols, T), dim3(kCombineThreads), 0, stream, y_rows,
+                     slot_to_row, w, y_shared, (int)k, (int)H, out);
+  return launch_status();
+}
+
+}  // namespace moe

@@ -1,0 +1,90 @@
+// Internal declarations shared by the HIP sources of libmoe_nvfp4 (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include <algorithm>
+
+#include "../../include/moe_nvfp4.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 h = (__bf16)f;  // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// Host-side launch helpers -----------------------------------------------------------------
+
+// Status of the last launch on this thread; MOE_ERR_HIP if the launch was rejected.
+inline moe_status_t launch_status() {
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// Permute -----------------------------------------------------------------------------------
+constexpr int kPermuteChunk = 2048;     // slots per workgroup of the multi-block path
+constexpr int kPermuteThreads = 512;    // 8 waves
+
+inline int permute_blocks(int64_t slots) { return (int)((slots + kPermuteChunk - 1) / kPermuteChunk); }
+
+moe_status_t launch_permute(const int32_t* ids, int32_t T, int32_t k, int32_t E, int32_t* counts,
+                            int32_t* offsets, int32_t* sorted_slot, int32_t* slot_to_row,
+                            int32_t* block_hist, hipStream_t stream);
+
+// Route -------------------------------------------------------------------------------------
+moe_status_t launch_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int32_t T,
+                          int32_t H, int32_t E, int32_t k, bool logits_given, float* logits,
+                          int32_t* ids, float* w, hipStream_t stream);
+
+// Grouped GEMM ------------------------------------------------------------------------------
+struct GemmBank {
+  const uint8_t* w;      // packed nibbles, [E][Nrows][K/2]
+  const uint8_t* ws;     // E4M3 block scales, [E][Nrows][K/16]
+  const float* gs;       // dequant global scales, [E][gs_per_expert]
+  int32_t gs_per_expert; // 2 (gate, up) or 1 (down)
+};
+
+struct GemmProblem {
+  int32_t stage;          // MOE_GEMM_GATE_UP or MOE_GEMM_DOWN
+  int32_t N;              // output columns (I for gate/up, H for down)
+  int32_t K;              // reduction length (H for gate/up, I for down)
+  // main bank: groups from device offsets
+  GemmBank bank;
+  const int32_t* offsets; // [G+1]
+  int32_t G;              // number of groups
+  int32_t M;              // rows of the main bank == offsets[G]
+  const uint16_t* a;      // A rows source (K columns)
+  const int32_t* row_index;  // NULL: identity
+  int32_t row_divisor;
+  uint16_t* out;          // [M (+ M_extra)][N]
+  // optional extra single-expert group (the shared expert): rows [0, M_extra) read a_extra[r]
+  // and write out[M + r]
+  int32_t has_extra;
+  GemmBank extra;
+  int32_t M_extra;
+  const uint16_t* a_extra;
+};
+
+moe_status_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream);
+
+// Combine -----------------------------------------------------------------------------------
+moe_status_t launch_combine(const uint16_t* y_rows, const int32_t* slot_to_row, const float* w,
+                            const uint16_t* y_shared, int32_t T, int32_t k, int32_t H, uint16_t* out,
+                            hipStream_t stream);
+
+// Quantize ----------------------------------------------------------------------------------
+moe_status_t launch_quantize(const float* w, int32_t num_tensors, int32_t rows, int32_t cols,
+                             const float* gscale, uint8_t* packed, uint8_t* scales, hipStream_t stream);
+
+}  // namespace moe

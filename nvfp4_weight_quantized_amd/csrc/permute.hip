@@ -1,0 +1,199 @@
+// Token permutation (S3) of the NVFP4 MoE layer, gfx950.
+//
+// Groups the S = T*k slots (slot = t*k + j) by expert, keeping slot order inside each group, and
+// writes per-expert counts, exclusive offsets, the sorted slot list and its inverse.  The result
+// is bit-exact and independent of scheduling: counts come from LDS integer atomics (order-free),
+// and every slot's position is its group offset plus the number of earlier slots of the same
+// expert, computed from per-block and per-wave histograms and in-wave ballots -- never from the
+// order in which atomics land.
+//
+// Small S (one workgroup): one launch does histogram, scan and scatter.  Large S: per-block
+// histograms -> one scan workgroup -> per-block stable scatter.
+// Source: the "Permute-Experts-Unpermute" stage of the modular fused MoE ("vLLM on the NVIDIA DGX
+// Spark: A Complete Technical Guide", section 7.1) and the token dispatch of the fused b12x MoE
+// (section 4).
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kWaves = kPermuteThreads / kWave;          // 8
+constexpr int kSlotsPerWave = kPermuteChunk / kWaves;    // 256
+constexpr int kMaxE = 1024;
+
+// Exclusive scan of cnt[0..E) into out[0..E) by wave 0, returning the total (valid in wave 0).
+__device__ int wave0_exclusive_scan(const int* cnt, int* out, int E) {
+  const int lane = threadIdx.x & 63;
+  int carry = 0;
+  for (int base = 0; base < E; base += 64) {
+    const int e = base + lane;
+    const int v = (e < E) ? cnt[e] : 0;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    if (e < E) out[e] = carry + incl - v;
+    carry += __shfl(incl, 63);
+  }
+  return carry;
+}
+
+// Stable scatter of one wave's slots [s_begin, s_end) using the per-wave running bases in `base`.
+__device__ void wave_stable_scatter(const int32_t* __restrict__ ids, int s_begin, int s_end, int* base,
+                                    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_to_row) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  for (int s0 = s_begin; s0 < s_end; s0 += 64) {
+    const int s = s0 + lane;
+    const bool valid = s < s_end;
+    const int e = valid ? ids[s] : -1;
+    uint64_t rem = __ballot(valid);
+    uint64_t peers = 0;
+    while (rem) {
+      const int leader = __ffsll((unsigned long long)rem) - 1;
+      const int le = __shfl(e, leader);
+      const uint64_t m = __ballot(valid && e == le);
+      if (valid && e == le) peers = m;
+      rem &= ~m;
+    }
+    if (valid) {
+      const int rank = __popcll(peers & below);
+      const int b = base[e];
+      const int pos = b + rank;
+      sorted_slot[pos] = s;
+      slot_to_row[s] = pos;
+      if (rank == 0) base[e] = b + __popcll(peers);
+    }
+  }
+}
+
+// One workgroup does everything (S <= kPermuteChunk).
+__global__ __launch_bounds__(kPermuteThreads) void permute_single_kernel(
+    const int32_t* __restrict__ ids, int S, int E, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_to_row) {
+  __shared__ int wave_hist[kWaves][kMaxE];
+  __shared__ int offs[kMaxE];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  for (int i = tid; i < kWaves * kMaxE; i += kPermuteThreads) (&wave_hist[0][0])[i] = 0;
+  __syncthreads();
+  const int s_begin = wave * kSlotsPerWave;
+  const int s_end = min(S, s_begin + kSlotsPerWave);
+  for (int s = s_begin + (tid & 63); s < s_end; s += 64) atomicAdd(&wave_hist[wave][ids[s]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += kPermuteThreads) {
+    int c = 0;
+    for (int w = 0; w < kWaves; ++w) c += wave_hist[w][e];
+    counts[e] = c;
+    offs[e] = c;  // scanned below
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int total = wave0_exclusive_scan(offs, offs, E);
+    if ((tid & 63) == 0) offsets[E] = total;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kPermuteThreads) {
+    offsets[e] = offs[e];
+    int run = offs[e];
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = wave_hist[w][e];
+      wave_hist[w][e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  if (s_begin < s_end) wave_stable_scatter(ids, s_begin, s_end, wave_hist[wave], sorted_slot, slot_to_row);
+}
+
+// Multi-block path, step 1: per-block histograms block_hist[b][e].
+__global__ __launch_bounds__(kPermuteThreads) void permute_hist_kernel(const int32_t* __restrict__ ids, int S,
+                                                                       int E, int32_t* __restrict__ block_hist) {
+  __shared__ int hist[kMaxE];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kPermuteThreads) hist[e] = 0;
+  __syncthreads();
+  const int s_begin = blockIdx.x * kPermuteChunk;
+  const int s_end = min(S, s_begin + kPermuteChunk);
+  for (int s = s_begin + tid; s < s_end; s += kPermuteThreads) atomicAdd(&hist[ids[s]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += kPermuteThreads) block_hist[(size_t)blockIdx.x * E + e] = hist[e];
+}
+
+// Step 2 (one workgroup): counts, offsets, and block_hist[b][e] -> first row of block b in group e.
+__global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict__ block_hist, int nb, int E,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets) {
+  __shared__ int offs[kMaxE];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 1024) {
+    int run = 0;
+    for (int b = 0; b < nb; ++b) {
+      const int c = block_hist[(size_t)b * E + e];
+      block_hist[(size_t)b * E + e] = run;
+      run += c;
+    }
+    counts[e] = run;
+    offs[e] = run;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int total = wave0_exclusive_scan(offs, offs, E);
+    if (tid == 0) offsets[E] = total;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) {
+    offsets[e] = offs[e];
+    for (int b = 0; b < nb; ++b) block_hist[(size_t)b * E + e] += offs[e];
+  }
+}
+
+// Step 3: per-block stable scatter from the block bases.
+__global__ __launch_bounds__(kPermuteThreads) void permute_scatter_kernel(
+    const int32_t* __restrict__ ids, int S, int E, const int32_t* __restrict__ block_base,
+    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_to_row) {
+  __shared__ int wave_hist[kWaves][kMaxE];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  for (int w = 0; w < kWaves; ++w)
+    for (int e = tid; e < E; e += kPermuteThreads) wave_hist[w][e] = 0;
+  __syncthreads();
+  const int blk0 = blockIdx.x * kPermuteChunk;
+  const int s_begin = blk0 + wave * kSlotsPerWave;
+  const int s_end = min(S, s_begin + kSlotsPerWave);
+  for (int s = s_begin + (tid & 63); s < s_end; s += 64) atomicAdd(&wave_hist[wave][ids[s]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += kPermuteThreads) {
+    int run = block_base[(size_t)blockIdx.x * E + e];
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = wave_hist[w][e];
+      wave_hist[w][e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  if (s_begin < s_end) wave_stable_scatter(ids, s_begin, s_end, wave_hist[wave], sorted_slot, slot_to_row);
+}
+
+}  // namespace
+
+moe_status_t launch_permute(const int32_t* ids, int32_t T, int32_t k, int32_t E, int32_t* counts,
+                            int32_t* offsets, int32_t* sorted_slot, int32_t* slot_to_row,
+                            int32_t* block_hist, hipStream_t stream) {
+  const int S = T * k;
+  if (S <= kPermuteChunk) {
+    hipLaunchKernelGGL(permute_single_kernel, dim3(1), dim3(kPermuteThreads), 0, stream, ids, S, (int)E, counts,
+                       offsets, sorted_slot, slot_to_row);
+    return launch_status();
+  }
+  const int nb = permute_blocks(S);
+  hipLaunchKernelGGL(permute_hist_kernel, dim3(nb), dim3(kPermuteThreads), 0, stream, ids, S, (int)E, block_hist);
+  if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, stream, block_hist, nb, (int)E, counts, offsets);
+  if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  hipLaunchKernelGGL(permute_scatter_kernel, dim3(nb), dim3(kPermuteThreads), 0, stream, ids, S, (int)E,
+                     block_hist, sorted_slot, slot_to_row);
+  return launch_status();
+}
+
+}  // namespace moe

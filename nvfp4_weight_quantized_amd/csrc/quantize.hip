@@ -1,0 +1,95 @@
+// On-device NVFP4 quantization of fp32 weights (weight preparation, not part of the layer pass).
+//
+// Recipe: group 16 along K, symmetric, FP8 E4M3 block scales, one fp32 global scale per tensor
+// ("GLM-5.3-Flash-NVFP4 deployment blocked on SM121" discussion, compressed-tensors follow-up);
+// block scales clamped to 448 ("Serving Solar Open 2 on DGX Spark", "Supporting real NVFP4
+// checkpoints"); E2M1 elements of at most 6.0 packed two per byte ("vLLM on the NVIDIA DGX Spark",
+// section 6.1).  Every step is an fp32 operation with round-to-nearest-even, done in this order:
+//   t = amax_group / (6 * d);  t = min(t, 448);  s = E4M3_RNE(t)
+//   q = w / (s * d) (0 when s * d == 0);  code = E2M1_RNE(q) saturated at 6, sign bit = (q < 0).
+#include "common.h"
+
+namespace moe {
+namespace {
+
+// Round t in [0, 448] to the nearest E4M3FN value (ties to even); returns the value and its byte.
+__device__ __forceinline__ float e4m3_rne(float t, uint32_t* code) {
+  if (!(t > 0.f)) {
+    *code = 0;
+    return 0.f;
+  }
+  int ex = ilogbf(t);                  // t in [2^ex, 2^(ex+1))
+  const int qexp = max(ex, -6) - 3;    // grid spacing 2^qexp
+  const float r = rintf(ldexpf(t, -qexp));
+  const float v = ldexpf(r, qexp);     // exact
+  if (v < 0x1p-6f) {                   // subnormal: m * 2^-9
+    *code = (uint32_t)r;
+  } else {
+    const int ev = ilogbf(v);
+    const uint32_t m = (uint32_t)(ldexpf(v, 3 - ev)) - 8u;   // v = (8 + m) * 2^(ev-3)
+    *code = ((uint32_t)(ev + 7) << 3) | m;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t e2m1_rne(float q) {
+  const float mag = fabsf(q);
+  const float step_inv = mag < 2.f ? 2.f : (mag < 4.f ? 1.f : 0.5f);
+  const float v = fminf(rintf(mag * step_inv) / step_inv, 6.f);
+  uint32_t c;
+  if (v <= 2.f) c = (uint32_t)(v * 2.f);        // 0, .5, 1, 1.5, 2 -> 0..4
+  else if (v == 3.f) c = 5u;
+  else if (v == 4.f) c = 6u;
+  else c = 7u;
+  return c | (q < 0.f ? 8u : 0u);
+}
+
+// One thread per 16-element group.
+__global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ w, long long groups_per_tensor,
+                                                       long long total_groups, const float* __restrict__ gscale,
+                                                       uint8_t* __restrict__ packed, uint8_t* __restrict__ scales) {
+  const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (g >= total_groups) return;
+  const float d = gscale[g / groups_per_tensor];
+  const float4* src = reinterpret_cast<const float4*>(w + g * 16);
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 x = src[i];
+    v[4 * i] = x.x; v[4 * i + 1] = x.y; v[4 * i + 2] = x.z; v[4 * i + 3] = x.w;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  float t = __fdiv_rn(amax, __fmul_rn(6.0f, d));
+  t = fminf(t, 448.0f);
+  uint32_t scode;
+  const float s = e4m3_rne(t, &scode);
+  const float sd = __fmul_rn(s, d);
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float qv = (sd > 0.f) ? __fdiv_rn(v[i], sd) : 0.f;
+    const uint32_t c = e2m1_rne(qv);
+    if (i < 8) lo |= c << (4 * i);
+    else hi |= c << (4 * (i - 8));
+  }
+  *reinterpret_cast<uint2*>(packed + g * 8) = uint2{lo, hi};
+  scales[g] = (uint8_t)scode;
+}
+
+}  // namespace
+
+moe_status_t launch_quantize(const float* w, int32_t num_tensors, int32_t rows, int32_t cols,
+                             const float* gscale, uint8_t* packed, uint8_t* scales, hipStream_t stream) {
+  const long long gpt = (long long)rows * (cols / 16);
+  const long long total = gpt * num_tensors;
+  if (total == 0) return MOE_OK;
+  const long long blocks = (total + 255) / 256;
+  if (blocks > 0x7FFFFFFFLL) return MOE_ERR_INVALID_ARGUMENT;
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w, gpt, total, gscale, packed,
+                     scales);
+  return launch_status();
+}
+
+}  // namespace moe

@@ -1,0 +1,320 @@
+"""torch-facing wrappers of the C ABI: argument checks and marshalling only.
+
+PyTorch supplies device memory and the current stream; every step of the layer runs in the
+HIP kernels of libmoe_nvfp4.so.  There is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: Optional[int] = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got {tuple(t.shape)}")
+
+
+# ----------------------------------------------------------------------------- weights
+
+@dataclass
+class NvFp4Experts:
+    """A bank of NVFP4 experts on the GPU (layouts as in include/moe_nvfp4.h)."""
+    w13: torch.Tensor          # uint8 [E, 2I, H/2]
+    w13_scale: torch.Tensor    # uint8 [E, 2I, H/16]
+    w13_gscale: torch.Tensor   # float32 [E, 2]
+    w2: torch.Tensor           # uint8 [E, H, I/2]
+    w2_scale: torch.Tensor     # uint8 [E, H, I/16]
+    w2_gscale: torch.Tensor    # float32 [E]
+
+    @property
+    def num_experts(self) -> int:
+        return self.w13.shape[0]
+
+    @property
+    def hidden(self) -> int:
+        return self.w13.shape[2] * 2
+
+    @property
+    def inter(self) -> int:
+        return self.w13.shape[1] // 2
+
+    def check(self) -> None:
+        e, h, i = self.num_experts, self.hidden, self.inter
+        for name, t, dt, shape in [("w13", self.w13, torch.uint8, (e, 2 * i, h // 2)),
+                                   ("w13_scale", self.w13_scale, torch.uint8, (e, 2 * i, h // 16)),
+                                   ("w13_gscale", self.w13_gscale, torch.float32, (e, 2)),
+                                   ("w2", self.w2, torch.uint8, (e, h, i // 2)),
+                                   ("w2_scale", self.w2_scale, torch.uint8, (e, h, i // 16)),
+                                   ("w2_gscale", self.w2_gscale, torch.float32, (e,))]:
+            _need(t, name, dt)
+            if tuple(t.shape) != shape:
+                raise ValueError(f"{name}: expected shape {shape}, got {tuple(t.shape)}")
+
+    def c_struct(self) -> L.Experts:
+        return L.Experts(self.num_experts, self.hidden, self.inter,
+                         self.w13.data_ptr(), self.w13_scale.data_ptr(), self.w13_gscale.data_ptr(),
+                         self.w2.data_ptr(), self.w2_scale.data_ptr(), self.w2_gscale.data_ptr())
+
+
+@dataclass
+class NvFp4MoELayer:
+    """Router + routed experts + optional shared expert, all on one GPU."""
+    w_router: torch.Tensor                 # bf16 [E, H]
+    router_bias: Optional[torch.Tensor]    # float32 [E] or None
+    routed: NvFp4Experts
+    shared: Optional[NvFp4Experts]
+    top_k: int
+
+    @property
+    def hidden(self) -> int:
+        return self.routed.hidden
+
+    @property
+    def num_experts(self) -> int:
+        return self.routed.num_experts
+
+    def c_struct(self) -> L.Layer:
+        empty = L.Experts()
+        return L.Layer(self.hidden, self.num_experts, self.top_k, self.w_router.data_ptr(),
+                       self.router_bias.data_ptr() if self.router_bias is not None else None,
+                       self.routed.c_struct(), self.shared.c_struct() if self.shared is not None else empty)
+
+    @classmethod
+    def from_tensors(cls, tensors: dict, top_k: int, global_scale_convention: str = "modelopt",
+                     device="cuda") -> "NvFp4MoELayer":
+        """Build a layer from a checkpoint-like dict.
+
+        Keys: router.weight, router.bias (optional), experts.{w13, w13_scale, w13_global_scale,
+        w2, w2_scale, w2_global_scale} and the same under shared_expert.* (optional).
+        Global scales in the "compressed_tensors" convention are quant scales (448*6)/amax and are
+        inverted on load; "modelopt" global scales are dequant scales and are used as stored.
+        Any activation-scale key (``*input_scale*``) is ignored: the layer is weight-only.
+        """
+        if global_scale_convention not in ("modelopt", "compressed_tensors"):
+            raise ValueError(global_scale_convention)
+
+        def dev(t, dtype):
+            return torch.as_tensor(t).to(device=device, dtype=dtype).contiguous()
+
+        def gscale(t):
+            a = torch.as_tensor(t).detach().to("cpu", torch.float32).contiguous()
+            if global_scale_convention == "compressed_tensors":
+                a = torch.from_numpy(gscale_from_quant_scale(a.numpy()))
+            return a.to(device)
+
+        def bank(prefix):
+            if prefix + "w13" not in tensors:
+                return None
+            return NvFp4Experts(dev(tensors[prefix + "w13"], torch.uint8), dev(tensors[prefix + "w13_scale"], torch.uint8),
+                                gscale(tensors[prefix + "w13_global_scale"]),
+                                dev(tensors[prefix + "w2"], torch.uint8), dev(tensors[prefix + "w2_scale"], torch.uint8),
+                                gscale(tensors[prefix + "w2_global_scale"]))
+
+        routed = bank("experts.")
+        shared = bank("shared_expert.")
+        bias = tensors.get("router.bias")
+        layer = cls(dev(tensors["router.weight"], torch.bfloat16),
+                    dev(bias, torch.float32) if bias is not None else None, routed, shared, top_k)
+        routed.check()
+        if shared is not None:
+            shared.check()
+        return layer
+
+
+# ----------------------------------------------------------------------------- stages
+
+def route(x: torch.Tensor, w_router: torch.Tensor, router_bias: Optional[torch.Tensor], k: int):
+    """S1+S2: (logits fp32 [T, E], topk_ids int32 [T, k], topk_w fp32 [T, k])."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w_router, "w_router", torch.bfloat16, 2)
+    if router_bias is not None:
+        _need(router_bias, "router_bias", torch.float32, 1)
+    t, h = x.shape
+    e = w_router.shape[0]
+    logits = torch.empty(t, e, dtype=torch.float32, device=x.device)
+    ids = torch.empty(t, k, dtype=torch.int32, device=x.device)
+    w = torch.empty(t, k, dtype=torch.float32, device=x.device)
+    L.check("moe_route", L.lib().moe_route(_ptr(x), _ptr(w_router), _ptr(router_bias), t, h, e, k, 0,
+                                           _ptr(logits), _ptr(ids), _ptr(w), _stream(x.device)))
+    return logits, ids, w
+
+
+def route_from_logits(logits: torch.Tensor, k: int):
+    """S2 only, on given fp32 logits [T, E]: (topk_ids, topk_w)."""
+    _need(logits, "logits", torch.float32, 2)
+    t, e = logits.shape
+    ids = torch.empty(t, k, dtype=torch.int32, device=logits.device)
+    w = torch.empty(t, k, dtype=torch.float32, device=logits.device)
+    L.check("moe_route", L.lib().moe_route(None, None, None, t, 0, e, k, L.MOE_ROUTE_LOGITS_GIVEN, _ptr(logits),
+                                           _ptr(ids), _ptr(w), _stream(logits.device)))
+    return ids, w
+
+
+def permute(topk_ids: torch.Tensor, num_experts: int):
+    """S3: (counts [E], offsets [E+1], sorted_slot [S], slot_to_row [S]), all int32."""
+    _need(topk_ids, "topk_ids", torch.int32, 2)
+    t, k = topk_ids.shape
+    dev = topk_ids.device
+    counts = torch.empty(num_experts, dtype=torch.int32, device=dev)
+    offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+    sorted_slot = torch.empty(t * k, dtype=torch.int32, device=dev)
+    slot_to_row = torch.empty(t * k, dtype=torch.int32, device=dev)
+    ws_bytes = L.lib().moe_permute_workspace_size(t, k, num_experts)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    L.check("moe_permute", L.lib().moe_permute(_ptr(topk_ids), t, k, num_experts, _ptr(counts), _ptr(offsets),
+                                               _ptr(sorted_slot), _ptr(slot_to_row), _ptr(ws), ws_bytes,
+                                               _stream(dev)))
+    return counts, offsets, sorted_slot, slot_to_row
+
+
+def grouped_gemm(stage: int, experts: NvFp4Experts, a: torch.Tensor, expert_offsets: torch.Tensor, m_total: int,
+                 row_index: Optional[torch.Tensor] = None, row_divisor: int = 1) -> torch.Tensor:
+    """S4 (stage 0: gate/up + SiLU*up -> [M, I]) or S5 (stage 1: down -> [M, H]), bf16."""
+    experts.check()
+    _need(a, "a", torch.bfloat16, 2)
+    _need(expert_offsets, "expert_offsets", torch.int32, 1)
+    if row_index is not None:
+        _need(row_index, "row_index", torch.int32, 1)
+    n = experts.inter if stage == L.MOE_GEMM_GATE_UP else experts.hidden
+    out = torch.empty(m_total, n, dtype=torch.bfloat16, device=a.device)
+    st = experts.c_struct()
+    L.check("moe_nvfp4_grouped_gemm",
+            L.lib().moe_nvfp4_grouped_gemm(stage, ctypes.byref(st), _ptr(a), _ptr(row_index), row_divisor,
+                                           _ptr(expert_offsets), m_total, _ptr(out), _stream(a.device)))
+    return out
+
+
+def combine(y_rows: torch.Tensor, slot_to_row: torch.Tensor, topk_w: torch.Tensor,
+            y_shared: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """S6: out [T, H] bf16."""
+    _need(y_rows, "y_rows", torch.bfloat16, 2)
+    _need(slot_to_row, "slot_to_row", torch.int32, 1)
+    _need(topk_w, "topk_w", torch.float32, 2)
+    t, k = topk_w.shape
+    h = y_rows.shape[1]
+    if y_shared is not None:
+        _need(y_shared, "y_shared", torch.bfloat16, 2)
+    out = torch.empty(t, h, dtype=torch.bfloat16, device=y_rows.device)
+    L.check("moe_combine", L.lib().moe_combine(_ptr(y_rows), _ptr(slot_to_row), _ptr(topk_w), _ptr(y_shared), t, k,
+                                               h, _ptr(out), _stream(y_rows.device)))
+    return out
+
+
+# ----------------------------------------------------------------------------- whole layer
+
+def forward_workspace_size(T: int, H: int, I: int, I_shared: int, E: int, k: int) -> int:
+    return int(L.lib().moe_nvfp4_forward_workspace_size(T, H, I, I_shared, E, k))
+
+
+_POOL = {}
+
+
+def workspace_for(layer: NvFp4MoELayer, T: int, device) -> torch.Tensor:
+    """One module-level workspace per device, grown on demand and shared by every layer."""
+    i_sh = layer.shared.inter if layer.shared is not None else 0
+    need = forward_workspace_size(T, layer.hidden, layer.routed.inter, i_sh, layer.num_experts, layer.top_k)
+    dev = torch.device(device)
+    cur = _POOL.get(dev)
+    if cur is None or cur.numel() < need:
+        cur = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        _POOL[dev] = cur
+    return cur
+
+
+def forward(layer: NvFp4MoELayer, x: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+            out: Optional[torch.Tensor] = None, return_aux: bool = False, stage_events=None):
+    """The whole layer on x [T, H] bf16 -> [T, H] bf16 (and, if asked, logits/ids/weights/counts).
+
+    ``stage_events``: optional sequence of 6 raw hipEvent_t handles (ints or None) recorded at the
+    stage boundaries (before S1, after S2, S3, S4, S5, S6) on the current stream.
+    """
+    _need(x, "x", torch.bfloat16, 2)
+    t = x.shape[0]
+    if workspace is None:
+        workspace = workspace_for(layer, t, x.device)
+    _need(workspace, "workspace", torch.uint8)
+    if out is None:
+        out = torch.empty_like(x)
+    aux = None
+    aux_t = None
+    if return_aux or stage_events is not None:
+        aux = L.ForwardAux()
+    if return_aux:
+        e, k = layer.num_experts, layer.top_k
+        aux_t = dict(logits=torch.empty(t, e, dtype=torch.float32, device=x.device),
+                     topk_ids=torch.empty(t, k, dtype=torch.int32, device=x.device),
+                     topk_w=torch.empty(t, k, dtype=torch.float32, device=x.device),
+                     expert_counts=torch.empty(e, dtype=torch.int32, device=x.device))
+        aux.logits, aux.topk_ids, aux.topk_w, aux.expert_counts = (v.data_ptr() for v in aux_t.values())
+    if stage_events is not None:
+        if len(stage_events) != L.NUM_STAGE_EVENTS:
+            raise ValueError(f"stage_events: {L.NUM_STAGE_EVENTS} entries expected")
+        arr = (ctypes.c_void_p * L.NUM_STAGE_EVENTS)(*stage_events)
+        aux.stage_events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    st = layer.c_struct()
+    L.check("moe_nvfp4_forward",
+            L.lib().moe_nvfp4_forward(ctypes.byref(st), _ptr(x), t, _ptr(out), _ptr(workspace), workspace.numel(),
+                                      ctypes.byref(aux) if aux is not None else None, _stream(x.device)))
+    return (out, aux_t) if return_aux else out
+
+
+def validate_forward(layer_struct: L.Layer, T: int, workspace_bytes: int, arch: Optional[str] = "gfx950") -> int:
+    """Pure-host validation status (needs no GPU when ``arch`` is given)."""
+    return int(L.lib().moe_validate_forward(ctypes.byref(layer_struct), T, workspace_bytes,
+                                            arch.encode() if arch is not None else None))
+
+
+# ----------------------------------------------------------------------------- weight preparation
+
+def gscale_from_quant_scale(q) -> np.ndarray:
+    """compressed-tensors quant scales -> dequant scales (host, fp32)."""
+    q = np.ascontiguousarray(np.asarray(q, dtype=np.float32))
+    d = np.empty_like(q)
+    L.check("moe_gscale_from_quant_scale",
+            L.lib().moe_gscale_from_quant_scale(q.ctypes.data_as(ctypes.c_void_p), d.ctypes.data_as(ctypes.c_void_p),
+                                                q.size))
+    return d
+
+
+def quantize(w: torch.Tensor, gscale: torch.Tensor, packed: Optional[torch.Tensor] = None,
+             scales: Optional[torch.Tensor] = None):
+    """On-device NVFP4 quantization of fp32 [..., rows, cols] with one dequant scale per leading index."""
+    _need(w, "w", torch.float32)
+    _need(gscale, "gscale", torch.float32)
+    rows, cols = w.shape[-2], w.shape[-1]
+    nt = int(np.prod(w.shape[:-2])) if w.dim() > 2 else 1
+    if gscale.numel() != nt:
+        raise ValueError("one global scale per tensor expected")
+    lead = tuple(w.shape[:-2])
+    if packed is None:
+        packed = torch.empty(*lead, rows, cols // 2, dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty(*lead, rows, cols // 16, dtype=torch.uint8, device=w.device)
+    _need(packed, "packed", torch.uint8)
+    _need(scales, "scales", torch.uint8)
+    L.check("moe_nvfp4_quantize", L.lib().moe_nvfp4_quantize(_ptr(w), nt, rows, cols, _ptr(gscale), _ptr(packed),
+                                                             _ptr(scales), _stream(w.device)))
+    return packed, scales

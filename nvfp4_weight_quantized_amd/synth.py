@@ -15,7 +15,9 @@ It produces:
     (the two conventions of the GLM-5.3-Flash-NVFP4 discussion page).
 
 Every stream comes from a torch.Generator seeded from (workload seed, stream
-name, index), so any single expert can be regenerated on its own.  The same
+name, index), so any single expert can be regenerated on its own.  The three
+H=4096, I=1536, E=320 workloads (decode, prefill, skewed) share one expert bank
+(same recipe, same weight seed) and differ in activations and router.  The same
 seed gives different numbers on 'cpu' and on 'cuda' (different generators):
 one test or bench run always draws everything on one device.
 """
@@ -48,10 +50,15 @@ class Workload:
     outlier_frac: float = 0.0
     outlier_mult: float = 20.0
     gscale_convention: str = "modelopt"   # or "compressed_tensors"
+    weight_seed: int = -1   # >= 0: expert weights drawn from this seed instead of ``seed``
 
     @property
     def slots(self) -> int:
         return self.T * self.k
+
+    @property
+    def wseed(self) -> int:
+        return self.weight_seed if self.weight_seed >= 0 else self.seed
 
 
 WORKLOADS = {
@@ -60,9 +67,9 @@ WORKLOADS = {
     "decode": Workload("decode", T=8, H=4096, I=1536, E=320, k=8, I_shared=1536,
                        sigma_router=0.02, sigma_w=0.02, seed=1001),
     "prefill": Workload("prefill", T=4096, H=4096, I=1536, E=320, k=8, I_shared=1536,
-                        sigma_router=1.0 / 64.0, sigma_w=0.02, seed=1002),
+                        sigma_router=1.0 / 64.0, sigma_w=0.02, seed=1002, weight_seed=1001),
     "skewed": Workload("skewed", T=2048, H=4096, I=1536, E=320, k=8, I_shared=1536,
-                       sigma_router=1.0 / 64.0, sigma_w=0.02, seed=1003, zipf_s=1.2),
+                       sigma_router=1.0 / 64.0, sigma_w=0.02, seed=1003, zipf_s=1.2, weight_seed=1001),
     "long_prefill": Workload("long_prefill", T=16384, H=6144, I=2048, E=256, k=8, I_shared=2048,
                              sigma_router=0.015, sigma_w=0.015, seed=1004,
                              outlier_frac=0.01, outlier_mult=20.0,
@@ -122,7 +129,7 @@ def expert_fp32(wl: Workload, bank: str, e: int, device="cpu"):
     ``bank`` is "routed" (I = wl.I) or "shared" (I = wl.I_shared, e = 0).
     """
     inter = wl.I if bank == "routed" else wl.I_shared
-    g = _gen(device, wl.seed, "w_" + bank, e)
+    g = _gen(device, wl.wseed, "w_" + bank, e)
     w13 = torch.randn(2 * inter, wl.H, generator=g, device=device, dtype=torch.float32) * wl.sigma_w
     w2 = torch.randn(wl.H, inter, generator=g, device=device, dtype=torch.float32) * wl.sigma_w
     if wl.outlier_frac > 0.0:

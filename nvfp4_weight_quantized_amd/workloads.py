@@ -1,0 +1,51 @@
+"""Synthetic NVFP4 MoE layers on the GPU: seeded fp32 weights quantized by the library's own
+on-device quantizer (moe_nvfp4_quantize), global scales in the workload's checkpoint convention
+and converted on load like a real checkpoint."""
+
+from __future__ import annotations
+
+import torch
+
+from . import ops, synth
+
+
+def _dequant_scales(amax, convention: str):
+    gs = synth.checkpoint_global_scales(amax, convention)
+    if convention == "compressed_tensors":
+        return ops.gscale_from_quant_scale(gs)
+    return gs
+
+
+def build_bank(wl: synth.Workload, bank: str, device="cuda") -> ops.NvFp4Experts:
+    """Quantize every expert of a bank ("routed": E experts of width I; "shared": 1 of width I_shared)."""
+    count = wl.E if bank == "routed" else 1
+    inter = wl.I if bank == "routed" else wl.I_shared
+    h = wl.H
+    dev = torch.device(device)
+    w13 = torch.empty(count, 2 * inter, h // 2, dtype=torch.uint8, device=dev)
+    w13_s = torch.empty(count, 2 * inter, h // 16, dtype=torch.uint8, device=dev)
+    w2 = torch.empty(count, h, inter // 2, dtype=torch.uint8, device=dev)
+    w2_s = torch.empty(count, h, inter // 16, dtype=torch.uint8, device=dev)
+    gs13 = torch.empty(count, 2, dtype=torch.float32)
+    gs2 = torch.empty(count, dtype=torch.float32)
+    for e in range(count):
+        f13, f2 = synth.expert_fp32(wl, bank, e, dev)
+        d = _dequant_scales(synth.expert_amax(f13, f2), wl.gscale_convention)
+        d_dev = torch.from_numpy(d).to(dev)
+        ops.quantize(f13.view(2, inter, h), d_dev[0:2], packed=w13[e].view(2, inter, h // 2),
+                     scales=w13_s[e].view(2, inter, h // 16))
+        ops.quantize(f2, d_dev[2:3], packed=w2[e], scales=w2_s[e])
+        gs13[e] = torch.from_numpy(d[0:2])
+        gs2[e] = float(d[2])
+        del f13, f2
+    return ops.NvFp4Experts(w13, w13_s, gs13.to(dev), w2, w2_s, gs2.to(dev))
+
+
+def build_layer(wl: synth.Workload, device="cuda") -> ops.NvFp4MoELayer:
+    bias = synth.router_bias(wl)
+    return ops.NvFp4MoELayer(
+        w_router=synth.router_weight(wl, device).contiguous(),
+        router_bias=torch.from_numpy(bias).to(device) if bias is not None else None,
+        routed=build_bank(wl, "routed", device),
+        shared=build_bank(wl, "shared", device) if wl.I_shared > 0 else None,
+        top_k=wl.k)

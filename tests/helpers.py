@@ -39,20 +39,37 @@ def oracle_expert(wl, bank: str, e: int, device="cpu") -> omoe.ExpertWeights:
                               np.array([d[0], d[1]], np.float32), pd, sd, float(d[2]))
 
 
+_EXPERT_CACHE = {}
+
+
 class LazyBank:
-    """Sequence of oracle experts quantized on first access (for layers too big to hold)."""
+    """Sequence of oracle experts quantized on first access (for layers too big to hold).
+
+    Experts are cached per (weight seed, bank, index, device) across tests, since several
+    workloads share one bank.  ``prefetch`` quantizes a set of experts on a thread pool.
+    """
 
     def __init__(self, wl, bank: str, count: int, device="cpu"):
         self.wl, self.bank, self.count, self.device = wl, bank, count, device
-        self.cache = {}
+
+    def _key(self, e):
+        return (self.wl.wseed, self.wl.H, self.wl.I, self.bank, int(e), str(self.device))
 
     def __len__(self):
         return self.count
 
     def __getitem__(self, e):
-        if e not in self.cache:
-            self.cache[e] = oracle_expert(self.wl, self.bank, e, self.device)
-        return self.cache[e]
+        key = self._key(e)
+        if key not in _EXPERT_CACHE:
+            _EXPERT_CACHE[key] = oracle_expert(self.wl, self.bank, int(e), self.device)
+        return _EXPERT_CACHE[key]
+
+    def prefetch(self, experts, threads=8):
+        from concurrent.futures import ThreadPoolExecutor
+        todo = sorted({int(e) for e in experts if self._key(e) not in _EXPERT_CACHE})
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            for e, ew in zip(todo, ex.map(lambda i: oracle_expert(self.wl, self.bank, i, self.device), todo)):
+                _EXPERT_CACHE[self._key(e)] = ew
 
 
 def oracle_layer(wl, device="cpu") -> omoe.Layer:
@@ -70,7 +87,7 @@ def stack_bank(bank) -> omoe.ArrayBank:
                           np.array([i.w2_gscale for i in items], np.float32))
 
 
-def random_layer(rng, H, I, E, k, shared=True, sigma=0.05, bias=False) -> omoe.Layer:
+def random_layer(rng, H, I, E, k, shared=True, sigma=0.05, bias=False, i_shared=None) -> omoe.Layer:
     """A small random layer quantized by the oracle (for brute-force comparisons)."""
     def one(i_dim):
         w13 = rng.normal(0, sigma, (2 * i_dim, H)).astype(np.float32)
@@ -84,7 +101,7 @@ def random_layer(rng, H, I, E, k, shared=True, sigma=0.05, bias=False) -> omoe.L
     wr = torch.from_numpy(rng.normal(0, 0.3, (E, H)).astype(np.float32)).to(torch.bfloat16)
     b = rng.normal(0, 0.5, E).astype(np.float32) if bias else None
     return omoe.Layer(w_router=bf16_bits(wr), router_bias=b, routed=[one(I) for _ in range(E)],
-                      shared=[one(I)] if shared else None, top_k=k)
+                      shared=[one(i_shared or I)] if shared else None, top_k=k)
 
 
 def random_x(rng, T, H) -> np.ndarray:

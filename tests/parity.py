@@ -1,0 +1,107 @@
+"""Parity helpers shared by the GPU tests: oracle layers -> GPU tensors, and the tolerance checks.
+
+Tolerances (fixed by the layer's specification of "matching"):
+  * router logits: |gpu - exact| <= H * 2^-24 * sum_h |x_h * w_h| + 2^-24 * |logit| (fp32 recursive
+    summation bound plus the rounding of the bias add);
+  * top-k ids: bit-exact against the oracle's selection applied to the GPU's own fp32 logits;
+    weights within 1e-5;
+  * permutation, counts, offsets: bit-exact;
+  * layer / GEMM outputs: rel-L2 <= 5e-3 and max-abs <= 2e-2 * max|ref|.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import helpers
+from nvfp4_weight_quantized_amd import ops
+from oracle import moe as omoe
+
+REL_L2 = 5e-3
+MAX_ABS_FRAC = 2e-2
+
+
+def to_gpu_bank(bank, device="cuda") -> ops.NvFp4Experts:
+    items = [bank[e] for e in range(len(bank))]
+
+    def st(name, dtype):
+        return torch.from_numpy(np.ascontiguousarray(np.stack([getattr(i, name) for i in items]))).to(device, dtype)
+
+    return ops.NvFp4Experts(st("w13", torch.uint8), st("w13_scale", torch.uint8),
+                            torch.tensor(np.stack([i.w13_gscale for i in items]), dtype=torch.float32, device=device),
+                            st("w2", torch.uint8), st("w2_scale", torch.uint8),
+                            torch.tensor([i.w2_gscale for i in items], dtype=torch.float32, device=device))
+
+
+def bits_to_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def to_gpu_layer(layer: omoe.Layer, device="cuda") -> ops.NvFp4MoELayer:
+    bias = None if layer.router_bias is None else torch.from_numpy(layer.router_bias).to(device)
+    return ops.NvFp4MoELayer(bits_to_bf16(layer.w_router, device), bias, to_gpu_bank(layer.routed, device),
+                             to_gpu_bank(layer.shared, device) if layer.shared is not None else None, layer.top_k)
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def errors(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
+    mx = np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-300)
+    return rel, mx
+
+
+def assert_close(got, ref, what=""):
+    rel, mx = errors(got, ref)
+    assert rel <= REL_L2 and mx <= MAX_ABS_FRAC, f"{what}: rel-L2 {rel:.3e} (<= {REL_L2}), max-abs/max|ref| {mx:.3e}"
+    return rel, mx
+
+
+def logit_bound(x_bits, wr_bits, bias=None):
+    x = np.abs(omoe.bf16_to_float(x_bits))
+    w = np.abs(omoe.bf16_to_float(wr_bits))
+    h = x.shape[1]
+    b = h * 2.0 ** -24 * (x @ w.T) + 1e-30
+    if bias is not None:
+        exact = omoe.router_logits(x_bits, wr_bits, bias)
+        b = b + 2.0 ** -24 * np.abs(exact)
+    return b
+
+
+def check_route(logits_gpu, ids_gpu, w_gpu, x_bits, wr_bits, bias, k):
+    """GEMM logits within the fp32 bound; selection bit-exact on the GPU's logits; weights within 1e-5."""
+    lg = logits_gpu.cpu().numpy().astype(np.float64)
+    exact = omoe.router_logits(x_bits, wr_bits, bias)
+    bound = logit_bound(x_bits, wr_bits, bias)
+    assert np.all(np.abs(lg - exact) <= bound), f"logits off by {np.abs(lg - exact).max():.3e}"
+    ids_ref, w_ref = omoe.topk(lg, k)
+    ids = ids_gpu.cpu().numpy()
+    assert np.array_equal(ids, ids_ref)
+    np.testing.assert_allclose(w_gpu.cpu().numpy(), w_ref, rtol=0, atol=1e-5)
+    return lg
+
+
+def ambiguous(logits_exact, k, margin=1e-3):
+    """Tokens whose k-th and (k+1)-th exact logits are closer than ``margin``."""
+    s = -np.sort(-logits_exact, axis=1)
+    if s.shape[1] <= k:
+        return np.zeros(s.shape[0], bool)
+    return (s[:, k - 1] - s[:, k]) < margin
+
+
+def reference_for_selection(x_bits, layer, ids_gpu):
+    """Oracle forward where tokens with an ambiguous k-th choice take the GPU's selection."""
+    res = omoe.forward(x_bits, layer)
+    amb = ambiguous(res["logits"], layer.top_k)
+    ids = ids_gpu.copy()
+    mismatch = np.any(ids != res["ids"], axis=1)
+    assert not np.any(mismatch & ~amb), f"unambiguous tokens routed differently: {np.where(mismatch & ~amb)[0][:10]}"
+    if np.any(mismatch):
+        route = np.where(mismatch[:, None], ids, res["ids"])
+        res = omoe.forward(x_bits, layer, route=route)
+    return res

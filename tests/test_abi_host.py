@@ -1,0 +1,101 @@
+"""The C-ABI library loads, exports every declared symbol, and its host-only logic is right (CPU only)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import nvfp4_weight_quantized_amd as moe
+from nvfp4_weight_quantized_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_nvfp4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 11
+    lib = L.lib()
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(L.SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings():
+    assert L.status_string(0) == "MOE_OK"
+    assert "WORKSPACE" in L.status_string(3)
+    assert "gfx950" in L.status_string(2)
+
+
+def test_gscale_conversion_worked_example_and_errors():
+    d = moe.gscale_from_quant_scale(np.array([21504.0], np.float32))
+    assert float(d[0]) == 4.650297705666162e-05
+    q = np.exp2(np.random.default_rng(0).uniform(-10, 14, 1000)).astype(np.float32)
+    assert np.array_equal(moe.gscale_from_quant_scale(q), (np.float32(1) / q).astype(np.float32))
+    for bad in (0.0, np.inf, np.nan):
+        with pytest.raises(moe.MoeError):
+            moe.gscale_from_quant_scale(np.array([1.0, bad], np.float32))
+
+
+def _fake_bank(e, h, i, base=0x1000):
+    return L.Experts(e, h, i, base, base + 1, base + 2, base + 3, base + 4, base + 5)
+
+
+def _fake_layer(h=4096, e=320, k=8, i=1536, i_sh=1536, shared=True):
+    return L.Layer(h, e, k, 0x2000, None, _fake_bank(e, h, i), _fake_bank(1, h, i_sh) if shared else L.Experts())
+
+
+def test_validate_forward_host_only():
+    lay = _fake_layer()
+    need = moe.forward_workspace_size(8, 4096, 1536, 1536, 320, 8)
+    assert moe.validate_forward(lay, 8, need) == L.MOE_OK
+    assert moe.validate_forward(lay, 8, need - 1) == L.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert moe.validate_forward(lay, 8, need, arch="gfx942") == L.MOE_ERR_UNSUPPORTED_DEVICE
+    assert moe.validate_forward(lay, 0, 0) == L.MOE_OK
+    assert moe.validate_forward(lay, -1, need) == L.MOE_ERR_INVALID_ARGUMENT
+    # k out of range, E too large, H/I not multiples of 128, bank/layer mismatch, null pointers
+    for bad in (_fake_layer(k=0), _fake_layer(k=321), _fake_layer(k=65, e=100), _fake_layer(e=1025, k=8),
+                _fake_layer(h=4000), _fake_layer(i=1500), _fake_layer(i_sh=100)):
+        assert moe.validate_forward(bad, 8, 1 << 40) == L.MOE_ERR_INVALID_ARGUMENT
+    lay2 = _fake_layer()
+    lay2.routed.w2_scale = None
+    assert moe.validate_forward(lay2, 8, 1 << 40) == L.MOE_ERR_INVALID_ARGUMENT
+    lay3 = _fake_layer()
+    lay3.w_router = None
+    assert moe.validate_forward(lay3, 8, 1 << 40) == L.MOE_ERR_INVALID_ARGUMENT
+    lay4 = _fake_layer()
+    lay4.shared.hidden = 2048
+    assert moe.validate_forward(lay4, 8, 1 << 40) == L.MOE_ERR_INVALID_ARGUMENT
+    # no shared expert is valid
+    lay5 = _fake_layer(shared=False)
+    assert moe.validate_forward(lay5, 8, moe.forward_workspace_size(8, 4096, 1536, 0, 320, 8)) == L.MOE_OK
+
+
+def test_workspace_size_covers_intermediates():
+    t, h, i, e, k = 4096, 4096, 1536, 320, 8
+    s = t * k
+    need = moe.forward_workspace_size(t, h, i, i, e, k)
+    # h rows (S+T) x I bf16 and y rows (S+T) x H bf16 dominate
+    assert need >= (s + t) * i * 2 + (s + t) * h * 2 + t * e * 4
+    assert need < 1.01 * ((s + t) * i * 2 + (s + t) * h * 2) + (64 << 20)
+    assert moe.forward_workspace_size(0, h, i, i, e, k) > 0
+    assert L.lib().moe_permute_workspace_size(8, 8, 320) == 0
+    assert L.lib().moe_permute_workspace_size(4096, 8, 320) >= (4096 * 8 // 2048) * 320 * 4
+
+
+def test_product_path_has_no_oracle_dependency():
+    """The package never imports the oracle (the oracle is test infrastructure only)."""
+    pkg = os.path.join(ROOT, "nvfp4_weight_quantized_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f

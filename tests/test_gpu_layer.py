@@ -1,0 +1,193 @@
+"""GPU parity of the whole layer (moe_nvfp4_forward through the C ABI) against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import helpers
+import parity
+from nvfp4_weight_quantized_amd import _lib as L
+from nvfp4_weight_quantized_amd import build_bank, build_layer, ops, synth
+from oracle import moe as omoe
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# ----------------------------------------------------------------------------- small layers
+
+SMALL = [
+    # T, H, I, E, k, shared, bias, I_shared
+    (5, 256, 128, 8, 2, True, False, None),
+    (64, 512, 256, 16, 4, True, True, None),
+    (300, 512, 256, 16, 4, True, False, None),
+    (37, 384, 256, 12, 3, False, True, None),
+    (50, 256, 128, 6, 2, True, False, 256),
+    (1, 256, 128, 4, 4, True, False, None),
+    (129, 256, 128, 64, 8, True, True, None),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"T{c[0]}_H{c[1]}_I{c[2]}_E{c[3]}_k{c[4]}" for c in SMALL])
+def test_small_layer_end_to_end(case):
+    T, H, I, E, k, shared, bias, i_sh = case
+    rng = np.random.default_rng(sum(case[:5]))
+    layer = helpers.random_layer(rng, H, I, E, k, shared=shared, bias=bias, i_shared=i_sh)
+    x = helpers.random_x(rng, T, H)
+    glayer = parity.to_gpu_layer(layer)
+    xg = parity.bits_to_bf16(x)
+    out, aux = ops.forward(glayer, xg, return_aux=True)
+    parity.check_route(aux["logits"], aux["topk_ids"], aux["topk_w"], x, layer.w_router, layer.router_bias, k)
+    ids = aux["topk_ids"].cpu().numpy()
+    res = parity.reference_for_selection(x, layer, ids)
+    assert np.array_equal(aux["expert_counts"].cpu().numpy(), omoe.permute(ids, E)[0])
+    parity.assert_close(parity.f64(out), res["out"], "layer")
+    out2 = ops.forward(glayer, xg)
+    assert torch.equal(out, out2), "two runs differ"
+
+
+def test_zero_tokens_is_a_no_op():
+    rng = np.random.default_rng(1)
+    glayer = parity.to_gpu_layer(helpers.random_layer(rng, 256, 128, 4, 2))
+    out = ops.forward(glayer, torch.zeros(0, 256, dtype=torch.bfloat16, device=DEV))
+    assert out.shape == (0, 256)
+
+
+# ----------------------------------------------------------------------------- tiny workload
+
+def _oracle_bank_equal(gbank, obank, experts):
+    for e in experts:
+        ow = obank[e]
+        assert np.array_equal(gbank.w13[e].cpu().numpy(), ow.w13), e
+        assert np.array_equal(gbank.w13_scale[e].cpu().numpy(), ow.w13_scale), e
+        assert np.array_equal(gbank.w2[e].cpu().numpy(), ow.w2), e
+        assert np.array_equal(gbank.w2_scale[e].cpu().numpy(), ow.w2_scale), e
+        assert np.array_equal(gbank.w13_gscale[e].cpu().numpy(), ow.w13_gscale), e
+        assert float(gbank.w2_gscale[e]) == ow.w2_gscale, e
+
+
+def test_tiny_workload_end_to_end_and_staged():
+    wl = synth.WORKLOADS["tiny"]
+    glayer = build_layer(wl, DEV)
+    olayer = helpers.oracle_layer(wl, DEV)
+    _oracle_bank_equal(glayer.routed, olayer.routed, range(wl.E))
+    _oracle_bank_equal(glayer.shared, olayer.shared, [0])
+    x = synth.activations(wl, DEV)
+    xb = helpers.bf16_bits(x)
+    out, aux = ops.forward(glayer, x, return_aux=True)
+    parity.check_route(aux["logits"], aux["topk_ids"], aux["topk_w"], xb, olayer.w_router, None, wl.k)
+    res = parity.reference_for_selection(xb, olayer, aux["topk_ids"].cpu().numpy())
+    parity.assert_close(parity.f64(out), res["out"], "forward")
+    # the same layer through the per-stage entry points
+    logits, ids, w = ops.route(x, glayer.w_router, None, wl.k)
+    counts, offsets, sorted_slot, slot_to_row = ops.permute(ids, wl.E)
+    S = wl.T * wl.k
+    h = ops.grouped_gemm(L.MOE_GEMM_GATE_UP, glayer.routed, x, offsets, S, sorted_slot, wl.k)
+    y = ops.grouped_gemm(L.MOE_GEMM_DOWN, glayer.routed, h, offsets, S)
+    one = torch.tensor([0, wl.T], dtype=torch.int32, device=DEV)
+    hs = ops.grouped_gemm(L.MOE_GEMM_GATE_UP, glayer.shared, x, one, wl.T)
+    ys = ops.grouped_gemm(L.MOE_GEMM_DOWN, glayer.shared, hs, one, wl.T)
+    staged = ops.combine(y, slot_to_row, w, ys)
+    parity.assert_close(parity.f64(staged), res["out"], "staged")
+    assert torch.equal(ids, aux["topk_ids"])
+
+
+def test_loader_ignores_activation_scales_and_converts_reciprocal_scales():
+    """A checkpoint dict with input_scale entries (even 0) gives the same nonzero output; a
+    compressed-tensors checkpoint (quant scales) is inverted on load."""
+    wl = synth.WORKLOADS["tiny"]
+    glayer = build_layer(wl, DEV)
+    x = synth.activations(wl, DEV)
+    ref = ops.forward(glayer, x)
+    tensors = {"router.weight": glayer.w_router}
+    for pre, b in (("experts.", glayer.routed), ("shared_expert.", glayer.shared)):
+        tensors.update({pre + "w13": b.w13, pre + "w13_scale": b.w13_scale, pre + "w13_global_scale": b.w13_gscale,
+                        pre + "w2": b.w2, pre + "w2_scale": b.w2_scale, pre + "w2_global_scale": b.w2_gscale,
+                        pre + "w13_input_scale": torch.zeros(wl.E if pre == "experts." else 1, 2),
+                        pre + "w2_input_scale": torch.zeros(wl.E if pre == "experts." else 1)})
+    lay = ops.NvFp4MoELayer.from_tensors(tensors, wl.k, "modelopt", DEV)
+    out = ops.forward(lay, x)
+    assert torch.equal(out, ref)
+    assert bool((out.float().abs().amax(dim=1) > 0).all())
+    ct = dict(tensors)
+    for pre, b in (("experts.", glayer.routed), ("shared_expert.", glayer.shared)):
+        ct[pre + "w13_global_scale"] = torch.from_numpy(np.float32(1) / b.w13_gscale.cpu().numpy())
+        ct[pre + "w2_global_scale"] = torch.from_numpy(np.float32(1) / b.w2_gscale.cpu().numpy())
+    lay_ct = ops.NvFp4MoELayer.from_tensors(ct, wl.k, "compressed_tensors", DEV)
+    want = (np.float32(1) / (np.float32(1) / glayer.routed.w13_gscale.cpu().numpy())).astype(np.float32)
+    assert np.array_equal(lay_ct.routed.w13_gscale.cpu().numpy(), want)
+
+
+# ----------------------------------------------------------------------------- full-size workloads
+
+_BANKS = {}
+
+
+def _gpu_layer(wl):
+    key = (wl.wseed, wl.H, wl.I, wl.E)
+    if key not in _BANKS:
+        _BANKS.clear()
+        torch.cuda.empty_cache()
+        _BANKS[key] = (build_bank(wl, "routed", DEV), build_bank(wl, "shared", DEV))
+    routed, shared = _BANKS[key]
+    bias = synth.router_bias(wl)
+    return ops.NvFp4MoELayer(synth.router_weight(wl, DEV).contiguous(),
+                             torch.from_numpy(bias).to(DEV) if bias is not None else None, routed, shared, wl.k)
+
+
+SAMPLE_TOKENS = {"decode": 2, "prefill": 1, "skewed": 1, "long_prefill": 1}
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["decode", "prefill", "skewed", "long_prefill"])
+def test_full_size_workload(name):
+    wl = synth.WORKLOADS[name]
+    _say(f"[full-size {name}] building layer T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.k}")
+    glayer = _gpu_layer(wl)
+    x = synth.activations(wl, DEV)
+    out, aux = ops.forward(glayer, x, return_aux=True)
+    torch.cuda.synchronize()
+    _say(f"[full-size {name}] forward done")
+    xb = helpers.bf16_bits(x)
+    wrb = helpers.bf16_bits(glayer.w_router)
+    bias = synth.router_bias(wl)
+    lg = aux["logits"].cpu().numpy().astype(np.float64)
+    ids = aux["topk_ids"].cpu().numpy()
+    # selection: bit-exact for every token on the GPU's logits
+    ids_ref, w_ref = omoe.topk(lg, wl.k)
+    assert np.array_equal(ids, ids_ref)
+    np.testing.assert_allclose(aux["topk_w"].cpu().numpy(), w_ref, rtol=0, atol=1e-5)
+    # router GEMM: a token sample within the fp32 bound
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([rng.choice(wl.T, min(wl.T, 48), replace=False), [0, wl.T - 1]]))
+    exact = omoe.router_logits(xb[rows], wrb, bias)
+    assert np.all(np.abs(lg[rows] - exact) <= parity.logit_bound(xb[rows], wrb, bias))
+    # permutation: bit-exact for every slot
+    counts, offsets, sorted_slot, slot_to_row = ops.permute(aux["topk_ids"], wl.E)
+    c, o, s, r = omoe.permute(ids, wl.E)
+    assert np.array_equal(aux["expert_counts"].cpu().numpy(), c)
+    assert np.array_equal(counts.cpu().numpy(), c) and np.array_equal(offsets.cpu().numpy(), o)
+    assert np.array_equal(sorted_slot.cpu().numpy(), s) and np.array_equal(slot_to_row.cpu().numpy(), r)
+    _say(f"[full-size {name}] route/permute exact; {int((c > 0).sum())} experts used, max count {int(c.max())}")
+
+    olayer = helpers.oracle_layer(wl, DEV)
+    # gate/up rows of the most loaded expert (all of its tiles), through the per-stage entry point
+    e_max = int(np.argmax(c))
+    olayer.routed.prefetch([e_max])
+    h = ops.grouped_gemm(L.MOE_GEMM_GATE_UP, glayer.routed, x, offsets, wl.T * wl.k, sorted_slot, wl.k)
+    r0, r1 = int(o[e_max]), int(o[e_max + 1])
+    a_rows = omoe.bf16_to_float(xb[s[r0:r1] // wl.k])
+    h_ref = omoe.gate_up(a_rows, olayer.routed[e_max])
+    parity.assert_close(parity.f64(h[r0:r1]), h_ref, f"gate/up rows of expert {e_max}")
+    _oracle_bank_equal(glayer.routed, olayer.routed, [e_max])
+    # whole-layer output on sampled tokens
+    tokens = np.unique(np.concatenate([[wl.T - 1], s[r0:r0 + 1] // wl.k]))[:SAMPLE_TOKENS[name]]
+    olayer.routed.prefetch(np.unique(ids[tokens]))
+    res = parity.reference_for_selection(xb[tokens], olayer, ids[tokens])
+    rel, mx = parity.assert_close(parity.f64(out[torch.from_numpy(tokens).to(DEV)]), res["out"], "sampled tokens")
+    _oracle_bank_equal(glayer.routed, olayer.routed, np.unique(ids[tokens]))
+    _say(f"[full-size {name}] tokens {tokens.tolist()}: rel-L2 {rel:.2e}, max-abs {mx:.2e}")
