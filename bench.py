@@ -148,6 +148,20 @@ def main():
     ids = aux["topk_ids"].cpu().numpy()
     touched = int((counts > 0).sum())
 
+    # plain device-to-device copy of 1 GiB: the HBM bandwidth a streaming kernel reaches on this
+    # box, and the known-size kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * src.numel() / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+
     for i in range(warmup):
         ops.forward(layers[i % copies], x, ws, out)
     torch.cuda.synchronize()
@@ -167,6 +181,14 @@ def main():
     total_ms = start.elapsed_time(end)
     gate_up_ms = float(np.mean([hip.elapsed_ms(e[0], e[1]) for e in evs]))
     down_ms = float(np.mean([hip.elapsed_ms(e[1], e[2]) for e in evs]))
+    # per-stage breakdown, outside the timed region: all six stage boundaries
+    bevs = [[hip.create() for _ in range(6)] for _ in range(min(steps, 50))]
+    torch.cuda.synchronize()
+    for i, e in enumerate(bevs):
+        ops.forward(layers[i % copies], x, ws, out, stage_events=e)
+    torch.cuda.synchronize()
+    names = ["router", "topk_permute", "gate_up", "down", "combine"]
+    stages_us = {n: float(np.mean([hip.elapsed_ms(e[i], e[i + 1]) for e in bevs])) * 1e3 for i, n in enumerate(names)}
     hip.destroy_all()
 
     T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
@@ -206,7 +228,9 @@ def main():
                                f"NVFP4 W4A16", "tokens": T, "hidden": H, "inter": I, "experts": E, "top_k": k,
                    "weight_copies": copies, "experts_touched": touched},
         "roofline": roof,
-        "stages_us": {"gate_up": gate_up_ms * 1e3, "down": down_ms * 1e3},
+        "stages_us": stages_us,
+        "measured_copy_GBs": copy_gbs,
+        "timed_stages_us": {"gate_up": gate_up_ms * 1e3, "down": down_ms * 1e3},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -161,7 +161,7 @@ moe_status_t moe_combine(const uint16_t* y_rows, const int32_t* slot_to_row, con
  * Optional extra outputs of moe_nvfp4_forward (each may be NULL): the router logits [T][E],
  * the selection topk_ids [T][k], topk_w [T][k], and expert_counts [E] (device pointers).
  * stage_events (host array of MOE_NUM_STAGE_EVENTS hipEvent_t handles, or NULL): when given,
- * event i is recorded on the stream at stage boundary i -- 0 before S1, 1 after S2, 2 after S3,
+ * event i is recorded on the stream at stage boundary i -- 0 before S1, 1 after S1, 2 after S2+S3,
  * 3 after S4, 4 after S5, 5 after S6 -- so callers can time each stage; NULL entries are skipped.
  * The events are created and owned by the caller. */
 #define MOE_NUM_STAGE_EVENTS 6

@@ -225,9 +225,16 @@ moe_status_t moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x
 
   moe_status_t st = mark(0);
   if (st) return st;
-  st = moe::launch_route(x, layer->w_router, layer->router_bias, T, H, E, k, false, logits, ids, w, stream);
+  st = moe::launch_router_logits(x, layer->w_router, layer->router_bias, T, H, E, logits, stream);
   if (st || (st = mark(1))) return st;
-  st = moe::launch_permute(ids, T, k, E, counts, offsets, sorted_slot, slot_to_row, block_hist, stream);
+  if (S <= moe::kPermuteChunk) {
+    // few tokens: top-k and permutation together in one workgroup
+    st = moe::launch_topk_permute_small(logits, T, E, k, ids, w, counts, offsets, sorted_slot, slot_to_row, stream);
+  } else {
+    st = moe::launch_route(nullptr, nullptr, nullptr, T, H, E, k, true, logits, ids, w, stream);
+    if (st) return st;
+    st = moe::launch_permute(ids, T, k, E, counts, offsets, sorted_slot, slot_to_row, block_hist, stream);
+  }
   if (st || (st = mark(2))) return st;
 
   // S4: routed rows gathered through sorted_slot; the shared expert rides in the same launch when

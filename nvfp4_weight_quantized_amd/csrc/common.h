@@ -42,7 +42,14 @@ moe_status_t launch_permute(const int32_t* ids, int32_t T, int32_t k, int32_t E,
                             int32_t* offsets, int32_t* sorted_slot, int32_t* slot_to_row,
                             int32_t* block_hist, hipStream_t stream);
 
+// S2 + S3 in one workgroup for T*k <= kPermuteChunk.
+moe_status_t launch_topk_permute_small(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* ids, float* w,
+                                       int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                                       int32_t* slot_to_row, hipStream_t stream);
+
 // Route -------------------------------------------------------------------------------------
+moe_status_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, const float* bias, int32_t T,
+                                  int32_t H, int32_t E, float* logits, hipStream_t stream);
 moe_status_t launch_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int32_t T,
                           int32_t H, int32_t E, int32_t k, bool logits_given, float* logits,
                           int32_t* ids, float* w, hipStream_t stream);

@@ -7,110 +7,54 @@
 // expert, computed from per-block and per-wave histograms and in-wave ballots -- never from the
 // order in which atomics land.
 //
-// Small S (one workgroup): one launch does histogram, scan and scatter.  Large S: per-block
-// histograms -> one scan workgroup -> per-block stable scatter.
+// Small S (one workgroup): one launch does histogram, scan and scatter; for few tokens the top-k
+// selection (S2) runs in the same launch.  Large S: per-block histograms -> one scan workgroup ->
+// per-block stable scatter.
 // Source: the "Permute-Experts-Unpermute" stage of the modular fused MoE ("vLLM on the NVIDIA DGX
 // Spark: A Complete Technical Guide", section 7.1) and the token dispatch of the fused b12x MoE
 // (section 4).
-#include "common.h"
+#include "device_util.h"
 
 namespace moe {
 namespace {
-
-constexpr int kWaves = kPermuteThreads / kWave;          // 8
-constexpr int kSlotsPerWave = kPermuteChunk / kWaves;    // 256
-constexpr int kMaxE = 1024;
-
-// Exclusive scan of cnt[0..E) into out[0..E) by wave 0, returning the total (valid in wave 0).
-__device__ int wave0_exclusive_scan(const int* cnt, int* out, int E) {
-  const int lane = threadIdx.x & 63;
-  int carry = 0;
-  for (int base = 0; base < E; base += 64) {
-    const int e = base + lane;
-    const int v = (e < E) ? cnt[e] : 0;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(incl, off);
-      if (lane >= off) incl += o;
-    }
-    if (e < E) out[e] = carry + incl - v;
-    carry += __shfl(incl, 63);
-  }
-  return carry;
-}
-
-// Stable scatter of one wave's slots [s_begin, s_end) using the per-wave running bases in `base`.
-__device__ void wave_stable_scatter(const int32_t* __restrict__ ids, int s_begin, int s_end, int* base,
-                                    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_to_row) {
-  const int lane = threadIdx.x & 63;
-  const uint64_t below = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
-  for (int s0 = s_begin; s0 < s_end; s0 += 64) {
-    const int s = s0 + lane;
-    const bool valid = s < s_end;
-    const int e = valid ? ids[s] : -1;
-    uint64_t rem = __ballot(valid);
-    uint64_t peers = 0;
-    while (rem) {
-      const int leader = __ffsll((unsigned long long)rem) - 1;
-      const int le = __shfl(e, leader);
-      const uint64_t m = __ballot(valid && e == le);
-      if (valid && e == le) peers = m;
-      rem &= ~m;
-    }
-    if (valid) {
-      const int rank = __popcll(peers & below);
-      const int b = base[e];
-      const int pos = b + rank;
-      sorted_slot[pos] = s;
-      slot_to_row[s] = pos;
-      if (rank == 0) base[e] = b + __popcll(peers);
-    }
-  }
-}
 
 // One workgroup does everything (S <= kPermuteChunk).
 __global__ __launch_bounds__(kPermuteThreads) void permute_single_kernel(
     const int32_t* __restrict__ ids, int S, int E, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_to_row) {
-  __shared__ int wave_hist[kWaves][kMaxE];
-  __shared__ int offs[kMaxE];
-  const int tid = threadIdx.x, wave = tid >> 6;
-  for (int i = tid; i < kWaves * kMaxE; i += kPermuteThreads) (&wave_hist[0][0])[i] = 0;
-  __syncthreads();
-  const int s_begin = wave * kSlotsPerWave;
-  const int s_end = min(S, s_begin + kSlotsPerWave);
-  for (int s = s_begin + (tid & 63); s < s_end; s += 64) atomicAdd(&wave_hist[wave][ids[s]], 1);
-  __syncthreads();
-  for (int e = tid; e < E; e += kPermuteThreads) {
-    int c = 0;
-    for (int w = 0; w < kWaves; ++w) c += wave_hist[w][e];
-    counts[e] = c;
-    offs[e] = c;  // scanned below
-  }
-  __syncthreads();
-  if (wave == 0) {
-    const int total = wave0_exclusive_scan(offs, offs, E);
-    if ((tid & 63) == 0) offsets[E] = total;
-  }
-  __syncthreads();
-  for (int e = tid; e < E; e += kPermuteThreads) {
-    offsets[e] = offs[e];
-    int run = offs[e];
-    for (int w = 0; w < kWaves; ++w) {
-      const int c = wave_hist[w][e];
-      wave_hist[w][e] = run;
-      run += c;
+  __shared__ int wave_hist[kPermWaves][kPermMaxE];
+  __shared__ int offs[kPermMaxE];
+  permute_block(ids, S, E, counts, offsets, sorted_slot, slot_to_row, wave_hist, offs);
+}
+
+// S2 + S3 for few tokens in one workgroup: each wave selects the top-k of its tokens, then the
+// block permutes the selection from LDS.
+__global__ __launch_bounds__(kPermuteThreads) void topk_permute_small_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
+    int32_t* __restrict__ slot_to_row) {
+  __shared__ int wave_hist[kPermWaves][kPermMaxE];
+  __shared__ int offs[kPermMaxE];
+  __shared__ int ids_s[kPermuteChunk];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int t = wave; t < T; t += kPermWaves) {
+    int id;
+    float wt;
+    topk_token(logits + (size_t)t * E, E, k, &id, &wt);
+    if (lane < k) {
+      ids[(size_t)t * k + lane] = id;
+      w[(size_t)t * k + lane] = wt;
+      ids_s[t * k + lane] = id;
     }
   }
   __syncthreads();
-  if (s_begin < s_end) wave_stable_scatter(ids, s_begin, s_end, wave_hist[wave], sorted_slot, slot_to_row);
+  permute_block(ids_s, T * k, E, counts, offsets, sorted_slot, slot_to_row, wave_hist, offs);
 }
 
 // Multi-block path, step 1: per-block histograms block_hist[b][e].
 __global__ __launch_bounds__(kPermuteThreads) void permute_hist_kernel(const int32_t* __restrict__ ids, int S,
                                                                        int E, int32_t* __restrict__ block_hist) {
-  __shared__ int hist[kMaxE];
+  __shared__ int hist[kPermMaxE];
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += kPermuteThreads) hist[e] = 0;
   __syncthreads();
@@ -125,7 +69,7 @@ __global__ __launch_bounds__(kPermuteThreads) void permute_hist_kernel(const int
 __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict__ block_hist, int nb, int E,
                                                             int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ offsets) {
-  __shared__ int offs[kMaxE];
+  __shared__ int offs[kPermMaxE];
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += 1024) {
     int run = 0;
@@ -139,7 +83,7 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict_
   }
   __syncthreads();
   if (tid < 64) {
-    const int total = wave0_exclusive_scan(offs, offs, E);
+    const int total = wave_exclusive_scan(offs, offs, E);
     if (tid == 0) offsets[E] = total;
   }
   __syncthreads();
@@ -153,19 +97,19 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict_
 __global__ __launch_bounds__(kPermuteThreads) void permute_scatter_kernel(
     const int32_t* __restrict__ ids, int S, int E, const int32_t* __restrict__ block_base,
     int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_to_row) {
-  __shared__ int wave_hist[kWaves][kMaxE];
+  __shared__ int wave_hist[kPermWaves][kPermMaxE];
   const int tid = threadIdx.x, wave = tid >> 6;
-  for (int w = 0; w < kWaves; ++w)
+  for (int w = 0; w < kPermWaves; ++w)
     for (int e = tid; e < E; e += kPermuteThreads) wave_hist[w][e] = 0;
   __syncthreads();
   const int blk0 = blockIdx.x * kPermuteChunk;
-  const int s_begin = blk0 + wave * kSlotsPerWave;
-  const int s_end = min(S, s_begin + kSlotsPerWave);
+  const int s_begin = blk0 + wave * kPermSlotsPerWave;
+  const int s_end = min(S, s_begin + kPermSlotsPerWave);
   for (int s = s_begin + (tid & 63); s < s_end; s += 64) atomicAdd(&wave_hist[wave][ids[s]], 1);
   __syncthreads();
   for (int e = tid; e < E; e += kPermuteThreads) {
     int run = block_base[(size_t)blockIdx.x * E + e];
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < kPermWaves; ++w) {
       const int c = wave_hist[w][e];
       wave_hist[w][e] = run;
       run += c;
@@ -193,6 +137,14 @@ moe_status_t launch_permute(const int32_t* ids, int32_t T, int32_t k, int32_t E,
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   hipLaunchKernelGGL(permute_scatter_kernel, dim3(nb), dim3(kPermuteThreads), 0, stream, ids, S, (int)E,
                      block_hist, sorted_slot, slot_to_row);
+  return launch_status();
+}
+
+moe_status_t launch_topk_permute_small(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* ids, float* w,
+                                       int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                                       int32_t* slot_to_row, hipStream_t stream) {
+  hipLaunchKernelGGL(topk_permute_small_kernel, dim3(1), dim3(kPermuteThreads), 0, stream, logits, (int)T, (int)E,
+                     (int)k, ids, w, counts, offsets, sorted_slot, slot_to_row);
   return launch_status();
 }
 

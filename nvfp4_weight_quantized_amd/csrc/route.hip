@@ -1,7 +1,7 @@
 // Router (S1) and top-k selection (S2) of the NVFP4 MoE layer, gfx950.
 //
 // S1: logits[t][e] = sum_h x[t][h] * Wr[e][h] (+ bias[e]), bf16 inputs, fp32 accumulation.
-//     Few tokens: one wavefront per expert streams its router row once and dots it with every
+//     Few tokens: one workgroup per expert streams its router row once and dots it with every
 //     token (the router weight is the only real traffic).  Many tokens: an LDS-tiled bf16 MFMA
 //     GEMM (16x16x32 fragments).
 // S2: one wavefront per token: k rounds of a wave-wide argmax (equal logits -> lower index),
@@ -10,59 +10,43 @@
 // Sources: router -> top-k stage of the modular fused MoE ("vLLM on the NVIDIA DGX Spark: A
 // Complete Technical Guide", section 7.1); top-8 of 320 routed experts ("Serving Solar Open 2 on
 // DGX Spark", "Solar Open 2 in brief").
-#include "common.h"
+#include "device_util.h"
 
 namespace moe {
 namespace {
 
 constexpr int kGemvMaxTokens = 32;
 
-// One wave per expert; 4 waves per workgroup.
-__global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t* __restrict__ x,
-                                                          const uint16_t* __restrict__ wr,
-                                                          const float* __restrict__ bias, int T, int H,
-                                                          int E, float* __restrict__ logits) {
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= E) return;
-  float acc[kGemvMaxTokens];
-#pragma unroll
-  for (int t = 0; t < kGemvMaxTokens; ++t) acc[t] = 0.f;
+// Few tokens: one workgroup per expert.  The 256 threads form T_P groups (T_P = T rounded up to a
+// power of two); group t dots token t with the expert's router row, each thread over a strided
+// slice of H, then a shuffle reduction inside the group.  All loads of a thread are independent.
+template <int T_P>
+__global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ wr,
+                                                           const float* __restrict__ bias, int T, int H, int E,
+                                                           float* __restrict__ logits) {
+  constexpr int G = 256 / T_P;      // threads per token (power of two, <= 64)
+  const int e = blockIdx.x;
+  const int t = threadIdx.x / G;
+  const int g = threadIdx.x % G;
   const uint16_t* wrow = wr + (size_t)e * H;
-  for (int h0 = lane * 8; h0 < H; h0 += 512) {
+  const uint16_t* xrow = x + (size_t)min(t, T - 1) * H;
+  float acc0 = 0.f, acc1 = 0.f;
+  for (int h0 = g * 8; h0 < H; h0 += G * 8) {
     const uint4 wv = *reinterpret_cast<const uint4*>(wrow + h0);
+    const uint4 xv = *reinterpret_cast<const uint4*>(xrow + h0);
     const uint32_t wq[4] = {wv.x, wv.y, wv.z, wv.w};
-    float wf[8];
+    const uint32_t xq[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      wf[2 * i] = __uint_as_float(wq[i] << 16);
-      wf[2 * i + 1] = __uint_as_float(wq[i] & 0xFFFF0000u);
-    }
-#pragma unroll
-    for (int t = 0; t < kGemvMaxTokens; ++t) {
-      if (t < T) {
-        const uint4 xv = *reinterpret_cast<const uint4*>(x + (size_t)t * H + h0);
-        const uint32_t xq[4] = {xv.x, xv.y, xv.z, xv.w};
-        float s = acc[t];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          s = fmaf(__uint_as_float(xq[i] << 16), wf[2 * i], s);
-          s = fmaf(__uint_as_float(xq[i] & 0xFFFF0000u), wf[2 * i + 1], s);
-        }
-        acc[t] = s;
-      }
+      acc0 = fmaf(__uint_as_float(xq[i] << 16), __uint_as_float(wq[i] << 16), acc0);
+      acc1 = fmaf(__uint_as_float(xq[i] & 0xFFFF0000u), __uint_as_float(wq[i] & 0xFFFF0000u), acc1);
     }
   }
-  const float b = bias ? bias[e] : 0.f;
+  float v = acc0 + acc1;
 #pragma unroll
-  for (int t = 0; t < kGemvMaxTokens; ++t) {
-    if (t < T) {
-      float v = acc[t];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-      if (lane == 0) logits[(size_t)t * E + e] = v + b;
-    }
-  }
+  for (int off = G / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  if (g == 0 && t < T) logits[(size_t)t * E + e] = v + (bias ? bias[e] : 0.f);
 }
 
 // C[T][E] = X[T][H] . Wr[E][H]^T with bf16 MFMA; 64x64 tile per workgroup, 4 waves of 32x32.
@@ -145,74 +129,41 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* row = logits + (size_t)t * E;
-  float v[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int e = lane + 64 * i;
-    float val = (e < E) ? row[e] : -INFINITY;
-    v[i] = (val != val) ? -INFINITY : val;  // NaN ranks lowest
-  }
-  uint32_t taken = 0;
-  for (int i = 0; i < 16; ++i)
-    if (lane + 64 * i >= E) taken |= 1u << i;
-  float my_val = -INFINITY;
-  int my_id = 0;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int e = lane + 64 * i;
-      if (!((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < bi))) {
-        bv = v[i];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == j) {
-      my_val = bv;
-      my_id = bi;
-    }
-  }
-  const float top = __shfl(my_val, 0);
-  float z = (lane < k) ? expf(my_val - top) : 0.f;
-  float s = z;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  int id;
+  float wt;
+  topk_token(logits + (size_t)t * E, E, k, &id, &wt);
   if (lane < k) {
-    ids[(size_t)t * k + lane] = my_id;
-    w[(size_t)t * k + lane] = z / s;
+    ids[(size_t)t * k + lane] = id;
+    w[(size_t)t * k + lane] = wt;
   }
 }
 
 }  // namespace
+
+moe_status_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, const float* bias, int32_t T,
+                                  int32_t H, int32_t E, float* logits, hipStream_t stream) {
+  if (T == 0) return MOE_OK;
+  if (T <= kGemvMaxTokens) {
+    const dim3 grid(E), block(256);
+    if (T <= 4) hipLaunchKernelGGL(router_small_kernel<4>, grid, block, 0, stream, x, w_router, bias, T, H, E, logits);
+    else if (T <= 8) hipLaunchKernelGGL(router_small_kernel<8>, grid, block, 0, stream, x, w_router, bias, T, H, E, logits);
+    else if (T <= 16) hipLaunchKernelGGL(router_small_kernel<16>, grid, block, 0, stream, x, w_router, bias, T, H, E, logits);
+    else hipLaunchKernelGGL(router_small_kernel<32>, grid, block, 0, stream, x, w_router, bias, T, H, E, logits);
+  } else {
+    hipLaunchKernelGGL(router_mfma_kernel, dim3((E + kRB - 1) / kRB, (T + kRB - 1) / kRB), dim3(256), 0, stream, x,
+                       w_router, bias, (int)T, (int)H, (int)E, logits);
+  }
+  return launch_status();
+}
 
 moe_status_t launch_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int32_t T,
                           int32_t H, int32_t E, int32_t k, bool logits_given, float* logits,
                           int32_t* ids, float* w, hipStream_t stream) {
   if (T == 0) return MOE_OK;
   if (!logits_given) {
-    if (T <= kGemvMaxTokens) {
-      hipLaunchKernelGGL(router_gemv_kernel, dim3((E + 3) / 4), dim3(256), 0, stream, x, w_router, bias,
-                         (int)T, (int)H, (int)E, logits);
-    } else {
-      hipLaunchKernelGGL(router_mfma_kernel, dim3((E + kRB - 1) / kRB, (T + kRB - 1) / kRB), dim3(256), 0,
-                         stream, x, w_router, bias, (int)T, (int)H, (int)E, logits);
-    }
-    if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+    if (moe_status_t st = launch_router_logits(x, w_router, bias, T, H, E, logits, stream)) return st;
   }
-  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits, (int)T, (int)E, (int)k,
-                     ids, w);
+  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits, (int)T, (int)E, (int)k, ids, w);
   return launch_status();
 }
 

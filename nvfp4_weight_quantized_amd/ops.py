@@ -249,7 +249,7 @@ def forward(layer: NvFp4MoELayer, x: torch.Tensor, workspace: Optional[torch.Ten
     """The whole layer on x [T, H] bf16 -> [T, H] bf16 (and, if asked, logits/ids/weights/counts).
 
     ``stage_events``: optional sequence of 6 raw hipEvent_t handles (ints or None) recorded at the
-    stage boundaries (before S1, after S2, S3, S4, S5, S6) on the current stream.
+    stage boundaries (before S1, after S1, after S2+S3, after S4, S5, S6) on the current stream.
     """
     _need(x, "x", torch.bfloat16, 2)
     t = x.shape[0]
