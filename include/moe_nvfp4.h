@@ -38,6 +38,8 @@
  *   - Its block scales are [N][K/16] E4M3FN bytes (bias 7, max 448, no infinities).
  *   - Fused gate/up weights w13 are [2I][H]: rows 0..I-1 gate, rows I..2I-1 up, each half with its
  *     own dequant global scale.
+ *   - Checkpoints use the canonical layout above; the GEMM entry points read the weights after a
+ *     one-time repack into the MFMA tile layout (moe_nvfp4_pack_tiles).
  *   - There is no activation-scale argument anywhere (W4A16): nothing can zero an expert.
  *
  * Conventions of every entry point:
@@ -78,16 +80,19 @@ typedef enum {
 /* Static, human-readable name of a status code (host). */
 const char* moe_status_string(moe_status_t s);
 
-/* One bank of NVFP4 experts (routed: num_experts = E; shared: num_experts = 1), device pointers. */
+/* One bank of NVFP4 experts (routed: num_experts = E; shared: num_experts = 1), device pointers.
+ * The packed weights and block scales are in the MFMA TILE LAYOUT produced by
+ * moe_nvfp4_pack_tiles from the canonical layout: per expert, the canonical [2I][H/2] (w13) or
+ * [H][I/2] (w2) bytes and their scale bytes, permuted tile by tile (same sizes). */
 typedef struct {
   int32_t num_experts;
   int32_t hidden;            /* H */
   int32_t inter;             /* I */
-  const uint8_t* w13;        /* [E][2I][H/2]  packed E2M1, gate rows then up rows */
-  const uint8_t* w13_scale;  /* [E][2I][H/16] E4M3FN block scales */
+  const uint8_t* w13;        /* [E] x tiled [2I][H/2]  packed E2M1, gate rows then up rows */
+  const uint8_t* w13_scale;  /* [E] x tiled [2I][H/16] E4M3FN block scales */
   const float* w13_gscale;   /* [E][2] dequant global scales (gate, up) */
-  const uint8_t* w2;         /* [E][H][I/2] */
-  const uint8_t* w2_scale;   /* [E][H][I/16] */
+  const uint8_t* w2;         /* [E] x tiled [H][I/2] */
+  const uint8_t* w2_scale;   /* [E] x tiled [H][I/16] */
   const float* w2_gscale;    /* [E] */
 } moe_nvfp4_experts_t;
 
@@ -195,6 +200,19 @@ moe_status_t moe_validate_forward(const moe_nvfp4_layer_t* layer, int32_t T, siz
  * Source: the reciprocal between ModelOpt and compressed-tensors global scales ("GLM-5.3-Flash-
  * NVFP4" discussion, compressed-tensors follow-up).  Fails on q == 0 or non-finite q. */
 moe_status_t moe_gscale_from_quant_scale(const float* q_host, float* d_host, int32_t n);
+
+/* Load-time repack of canonical NVFP4 tensors into the MFMA tile layout every GEMM entry point
+ * reads.  Input: num_tensors tensors of [rows][cols] weights as canonical packed bytes
+ * [rows][cols/2] and scale bytes [rows][cols/16] (rows % 16 == 0, cols % 128 == 0).  Output (same
+ * sizes, out of place): tile t = (rows/16 block nb) * (cols/128) + (128-column chunk c) of each
+ * tensor holds 1024 nibble bytes, where bytes [16l, 16l+16) (l = 16q + n) are canonical bytes
+ * [64c + 16q, 64c + 16q + 16) of row 16nb + n, and 128 scale bytes, where bytes [2l, 2l+2) are
+ * canonical scale bytes 8c + 2q and 8c + 2q + 1 of that row.  A fused gate/up tensor of one expert
+ * is one [2I][H] tensor.  One wave then reads a whole tile with one contiguous 1 KB load.
+ * Source: the checkpoint-preparation step that swizzles weights into a kernel's MMA tile layout
+ * ("Serving Solar Open 2 on DGX Spark", "Supporting real NVFP4 checkpoints"). */
+moe_status_t moe_nvfp4_pack_tiles(const uint8_t* packed, const uint8_t* scales, int32_t num_tensors, int32_t rows,
+                                  int32_t cols, uint8_t* tiled, uint8_t* tiled_scales, void* stream);
 
 /* On-device NVFP4 quantization of fp32 weights (the on-the-fly quantization path a checkpoint
  * without pre-quantized weights needs).  w: num_tensors tensors of [rows][cols] fp32, contiguous;

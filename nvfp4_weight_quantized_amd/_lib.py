@@ -71,6 +71,7 @@ SIGNATURES = {
                                 ctypes.POINTER(ForwardAux), c_void_p]),
     "moe_validate_forward": (i32, [ctypes.POINTER(Layer), i32, size_t, ctypes.c_char_p]),
     "moe_gscale_from_quant_scale": (i32, [c_void_p, c_void_p, i32]),
+    "moe_nvfp4_pack_tiles": (i32, [c_void_p, c_void_p, i32, i32, i32, c_void_p, c_void_p, c_void_p]),
     "moe_nvfp4_quantize": (i32, [c_void_p, i32, i32, i32, c_void_p, c_void_p, c_void_p, c_void_p]),
 }
 

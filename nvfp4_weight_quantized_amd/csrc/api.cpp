@@ -328,6 +328,16 @@ moe_status_t moe_gscale_from_quant_scale(const float* q_host, float* d_host, int
   return MOE_OK;
 }
 
+moe_status_t moe_nvfp4_pack_tiles(const uint8_t* packed, const uint8_t* scales, int32_t num_tensors, int32_t rows,
+                                  int32_t cols, uint8_t* tiled, uint8_t* tiled_scales, void* stream) {
+  if (num_tensors < 0 || rows < 0 || cols < 0 || rows % 16 != 0 || cols % 128 != 0) return MOE_ERR_INVALID_ARGUMENT;
+  if ((int64_t)num_tensors * rows * cols == 0) return MOE_OK;
+  if (!packed || !scales || !tiled || !tiled_scales) return MOE_ERR_INVALID_ARGUMENT;
+  if (moe_status_t st = check_arch(nullptr)) return st;
+  return moe::launch_pack_tiles(packed, scales, num_tensors, rows, cols, tiled, tiled_scales,
+                                static_cast<hipStream_t>(stream));
+}
+
 moe_status_t moe_nvfp4_quantize(const float* w, int32_t num_tensors, int32_t rows, int32_t cols, const float* gscale,
                                 uint8_t* packed, uint8_t* scales, void* stream) {
   if (num_tensors < 0 || rows < 0 || cols < 0 || cols % 16 != 0) return MOE_ERR_INVALID_ARGUMENT;

@@ -56,8 +56,8 @@ moe_status_t launch_route(const uint16_t* x, const uint16_t* w_router, const flo
 
 // Grouped GEMM ------------------------------------------------------------------------------
 struct GemmBank {
-  const uint8_t* w;      // packed nibbles, [E][Nrows][K/2]
-  const uint8_t* ws;     // E4M3 block scales, [E][Nrows][K/16]
+  const uint8_t* w;      // packed nibbles, [E][Nrows][K/2] bytes in the MFMA tile layout (layout.hip)
+  const uint8_t* ws;     // E4M3 block scales, [E][Nrows][K/16] bytes in the MFMA tile layout
   const float* gs;       // dequant global scales, [E][gs_per_expert]
   int32_t gs_per_expert; // 2 (gate, up) or 1 (down)
 };
@@ -89,6 +89,10 @@ moe_status_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream);
 moe_status_t launch_combine(const uint16_t* y_rows, const int32_t* slot_to_row, const float* w,
                             const uint16_t* y_shared, int32_t T, int32_t k, int32_t H, uint16_t* out,
                             hipStream_t stream);
+
+// Weight tile layout ------------------------------------------------------------------------
+moe_status_t launch_pack_tiles(const uint8_t* packed, const uint8_t* scales, int32_t num_tensors, int32_t rows,
+                               int32_t cols, uint8_t* tiled, uint8_t* tiled_scales, hipStream_t stream);
 
 // Quantize ----------------------------------------------------------------------------------
 moe_status_t launch_quantize(const float* w, int32_t num_tensors, int32_t rows, int32_t cols,

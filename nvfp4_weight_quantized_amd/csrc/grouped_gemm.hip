@@ -7,17 +7,18 @@
 // fused MoE of section 4.
 //
 // CDNA4 design:
+//  * Weights are read in the MFMA tile layout (see layout.hip): one 16-row x 128-K tile is 1 KB of
+//    nibbles in lane order plus 128 B of scales, so every weight load of a wave is one contiguous
+//    1 KB (or 128 B) request.  Lane l = 16q + n of a 16x16x32 B fragment owns row n, K range
+//    [32q, 32q+32) of each 128-K tile: 16 bytes of nibbles and 2 scale bytes.
+//  * Those bytes are dequantized in registers straight into the bf16 MFMA operand:
+//    v_cvt_scalef32_pk_f32_fp4 (scale 1) gives the E2M1 values, one fp32 multiply applies the
+//    block scale and v_cvt_pk_bf16_f32 packs the result.  element * block scale has at most 6
+//    significant bits, so the bf16 operand is exact.
+//  * The MFMA reduction order over K is permuted consistently for A and B (MFMA step j of a
+//    128-K tile uses K 32q + 8j .. 32q + 8j + 7 in lane group q); the sum is over the same products.
 //  * A (activation rows, bf16) is gathered row by row through the sorted slot list straight from
-//    the token matrix -- no permuted copy -- and staged in LDS per K chunk (BK = 128 for tall
-//    tiles, up to 512 for the 16-row tiles of decode-sized groups).
-//  * B (weights) never goes through LDS: each lane loads BK/8 contiguous bytes of packed nibbles
-//    of one weight row per chunk plus their BK/64 E4M3 scale bytes and dequantizes them in
-//    registers into the bf16 MFMA operand: v_cvt_scalef32_pk_f32_fp4 (scale 1) gives the E2M1
-//    values, one fp32 multiply applies the block scale and v_cvt_pk_bf16_f32 packs the result.
-//    element * block scale has at most 6 significant bits, so the bf16 operand is exact.
-//  * The MFMA reduction order over K is permuted consistently for A and B (lane group q of a
-//    16x16x32 fragment owns K range [q*BK/4, (q+1)*BK/4) of the chunk), which makes every lane's
-//    weight bytes contiguous; the sum is over the same products.
+//    the token matrix -- no permuted copy -- and staged in LDS per K chunk.
 //  * fp32 accumulation; the per-tensor global scales multiply the accumulators in the epilogue;
 //    gate/up workgroups hold matching gate and up columns so h = silu(g)*u is formed in registers.
 //  * Groups (experts) are found on the device from the offsets array: no host synchronisation.
@@ -27,7 +28,7 @@
 namespace moe {
 namespace {
 
-constexpr int kAPad = 8;       // bf16 of padding per LDS row (16 bytes) against bank conflicts
+constexpr int kAPad = 8;        // bf16 of padding per LDS row (16 bytes) against bank conflicts
 constexpr int kThreads = 256;   // 4 waves
 
 struct TileInfo {
@@ -58,7 +59,14 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t q, float s) {
   return r;
 }
 
-// Find the tile `mtile` (numbered over the groups in order, then the extra group).  Wave 0 only.
+// B operand of MFMA step j (0..3) of one 128-K tile from the lane's 16 nibble bytes and 2 scale bytes.
+__device__ __forceinline__ bf16x8 b_operand(const uint4& w, uint32_t sc, int j) {
+  const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+  const float s = (j < 2) ? __builtin_amdgcn_cvt_f32_fp8((int)sc, 0) : __builtin_amdgcn_cvt_f32_fp8((int)sc, 1);
+  return dequant8(words[j], s);
+}
+
+// Tile `mtile` (numbered over the groups in order, then the extra group).  Wave 0 only.
 template <int BM>
 __device__ bool find_tile(const GemmProblem& p, int mtile, TileInfo* out) {
   const int lane = threadIdx.x & 63;
@@ -117,168 +125,39 @@ __device__ bool find_tile(const GemmProblem& p, int mtile, TileInfo* out) {
   return false;
 }
 
-// MI: 16-row A fragments per wave (BM = 16*MI).  NB: 16-column B fragments per wave.
-// BK: K chunk (128, 256 or 512); lane group q of a fragment owns K range [q*BK/4, (q+1)*BK/4) of
-// the chunk, i.e. BK/8 contiguous weight bytes and BK/64 contiguous scale bytes of its row.
-// GATE_UP: fragments [0, NB/2) are gate columns, [NB/2, NB) the matching up columns.
-template <int MI, int NB, int BK, bool GATE_UP>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmProblem p) {
-  constexpr int BM = 16 * MI;
-  constexpr int COLS_PER_WAVE = GATE_UP ? 16 * (NB / 2) : 16 * NB;   // output columns per wave
-  constexpr int BN = 4 * COLS_PER_WAVE;                               // output columns per workgroup
-  constexpr int LANE_K = BK / 4;        // K values per lane per chunk
-  constexpr int NV = LANE_K / 32;       // 16-byte nibble loads per lane per fragment per chunk
-  constexpr int LANE_S = LANE_K / 16;   // scale bytes per lane per chunk (2, 4 or 8)
-  constexpr int STEPS = BK / 32;        // MFMA k-steps per chunk
-  constexpr int A_TPR = BK / 8;         // threads per A row (16 bytes each)
-  constexpr int A_RPP = kThreads / A_TPR;   // A rows per pass
-  constexpr int A_ITERS = BM / A_RPP;       // passes
-  static_assert(BM % A_RPP == 0, "A tile must be a whole number of passes");
-  static_assert(LANE_S == 2 || LANE_S == 4 || LANE_S == 8, "BK must be 128, 256 or 512");
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM][BK + kAPad];
-  __shared__ TileInfo tile;
-  __shared__ int tile_ok;
+// Wave 0: number of BM-row tiles over the groups (+ extra group).
+template <int BM>
+__device__ int count_tiles(const GemmProblem& p) {
+  const int lane = threadIdx.x & 63;
+  int t = 0;
+  for (int g = lane; g < p.G; g += 64) t += (p.offsets[g + 1] - p.offsets[g] + BM - 1) / BM;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
+  if (p.has_extra) t += (p.M_extra + BM - 1) / BM;
+  return t;
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int NT = p.N / BN;
-  const int mtile = blockIdx.x / NT;
-  const int ntile = blockIdx.x - mtile * NT;
-
-  if (wave == 0) {
-    const bool ok = find_tile<BM>(p, mtile, &tile);
-    if (lane == 0) tile_ok = ok ? 1 : 0;
+// Weight-row block (16 rows) of B fragment f of `wave` in output-column tile `ntile`.
+template <int NB, bool GATE_UP, int BN, int COLS_PER_WAVE>
+__device__ __forceinline__ int frag_row_block(int f, int ntile, int wave, int N) {
+  int n;
+  if (GATE_UP) {
+    const int fg = (f < NB / 2) ? f : f - NB / 2;
+    n = ntile * BN + wave * COLS_PER_WAVE + 16 * fg;
+    if (f >= NB / 2) n += N;  // up rows follow the gate rows
+  } else {
+    n = ntile * BN + wave * COLS_PER_WAVE + 16 * f;
   }
-  __syncthreads();
-  if (!tile_ok) return;
-  const TileInfo ti = tile;
-  const GemmBank& bank = ti.extra ? p.extra : p.bank;
-  const int K = p.K;
-  const int nK = K / BK;
+  return n >> 4;
+}
 
-  // A rows this thread copies: r = tid/A_TPR + A_RPP*it, 16 bytes at column (tid%A_TPR)*8
-  const uint16_t* arow[A_ITERS];
-#pragma unroll
-  for (int it = 0; it < A_ITERS; ++it) {
-    const int r = tid / A_TPR + A_RPP * it;
-    arow[it] = nullptr;
-    if (r < ti.rows) {
-      const int R = ti.a_row0 + r;
-      if (ti.extra) {
-        arow[it] = p.a_extra + (size_t)R * K;
-      } else {
-        const int src = p.row_index ? p.row_index[R] / p.row_divisor : R;
-        arow[it] = p.a + (size_t)src * K;
-      }
-    }
-  }
-  const int acol = (tid % A_TPR) * 8;
-
-  // B rows this lane reads: weight row n for fragment f
-  const int q = lane >> 4;
-  const int nl = lane & 15;
-  const size_t wrow_bytes = (size_t)K / 2;
-  const size_t srow_bytes = (size_t)K / 16;
-  const size_t rows_per_expert = GATE_UP ? 2 * (size_t)p.N : (size_t)p.N;
-  const uint8_t* wbase = bank.w + (size_t)ti.group * rows_per_expert * wrow_bytes;
-  const uint8_t* sbase = bank.ws + (size_t)ti.group * rows_per_expert * srow_bytes;
-  const uint8_t* wptr[NB];
-  const uint8_t* sptr[NB];
-#pragma unroll
-  for (int f = 0; f < NB; ++f) {
-    int n;
-    if (GATE_UP) {
-      const int fg = (f < NB / 2) ? f : f - NB / 2;
-      n = ntile * BN + wave * COLS_PER_WAVE + 16 * fg + nl;
-      if (f >= NB / 2) n += p.N;  // up rows follow the gate rows
-    } else {
-      n = ntile * BN + wave * COLS_PER_WAVE + 16 * f + nl;
-    }
-    wptr[f] = wbase + (size_t)n * wrow_bytes + (LANE_K / 2) * q;
-    sptr[f] = sbase + (size_t)n * srow_bytes + LANE_S * q;
-  }
-
-  f32x4 acc[MI][NB];
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int f = 0; f < NB; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  uint4 a_next[A_ITERS];
-  uint4 b_next[NB][NV];
-  uint32_t s_next[NB][2];
-  auto load_chunk = [&](int c) {
-#pragma unroll
-    for (int it = 0; it < A_ITERS; ++it)
-      a_next[it] = arow[it] ? *reinterpret_cast<const uint4*>(arow[it] + (size_t)c * BK + acol) : uint4{0, 0, 0, 0};
-#pragma unroll
-    for (int f = 0; f < NB; ++f) {
-      const uint8_t* wp = wptr[f] + (size_t)c * (BK / 2);
-#pragma unroll
-      for (int v = 0; v < NV; ++v) b_next[f][v] = *reinterpret_cast<const uint4*>(wp + 16 * v);
-      const uint8_t* sp = sptr[f] + (size_t)c * (BK / 16);
-      if constexpr (LANE_S == 2) {
-        s_next[f][0] = *reinterpret_cast<const uint16_t*>(sp);
-        s_next[f][1] = 0;
-      } else if constexpr (LANE_S == 4) {
-        s_next[f][0] = *reinterpret_cast<const uint32_t*>(sp);
-        s_next[f][1] = 0;
-      } else {
-        const uint2 sv = *reinterpret_cast<const uint2*>(sp);
-        s_next[f][0] = sv.x;
-        s_next[f][1] = sv.y;
-      }
-    }
-  };
-  load_chunk(0);
-
-  for (int c = 0; c < nK; ++c) {
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < A_ITERS; ++it)
-      *reinterpret_cast<uint4*>(&As[tid / A_TPR + A_RPP * it][acol]) = a_next[it];
-    uint4 bq[NB][NV];
-    uint32_t sc[NB][2];
-#pragma unroll
-    for (int f = 0; f < NB; ++f) {
-#pragma unroll
-      for (int v = 0; v < NV; ++v) bq[f][v] = b_next[f][v];
-      sc[f][0] = s_next[f][0];
-      sc[f][1] = s_next[f][1];
-    }
-    __syncthreads();
-    if (c + 1 < nK) load_chunk(c + 1);
-
-#pragma unroll
-    for (int j = 0; j < STEPS; ++j) {
-      bf16x8 bfrag[NB];
-#pragma unroll
-      for (int f = 0; f < NB; ++f) {
-        const uint4 bv = bq[f][j / 4];
-        const uint32_t words[4] = {bv.x, bv.y, bv.z, bv.w};
-        const int sb = j / 2;   // scale byte of this k-step within the lane's scale bytes
-        const uint32_t sw = sc[f][sb / 4];
-        float s;
-        switch (sb % 4) {
-          case 0: s = __builtin_amdgcn_cvt_f32_fp8((int)sw, 0); break;
-          case 1: s = __builtin_amdgcn_cvt_f32_fp8((int)sw, 1); break;
-          case 2: s = __builtin_amdgcn_cvt_f32_fp8((int)sw, 2); break;
-          default: s = __builtin_amdgcn_cvt_f32_fp8((int)sw, 3); break;
-        }
-        bfrag[f] = dequant8(words[j % 4], s);
-      }
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const bf16x8 afrag = *reinterpret_cast<const bf16x8*>(&As[16 * i + nl][LANE_K * q + 8 * j]);
-#pragma unroll
-        for (int f = 0; f < NB; ++f)
-          acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag[f], acc[i][f], 0, 0, 0);
-      }
-    }
-  }
-
-  // epilogue
+// Epilogue: scale the accumulators by the global scale(s), SiLU(gate)*up for gate/up, store bf16.
+template <int MI, int NB, bool GATE_UP, int BN, int COLS_PER_WAVE>
+__device__ __forceinline__ void epilogue(const GemmProblem& p, const GemmBank& bank, const TileInfo& ti, int ntile,
+                                         const f32x4 (&acc)[MI][NB]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int q = lane >> 4, nl = lane & 15;
   const float* gs = bank.gs + (size_t)ti.group * bank.gs_per_expert;
   if (GATE_UP) {
     const float dg = gs[0], du = gs[1];
@@ -313,6 +192,300 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmProblem p) {
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Short and medium tiles.  MI: 16-row A fragments per wave (BM = 16*MI); NB: 16-column B
+// fragments per wave; BK: K chunk staged in LDS per barrier (a multiple of 128: BK/128 weight
+// tiles per fragment per chunk).  A is copied global -> registers -> LDS one chunk ahead.
+template <int MI, int NB, int BK, bool GATE_UP>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmProblem p) {
+  constexpr int BM = 16 * MI;
+  constexpr int COLS_PER_WAVE = GATE_UP ? 16 * (NB / 2) : 16 * NB;   // output columns per wave
+  constexpr int BN = 4 * COLS_PER_WAVE;                               // output columns per workgroup
+  constexpr int NS = BK / 128;          // weight tiles per fragment per chunk
+  constexpr int A_TPR = BK / 8;         // threads per A row (16 bytes each)
+  constexpr int A_RPP = kThreads / A_TPR;   // A rows per pass
+  constexpr int A_ITERS = (BM + A_RPP - 1) / A_RPP;
+  static_assert(BK % 128 == 0 && BK <= 512, "BK must be 128, 256 or 512");
+  __shared__ __attribute__((aligned(16))) uint16_t As[A_ITERS * A_RPP][BK + kAPad];
+  __shared__ TileInfo tile;
+  __shared__ int tile_ok;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int NT = p.N / BN;
+  const int mtile = blockIdx.x / NT;
+  const int ntile = blockIdx.x - mtile * NT;
+
+  if (wave == 0) {
+    const bool ok = find_tile<BM>(p, mtile, &tile);
+    if (lane == 0) tile_ok = ok ? 1 : 0;
+  }
+  __syncthreads();
+  if (!tile_ok) return;
+  const TileInfo ti = tile;
+  const GemmBank& bank = ti.extra ? p.extra : p.bank;
+  const int K = p.K;
+  const int nK = K / BK;
+  const int ktiles = K / 128;
+
+  // A rows this thread copies: r = tid/A_TPR + A_RPP*it, 16 bytes at column (tid%A_TPR)*8
+  const uint16_t* arow[A_ITERS];
+#pragma unroll
+  for (int it = 0; it < A_ITERS; ++it) {
+    const int r = tid / A_TPR + A_RPP * it;
+    arow[it] = nullptr;
+    if (r < ti.rows) {
+      const int R = ti.a_row0 + r;
+      if (ti.extra) {
+        arow[it] = p.a_extra + (size_t)R * K;
+      } else {
+        const int src = p.row_index ? p.row_index[R] / p.row_divisor : R;
+        arow[it] = p.a + (size_t)src * K;
+      }
+    }
+  }
+  const int acol = (tid % A_TPR) * 8;
+
+  // B tiles this lane reads
+  const int q = lane >> 4;
+  const int nl = lane & 15;
+  const size_t rows_per_expert = GATE_UP ? 2 * (size_t)p.N : (size_t)p.N;
+  const uint8_t* wexp = bank.w + (size_t)ti.group * rows_per_expert * (size_t)(K / 2) + 16 * lane;
+  const uint8_t* sexp = bank.ws + (size_t)ti.group * rows_per_expert * (size_t)(K / 16) + 2 * lane;
+  const uint8_t* wptr[NB];
+  const uint8_t* sptr[NB];
+#pragma unroll
+  for (int f = 0; f < NB; ++f) {
+    const size_t t0 = (size_t)frag_row_block<NB, GATE_UP, BN, COLS_PER_WAVE>(f, ntile, wave, p.N) * ktiles;
+    wptr[f] = wexp + t0 * 1024;
+    sptr[f] = sexp + t0 * 128;
+  }
+
+  f32x4 acc[MI][NB];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int f = 0; f < NB; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 a_next[A_ITERS];
+  uint4 b_next[NB][NS];
+  uint32_t s_next[NB][NS];
+  auto load_chunk = [&](int c) {
+#pragma unroll
+    for (int it = 0; it < A_ITERS; ++it)
+      a_next[it] = arow[it] ? *reinterpret_cast<const uint4*>(arow[it] + (size_t)c * BK + acol) : uint4{0, 0, 0, 0};
+#pragma unroll
+    for (int f = 0; f < NB; ++f)
+#pragma unroll
+      for (int v = 0; v < NS; ++v) {
+        const size_t t = (size_t)c * NS + v;
+        b_next[f][v] = *reinterpret_cast<const uint4*>(wptr[f] + t * 1024);
+        s_next[f][v] = *reinterpret_cast<const uint16_t*>(sptr[f] + t * 128);
+      }
+  };
+  load_chunk(0);
+
+  for (int c = 0; c < nK; ++c) {
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < A_ITERS; ++it)
+      *reinterpret_cast<uint4*>(&As[tid / A_TPR + A_RPP * it][acol]) = a_next[it];
+    uint4 bq[NB][NS];
+    uint32_t sc[NB][NS];
+#pragma unroll
+    for (int f = 0; f < NB; ++f)
+#pragma unroll
+      for (int v = 0; v < NS; ++v) {
+        bq[f][v] = b_next[f][v];
+        sc[f][v] = s_next[f][v];
+      }
+    __syncthreads();
+    if (c + 1 < nK) load_chunk(c + 1);
+
+#pragma unroll
+    for (int v = 0; v < NS; ++v)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x8 bfrag[NB];
+#pragma unroll
+        for (int f = 0; f < NB; ++f) bfrag[f] = b_operand(bq[f][v], sc[f][v], j);
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const bf16x8 afrag = *reinterpret_cast<const bf16x8*>(&As[16 * i + nl][128 * v + 32 * q + 8 * j]);
+#pragma unroll
+          for (int f = 0; f < NB; ++f)
+            acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag[f], acc[i][f], 0, 0, 0);
+        }
+      }
+  }
+  epilogue<MI, NB, GATE_UP, BN, COLS_PER_WAVE>(p, bank, ti, ntile, acc);
+}
+
+// ------------------------------------------------------------------------------------------
+// Tall tiles (many rows per expert): 128-row workgroup tiles, K chunk 128.
+//  * A chunks go global -> LDS directly (global_load_lds, 16 bytes per lane; lane i of a wave
+//    lands at LDS base + 16*i), double-buffered, one barrier per chunk.  Rows are 256 bytes with
+//    the 16-byte slot index XOR-swizzled by (row & 15), so the fragment reads of 16 rows at one
+//    K offset hit 16 different bank groups.
+//  * B tiles in registers, prefetched one chunk ahead.
+//  * 16-row blocks past the group's last row are skipped (no LDS reads, no MFMA).
+//  * Tile order is XCD-aware: workgroup b runs on XCD b % 8; each XCD walks a contiguous range of
+//    (m-tile, n-tile) pairs, n fastest, so the A rows of an m-tile are reused from that XCD's L2.
+//  * At most 256 registers per lane so that two workgroups share a CU.
+constexpr int kTallBK = 128;
+constexpr int kTallRows = 128;
+constexpr int kXcds = 8;
+
+template <int NB, bool GATE_UP>
+__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_tall_kernel(GemmProblem p) {
+  constexpr int MI = kTallRows / 16;
+  constexpr int BM = kTallRows;
+  constexpr int BK = kTallBK;
+  constexpr int COLS_PER_WAVE = GATE_UP ? 16 * (NB / 2) : 16 * NB;
+  constexpr int BN = 4 * COLS_PER_WAVE;
+  constexpr int ROW_BYTES = BK * 2;                    // 256
+  constexpr int BUF_BYTES = BM * ROW_BYTES;            // 32 KB
+  constexpr int A_ITERS = BUF_BYTES / (kThreads * 16); // 8 direct loads per thread per chunk
+  __shared__ __attribute__((aligned(1024))) uint8_t As[2][BUF_BYTES];
+  __shared__ uint32_t s_aoff[BM];
+  __shared__ TileInfo tile;
+  __shared__ int tile_ok;
+  __shared__ int tile_n;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int NT = p.N / BN;
+
+  if (wave == 0) {
+    const int total = count_tiles<BM>(p) * NT;
+    const int per_xcd = (total + kXcds - 1) / kXcds;
+    const int slot = blockIdx.x / kXcds;
+    const int L = (blockIdx.x % kXcds) * per_xcd + slot;
+    bool ok = slot < per_xcd && L < total;
+    if (ok) ok = find_tile<BM>(p, L / NT, &tile);
+    if (lane == 0) {
+      tile_ok = ok ? 1 : 0;
+      tile_n = ok ? L % NT : 0;
+    }
+  }
+  __syncthreads();
+  if (!tile_ok) return;
+  const TileInfo ti = tile;
+  const int ntile = tile_n;
+  const GemmBank& bank = ti.extra ? p.extra : p.bank;
+  const int K = p.K;
+  const int nK = K / BK;
+  const int row_blocks = (ti.rows + 15) / 16;          // 16-row MFMA blocks holding real rows
+
+  // A rows: element offset of each of the tile's rows (rows past the group repeat a valid row)
+  const uint16_t* abase = ti.extra ? p.a_extra : p.a;
+  if (tid < BM) {
+    const int R = ti.a_row0 + min(tid, ti.rows - 1);
+    const int src = (!ti.extra && p.row_index) ? p.row_index[R] / p.row_divisor : R;
+    s_aoff[tid] = (uint32_t)src * (uint32_t)K;
+  }
+  __syncthreads();
+  // Lane `lane` of wave `wave`, direct load `it`, fills LDS slot (lane & 15) of row
+  // r = 4*(4*it + wave) + lane/16 with the row's 16-byte chunk (lane & 15) ^ (r & 15).
+  const uint32_t acol = (uint32_t)(((lane & 15) ^ ((4 * wave + (lane >> 4)) & 15)) * 8);
+
+  // B tiles this lane reads
+  const int q = lane >> 4;
+  const int nl = lane & 15;
+  const int ktiles = K / 128;
+  const size_t rows_per_expert = GATE_UP ? 2 * (size_t)p.N : (size_t)p.N;
+  const uint8_t* wexp = bank.w + (size_t)ti.group * rows_per_expert * (size_t)(K / 2) + 16 * lane;
+  const uint8_t* sexp = bank.ws + (size_t)ti.group * rows_per_expert * (size_t)(K / 16) + 2 * lane;
+  uint32_t tile0[NB];
+#pragma unroll
+  for (int f = 0; f < NB; ++f)
+    tile0[f] = (uint32_t)(frag_row_block<NB, GATE_UP, BN, COLS_PER_WAVE>(f, ntile, wave, p.N) * ktiles);
+
+  f32x4 acc[MI][NB];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int f = 0; f < NB; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto issue_a = [&](int c, int buf) {
+#pragma unroll
+    for (int it = 0; it < A_ITERS; ++it) {
+      const uint32_t off = s_aoff[4 * (4 * it + wave) + (lane >> 4)];
+      __builtin_amdgcn_global_load_lds((const void*)(abase + off + (uint32_t)c * BK + acol),
+                                       (__attribute__((address_space(3))) void*)(&As[buf][(4 * it + wave) * 1024]),
+                                       16, 0, 0);
+    }
+  };
+  uint4 bn[NB];
+  uint32_t sn[NB];
+  auto load_b = [&](int c) {
+#pragma unroll
+    for (int f = 0; f < NB; ++f) {
+      const size_t t = (size_t)tile0[f] + (size_t)c;
+      bn[f] = *reinterpret_cast<const uint4*>(wexp + t * 1024);
+      sn[f] = *reinterpret_cast<const uint16_t*>(sexp + t * 128);
+    }
+  };
+
+  issue_a(0, 0);
+  load_b(0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  for (int c = 0; c < nK; ++c) {
+    uint4 bq[NB];
+    uint32_t sc[NB];
+#pragma unroll
+    for (int f = 0; f < NB; ++f) {
+      bq[f] = bn[f];
+      sc[f] = sn[f];
+    }
+    if (c + 1 < nK) {
+      issue_a(c + 1, (c + 1) & 1);
+      load_b(c + 1);
+    }
+    const uint8_t* abuf = As[c & 1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x8 bfrag[NB];
+#pragma unroll
+      for (int f = 0; f < NB; ++f) bfrag[f] = b_operand(bq[f], sc[f], j);
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        if (i < row_blocks) {
+          const int row = 16 * i + nl;
+          const bf16x8 afrag =
+              *reinterpret_cast<const bf16x8*>(abuf + row * ROW_BYTES + 16 * ((4 * q + j) ^ nl));
+#pragma unroll
+          for (int f = 0; f < NB; ++f)
+            acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag[f], acc[i][f], 0, 0, 0);
+        }
+      }
+    }
+    // the next A chunk (and B tile) must have landed before the buffer flips
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  epilogue<MI, NB, GATE_UP, BN, COLS_PER_WAVE>(p, bank, ti, ntile, acc);
+}
+
+template <int NB, bool GATE_UP>
+moe_status_t launch_tall(const GemmProblem& p, hipStream_t stream) {
+  constexpr int BN = GATE_UP ? 4 * 16 * (NB / 2) : 4 * 16 * NB;
+  if (p.N % BN != 0 || p.K % kTallBK != 0) return MOE_ERR_INVALID_ARGUMENT;
+  const int NT = p.N / BN;
+  const long long mt = (p.G > 0 ? (long long)std::min(p.G, p.M) + p.M / kTallRows : 0LL) +
+                       (p.has_extra ? (p.M_extra + kTallRows - 1) / kTallRows : 0);
+  long long grid = mt * NT;
+  if (grid == 0) return MOE_OK;
+  grid = (grid + kXcds - 1) / kXcds * kXcds;
+  if (grid > 0x7FFFFFFFLL) return MOE_ERR_INVALID_ARGUMENT;
+  hipLaunchKernelGGL((grouped_gemm_tall_kernel<NB, GATE_UP>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  return launch_status();
+}
+
 template <int MI, int NB, int BK, bool GATE_UP>
 moe_status_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
   constexpr int BM = 16 * MI;
@@ -329,8 +502,7 @@ moe_status_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
   return launch_status();
 }
 
-// Few rows per expert: 16-row tiles and the widest K chunk the reduction length allows, so that
-// each lane streams 64 contiguous weight bytes per fragment per chunk.
+// Few rows per expert: 16-row tiles and the widest K chunk the reduction length allows.
 template <bool GATE_UP>
 moe_status_t launch_small(const GemmProblem& p, hipStream_t stream) {
   if (p.K % 512 == 0) return launch_cfg<1, 2, 512, GATE_UP>(p, stream);
@@ -349,12 +521,12 @@ moe_status_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
   if (gate_up) {
     if (avg <= 16) return launch_small<true>(p, stream);
     if (avg <= 64) return launch_cfg<4, 4, 128, true>(p, stream);
-    return launch_cfg<8, 4, 128, true>(p, stream);
+    return launch_tall<4, true>(p, stream);
   }
   const bool wide = (p.N % 256) == 0;
   if (avg <= 16) return launch_small<false>(p, stream);
   if (avg <= 64) return wide ? launch_cfg<4, 4, 128, false>(p, stream) : launch_cfg<4, 2, 128, false>(p, stream);
-  return wide ? launch_cfg<8, 4, 128, false>(p, stream) : launch_cfg<8, 2, 128, false>(p, stream);
+  return wide ? launch_tall<4, false>(p, stream) : launch_tall<2, false>(p, stream);
 }
 
 }  // namespace moe

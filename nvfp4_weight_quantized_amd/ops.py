@@ -41,7 +41,12 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: Optional[int] = None):
 
 @dataclass
 class NvFp4Experts:
-    """A bank of NVFP4 experts on the GPU (layouts as in include/moe_nvfp4.h)."""
+    """A bank of NVFP4 experts on the GPU, weights and scales in the MFMA tile layout.
+
+    Shapes are those of the canonical tensors (include/moe_nvfp4.h); the bytes of each expert's
+    tensors are permuted by ``pack_tiles``.  Use ``NvFp4Experts.from_canonical`` to build one from
+    checkpoint-layout tensors.
+    """
     w13: torch.Tensor          # uint8 [E, 2I, H/2]
     w13_scale: torch.Tensor    # uint8 [E, 2I, H/16]
     w13_gscale: torch.Tensor   # float32 [E, 2]
@@ -72,6 +77,13 @@ class NvFp4Experts:
             _need(t, name, dt)
             if tuple(t.shape) != shape:
                 raise ValueError(f"{name}: expected shape {shape}, got {tuple(t.shape)}")
+
+    @classmethod
+    def from_canonical(cls, w13, w13_scale, w13_gscale, w2, w2_scale, w2_gscale) -> "NvFp4Experts":
+        """Repack canonical-layout device tensors into the tile layout (new tensors)."""
+        t13, s13 = pack_tiles(w13, w13_scale)
+        t2, s2 = pack_tiles(w2, w2_scale)
+        return cls(t13, s13, w13_gscale, t2, s2, w2_gscale)
 
     def c_struct(self) -> L.Experts:
         return L.Experts(self.num_experts, self.hidden, self.inter,
@@ -128,10 +140,11 @@ class NvFp4MoELayer:
         def bank(prefix):
             if prefix + "w13" not in tensors:
                 return None
-            return NvFp4Experts(dev(tensors[prefix + "w13"], torch.uint8), dev(tensors[prefix + "w13_scale"], torch.uint8),
-                                gscale(tensors[prefix + "w13_global_scale"]),
-                                dev(tensors[prefix + "w2"], torch.uint8), dev(tensors[prefix + "w2_scale"], torch.uint8),
-                                gscale(tensors[prefix + "w2_global_scale"]))
+            return NvFp4Experts.from_canonical(
+                dev(tensors[prefix + "w13"], torch.uint8), dev(tensors[prefix + "w13_scale"], torch.uint8),
+                gscale(tensors[prefix + "w13_global_scale"]),
+                dev(tensors[prefix + "w2"], torch.uint8), dev(tensors[prefix + "w2_scale"], torch.uint8),
+                gscale(tensors[prefix + "w2_global_scale"]))
 
         routed = bank("experts.")
         shared = bank("shared_expert.")
@@ -297,6 +310,24 @@ def gscale_from_quant_scale(q) -> np.ndarray:
             L.lib().moe_gscale_from_quant_scale(q.ctypes.data_as(ctypes.c_void_p), d.ctypes.data_as(ctypes.c_void_p),
                                                 q.size))
     return d
+
+
+def pack_tiles(packed: torch.Tensor, scales: torch.Tensor, tiled: Optional[torch.Tensor] = None,
+               tiled_scales: Optional[torch.Tensor] = None):
+    """Canonical [..., rows, cols/2] nibbles + [..., rows, cols/16] scales -> MFMA tile layout (same shapes)."""
+    _need(packed, "packed", torch.uint8)
+    _need(scales, "scales", torch.uint8)
+    rows, half = packed.shape[-2], packed.shape[-1]
+    cols = half * 2
+    nt = int(np.prod(packed.shape[:-2])) if packed.dim() > 2 else 1
+    if tuple(scales.shape) != tuple(packed.shape[:-1]) + (cols // 16,):
+        raise ValueError("scales shape does not match packed")
+    tiled = torch.empty_like(packed) if tiled is None else tiled
+    tiled_scales = torch.empty_like(scales) if tiled_scales is None else tiled_scales
+    L.check("moe_nvfp4_pack_tiles", L.lib().moe_nvfp4_pack_tiles(_ptr(packed), _ptr(scales), nt, rows, cols,
+                                                                 _ptr(tiled), _ptr(tiled_scales),
+                                                                 _stream(packed.device)))
+    return tiled, tiled_scales
 
 
 def quantize(w: torch.Tensor, gscale: torch.Tensor, packed: Optional[torch.Tensor] = None,

@@ -17,7 +17,8 @@ def _dequant_scales(amax, convention: str):
 
 
 def build_bank(wl: synth.Workload, bank: str, device="cuda") -> ops.NvFp4Experts:
-    """Quantize every expert of a bank ("routed": E experts of width I; "shared": 1 of width I_shared)."""
+    """Quantize every expert of a bank ("routed": E experts of width I; "shared": 1 of width I_shared)
+    on the GPU and repack it into the MFMA tile layout."""
     count = wl.E if bank == "routed" else 1
     inter = wl.I if bank == "routed" else wl.I_shared
     h = wl.H
@@ -28,13 +29,19 @@ def build_bank(wl: synth.Workload, bank: str, device="cuda") -> ops.NvFp4Experts
     w2_s = torch.empty(count, h, inter // 16, dtype=torch.uint8, device=dev)
     gs13 = torch.empty(count, 2, dtype=torch.float32)
     gs2 = torch.empty(count, dtype=torch.float32)
+    c13 = torch.empty(2 * inter, h // 2, dtype=torch.uint8, device=dev)      # canonical staging
+    c13_s = torch.empty(2 * inter, h // 16, dtype=torch.uint8, device=dev)
+    c2 = torch.empty(h, inter // 2, dtype=torch.uint8, device=dev)
+    c2_s = torch.empty(h, inter // 16, dtype=torch.uint8, device=dev)
     for e in range(count):
         f13, f2 = synth.expert_fp32(wl, bank, e, dev)
         d = _dequant_scales(synth.expert_amax(f13, f2), wl.gscale_convention)
         d_dev = torch.from_numpy(d).to(dev)
-        ops.quantize(f13.view(2, inter, h), d_dev[0:2], packed=w13[e].view(2, inter, h // 2),
-                     scales=w13_s[e].view(2, inter, h // 16))
-        ops.quantize(f2, d_dev[2:3], packed=w2[e], scales=w2_s[e])
+        ops.quantize(f13.view(2, inter, h), d_dev[0:2], packed=c13.view(2, inter, h // 2),
+                     scales=c13_s.view(2, inter, h // 16))
+        ops.quantize(f2, d_dev[2:3], packed=c2, scales=c2_s)
+        ops.pack_tiles(c13, c13_s, tiled=w13[e], tiled_scales=w13_s[e])
+        ops.pack_tiles(c2, c2_s, tiled=w2[e], tiled_scales=w2_s[e])
         gs13[e] = torch.from_numpy(d[0:2])
         gs2[e] = float(d[2])
         del f13, f2

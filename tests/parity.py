@@ -23,15 +23,30 @@ MAX_ABS_FRAC = 2e-2
 
 
 def to_gpu_bank(bank, device="cuda") -> ops.NvFp4Experts:
+    """Upload canonical oracle-side experts and repack them on the GPU into the tile layout."""
     items = [bank[e] for e in range(len(bank))]
 
     def st(name, dtype):
         return torch.from_numpy(np.ascontiguousarray(np.stack([getattr(i, name) for i in items]))).to(device, dtype)
 
-    return ops.NvFp4Experts(st("w13", torch.uint8), st("w13_scale", torch.uint8),
-                            torch.tensor(np.stack([i.w13_gscale for i in items]), dtype=torch.float32, device=device),
-                            st("w2", torch.uint8), st("w2_scale", torch.uint8),
-                            torch.tensor([i.w2_gscale for i in items], dtype=torch.float32, device=device))
+    return ops.NvFp4Experts.from_canonical(
+        st("w13", torch.uint8), st("w13_scale", torch.uint8),
+        torch.tensor(np.stack([i.w13_gscale for i in items]), dtype=torch.float32, device=device),
+        st("w2", torch.uint8), st("w2_scale", torch.uint8),
+        torch.tensor([i.w2_gscale for i in items], dtype=torch.float32, device=device))
+
+
+def tile_np(packed: np.ndarray, scales: np.ndarray):
+    """Test-side statement of the MFMA tile layout: canonical [R, K/2] + [R, K/16] -> tiled bytes.
+
+    Tile (nb, c) = rows [16nb, 16nb+16) x K [128c, 128c+128); lane l = 16q + n holds row 16nb + n,
+    canonical bytes [64c + 16q, +16) and scale bytes [8c + 2q, +2).  Tiles in (nb, c) order.
+    """
+    r, half = packed.shape
+    k = half * 2
+    t = packed.reshape(r // 16, 16, k // 128, 4, 16).transpose(0, 2, 3, 1, 4).reshape(r, half)
+    ts = scales.reshape(r // 16, 16, k // 128, 4, 2).transpose(0, 2, 3, 1, 4).reshape(r, k // 16)
+    return np.ascontiguousarray(t), np.ascontiguousarray(ts)
 
 
 def bits_to_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:

@@ -60,12 +60,15 @@ def test_zero_tokens_is_a_no_op():
 # ----------------------------------------------------------------------------- tiny workload
 
 def _oracle_bank_equal(gbank, obank, experts):
+    """GPU-quantized, tile-packed bank bytes == the oracle quantizer's bytes put in the tile layout."""
     for e in experts:
         ow = obank[e]
-        assert np.array_equal(gbank.w13[e].cpu().numpy(), ow.w13), e
-        assert np.array_equal(gbank.w13_scale[e].cpu().numpy(), ow.w13_scale), e
-        assert np.array_equal(gbank.w2[e].cpu().numpy(), ow.w2), e
-        assert np.array_equal(gbank.w2_scale[e].cpu().numpy(), ow.w2_scale), e
+        t13, s13 = parity.tile_np(ow.w13, ow.w13_scale)
+        t2, s2 = parity.tile_np(ow.w2, ow.w2_scale)
+        assert np.array_equal(gbank.w13[e].cpu().numpy(), t13), e
+        assert np.array_equal(gbank.w13_scale[e].cpu().numpy(), s13), e
+        assert np.array_equal(gbank.w2[e].cpu().numpy(), t2), e
+        assert np.array_equal(gbank.w2_scale[e].cpu().numpy(), s2), e
         assert np.array_equal(gbank.w13_gscale[e].cpu().numpy(), ow.w13_gscale), e
         assert float(gbank.w2_gscale[e]) == ow.w2_gscale, e
 
@@ -103,20 +106,24 @@ def test_loader_ignores_activation_scales_and_converts_reciprocal_scales():
     glayer = build_layer(wl, DEV)
     x = synth.activations(wl, DEV)
     ref = ops.forward(glayer, x)
+    # a checkpoint in the canonical layout: the oracle quantizer's bytes (equal to the GPU quantizer's)
+    olayer = helpers.oracle_layer(wl, DEV)
     tensors = {"router.weight": glayer.w_router}
-    for pre, b in (("experts.", glayer.routed), ("shared_expert.", glayer.shared)):
-        tensors.update({pre + "w13": b.w13, pre + "w13_scale": b.w13_scale, pre + "w13_global_scale": b.w13_gscale,
-                        pre + "w2": b.w2, pre + "w2_scale": b.w2_scale, pre + "w2_global_scale": b.w2_gscale,
-                        pre + "w13_input_scale": torch.zeros(wl.E if pre == "experts." else 1, 2),
-                        pre + "w2_input_scale": torch.zeros(wl.E if pre == "experts." else 1)})
+    for pre, ob, n in (("experts.", olayer.routed, wl.E), ("shared_expert.", olayer.shared, 1)):
+        b = helpers.stack_bank(ob)
+        tensors.update({pre + "w13": torch.from_numpy(b.w13), pre + "w13_scale": torch.from_numpy(b.w13_scale),
+                        pre + "w13_global_scale": torch.from_numpy(b.w13_gscale),
+                        pre + "w2": torch.from_numpy(b.w2), pre + "w2_scale": torch.from_numpy(b.w2_scale),
+                        pre + "w2_global_scale": torch.from_numpy(b.w2_gscale),
+                        pre + "w13_input_scale": torch.zeros(n, 2), pre + "w2_input_scale": torch.zeros(n)})
     lay = ops.NvFp4MoELayer.from_tensors(tensors, wl.k, "modelopt", DEV)
     out = ops.forward(lay, x)
     assert torch.equal(out, ref)
     assert bool((out.float().abs().amax(dim=1) > 0).all())
     ct = dict(tensors)
-    for pre, b in (("experts.", glayer.routed), ("shared_expert.", glayer.shared)):
-        ct[pre + "w13_global_scale"] = torch.from_numpy(np.float32(1) / b.w13_gscale.cpu().numpy())
-        ct[pre + "w2_global_scale"] = torch.from_numpy(np.float32(1) / b.w2_gscale.cpu().numpy())
+    for pre in ("experts.", "shared_expert."):
+        ct[pre + "w13_global_scale"] = torch.from_numpy(np.float32(1) / tensors[pre + "w13_global_scale"].numpy())
+        ct[pre + "w2_global_scale"] = torch.from_numpy(np.float32(1) / tensors[pre + "w2_global_scale"].numpy())
     lay_ct = ops.NvFp4MoELayer.from_tensors(ct, wl.k, "compressed_tensors", DEV)
     want = (np.float32(1) / (np.float32(1) / glayer.routed.w13_gscale.cpu().numpy())).astype(np.float32)
     assert np.array_equal(lay_ct.routed.w13_gscale.cpu().numpy(), want)

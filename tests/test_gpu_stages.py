@@ -46,6 +46,18 @@ def test_quantizer_bit_exact_against_oracle():
             assert np.array_equal(p[t].cpu().numpy(), pr), name
 
 
+def test_pack_tiles_is_the_stated_permutation():
+    rng = np.random.default_rng(22)
+    for nt, r, k in [(1, 16, 128), (3, 48, 384), (2, 256, 1024)]:
+        p = rng.integers(0, 256, (nt, r, k // 2), dtype=np.uint8)
+        s = rng.integers(0, 256, (nt, r, k // 16), dtype=np.uint8)
+        tp, ts = ops.pack_tiles(torch.from_numpy(p).to(DEV), torch.from_numpy(s).to(DEV))
+        for t in range(nt):
+            wp, ws = parity.tile_np(p[t], s[t])
+            assert np.array_equal(tp[t].cpu().numpy(), wp)
+            assert np.array_equal(ts[t].cpu().numpy(), ws)
+
+
 # ----------------------------------------------------------------------------- route
 
 @pytest.mark.parametrize("T,H,E,k,bias", [(1, 128, 8, 1, False), (8, 4096, 320, 8, False), (16, 256, 8, 2, True),
