@@ -1,9 +1,74 @@
 // Device helpers shared by the route and permute kernels (header-only, inlined into each kernel).
+// Wave-wide reductions and scans use DPP row operations and readlane (no LDS round trips).
 #pragma once
 
 #include "common.h"
 
 namespace moe {
+
+// v_mov_b32_dpp with the given control; lanes outside row_mask (or without a source) get `old`.
+template <int CTRL, int ROW_MASK = 0xF, bool BOUND_ZERO = false>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, BOUND_ZERO);
+}
+
+constexpr int kDppQuad1032 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuad2301 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+constexpr int kDppRowShr1 = 0x111;
+
+// (value, index) pair order: larger value first, equal values -> lower index first.
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi) {
+  if (ov > v || (ov == v && oi < i)) {
+    v = ov;
+    i = oi;
+  }
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ void argmax_dpp_step(float& v, int& i) {
+  const float ov = __int_as_float(dpp_i<CTRL, ROW_MASK>(__float_as_int(v), __float_as_int(v)));
+  const int oi = dpp_i<CTRL, ROW_MASK>(i, i);
+  argmax_merge(v, i, ov, oi);
+}
+
+// Wave-wide argmax of (v, i); the result is returned to every lane.  The merge is associative and
+// commutative, so the reduction order does not change the result.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax_dpp_step<kDppQuad1032>(v, i);
+  argmax_dpp_step<kDppQuad2301>(v, i);
+  argmax_dpp_step<kDppRowHalfMirror>(v, i);
+  argmax_dpp_step<kDppRowMirror>(v, i);
+  argmax_dpp_step<kDppRowBcast15, 0xA>(v, i);
+  argmax_dpp_step<kDppRowBcast31, 0xC>(v, i);
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
+}
+
+// Wave-wide sum returned to every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += __int_as_float(dpp_i<kDppQuad1032>(__float_as_int(v), __float_as_int(v)));
+  v += __int_as_float(dpp_i<kDppQuad2301>(__float_as_int(v), __float_as_int(v)));
+  v += __int_as_float(dpp_i<kDppRowHalfMirror>(__float_as_int(v), __float_as_int(v)));
+  v += __int_as_float(dpp_i<kDppRowMirror>(__float_as_int(v), __float_as_int(v)));
+  v += __int_as_float(dpp_i<kDppRowBcast15, 0xA>(0, __float_as_int(v)));
+  v += __int_as_float(dpp_i<kDppRowBcast31, 0xC>(0, __float_as_int(v)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Inclusive wave scan (lane order) of integers.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += dpp_i<kDppRowShr1, 0xF, true>(0, x);
+  x += dpp_i<kDppRowShr1 + 1, 0xF, true>(0, x);   // row_shr:2
+  x += dpp_i<kDppRowShr1 + 3, 0xF, true>(0, x);   // row_shr:4
+  x += dpp_i<kDppRowShr1 + 7, 0xF, true>(0, x);   // row_shr:8
+  x += dpp_i<kDppRowBcast15, 0xA>(0, x);
+  x += dpp_i<kDppRowBcast31, 0xC>(0, x);
+  return x;
+}
 
 // Top-k of one token's logits by one wavefront (E <= 1024, k <= 64).  Returns, in lane j < k, the
 // j-th selected expert and its renormalised softmax weight.  Equal logits -> lower index first;
@@ -27,33 +92,18 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E,
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int e = lane + 64 * i;
-      if (!((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < bi))) {
-        bv = v[i];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    for (int i = 0; i < 16; ++i)
+      if (!((taken >> i) & 1u)) argmax_merge(bv, bi, v[i], lane + 64 * i);
+    wave_argmax(bv, bi);
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     if (lane == j) {
       my_val = bv;
       my_id = bi;
     }
   }
-  const float top = __shfl(my_val, 0);
+  const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), 0));
   const float z = (lane < k) ? expf(my_val - top) : 0.f;
-  float s = z;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  const float s = wave_sum(z);
   *out_id = my_id;
   *out_w = z / s;
 }
@@ -65,14 +115,9 @@ __device__ __forceinline__ int wave_exclusive_scan(const int* cnt, int* out, int
   for (int base = 0; base < E; base += 64) {
     const int e = base + lane;
     const int v = (e < E) ? cnt[e] : 0;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(incl, off);
-      if (lane >= off) incl += o;
-    }
+    const int incl = wave_inclusive_scan(v);
     if (e < E) out[e] = carry + incl - v;
-    carry += __shfl(incl, 63);
+    carry += __builtin_amdgcn_readlane(incl, 63);
   }
   return carry;
 }
@@ -93,7 +138,7 @@ __device__ __forceinline__ void wave_stable_scatter(const int32_t* ids, int s_be
     uint64_t peers = 0;
     while (rem) {
       const int leader = __ffsll((unsigned long long)rem) - 1;
-      const int le = __shfl(e, leader);
+      const int le = __builtin_amdgcn_readlane(e, leader);
       const uint64_t m = __ballot(valid && e == le);
       if (valid && e == le) peers = m;
       rem &= ~m;

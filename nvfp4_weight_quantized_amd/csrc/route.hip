@@ -32,6 +32,7 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
   const uint16_t* wrow = wr + (size_t)e * H;
   const uint16_t* xrow = x + (size_t)min(t, T - 1) * H;
   float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll 4
   for (int h0 = g * 8; h0 < H; h0 += G * 8) {
     const uint4 wv = *reinterpret_cast<const uint4*>(wrow + h0);
     const uint4 xv = *reinterpret_cast<const uint4*>(xrow + h0);
