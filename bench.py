@@ -25,6 +25,29 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 NVFP4_BYTES_PER_WEIGHT = 0.5625
 
+# HBM traffic of the gate/up GEMM per launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this
+# script (profiles/traffic_<workload>.md), scaled by what the same counters read for the 1 GiB copy
+# (FETCH x 2.0, WRITE x 1.0).  Valid only for the kernel source it was measured on: reported as null
+# once grouped_gemm.hip has changed.
+_GEMM_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "nvfp4_weight_quantized_amd", "csrc",
+                         "grouped_gemm.hip")
+_TRAFFIC = {  # workload: (sha256 of grouped_gemm.hip, bytes read, bytes written) per gate/up launch
+    "decode": ("1859ab0d9413e9f5a066ea825bdfb9189bdc91fea4299a9177b52226eeb136fd", 434.13e6, 0.22e6),
+    "prefill": ("1859ab0d9413e9f5a066ea825bdfb9189bdc91fea4299a9177b52226eeb136fd", 2754.75e6, 113.25e6),
+}
+
+
+def gate_up_traffic(workload: str):
+    import hashlib
+    rec = _TRAFFIC.get(workload)
+    if rec is None:
+        return None
+    with open(_GEMM_SRC, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec[0]:
+            return None
+    return rec[1] + rec[2]
+
+
 _DEFAULTS = {  # steps, warmup, weight copies cycled through (decode: defeat the 256 MB last-level cache)
     "tiny": (200, 20, 1), "decode": (200, 20, 4), "prefill": (20, 3, 1), "skewed": (20, 3, 1),
     "long_prefill": (5, 2, 1),
@@ -207,8 +230,10 @@ def main():
         roof = {"bound": "mfma", "achieved": gu_flops / (gate_up_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    roof["kernel"] = "grouped_gemm_kernel gate/up (S4)"
+    roof["traffic"] = gate_up_traffic(wl.name)
+    roof["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)"
+    roof["algorithmic_bytes"] = gu_bytes
+    roof["kernel"] = "gate/up grouped GEMM (S4)"
     roof["kernel_us"] = gate_up_ms * 1e3
 
     cpu = None

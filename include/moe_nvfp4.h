@@ -45,6 +45,8 @@
  * Conventions of every entry point:
  *   - Pointers are DEVICE pointers unless marked (host).  All buffers are owned by the caller; the
  *     library never allocates, frees or keeps a pointer after the call returns.
+ *   - Activation, weight, scale, output and workspace pointers must be 16-byte aligned (the
+ *     kernels use 16-byte vector accesses); a misaligned one gives MOE_ERR_INVALID_ARGUMENT.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Work is only enqueued: no host
  *     synchronisation, no device-to-host copy, so calls can be captured in a HIP graph.
  *   - Arguments are validated on the host before anything is enqueued; on error nothing is
@@ -205,10 +207,12 @@ moe_status_t moe_gscale_from_quant_scale(const float* q_host, float* d_host, int
  * reads.  Input: num_tensors tensors of [rows][cols] weights as canonical packed bytes
  * [rows][cols/2] and scale bytes [rows][cols/16] (rows % 16 == 0, cols % 128 == 0).  Output (same
  * sizes, out of place): tile t = (rows/16 block nb) * (cols/128) + (128-column chunk c) of each
- * tensor holds 1024 nibble bytes, where bytes [16l, 16l+16) (l = 16q + n) are canonical bytes
- * [64c + 16q, 64c + 16q + 16) of row 16nb + n, and 128 scale bytes, where bytes [2l, 2l+2) are
- * canonical scale bytes 8c + 2q and 8c + 2q + 1 of that row.  A fused gate/up tensor of one expert
- * is one [2I][H] tensor.  One wave then reads a whole tile with one contiguous 1 KB load.
+ * tensor holds 1024 nibble bytes and 128 scale bytes.  With l = 16q + n (q, n in 0..3, 0..15) and
+ * j in 0..3, nibble bytes [16l + 4j, 16l + 4j + 4) are canonical bytes [64c + 16j + 4q, +4) of row
+ * 16nb + n (the elements [128c + 32j + 8q, +8)), and scale bytes [8n, 8n + 8) are that row's
+ * canonical scale bytes 8c + {0, 2, 4, 6, 1, 3, 5, 7}.  A fused gate/up tensor of one expert is one
+ * [2I][H] tensor.  One wave then reads a whole tile with one contiguous 1 KB load, each lane
+ * holding the operand of four 16x16x32 MFMA steps.
  * Source: the checkpoint-preparation step that swizzles weights into a kernel's MMA tile layout
  * ("Serving Solar Open 2 on DGX Spark", "Supporting real NVFP4 checkpoints"). */
 moe_status_t moe_nvfp4_pack_tiles(const uint8_t* packed, const uint8_t* scales, int32_t num_tensors, int32_t rows,

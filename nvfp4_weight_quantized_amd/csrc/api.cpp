@@ -33,10 +33,14 @@ moe_status_t check_arch(const char* arch) {
   return ok ? MOE_OK : MOE_ERR_UNSUPPORTED_DEVICE;
 }
 
+// The kernels move weights, activations and outputs with 16-byte vector accesses.
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 bool valid_bank(const moe_nvfp4_experts_t& b, int32_t H, int32_t expected_experts) {
   if (b.num_experts != expected_experts || b.hidden != H) return false;
   if (b.inter <= 0 || b.inter % 128 != 0) return false;
-  return b.w13 && b.w13_scale && b.w13_gscale && b.w2 && b.w2_scale && b.w2_gscale;
+  if (!(b.w13 && b.w13_scale && b.w13_gscale && b.w2 && b.w2_scale && b.w2_gscale)) return false;
+  return al16(b.w13) && al16(b.w13_scale) && al16(b.w2) && al16(b.w2_scale);
 }
 
 bool valid_route_dims(int32_t T, int32_t H, int32_t E, int32_t k) {
@@ -106,7 +110,7 @@ moe_status_t moe_route(const uint16_t* x, const uint16_t* w_router, const float*
   if (!given && !valid_route_dims(T, H, E, k)) return MOE_ERR_INVALID_ARGUMENT;
   if (T == 0) return MOE_OK;
   if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARGUMENT;
-  if (!given && (!x || !w_router)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!given && (!x || !w_router || !al16(x) || !al16(w_router))) return MOE_ERR_INVALID_ARGUMENT;
   if (moe_status_t st = check_arch(nullptr)) return st;
   return moe::launch_route(x, w_router, router_bias, T, H, E, k, given, logits, topk_ids, topk_w,
                            static_cast<hipStream_t>(stream));
@@ -144,7 +148,7 @@ moe_status_t moe_nvfp4_grouped_gemm(int32_t stage, const moe_nvfp4_experts_t* w,
   if (M_total < 0 || row_divisor < 1) return MOE_ERR_INVALID_ARGUMENT;
   if (stage == MOE_GEMM_DOWN && row_index) return MOE_ERR_INVALID_ARGUMENT;
   if (M_total == 0) return MOE_OK;
-  if (!a || !expert_offsets || !out) return MOE_ERR_INVALID_ARGUMENT;
+  if (!a || !expert_offsets || !out || !al16(a) || !al16(out)) return MOE_ERR_INVALID_ARGUMENT;
   if (moe_status_t st = check_arch(nullptr)) return st;
   GemmProblem p{};
   p.stage = stage;
@@ -168,6 +172,7 @@ moe_status_t moe_combine(const uint16_t* y_rows, const int32_t* slot_to_row, con
   if (T < 0 || k < 1 || k > 1024 || H <= 0 || H % 8 != 0) return MOE_ERR_INVALID_ARGUMENT;
   if (T == 0) return MOE_OK;
   if (!y_rows || !slot_to_row || !topk_w || !out) return MOE_ERR_INVALID_ARGUMENT;
+  if (!al16(y_rows) || !al16(out) || (y_shared && !al16(y_shared))) return MOE_ERR_INVALID_ARGUMENT;
   if (moe_status_t st = check_arch(nullptr)) return st;
   return moe::launch_combine(y_rows, slot_to_row, topk_w, y_shared, T, k, H, out, static_cast<hipStream_t>(stream));
 }
@@ -182,7 +187,7 @@ moe_status_t moe_validate_forward(const moe_nvfp4_layer_t* layer, int32_t T, siz
   if (!layer) return MOE_ERR_INVALID_ARGUMENT;
   const int32_t H = layer->hidden, E = layer->num_experts, k = layer->top_k;
   if (!valid_route_dims(T, H, E, k)) return MOE_ERR_INVALID_ARGUMENT;
-  if (!layer->w_router) return MOE_ERR_INVALID_ARGUMENT;
+  if (!layer->w_router || !al16(layer->w_router)) return MOE_ERR_INVALID_ARGUMENT;
   if (!valid_bank(layer->routed, H, E)) return MOE_ERR_INVALID_ARGUMENT;
   const bool has_shared = layer->shared.num_experts != 0;
   if (has_shared && !valid_bank(layer->shared, H, 1)) return MOE_ERR_INVALID_ARGUMENT;
@@ -197,7 +202,7 @@ moe_status_t moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x
                                void* stream_) {
   if (moe_status_t st = moe_validate_forward(layer, T, workspace_bytes, nullptr)) return st;
   if (T == 0) return MOE_OK;
-  if (!x || !out || !workspace) return MOE_ERR_INVALID_ARGUMENT;
+  if (!x || !out || !workspace || !al16(x) || !al16(out) || !al16(workspace)) return MOE_ERR_INVALID_ARGUMENT;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   const int32_t H = layer->hidden, E = layer->num_experts, k = layer->top_k;
   const bool has_shared = layer->shared.num_experts != 0;
@@ -333,6 +338,7 @@ moe_status_t moe_nvfp4_pack_tiles(const uint8_t* packed, const uint8_t* scales, 
   if (num_tensors < 0 || rows < 0 || cols < 0 || rows % 16 != 0 || cols % 128 != 0) return MOE_ERR_INVALID_ARGUMENT;
   if ((int64_t)num_tensors * rows * cols == 0) return MOE_OK;
   if (!packed || !scales || !tiled || !tiled_scales) return MOE_ERR_INVALID_ARGUMENT;
+  if (!al16(packed) || !al16(scales) || !al16(tiled) || !al16(tiled_scales)) return MOE_ERR_INVALID_ARGUMENT;
   if (moe_status_t st = check_arch(nullptr)) return st;
   return moe::launch_pack_tiles(packed, scales, num_tensors, rows, cols, tiled, tiled_scales,
                                 static_cast<hipStream_t>(stream));
@@ -343,6 +349,7 @@ moe_status_t moe_nvfp4_quantize(const float* w, int32_t num_tensors, int32_t row
   if (num_tensors < 0 || rows < 0 || cols < 0 || cols % 16 != 0) return MOE_ERR_INVALID_ARGUMENT;
   if ((int64_t)num_tensors * rows * cols == 0) return MOE_OK;
   if (!w || !gscale || !packed || !scales) return MOE_ERR_INVALID_ARGUMENT;
+  if (!al16(w) || !al16(packed)) return MOE_ERR_INVALID_ARGUMENT;
   if (moe_status_t st = check_arch(nullptr)) return st;
   return moe::launch_quantize(w, num_tensors, rows, cols, gscale, packed, scales, static_cast<hipStream_t>(stream));
 }

@@ -9,14 +9,15 @@
 // CDNA4 design:
 //  * Weights are read in the MFMA tile layout (see layout.hip): one 16-row x 128-K tile is 1 KB of
 //    nibbles in lane order plus 128 B of scales, so every weight load of a wave is one contiguous
-//    1 KB (or 128 B) request.  Lane l = 16q + n of a 16x16x32 B fragment owns row n, K range
-//    [32q, 32q+32) of each 128-K tile: 16 bytes of nibbles and 2 scale bytes.
+//    1 KB request.  Lane l = 16q + n owns weight row n; word j of its 16 bytes holds the 8
+//    elements K [32j + 8q, +8) of MFMA step j, and byte j of its scale dword their E4M3 scale.
 //  * Those bytes are dequantized in registers straight into the bf16 MFMA operand:
 //    v_cvt_scalef32_pk_f32_fp4 (scale 1) gives the E2M1 values, one fp32 multiply applies the
 //    block scale and v_cvt_pk_bf16_f32 packs the result.  element * block scale has at most 6
 //    significant bits, so the bf16 operand is exact.
-//  * The MFMA reduction order over K is permuted consistently for A and B (MFMA step j of a
-//    128-K tile uses K 32q + 8j .. 32q + 8j + 7 in lane group q); the sum is over the same products.
+//  * The weights are the MFMA's first operand and the activations its second, so the 16x16
+//    accumulator block is (weight row, token row): lane l = 16q + n holds token row n and four
+//    consecutive output columns 4q..4q+3, stored as one 8-byte write.
 //  * A (activation rows, bf16) is gathered row by row through the sorted slot list straight from
 //    the token matrix -- no permuted copy -- and staged in LDS per K chunk.
 //  * fp32 accumulation; the per-tensor global scales multiply the accumulators in the epilogue;
@@ -59,11 +60,36 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t q, float s) {
   return r;
 }
 
-// B operand of MFMA step j (0..3) of one 128-K tile from the lane's 16 nibble bytes and 2 scale bytes.
-__device__ __forceinline__ bf16x8 b_operand(const uint4& w, uint32_t sc, int j) {
+// E4M3 block scale held in byte j (0..3) of a scale dword (the byte select must fold to a constant).
+__device__ __forceinline__ float e4m3_byte(uint32_t sc, int j) {
+  switch (j) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8((int)sc, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8((int)sc, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8((int)sc, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8((int)sc, 3);
+  }
+}
+
+// Weight operand of MFMA step j (0..3) of one 128-K tile: word j of the lane's 16 nibble bytes
+// times byte j of its scale dword.
+__device__ __forceinline__ bf16x8 w_operand(const uint4& w, uint32_t sc, int j) {
   const uint32_t words[4] = {w.x, w.y, w.z, w.w};
-  const float s = (j < 2) ? __builtin_amdgcn_cvt_f32_fp8((int)sc, 0) : __builtin_amdgcn_cvt_f32_fp8((int)sc, 1);
-  return dequant8(words[j], s);
+  return dequant8(words[j], e4m3_byte(sc, j));
+}
+
+// acc[weight row][token row] += W(16x32) . X(16x32)^T
+__device__ __forceinline__ f32x4 mfma(const bf16x8& w, const bf16x8& x, const f32x4& acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, x, acc, 0, 0, 0);
+}
+
+// Byte offsets, within an expert's tiles, of the 16 nibble bytes and the scale dword of this lane.
+__device__ __forceinline__ int w_lane_offset(int lane) { return 16 * lane; }
+__device__ __forceinline__ int s_lane_offset(int lane) { return 8 * (lane & 15) + 4 * ((lane >> 4) >> 1); }
+
+__device__ __forceinline__ void store_bf16x4(uint16_t* dst, float a, float b, float c, float d) {
+  const uint32_t lo = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  const uint32_t hi = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
+  *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
 }
 
 // Tile `mtile` (numbered over the groups in order, then the extra group).  Wave 0 only.
@@ -152,6 +178,8 @@ __device__ __forceinline__ int frag_row_block(int f, int ntile, int wave, int N)
 }
 
 // Epilogue: scale the accumulators by the global scale(s), SiLU(gate)*up for gate/up, store bf16.
+// acc[i][f] holds, in lane l = 16q + n, output row 16i + n and the four columns 4q..4q+3 of
+// fragment f's 16 columns.
 template <int MI, int NB, bool GATE_UP, int BN, int COLS_PER_WAVE>
 __device__ __forceinline__ void epilogue(const GemmProblem& p, const GemmBank& bank, const TileInfo& ti, int ntile,
                                          const f32x4 (&acc)[MI][NB]) {
@@ -159,36 +187,33 @@ __device__ __forceinline__ void epilogue(const GemmProblem& p, const GemmBank& b
   const int wave = threadIdx.x >> 6;
   const int q = lane >> 4, nl = lane & 15;
   const float* gs = bank.gs + (size_t)ti.group * bank.gs_per_expert;
+  const int col0 = ntile * BN + wave * COLS_PER_WAVE + 4 * q;
   if (GATE_UP) {
     const float dg = gs[0], du = gs[1];
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i) {
+      const int row = 16 * i + nl;
+      if (row >= ti.rows) continue;
+      uint16_t* orow = p.out + (size_t)(ti.row0 + row) * p.N + col0;
 #pragma unroll
       for (int f = 0; f < NB / 2; ++f) {
-        const int col = ntile * BN + wave * COLS_PER_WAVE + 16 * f + nl;
+        float h[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * i + 4 * q + r;
-          if (row < ti.rows) {
-            const float g = acc[i][f][r] * dg;
-            const float u = acc[i][f + NB / 2][r] * du;
-            p.out[(size_t)(ti.row0 + row) * p.N + col] = f32_to_bf16(silu(g) * u);
-          }
-        }
+        for (int r = 0; r < 4; ++r) h[r] = silu(acc[i][f][r] * dg) * (acc[i][f + NB / 2][r] * du);
+        store_bf16x4(orow + 16 * f, h[0], h[1], h[2], h[3]);
       }
+    }
   } else {
     const float dd = gs[0];
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i) {
+      const int row = 16 * i + nl;
+      if (row >= ti.rows) continue;
+      uint16_t* orow = p.out + (size_t)(ti.row0 + row) * p.N + col0;
 #pragma unroll
-      for (int f = 0; f < NB; ++f) {
-        const int col = ntile * BN + wave * COLS_PER_WAVE + 16 * f + nl;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * i + 4 * q + r;
-          if (row < ti.rows) p.out[(size_t)(ti.row0 + row) * p.N + col] = f32_to_bf16(acc[i][f][r] * dd);
-        }
-      }
+      for (int f = 0; f < NB; ++f)
+        store_bf16x4(orow + 16 * f, acc[i][f][0] * dd, acc[i][f][1] * dd, acc[i][f][2] * dd, acc[i][f][3] * dd);
+    }
   }
 }
 
@@ -251,8 +276,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmProblem p) {
   const int q = lane >> 4;
   const int nl = lane & 15;
   const size_t rows_per_expert = GATE_UP ? 2 * (size_t)p.N : (size_t)p.N;
-  const uint8_t* wexp = bank.w + (size_t)ti.group * rows_per_expert * (size_t)(K / 2) + 16 * lane;
-  const uint8_t* sexp = bank.ws + (size_t)ti.group * rows_per_expert * (size_t)(K / 16) + 2 * lane;
+  const uint8_t* wexp = bank.w + (size_t)ti.group * rows_per_expert * (size_t)(K / 2) + w_lane_offset(lane);
+  const uint8_t* sexp = bank.ws + (size_t)ti.group * rows_per_expert * (size_t)(K / 16) + s_lane_offset(lane);
   const uint8_t* wptr[NB];
   const uint8_t* sptr[NB];
 #pragma unroll
@@ -281,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmProblem p) {
       for (int v = 0; v < NS; ++v) {
         const size_t t = (size_t)c * NS + v;
         b_next[f][v] = *reinterpret_cast<const uint4*>(wptr[f] + t * 1024);
-        s_next[f][v] = *reinterpret_cast<const uint16_t*>(sptr[f] + t * 128);
+        s_next[f][v] = *reinterpret_cast<const uint32_t*>(sptr[f] + t * 128);
       }
   };
   load_chunk(0);
@@ -307,15 +332,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmProblem p) {
     for (int v = 0; v < NS; ++v)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        bf16x8 bfrag[NB];
+        bf16x8 wfrag[NB];
 #pragma unroll
-        for (int f = 0; f < NB; ++f) bfrag[f] = b_operand(bq[f][v], sc[f][v], j);
+        for (int f = 0; f < NB; ++f) wfrag[f] = w_operand(bq[f][v], sc[f][v], j);
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
-          const bf16x8 afrag = *reinterpret_cast<const bf16x8*>(&As[16 * i + nl][128 * v + 32 * q + 8 * j]);
+          const bf16x8 xfrag = *reinterpret_cast<const bf16x8*>(&As[16 * i + nl][128 * v + 32 * j + 8 * q]);
 #pragma unroll
-          for (int f = 0; f < NB; ++f)
-            acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag[f], acc[i][f], 0, 0, 0);
+          for (int f = 0; f < NB; ++f) acc[i][f] = mfma(wfrag[f], xfrag, acc[i][f]);
         }
       }
   }
@@ -324,30 +348,60 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmProblem p) {
 
 // ------------------------------------------------------------------------------------------
 // Tall tiles (many rows per expert): 128-row workgroup tiles, K chunk 128.
-//  * A chunks go global -> LDS directly (global_load_lds, 16 bytes per lane; lane i of a wave
-//    lands at LDS base + 16*i), double-buffered, one barrier per chunk.  Rows are 256 bytes with
-//    the 16-byte slot index XOR-swizzled by (row & 15), so the fragment reads of 16 rows at one
-//    K offset hit 16 different bank groups.
-//  * B tiles in registers, prefetched one chunk ahead.
-//  * 16-row blocks past the group's last row are skipped (no LDS reads, no MFMA).
+//  * A chunks go global -> LDS directly (global_load_lds_dwordx4, 16 bytes per lane; lane i of a
+//    wave lands at LDS address M0 + 16*i), double-buffered, one barrier per chunk.  A chunk is
+//    stored as 32 MFMA fragments of 1 KB: fragment (i, j) holds, at 16*l for lane l = 16q + n, row
+//    16i + n and K [32j + 8q, +8) of the chunk.  Every fragment read is then one contiguous 1 KB
+//    ds_read_b128 (free of bank conflicts), and every direct load reads 64 contiguous bytes from
+//    each of 16 rows.
+//  * The direct loads are issued from inline assembly and waited for explicitly (vmcnt(0) and a
+//    barrier at the end of each chunk).  Issued through the compiler builtin, the compiler cannot
+//    tell that the loads in flight into one buffer leave the other alone and drains them before
+//    every LDS read, which serialises loading and computing.
+//  * B tiles in registers, prefetched one chunk ahead; the end-of-chunk wait names the prefetch
+//    registers, so the compiler waits for them there and nowhere earlier.
+//  * The number of 16-row blocks holding real rows is a template parameter of the main loop (one
+//    instantiation per count): blocks past the group's last row cost nothing and the loop body
+//    has no per-block branches.
 //  * Tile order is XCD-aware: workgroup b runs on XCD b % 8; each XCD walks a contiguous range of
 //    (m-tile, n-tile) pairs, n fastest, so the A rows of an m-tile are reused from that XCD's L2.
-//  * At most 256 registers per lane so that two workgroups share a CU.
+//  * WAVES = 8 (128 x 512-weight-row tiles, one workgroup per CU) where the output width allows,
+//    else WAVES = 4 (two workgroups per CU); either way two waves share each SIMD, at most 256
+//    registers per lane.
 constexpr int kTallBK = 128;
 constexpr int kTallRows = 128;
 constexpr int kXcds = 8;
 
-template <int NB, bool GATE_UP>
-__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_tall_kernel(GemmProblem p) {
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
+// 16 bytes per lane from global memory to LDS: lane i's bytes land at lds_addr + 16*i.
+// lds_addr must be wave-uniform.  Completion is tracked by vmcnt only.
+// The global address is a wave-uniform base plus a 32-bit per-lane byte offset.
+__device__ __forceinline__ void direct_load16(const void* base, uint32_t offset, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(offset), "s"(base), "s"(lds_addr)
+      : "memory", "m0");
+}
+
+template <int NB, bool GATE_UP, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kernel(GemmProblem p) {
   constexpr int MI = kTallRows / 16;
   constexpr int BM = kTallRows;
   constexpr int BK = kTallBK;
+  constexpr int STEPS = BK / 32;                       // MFMA k-steps per chunk
   constexpr int COLS_PER_WAVE = GATE_UP ? 16 * (NB / 2) : 16 * NB;
-  constexpr int BN = 4 * COLS_PER_WAVE;
-  constexpr int ROW_BYTES = BK * 2;                    // 256
-  constexpr int BUF_BYTES = BM * ROW_BYTES;            // 32 KB
-  constexpr int A_ITERS = BUF_BYTES / (kThreads * 16); // 8 direct loads per thread per chunk
-  __shared__ __attribute__((aligned(1024))) uint8_t As[2][BUF_BYTES];
+  constexpr int BN = WAVES * COLS_PER_WAVE;
+  constexpr int FRAGS = MI * STEPS;                    // 1 KB A fragments per chunk
+  constexpr int BUF_BYTES = FRAGS * 1024;              // 32 KB
+  constexpr int A_ITERS = FRAGS / WAVES;               // fragments (direct loads) per wave per chunk
+  static_assert(STEPS == 4 && FRAGS % WAVES == 0, "chunk layout");
+  __shared__ __attribute__((aligned(1024))) uint8_t As[2 * BUF_BYTES];
   __shared__ uint32_t s_aoff[BM];
   __shared__ TileInfo tile;
   __shared__ int tile_ok;
@@ -355,7 +409,9 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_tall_kernel(GemmProb
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4;
+  const int nl = lane & 15;
   const int NT = p.N / BN;
 
   if (wave == 0) {
@@ -372,32 +428,42 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_tall_kernel(GemmProb
   }
   __syncthreads();
   if (!tile_ok) return;
-  const TileInfo ti = tile;
-  const int ntile = tile_n;
+  TileInfo ti;   // wave-uniform copies (scalar registers)
+  ti.group = __builtin_amdgcn_readfirstlane(tile.group);
+  ti.row0 = __builtin_amdgcn_readfirstlane(tile.row0);
+  ti.rows = __builtin_amdgcn_readfirstlane(tile.rows);
+  ti.a_row0 = __builtin_amdgcn_readfirstlane(tile.a_row0);
+  ti.extra = __builtin_amdgcn_readfirstlane(tile.extra);
+  const int ntile = __builtin_amdgcn_readfirstlane(tile_n);
   const GemmBank& bank = ti.extra ? p.extra : p.bank;
   const int K = p.K;
   const int nK = K / BK;
-  const int row_blocks = (ti.rows + 15) / 16;          // 16-row MFMA blocks holding real rows
 
-  // A rows: element offset of each of the tile's rows (rows past the group repeat a valid row)
-  const uint16_t* abase = ti.extra ? p.a_extra : p.a;
+  // A rows: byte offset of each of the tile's rows (rows past the group repeat a valid row)
+  const uint8_t* abase = reinterpret_cast<const uint8_t*>(ti.extra ? p.a_extra : p.a);
   if (tid < BM) {
     const int R = ti.a_row0 + min(tid, ti.rows - 1);
     const int src = (!ti.extra && p.row_index) ? p.row_index[R] / p.row_divisor : R;
-    s_aoff[tid] = (uint32_t)src * (uint32_t)K;
+    s_aoff[tid] = (uint32_t)src * (uint32_t)K * 2u;
   }
   __syncthreads();
-  // Lane `lane` of wave `wave`, direct load `it`, fills LDS slot (lane & 15) of row
-  // r = 4*(4*it + wave) + lane/16 with the row's 16-byte chunk (lane & 15) ^ (r & 15).
-  const uint32_t acol = (uint32_t)(((lane & 15) ^ ((4 * wave + (lane >> 4)) & 15)) * 8);
+  // Direct load `it` of wave `wave` fills fragment F = wave + WAVES*it = (i = F/4, j = F%4): this
+  // lane fetches row 16*i + nl at chunk column 32*j + 8*q (byte offsets from the chunk's first column).
+  uint32_t aoff[A_ITERS];
+#pragma unroll
+  for (int it = 0; it < A_ITERS; ++it) {
+    const int F = wave + WAVES * it;
+    aoff[it] = s_aoff[16 * (F >> 2) + nl] + (uint32_t)(64 * (F & 3) + 16 * q);
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)As;
 
-  // B tiles this lane reads
-  const int q = lane >> 4;
-  const int nl = lane & 15;
+  // B tiles of this wave: wave-uniform tile bases plus a per-lane offset
   const int ktiles = K / 128;
   const size_t rows_per_expert = GATE_UP ? 2 * (size_t)p.N : (size_t)p.N;
-  const uint8_t* wexp = bank.w + (size_t)ti.group * rows_per_expert * (size_t)(K / 2) + 16 * lane;
-  const uint8_t* sexp = bank.ws + (size_t)ti.group * rows_per_expert * (size_t)(K / 16) + 2 * lane;
+  const uint8_t* wexp = bank.w + (size_t)ti.group * rows_per_expert * (size_t)(K / 2);
+  const uint8_t* sexp = bank.ws + (size_t)ti.group * rows_per_expert * (size_t)(K / 16);
+  const uint32_t w_lane = (uint32_t)w_lane_offset(lane);
+  const uint32_t s_lane = (uint32_t)s_lane_offset(lane);
   uint32_t tile0[NB];
 #pragma unroll
   for (int f = 0; f < NB; ++f)
@@ -409,71 +475,85 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_tall_kernel(GemmProb
 #pragma unroll
     for (int f = 0; f < NB; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto issue_a = [&](int c, int buf) {
-#pragma unroll
-    for (int it = 0; it < A_ITERS; ++it) {
-      const uint32_t off = s_aoff[4 * (4 * it + wave) + (lane >> 4)];
-      __builtin_amdgcn_global_load_lds((const void*)(abase + off + (uint32_t)c * BK + acol),
-                                       (__attribute__((address_space(3))) void*)(&As[buf][(4 * it + wave) * 1024]),
-                                       16, 0, 0);
-    }
-  };
   uint4 bn[NB];
   uint32_t sn[NB];
   auto load_b = [&](int c) {
 #pragma unroll
     for (int f = 0; f < NB; ++f) {
       const size_t t = (size_t)tile0[f] + (size_t)c;
-      bn[f] = *reinterpret_cast<const uint4*>(wexp + t * 1024);
-      sn[f] = *reinterpret_cast<const uint16_t*>(sexp + t * 128);
+      bn[f] = *reinterpret_cast<const uint4*>(wexp + t * 1024 + w_lane);
+      sn[f] = *reinterpret_cast<const uint32_t*>(sexp + t * 128 + s_lane);
     }
   };
-
-  issue_a(0, 0);
-  load_b(0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  for (int c = 0; c < nK; ++c) {
-    uint4 bq[NB];
-    uint32_t sc[NB];
+  auto issue_a = [&](int c, int buf) {
+    const uint8_t* src = abase + (size_t)c * (BK * 2);
 #pragma unroll
-    for (int f = 0; f < NB; ++f) {
-      bq[f] = bn[f];
-      sc[f] = sn[f];
-    }
-    if (c + 1 < nK) {
-      issue_a(c + 1, (c + 1) & 1);
-      load_b(c + 1);
-    }
-    const uint8_t* abuf = As[c & 1];
+    for (int it = 0; it < A_ITERS; ++it)
+      direct_load16(src, aoff[it], lds0 + (uint32_t)(buf * BUF_BYTES + (wave + WAVES * it) * 1024));
+  };
+  // Every load of the chunk in flight (direct A loads and the B prefetch) has landed; the B
+  // registers are operands so that the compiler places its own wait for them here.
+  auto wait_chunk = [&]() {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf16x8 bfrag[NB];
-#pragma unroll
-      for (int f = 0; f < NB; ++f) bfrag[f] = b_operand(bq[f], sc[f], j);
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        if (i < row_blocks) {
-          const int row = 16 * i + nl;
-          const bf16x8 afrag =
-              *reinterpret_cast<const bf16x8*>(abuf + row * ROW_BYTES + 16 * ((4 * q + j) ^ nl));
-#pragma unroll
-          for (int f = 0; f < NB; ++f)
-            acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag[f], acc[i][f], 0, 0, 0);
-        }
-      }
-    }
-    // the next A chunk (and B tile) must have landed before the buffer flips
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    for (int f = 0; f < NB; ++f)
+      asm volatile("s_waitcnt vmcnt(0)" : "+v"(bn[f].x), "+v"(bn[f].y), "+v"(bn[f].z), "+v"(bn[f].w), "+v"(sn[f])
+                   :
+                   : "memory");
+  };
+  // The main loop, for RB 16-row blocks of real rows.
+  auto run = [&](auto rb_const) {
+    constexpr int RB = decltype(rb_const)::value;
+    issue_a(0, 0);
+    load_b(0);
+    wait_chunk();
     __syncthreads();
+    for (int c = 0; c < nK; ++c) {
+      uint4 bq[NB];
+      uint32_t sc[NB];
+#pragma unroll
+      for (int f = 0; f < NB; ++f) {
+        bq[f] = bn[f];
+        sc[f] = sn[f];
+      }
+      if (c + 1 < nK) {
+        issue_a(c + 1, (c + 1) & 1);
+        load_b(c + 1);
+      }
+      const uint8_t* abuf = As + (c & 1) * BUF_BYTES + 16 * lane;
+#pragma unroll
+      for (int j = 0; j < STEPS; ++j) {
+        bf16x8 wfrag[NB];
+#pragma unroll
+        for (int f = 0; f < NB; ++f) wfrag[f] = w_operand(bq[f], sc[f], j);
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          const bf16x8 xfrag = *reinterpret_cast<const bf16x8*>(abuf + (STEPS * i + j) * 1024);
+#pragma unroll
+          for (int f = 0; f < NB; ++f) acc[i][f] = mfma(wfrag[f], xfrag, acc[i][f]);
+        }
+        // keep each step's LDS reads within the step (bounds the live fragment registers)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      wait_chunk();
+      __syncthreads();
+    }
+  };
+  switch ((ti.rows + 15) / 16) {
+    case 1: run(IntC<1>{}); break;
+    case 2: run(IntC<2>{}); break;
+    case 3: run(IntC<3>{}); break;
+    case 4: run(IntC<4>{}); break;
+    case 5: run(IntC<5>{}); break;
+    case 6: run(IntC<6>{}); break;
+    case 7: run(IntC<7>{}); break;
+    default: run(IntC<8>{}); break;
   }
   epilogue<MI, NB, GATE_UP, BN, COLS_PER_WAVE>(p, bank, ti, ntile, acc);
 }
 
-template <int NB, bool GATE_UP>
+template <int NB, bool GATE_UP, int WAVES>
 moe_status_t launch_tall(const GemmProblem& p, hipStream_t stream) {
-  constexpr int BN = GATE_UP ? 4 * 16 * (NB / 2) : 4 * 16 * NB;
+  constexpr int BN = WAVES * (GATE_UP ? 16 * (NB / 2) : 16 * NB);
   if (p.N % BN != 0 || p.K % kTallBK != 0) return MOE_ERR_INVALID_ARGUMENT;
   const int NT = p.N / BN;
   const long long mt = (p.G > 0 ? (long long)std::min(p.G, p.M) + p.M / kTallRows : 0LL) +
@@ -482,7 +562,8 @@ moe_status_t launch_tall(const GemmProblem& p, hipStream_t stream) {
   if (grid == 0) return MOE_OK;
   grid = (grid + kXcds - 1) / kXcds * kXcds;
   if (grid > 0x7FFFFFFFLL) return MOE_ERR_INVALID_ARGUMENT;
-  hipLaunchKernelGGL((grouped_gemm_tall_kernel<NB, GATE_UP>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((grouped_gemm_tall_kernel<NB, GATE_UP, WAVES>), dim3((unsigned)grid), dim3(64 * WAVES), 0, stream,
+                     p);
   return launch_status();
 }
 
@@ -521,12 +602,14 @@ moe_status_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
   if (gate_up) {
     if (avg <= 16) return launch_small<true>(p, stream);
     if (avg <= 64) return launch_cfg<4, 4, 128, true>(p, stream);
-    return launch_tall<4, true>(p, stream);
+    // eight waves (one workgroup per CU) where the width allows: half the A traffic per MFMA
+    return (p.N % 256 == 0) ? launch_tall<4, true, 8>(p, stream) : launch_tall<4, true, 4>(p, stream);
   }
   const bool wide = (p.N % 256) == 0;
   if (avg <= 16) return launch_small<false>(p, stream);
   if (avg <= 64) return wide ? launch_cfg<4, 4, 128, false>(p, stream) : launch_cfg<4, 2, 128, false>(p, stream);
-  return wide ? launch_tall<4, false>(p, stream) : launch_tall<2, false>(p, stream);
+  if (p.N % 512 == 0) return launch_tall<4, false, 8>(p, stream);
+  return wide ? launch_tall<4, false, 4>(p, stream) : launch_tall<2, false, 4>(p, stream);
 }
 
 }  // namespace moe

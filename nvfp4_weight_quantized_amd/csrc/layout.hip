@@ -3,17 +3,21 @@
 // The pages' fused-MoE kernels also swizzle checkpoint weights once into their MMA tile layout
 // ("Serving Solar Open 2 on DGX Spark", "Supporting real NVFP4 checkpoints"); this is the CDNA4
 // equivalent.  A tensor [rows][cols] (rows % 16 == 0, cols % 128 == 0) becomes a sequence of tiles
-// t = (rows/16 block nb) * (cols/128) + (128-column chunk c); tile t holds
-//   nibbles: 1024 bytes, lane l = 16*q + n at bytes [16*l, 16*l + 16) = row 16*nb + n,
-//            canonical bytes [64*c + 16*q, 64*c + 16*q + 16) (K range [128c + 32q, 128c + 32q + 32))
-//   scales:  128 bytes, lane l at bytes [2*l, 2*l + 2) = row 16*nb + n, scale bytes 8*c + 2*q, +1.
-// A wave reading one tile therefore issues one contiguous 1 KB load and one contiguous 128 B load.
+// t = (rows/16 block nb) * (cols/128) + (128-column chunk c).  In tile t, lane l = 16*q + n of a
+// 16x16x32 bf16 MFMA operand owns row r = 16*nb + n:
+//   nibbles: 1024 bytes; bytes [16*l + 4*j, 16*l + 4*j + 4) (j = 0..3, the MFMA k-step) are the
+//            canonical bytes [64*c + 16*j + 4*q, +4) of row r, i.e. K [128c + 32j + 8q, +8);
+//   scales:  128 bytes; bytes [8*n, 8*n + 8) are row r's eight scale bytes of the chunk in the
+//            order g0 g2 g4 g6 g1 g3 g5 g7 (g = canonical scale byte 8*c + g), so the dword at
+//            8*n + 4*(q >> 1) holds, in byte j, the scale of K [128c + 32j + 8q, +8).
+// A wave therefore reads a whole tile with one contiguous 1 KB load (and 128 B of scales).
 // The repack is a pure byte permutation (same total size as the canonical layout).
 #include "common.h"
 
 namespace moe {
 namespace {
 
+// One thread per (tile, lane): 16 nibble bytes; the first 16 lanes of a tile also move 8 scale bytes.
 __global__ __launch_bounds__(256) void pack_tiles_kernel(const uint8_t* __restrict__ packed,
                                                          const uint8_t* __restrict__ scales, long long total_lanes,
                                                          int rows, int cols, uint8_t* __restrict__ tiled,
@@ -30,10 +34,18 @@ __global__ __launch_bounds__(256) void pack_tiles_kernel(const uint8_t* __restri
   const int c = (int)(t - (long long)nb * ct);
   const int q = l >> 4, n = l & 15;
   const long long row = b * rows + 16LL * nb + n;
-  const uint4 v = *reinterpret_cast<const uint4*>(packed + row * (cols / 2) + 64 * c + 16 * q);
-  *reinterpret_cast<uint4*>(tiled + tile * 1024 + 16 * l) = v;
-  const uint16_t s = *reinterpret_cast<const uint16_t*>(scales + row * (cols / 16) + 8 * c + 2 * q);
-  *reinterpret_cast<uint16_t*>(tiled_scales + tile * 128 + 2 * l) = s;
+  const uint8_t* src = packed + row * (cols / 2) + 64 * c + 4 * q;
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint32_t*>(src + 16 * j);
+  *reinterpret_cast<uint4*>(tiled + tile * 1024 + 16 * l) = uint4{w[0], w[1], w[2], w[3]};
+  if (q == 0) {
+    const uint2 sv = *reinterpret_cast<const uint2*>(scales + row * (cols / 16) + 8 * c);
+    const uint32_t lo = sv.x, hi = sv.y;   // bytes g0..g3, g4..g7
+    const uint32_t even = (lo & 0xFFu) | ((lo >> 8) & 0xFF00u) | ((hi << 16) & 0xFF0000u) | ((hi << 8) & 0xFF000000u);
+    const uint32_t odd = ((lo >> 8) & 0xFFu) | ((lo >> 16) & 0xFF00u) | ((hi << 8) & 0xFF0000u) | (hi & 0xFF000000u);
+    *reinterpret_cast<uint2*>(tiled_scales + tile * 128 + 8 * n) = uint2{even, odd};
+  }
 }
 
 }  // namespace

@@ -39,13 +39,16 @@ def to_gpu_bank(bank, device="cuda") -> ops.NvFp4Experts:
 def tile_np(packed: np.ndarray, scales: np.ndarray):
     """Test-side statement of the MFMA tile layout: canonical [R, K/2] + [R, K/16] -> tiled bytes.
 
-    Tile (nb, c) = rows [16nb, 16nb+16) x K [128c, 128c+128); lane l = 16q + n holds row 16nb + n,
-    canonical bytes [64c + 16q, +16) and scale bytes [8c + 2q, +2).  Tiles in (nb, c) order.
+    Tile (nb, c) = rows [16nb, 16nb+16) x K [128c, 128c+128), tiles in (nb, c) order.  Nibbles:
+    lane l = 16q + n, word j holds canonical row 16nb + n bytes [64c + 16j + 4q, +4).  Scales: row
+    n's 8 bytes of the chunk, even-numbered groups first.
     """
     r, half = packed.shape
     k = half * 2
-    t = packed.reshape(r // 16, 16, k // 128, 4, 16).transpose(0, 2, 3, 1, 4).reshape(r, half)
-    ts = scales.reshape(r // 16, 16, k // 128, 4, 2).transpose(0, 2, 3, 1, 4).reshape(r, k // 16)
+    # canonical chunk bytes b = 16j + 4q + u  ->  tile order (q, n, j, u)
+    t = packed.reshape(r // 16, 16, k // 128, 4, 4, 4).transpose(0, 2, 4, 1, 3, 5).reshape(r, half)
+    # canonical scale byte g = 2jj + parity  ->  tile order (n, parity, jj)
+    ts = scales.reshape(r // 16, 16, k // 128, 4, 2).transpose(0, 2, 1, 4, 3).reshape(r, k // 16)
     return np.ascontiguousarray(t), np.ascontiguousarray(ts)
 
 

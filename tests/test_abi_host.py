@@ -46,7 +46,7 @@ def test_gscale_conversion_worked_example_and_errors():
 
 
 def _fake_bank(e, h, i, base=0x1000):
-    return L.Experts(e, h, i, base, base + 1, base + 2, base + 3, base + 4, base + 5)
+    return L.Experts(e, h, i, base, base + 0x10, base + 0x20, base + 0x30, base + 0x40, base + 0x50)
 
 
 def _fake_layer(h=4096, e=320, k=8, i=1536, i_sh=1536, shared=True):
@@ -74,6 +74,13 @@ def test_validate_forward_host_only():
     lay4 = _fake_layer()
     lay4.shared.hidden = 2048
     assert moe.validate_forward(lay4, 8, 1 << 40) == L.MOE_ERR_INVALID_ARGUMENT
+    # device pointers the kernels read with 16-byte vectors must be 16-byte aligned
+    lay6 = _fake_layer()
+    lay6.routed.w13 = 0x1008
+    assert moe.validate_forward(lay6, 8, 1 << 40) == L.MOE_ERR_INVALID_ARGUMENT
+    lay7 = _fake_layer()
+    lay7.w_router = 0x2004
+    assert moe.validate_forward(lay7, 8, 1 << 40) == L.MOE_ERR_INVALID_ARGUMENT
     # no shared expert is valid
     lay5 = _fake_layer(shared=False)
     assert moe.validate_forward(lay5, 8, moe.forward_workspace_size(8, 4096, 1536, 0, 320, 8)) == L.MOE_OK

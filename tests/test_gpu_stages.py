@@ -126,6 +126,7 @@ def _offsets(counts):
     (512, 256, [0, 17, 16, 15, 1, 33, 0, 64]),      # 64-row tiles, ragged tails
     (384, 256, [129, 0, 128, 127, 300, 5]),         # 128-row tiles; H % 256 != 0 -> narrow down tiles
     (256, 384, [200, 70, 0, 1]),
+    (512, 256, [100, 0, 200, 77, 129]),            # eight-wave tall tiles for both GEMMs
 ])
 def test_grouped_gemm_random_matches_oracle(H, I, counts):
     rng = np.random.default_rng(H + I + sum(counts))
