@@ -180,7 +180,10 @@ typedef struct {
   void* const* stage_events;
 } moe_forward_aux_t;
 
-/* Workspace bytes moe_nvfp4_forward needs for T tokens (I_shared = 0: no shared expert). */
+/* Workspace bytes moe_nvfp4_forward needs for T tokens (I_shared = 0: no shared expert).  It holds
+ * the router logits, the selection, the permutation, the intermediate h (row-major, or in the
+ * 128-row-tile fragment order the prefill-shaped GEMMs exchange it in: up to
+ * (min(E, T*k) + T*k/128 + ceil(T/128)) * 128 rows) and the expert outputs y [(T*k + T)][H]. */
 size_t moe_nvfp4_forward_workspace_size(int32_t T, int32_t H, int32_t I, int32_t I_shared,
                                         int32_t E, int32_t k);
 

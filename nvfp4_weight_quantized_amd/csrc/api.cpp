@@ -74,8 +74,13 @@ ForwardLayout forward_layout(int32_t T, int32_t H, int32_t I, int32_t I_shared, 
   L.sorted_slot = take(S * 4);
   L.slot_to_row = take(S * 4);
   L.block_hist = take(S > (size_t)moe::kPermuteChunk ? (size_t)moe::permute_blocks((int64_t)S) * E * 4 : 0);
-  L.h = take(S * I * 2);
-  L.h_shared = take((size_t)T * I_shared * 2);
+  // h rows (row-major, shared-expert rows right after the routed ones), or the same bytes reused
+  // for h in the fragment-tiled layout of the 128-row GEMM path (one 128-row block per m-tile)
+  const size_t h_rows_bytes = align_up(S * I * 2) + align_up((size_t)T * I_shared * 2);
+  const size_t mt_bound = std::min<size_t>((size_t)E, S) + S / 128 + ((size_t)T + 127) / 128;
+  const size_t h_tiled_bytes = I_shared == 0 || I_shared == I ? mt_bound * 128 * (size_t)I * 2 : 0;
+  L.h = take(std::max(h_rows_bytes, h_tiled_bytes));
+  L.h_shared = L.h + align_up(S * I * 2);
   L.y = take((S + (I_shared > 0 ? (size_t)T : 0)) * H * 2);
   L.total = off;
   return L;
@@ -264,6 +269,10 @@ moe_status_t moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x
     gu.M_extra = T;
     gu.a_extra = x;
   }
+  // 128-row tiles for both GEMMs (and one m-tile numbering): h goes through the fragment-tiled
+  // layout, so the down GEMM's A tiles are contiguous 1 KB loads
+  const bool tiled = (fuse_shared || !has_shared) && moe::grouped_gemm_uses_tall_tiles(gu);
+  if (tiled) gu.out_tiled = h;
   if ((st = moe::launch_grouped_gemm(gu, stream))) return st;
   if (has_shared && !fuse_shared) {
     GemmProblem gs{};
@@ -301,6 +310,7 @@ moe_status_t moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x
     dn.M_extra = T;
     dn.a_extra = h + (size_t)S * I;
   }
+  dn.a_tiled = tiled ? 1 : 0;
   if ((st = moe::launch_grouped_gemm(dn, stream))) return st;
   if (has_shared && !fuse_shared) {
     GemmProblem ds{};

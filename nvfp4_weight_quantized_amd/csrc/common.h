@@ -81,7 +81,25 @@ struct GemmProblem {
   GemmBank extra;
   int32_t M_extra;
   const uint16_t* a_extra;
+  // Tall-tile path only: activations in the fragment-tiled layout.  Tile m of the problem's
+  // 128-row m-tiles (numbered over the groups in order, then the extra group) holds, for each
+  // 128-column chunk c of the K dimension, 32 fragments of 1 KB: fragment F = 4*i + j holds at
+  // byte 16*l (l = 16*q + n) row 16*i + n, columns [128*c + 32*j + 8*q, +8) of the tile, i.e.
+  // byte offset ((m * (K/128) + c) * 32 + F) * 1024 + 16 * l.  Rows past a group's end are
+  // undefined.
+  int32_t a_tiled;        // 1: `a` (and the extra group's rows) are read in that layout
+  uint16_t* out_tiled;    // gate/up: write h in that layout (K = N columns) instead of `out`
 };
+
+// Bound on the number of 128-row m-tiles of a problem (every non-empty group adds at most one
+// partial tile), the size of the tiled layouts above.
+inline long long tall_mtiles_bound(const GemmProblem& p) {
+  return (p.G > 0 ? (long long)std::min(p.G, p.M) + p.M / 128 : 0LL) + (p.has_extra ? (p.M_extra + 127) / 128 : 0);
+}
+
+// True if launch_grouped_gemm runs this problem with 128-row tiles (the only path that reads or
+// writes the tiled layouts).
+bool grouped_gemm_uses_tall_tiles(const GemmProblem& p);
 
 moe_status_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream);
 

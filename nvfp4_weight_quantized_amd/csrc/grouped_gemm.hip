@@ -182,7 +182,7 @@ __device__ __forceinline__ int frag_row_block(int f, int ntile, int wave, int N)
 // fragment f's 16 columns.
 template <int MI, int NB, bool GATE_UP, int BN, int COLS_PER_WAVE>
 __device__ __forceinline__ void epilogue(const GemmProblem& p, const GemmBank& bank, const TileInfo& ti, int ntile,
-                                         const f32x4 (&acc)[MI][NB]) {
+                                         const f32x4 (&acc)[MI][NB], int mtile = 0) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int q = lane >> 4, nl = lane & 15;
@@ -200,7 +200,16 @@ __device__ __forceinline__ void epilogue(const GemmProblem& p, const GemmBank& b
         float h[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) h[r] = silu(acc[i][f][r] * dg) * (acc[i][f + NB / 2][r] * du);
-        store_bf16x4(orow + 16 * f, h[0], h[1], h[2], h[3]);
+        if (p.out_tiled) {
+          // tiled layout: column col -> chunk col/128, step (col%128)/32, lane group (col%32)/8
+          const int col = col0 + 16 * f;
+          const int kk = col & 127;
+          const size_t byte = ((size_t)(mtile * (p.N >> 7) + (col >> 7)) * 32 + 4 * i + (kk >> 5)) * 1024 +
+                              (size_t)(16 * (((kk >> 3) & 3) * 16 + nl) + 2 * (kk & 7));
+          store_bf16x4(p.out_tiled + byte / 2, h[0], h[1], h[2], h[3]);
+        } else {
+          store_bf16x4(orow + 16 * f, h[0], h[1], h[2], h[3]);
+        }
       }
     }
   } else {
@@ -406,6 +415,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
   __shared__ TileInfo tile;
   __shared__ int tile_ok;
   __shared__ int tile_n;
+  __shared__ int tile_m;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -424,6 +434,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
     if (lane == 0) {
       tile_ok = ok ? 1 : 0;
       tile_n = ok ? L % NT : 0;
+      tile_m = ok ? L / NT : 0;
     }
   }
   __syncthreads();
@@ -435,13 +446,16 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
   ti.a_row0 = __builtin_amdgcn_readfirstlane(tile.a_row0);
   ti.extra = __builtin_amdgcn_readfirstlane(tile.extra);
   const int ntile = __builtin_amdgcn_readfirstlane(tile_n);
+  const int mtile = __builtin_amdgcn_readfirstlane(tile_m);
   const GemmBank& bank = ti.extra ? p.extra : p.bank;
   const int K = p.K;
   const int nK = K / BK;
 
-  // A rows: byte offset of each of the tile's rows (rows past the group repeat a valid row)
-  const uint8_t* abase = reinterpret_cast<const uint8_t*>(ti.extra ? p.a_extra : p.a);
-  if (tid < BM) {
+  // A rows: byte offset of each of the tile's rows (rows past the group repeat a valid row).
+  // Tiled A: the tile's chunks are contiguous 32 KB blocks already in fragment order.
+  const uint8_t* abase = reinterpret_cast<const uint8_t*>(p.a_tiled ? p.a : (ti.extra ? p.a_extra : p.a));
+  if (p.a_tiled) abase += (size_t)mtile * nK * BUF_BYTES;
+  if (tid < BM && !p.a_tiled) {
     const int R = ti.a_row0 + min(tid, ti.rows - 1);
     const int src = (!ti.extra && p.row_index) ? p.row_index[R] / p.row_divisor : R;
     s_aoff[tid] = (uint32_t)src * (uint32_t)K * 2u;
@@ -453,7 +467,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
 #pragma unroll
   for (int it = 0; it < A_ITERS; ++it) {
     const int F = wave + WAVES * it;
-    aoff[it] = s_aoff[16 * (F >> 2) + nl] + (uint32_t)(64 * (F & 3) + 16 * q);
+    aoff[it] = p.a_tiled ? (uint32_t)(F * 1024 + 16 * lane)
+                         : s_aoff[16 * (F >> 2) + nl] + (uint32_t)(64 * (F & 3) + 16 * q);
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)As;
 
@@ -486,7 +501,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
     }
   };
   auto issue_a = [&](int c, int buf) {
-    const uint8_t* src = abase + (size_t)c * (BK * 2);
+    const uint8_t* src = abase + (size_t)c * (p.a_tiled ? BUF_BYTES : BK * 2);
 #pragma unroll
     for (int it = 0; it < A_ITERS; ++it)
       direct_load16(src, aoff[it], lds0 + (uint32_t)(buf * BUF_BYTES + (wave + WAVES * it) * 1024));
@@ -548,7 +563,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
     case 7: run(IntC<7>{}); break;
     default: run(IntC<8>{}); break;
   }
-  epilogue<MI, NB, GATE_UP, BN, COLS_PER_WAVE>(p, bank, ti, ntile, acc);
+  epilogue<MI, NB, GATE_UP, BN, COLS_PER_WAVE>(p, bank, ti, ntile, acc, mtile);
 }
 
 template <int NB, bool GATE_UP, int WAVES>
@@ -593,12 +608,23 @@ moe_status_t launch_small(const GemmProblem& p, hipStream_t stream) {
 
 }  // namespace
 
-moe_status_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
-  const bool gate_up = p.stage == MOE_GEMM_GATE_UP;
-  // rows per group on average decides the tile height
+namespace {
+// rows per group on average decides the tile height
+long long avg_rows(const GemmProblem& p) {
   const long long rows = (long long)p.M + (p.has_extra ? p.M_extra : 0);
   const long long groups = (long long)p.G + (p.has_extra ? 1 : 0);
-  const long long avg = groups ? rows / groups : 0;
+  return groups ? rows / groups : 0;
+}
+}  // namespace
+
+bool grouped_gemm_uses_tall_tiles(const GemmProblem& p) { return avg_rows(p) > 64; }
+
+moe_status_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
+  const bool gate_up = p.stage == MOE_GEMM_GATE_UP;
+  const long long avg = avg_rows(p);
+  // the tiled activation layouts exist only on the 128-row path
+  if ((p.a_tiled || p.out_tiled) && !grouped_gemm_uses_tall_tiles(p)) return MOE_ERR_INVALID_ARGUMENT;
+  if (p.out_tiled && !gate_up) return MOE_ERR_INVALID_ARGUMENT;
   if (gate_up) {
     if (avg <= 16) return launch_small<true>(p, stream);
     if (avg <= 64) return launch_cfg<4, 4, 128, true>(p, stream);

@@ -90,9 +90,11 @@ def test_workspace_size_covers_intermediates():
     t, h, i, e, k = 4096, 4096, 1536, 320, 8
     s = t * k
     need = moe.forward_workspace_size(t, h, i, i, e, k)
-    # h rows (S+T) x I bf16 and y rows (S+T) x H bf16 dominate
-    assert need >= (s + t) * i * 2 + (s + t) * h * 2 + t * e * 4
-    assert need < 1.01 * ((s + t) * i * 2 + (s + t) * h * 2) + (64 << 20)
+    # h (row-major (S+T) rows, or one 128-row block per m-tile in the tiled layout) and the
+    # y rows (S+T) x H bf16 dominate
+    h_rows = max(s + t, (min(e, s) + s // 128 + (t + 127) // 128) * 128)
+    assert need >= h_rows * i * 2 + (s + t) * h * 2 + t * e * 4
+    assert need < 1.01 * (h_rows * i * 2 + (s + t) * h * 2) + (64 << 20)
     assert moe.forward_workspace_size(0, h, i, i, e, k) > 0
     assert L.lib().moe_permute_workspace_size(8, 8, 320) == 0
     assert L.lib().moe_permute_workspace_size(4096, 8, 320) >= (4096 * 8 // 2048) * 320 * 4
