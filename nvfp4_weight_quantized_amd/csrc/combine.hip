@@ -25,15 +25,30 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const float wj = w[(size_t)t * k + j];
-    const int row = slot_to_row[(size_t)t * k + j];
-    const uint4 v = *reinterpret_cast<const uint4*>(y + (size_t)row * H + h0);
-    const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+  // the k source rows in groups of 8: indices and weights first, then all row loads, then the
+  // fma chain in j order (every load of a group in flight together)
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    int rows[8];
+    float wj[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] = fmaf(wj, __uint_as_float(q[i] << 16), acc[2 * i]);
-      acc[2 * i + 1] = fmaf(wj, __uint_as_float(q[i] & 0xFFFF0000u), acc[2 * i + 1]);
+    for (int u = 0; u < 8; ++u) {
+      const int j = min(j0 + u, k - 1);
+      rows[u] = slot_to_row[(size_t)t * k + j];
+      wj[u] = w[(size_t)t * k + j];
+    }
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const uint4*>(y + (size_t)rows[u] * H + h0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (j0 + u < k) {
+        const uint32_t q[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = fmaf(wj[u], __uint_as_float(q[i] << 16), acc[2 * i]);
+          acc[2 * i + 1] = fmaf(wj[u], __uint_as_float(q[i] & 0xFFFF0000u), acc[2 * i + 1]);
+        }
+      }
     }
   }
   if (y_shared) {

@@ -70,32 +70,52 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
   return x;
 }
 
-// Top-k of one token's logits by one wavefront (E <= 1024, k <= 64).  Returns, in lane j < k, the
-// j-th selected expert and its renormalised softmax weight.  Equal logits -> lower index first;
-// NaN ranks lowest.
+// Top-k of one token's logits by one wavefront (E <= 64 * VPL, k <= 64).  Returns, in lane j < k,
+// the j-th selected expert and its renormalised softmax weight.  Equal logits -> lower index
+// first; NaN ranks lowest.
+// Lane l holds the logits of experts l, l + 64, ..., sorted descending (ties keep expert order);
+// each of the k rounds is one wave-wide argmax over the lanes' heads, after which the winning
+// lane drops its head.
+template <int VPL>
 __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E, int k, int* out_id, float* out_w) {
   const int lane = threadIdx.x & 63;
-  float v[16];
+  float v[VPL];
+  int vi[VPL];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < VPL; ++i) {
     const int e = lane + 64 * i;
     const float val = (e < E) ? row[e] : -INFINITY;
     v[i] = (val != val) ? -INFINITY : val;
+    vi[i] = e;
   }
-  uint32_t taken = 0;
+  // insertion sort, descending; a later slot (higher expert index) moves up only if strictly larger
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    if (lane + 64 * i >= E) taken |= 1u << i;
+  for (int i = 1; i < VPL; ++i)
+#pragma unroll
+    for (int j = i; j > 0; --j) {
+      const bool swap = v[j] > v[j - 1];
+      const float tv = v[j];
+      const int ti = vi[j];
+      v[j] = swap ? v[j - 1] : v[j];
+      vi[j] = swap ? vi[j - 1] : vi[j];
+      v[j - 1] = swap ? tv : v[j - 1];
+      vi[j - 1] = swap ? ti : vi[j - 1];
+    }
   float my_val = -INFINITY;
   int my_id = 0;
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (!((taken >> i) & 1u)) argmax_merge(bv, bi, v[i], lane + 64 * i);
+    float bv = v[0];
+    int bi = vi[0];
     wave_argmax(bv, bi);
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if ((bi & 63) == lane) {   // the winner drops its head
+#pragma unroll
+      for (int i = 0; i + 1 < VPL; ++i) {
+        v[i] = v[i + 1];
+        vi[i] = vi[i + 1];
+      }
+      v[VPL - 1] = -INFINITY;
+      vi[VPL - 1] = 0x7FFFFFFF;
+    }
     if (lane == j) {
       my_val = bv;
       my_id = bi;
@@ -106,6 +126,23 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E,
   const float s = wave_sum(z);
   *out_id = my_id;
   *out_w = z / s;
+}
+
+// Calls f(IntC-like tag) with the smallest supported logits-per-lane count covering E (<= 1024).
+template <int N>
+struct Vpl {
+  static constexpr int value = N;
+};
+template <typename F>
+__device__ __forceinline__ void with_vpl(int E, F&& f) {
+  if (E <= 64) f(Vpl<1>{});
+  else if (E <= 128) f(Vpl<2>{});
+  else if (E <= 192) f(Vpl<3>{});
+  else if (E <= 256) f(Vpl<4>{});
+  else if (E <= 320) f(Vpl<5>{});
+  else if (E <= 384) f(Vpl<6>{});
+  else if (E <= 512) f(Vpl<8>{});
+  else f(Vpl<16>{});
 }
 
 // Exclusive scan of cnt[0..E) into out[0..E) by one wavefront (may be in place); returns the total.
@@ -123,33 +160,32 @@ __device__ __forceinline__ int wave_exclusive_scan(const int* cnt, int* out, int
 }
 
 // Stable scatter of one wave's slots [s_begin, s_end): position = base[e] + rank among the earlier
-// slots of the same expert in this wave's range; base[e] advances by the wave's count.  Ranks
-// come from ballots over the lanes holding the same expert, so no atomic ordering is involved.
-__device__ __forceinline__ void wave_stable_scatter(const int32_t* ids, int s_begin, int s_end, int* base,
+// slots of the same expert in this wave's range; base[e] advances by the wave's count.  The lanes
+// holding the same expert are found with one ballot per bit of the expert index (E <= 1024: at
+// most 10), so no atomic ordering and no loop over distinct experts is involved.
+__device__ __forceinline__ void wave_stable_scatter(const int32_t* ids, int s_begin, int s_end, int E, int* base,
                                                     int32_t* __restrict__ sorted_slot,
                                                     int32_t* __restrict__ slot_to_row) {
   const int lane = threadIdx.x & 63;
   const uint64_t below = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  const int nbits = E > 1 ? 32 - __builtin_clz((unsigned)(E - 1)) : 0;
   for (int s0 = s_begin; s0 < s_end; s0 += 64) {
     const int s = s0 + lane;
     const bool valid = s < s_end;
-    const int e = valid ? ids[s] : -1;
-    uint64_t rem = __ballot(valid);
-    uint64_t peers = 0;
-    while (rem) {
-      const int leader = __ffsll((unsigned long long)rem) - 1;
-      const int le = __builtin_amdgcn_readlane(e, leader);
-      const uint64_t m = __ballot(valid && e == le);
-      if (valid && e == le) peers = m;
-      rem &= ~m;
+    const int e = valid ? ids[s] : 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(valid && bit);
+      peers &= bit ? m : ~m;
     }
     if (valid) {
       const int rank = __popcll(peers & below);
-      const int b = base[e];
-      const int pos = b + rank;
+      const int bb = base[e];
+      const int pos = bb + rank;
       sorted_slot[pos] = s;
       slot_to_row[s] = pos;
-      if (rank == 0) base[e] = b + __popcll(peers);
+      if (rank == 0) base[e] = bb + __popcll(peers);
     }
   }
 }
@@ -194,7 +230,7 @@ __device__ __forceinline__ void permute_block(const int32_t* ids, int S, int E, 
     }
   }
   __syncthreads();
-  if (s_begin < s_end) wave_stable_scatter(ids, s_begin, s_end, wave_hist[wave], sorted_slot, slot_to_row);
+  if (s_begin < s_end) wave_stable_scatter(ids, s_begin, s_end, E, wave_hist[wave], sorted_slot, slot_to_row);
 }
 
 }  // namespace moe

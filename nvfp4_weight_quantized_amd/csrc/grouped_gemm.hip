@@ -86,6 +86,16 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& w, const bf16x8& x, const f3
 __device__ __forceinline__ int w_lane_offset(int lane) { return 16 * lane; }
 __device__ __forceinline__ int s_lane_offset(int lane) { return 8 * (lane & 15) + 4 * ((lane >> 4) >> 1); }
 
+// Streaming (non-temporal) loads for weight bytes that are read once per pass.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream16(const uint8_t* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return uint4{v[0], v[1], v[2], v[3]};
+}
+__device__ __forceinline__ uint32_t load_stream4(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
 __device__ __forceinline__ void store_bf16x4(uint16_t* dst, float a, float b, float c, float d) {
   const uint32_t lo = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
   const uint32_t hi = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
@@ -314,8 +324,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmProblem p) {
 #pragma unroll
       for (int v = 0; v < NS; ++v) {
         const size_t t = (size_t)c * NS + v;
-        b_next[f][v] = *reinterpret_cast<const uint4*>(wptr[f] + t * 1024);
-        s_next[f][v] = *reinterpret_cast<const uint32_t*>(sptr[f] + t * 128);
+        b_next[f][v] = load_stream16(wptr[f] + t * 1024);
+        s_next[f][v] = load_stream4(sptr[f] + t * 128);
       }
   };
   load_chunk(0);

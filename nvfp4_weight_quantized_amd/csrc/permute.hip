@@ -5,7 +5,7 @@
 // is bit-exact and independent of scheduling: counts come from LDS integer atomics (order-free),
 // and every slot's position is its group offset plus the number of earlier slots of the same
 // expert, computed from per-block and per-wave histograms and in-wave ballots -- never from the
-// order in which atomics land.
+// order in which atomics land; lanes of one wave holding the same expert are found with ballots.
 //
 // Small S (one workgroup): one launch does histogram, scan and scatter; for few tokens the top-k
 // selection (S2) runs in the same launch.  Large S: per-block histograms -> one scan workgroup ->
@@ -40,7 +40,7 @@ __global__ __launch_bounds__(kPermuteThreads) void topk_permute_small_kernel(
   for (int t = wave; t < T; t += kPermWaves) {
     int id;
     float wt;
-    topk_token(logits + (size_t)t * E, E, k, &id, &wt);
+    with_vpl(E, [&](auto vpl) { topk_token<decltype(vpl)::value>(logits + (size_t)t * E, E, k, &id, &wt); });
     if (lane < k) {
       ids[(size_t)t * k + lane] = id;
       w[(size_t)t * k + lane] = wt;
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kPermuteThreads) void permute_scatter_kernel(
     }
   }
   __syncthreads();
-  if (s_begin < s_end) wave_stable_scatter(ids, s_begin, s_end, wave_hist[wave], sorted_slot, slot_to_row);
+  if (s_begin < s_end) wave_stable_scatter(ids, s_begin, s_end, E, wave_hist[wave], sorted_slot, slot_to_row);
 }
 
 }  // namespace

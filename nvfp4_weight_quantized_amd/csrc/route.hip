@@ -1,12 +1,12 @@
 // Router (S1) and top-k selection (S2) of the NVFP4 MoE layer, gfx950.
 //
 // S1: logits[t][e] = sum_h x[t][h] * Wr[e][h] (+ bias[e]), bf16 inputs, fp32 accumulation.
-//     Few tokens: one workgroup per expert streams its router row once and dots it with every
-//     token (the router weight is the only real traffic).  Many tokens: an LDS-tiled bf16 MFMA
-//     GEMM (16x16x32 fragments).
-// S2: one wavefront per token: k rounds of a wave-wide argmax (equal logits -> lower index),
-//     then the softmax over the k selected logits (equal to the full softmax renormalised over
-//     the selection).
+//     Few tokens: one workgroup per (expert, 8 tokens) streams the expert's router row once with
+//     every load of a pass in flight together (the router weight is the only real traffic).  Many
+//     tokens: an LDS-tiled bf16 MFMA GEMM (16x16x32 fragments).
+// S2: one wavefront per token: each lane sorts its few logits, then k rounds of a wave-wide
+//     argmax over the lanes' heads (equal logits -> lower index), then the softmax over the k
+//     selected logits (equal to the full softmax renormalised over the selection).
 // Sources: router -> top-k stage of the modular fused MoE ("vLLM on the NVIDIA DGX Spark: A
 // Complete Technical Guide", section 7.1); top-8 of 320 routed experts ("Serving Solar Open 2 on
 // DGX Spark", "Solar Open 2 in brief").
@@ -16,38 +16,54 @@ namespace moe {
 namespace {
 
 constexpr int kGemvMaxTokens = 32;
+constexpr int kGemvTokens = 8;     // tokens per workgroup
 
-// Few tokens: one workgroup per expert.  The 256 threads form T_P groups (T_P = T rounded up to a
-// power of two); group t dots token t with the expert's router row, each thread over a strided
-// slice of H, then a shuffle reduction inside the group.  All loads of a thread are independent.
-template <int T_P>
+// Few tokens: one workgroup per (expert, group of up to 8 tokens).  Each thread takes 8
+// consecutive h of the expert's router row per 2048-wide pass and dots them with the same h of
+// every token, all loads of a pass issued together; the per-token sums are then reduced across
+// the workgroup (wave sums, then the four waves in order).
 __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ wr,
                                                            const float* __restrict__ bias, int T, int H, int E,
                                                            float* __restrict__ logits) {
-  constexpr int G = 256 / T_P;      // threads per token (power of two, <= 64)
+  __shared__ float part[4][kGemvTokens];
   const int e = blockIdx.x;
-  const int t = threadIdx.x / G;
-  const int g = threadIdx.x % G;
+  const int t0 = blockIdx.y * kGemvTokens;
+  const int tn = min(kGemvTokens, T - t0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint16_t* wrow = wr + (size_t)e * H;
-  const uint16_t* xrow = x + (size_t)min(t, T - 1) * H;
-  float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll 4
-  for (int h0 = g * 8; h0 < H; h0 += G * 8) {
-    const uint4 wv = *reinterpret_cast<const uint4*>(wrow + h0);
-    const uint4 xv = *reinterpret_cast<const uint4*>(xrow + h0);
-    const uint32_t wq[4] = {wv.x, wv.y, wv.z, wv.w};
-    const uint32_t xq[4] = {xv.x, xv.y, xv.z, xv.w};
+  float acc[kGemvTokens];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc0 = fmaf(__uint_as_float(xq[i] << 16), __uint_as_float(wq[i] << 16), acc0);
-      acc1 = fmaf(__uint_as_float(xq[i] & 0xFFFF0000u), __uint_as_float(wq[i] & 0xFFFF0000u), acc1);
+  for (int t = 0; t < kGemvTokens; ++t) acc[t] = 0.f;
+#pragma unroll 2
+  for (int h0 = threadIdx.x * 8; h0 < H; h0 += 256 * 8) {
+    const uint4 wv = *reinterpret_cast<const uint4*>(wrow + h0);
+    uint4 xv[kGemvTokens];
+#pragma unroll
+    for (int t = 0; t < kGemvTokens; ++t)
+      xv[t] = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + min(t, tn - 1)) * H + h0);
+    const uint32_t wq[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+    for (int t = 0; t < kGemvTokens; ++t) {
+      const uint32_t xq[4] = {xv[t].x, xv[t].y, xv[t].z, xv[t].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[t] = fmaf(__uint_as_float(xq[i] << 16), __uint_as_float(wq[i] << 16), acc[t]);
+        acc[t] = fmaf(__uint_as_float(xq[i] & 0xFFFF0000u), __uint_as_float(wq[i] & 0xFFFF0000u), acc[t]);
+      }
     }
   }
-  float v = acc0 + acc1;
 #pragma unroll
-  for (int off = G / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  if (g == 0 && t < T) logits[(size_t)t * E + e] = v + (bias ? bias[e] : 0.f);
+  for (int t = 0; t < kGemvTokens; ++t) {
+    const float v = wave_sum(acc[t]);
+    if (lane == 0) part[wave][t] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < tn) {
+    const int t = threadIdx.x;
+    const float v = ((part[0][t] + part[1][t]) + part[2][t]) + part[3][t];
+    logits[(size_t)(t0 + t) * E + e] = v + (bias ? bias[e] : 0.f);
+  }
 }
 
 // C[T][E] = X[T][H] . Wr[E][H]^T with bf16 MFMA; 64x64 tile per workgroup, 4 waves of 32x32.
@@ -132,7 +148,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   if (t >= T) return;
   int id;
   float wt;
-  topk_token(logits + (size_t)t * E, E, k, &id, &wt);
+  with_vpl(E, [&](auto vpl) { topk_token<decltype(vpl)::value>(logits + (size_t)t * E, E, k, &id, &wt); });
   if (lane < k) {
     ids[(size_t)t * k + lane] = id;
     w[(size_t)t * k + lane] = wt;
@@ -145,11 +161,8 @@ moe_status_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, c
                                   int32_t H, int32_t E, float* logits, hipStream_t stream) {
   if (T == 0) return MOE_OK;
   if (T <= kGemvMaxTokens) {
-    const dim3 grid(E), block(256);
-    if (T <= 4) hipLaunchKernelGGL(router_small_kernel<4>, grid, block, 0, stream, x, w_router, bias, T, H, E, logits);
-    else if (T <= 8) hipLaunchKernelGGL(router_small_kernel<8>, grid, block, 0, stream, x, w_router, bias, T, H, E, logits);
-    else if (T <= 16) hipLaunchKernelGGL(router_small_kernel<16>, grid, block, 0, stream, x, w_router, bias, T, H, E, logits);
-    else hipLaunchKernelGGL(router_small_kernel<32>, grid, block, 0, stream, x, w_router, bias, T, H, E, logits);
+    hipLaunchKernelGGL(router_small_kernel, dim3(E, (T + kGemvTokens - 1) / kGemvTokens), dim3(256), 0, stream, x,
+                       w_router, bias, (int)T, (int)H, (int)E, logits);
   } else {
     hipLaunchKernelGGL(router_mfma_kernel, dim3((E + kRB - 1) / kRB, (T + kRB - 1) / kRB), dim3(256), 0, stream, x,
                        w_router, bias, (int)T, (int)H, (int)E, logits);
