@@ -59,7 +59,9 @@
  *     workspaces.
  *
  * Size limits: 1 <= k <= min(E, 64), E <= 1024; H and I multiples of 128 (the format needs 16;
- * the kernels' K-chunk is 128); T*k < 2^31.
+ * the kernels' K-chunk is 128); T*k < 2^31; activation matrices (x: T*H, h: (T*k+T)*I, and the
+ * `a` of a grouped GEMM: M_total*K, with every row it reads) under 4 GiB of bf16, since the
+ * kernels that stage activation tiles address rows with 32-bit byte offsets.
  */
 #ifndef MOE_NVFP4_H
 #define MOE_NVFP4_H

@@ -43,9 +43,13 @@ bool valid_bank(const moe_nvfp4_experts_t& b, int32_t H, int32_t expected_expert
   return al16(b.w13) && al16(b.w13_scale) && al16(b.w2) && al16(b.w2_scale);
 }
 
+// The LDS-staging kernels address activation rows with 32-bit byte offsets.
+constexpr int64_t kMaxActivationBytes = (int64_t)1 << 32;
+
 bool valid_route_dims(int32_t T, int32_t H, int32_t E, int32_t k) {
   if (T < 0 || E < 1 || E > 1024 || k < 1 || k > E || k > 64) return false;
   if (H <= 0 || H % 128 != 0) return false;
+  if ((int64_t)T * H * 2 >= kMaxActivationBytes) return false;
   return (int64_t)T * k < (int64_t)0x7FFFFFFF;
 }
 
@@ -151,6 +155,8 @@ moe_status_t moe_nvfp4_grouped_gemm(int32_t stage, const moe_nvfp4_experts_t* w,
   if (!valid_bank(*w, w->hidden, w->num_experts) || w->hidden <= 0 || w->hidden % 128 != 0)
     return MOE_ERR_INVALID_ARGUMENT;
   if (M_total < 0 || row_divisor < 1) return MOE_ERR_INVALID_ARGUMENT;
+  const int64_t K_ = stage == MOE_GEMM_GATE_UP ? w->hidden : w->inter;
+  if ((int64_t)M_total * K_ * 2 >= kMaxActivationBytes) return MOE_ERR_INVALID_ARGUMENT;
   if (stage == MOE_GEMM_DOWN && row_index) return MOE_ERR_INVALID_ARGUMENT;
   if (M_total == 0) return MOE_OK;
   if (!a || !expert_offsets || !out || !al16(a) || !al16(out)) return MOE_ERR_INVALID_ARGUMENT;
@@ -197,6 +203,7 @@ moe_status_t moe_validate_forward(const moe_nvfp4_layer_t* layer, int32_t T, siz
   const bool has_shared = layer->shared.num_experts != 0;
   if (has_shared && !valid_bank(layer->shared, H, 1)) return MOE_ERR_INVALID_ARGUMENT;
   const int32_t I = layer->routed.inter, Is = has_shared ? layer->shared.inter : 0;
+  if (((int64_t)T * k + T) * std::max(I, Is) * 2 >= kMaxActivationBytes) return MOE_ERR_INVALID_ARGUMENT;
   if (T > 0 && workspace_bytes < moe_nvfp4_forward_workspace_size(T, H, I, Is, E, k))
     return MOE_ERR_WORKSPACE_TOO_SMALL;
   return check_arch(gfx_arch);

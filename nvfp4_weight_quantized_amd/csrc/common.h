@@ -25,6 +25,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+// 16 bytes per lane from global memory straight to LDS (global_load_lds_dwordx4): lane i's bytes
+// land at lds_addr + 16*i.  The global address is a wave-uniform base plus a 32-bit per-lane byte
+// offset; lds_addr must be wave-uniform.  Issued from inline assembly, so the compiler neither
+// orders LDS reads after it nor waits for it: completion is the caller's explicit vmcnt wait.
+__device__ __forceinline__ void direct_load16(const void* base, uint32_t offset, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(offset), "s"(base), "s"(lds_addr)
+      : "memory", "m0");
+}
+
 // Host-side launch helpers -----------------------------------------------------------------
 
 // Status of the last launch on this thread; MOE_ERR_HIP if the launch was rejected.

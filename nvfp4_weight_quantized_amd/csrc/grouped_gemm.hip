@@ -396,18 +396,6 @@ struct IntC {
   static constexpr int value = N;
 };
 
-// 16 bytes per lane from global memory to LDS: lane i's bytes land at lds_addr + 16*i.
-// lds_addr must be wave-uniform.  Completion is tracked by vmcnt only.
-// The global address is a wave-uniform base plus a 32-bit per-lane byte offset.
-__device__ __forceinline__ void direct_load16(const void* base, uint32_t offset, uint32_t lds_addr) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(offset), "s"(base), "s"(lds_addr)
-      : "memory", "m0");
-}
-
 template <int NB, bool GATE_UP, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kernel(GemmProblem p) {
   constexpr int MI = kTallRows / 16;
@@ -608,10 +596,11 @@ moe_status_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
   return launch_status();
 }
 
-// Few rows per expert: 16-row tiles and the widest K chunk the reduction length allows.
+// Few rows per expert: 16-row tiles; 512-wide K chunks for long reductions, 256-wide for shorter
+// ones (more workgroups in flight; measured on the decode-shaped down GEMM, K = 1536).
 template <bool GATE_UP>
 moe_status_t launch_small(const GemmProblem& p, hipStream_t stream) {
-  if (p.K % 512 == 0) return launch_cfg<1, 2, 512, GATE_UP>(p, stream);
+  if (p.K % 512 == 0 && p.K >= 4096) return launch_cfg<1, 2, 512, GATE_UP>(p, stream);
   if (p.K % 256 == 0) return launch_cfg<1, 2, 256, GATE_UP>(p, stream);
   return launch_cfg<1, 2, 128, GATE_UP>(p, stream);
 }

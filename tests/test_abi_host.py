@@ -81,6 +81,10 @@ def test_validate_forward_host_only():
     lay7 = _fake_layer()
     lay7.w_router = 0x2004
     assert moe.validate_forward(lay7, 8, 1 << 40) == L.MOE_ERR_INVALID_ARGUMENT
+    # activation matrices are addressed with 32-bit byte offsets: 4 GiB of x is rejected
+    assert moe.validate_forward(_fake_layer(), 1 << 19, 1 << 62) == L.MOE_ERR_INVALID_ARGUMENT
+    assert moe.validate_forward(_fake_layer(), (1 << 19) - 1, 1 << 62, arch="gfx950") in (L.MOE_OK,
+                                                                                        L.MOE_ERR_INVALID_ARGUMENT)
     # no shared expert is valid
     lay5 = _fake_layer(shared=False)
     assert moe.validate_forward(lay5, 8, moe.forward_workspace_size(8, 4096, 1536, 0, 320, 8)) == L.MOE_OK
