@@ -32,8 +32,8 @@ NVFP4_BYTES_PER_WEIGHT = 0.5625
 _GEMM_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "nvfp4_weight_quantized_amd", "csrc",
                          "grouped_gemm.hip")
 _TRAFFIC = {  # workload: (sha256 of grouped_gemm.hip, bytes read, bytes written) per gate/up launch
-    "decode": ("1859ab0d9413e9f5a066ea825bdfb9189bdc91fea4299a9177b52226eeb136fd", 434.13e6, 0.22e6),
-    "prefill": ("1859ab0d9413e9f5a066ea825bdfb9189bdc91fea4299a9177b52226eeb136fd", 2754.75e6, 113.25e6),
+    "decode": ("dbda343b4f147041d2ec03c32d4f2fcf0c326f830c47e1da7a0e5ac0a6edf085", 432.52e6, 0.22e6),
+    "prefill": ("dbda343b4f147041d2ec03c32d4f2fcf0c326f830c47e1da7a0e5ac0a6edf085", 2768.74e6, 113.70e6),
 }
 
 
@@ -184,6 +184,22 @@ def main():
     torch.cuda.synchronize()
     copy_gbs = 5 * 2 * src.numel() / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
+    # dense bf16 GEMM of the gate/up shape through the vendor library (torch.mm -> hipBLASLt): the
+    # practical MFMA ceiling of this machine for that shape (context only; not part of the layer)
+    dense_tflops = None
+    if wl.name not in ("tiny", "decode"):
+        m_rows, n_cols = wl.T * wl.k + wl.T, 2 * wl.I
+        a_ = torch.randn(m_rows, wl.H, device=dev, dtype=torch.bfloat16)
+        b_ = torch.randn(n_cols, wl.H, device=dev, dtype=torch.bfloat16)
+        c_ = a_ @ b_.t()
+        c0.record()
+        for _ in range(3):
+            c_ = a_ @ b_.t()
+        c1.record()
+        torch.cuda.synchronize()
+        dense_tflops = 3 * 2.0 * m_rows * n_cols * wl.H / (c0.elapsed_time(c1) * 1e-3) / 1e12
+        del a_, b_, c_
+        torch.cuda.empty_cache()
 
     for i in range(warmup):
         ops.forward(layers[i % copies], x, ws, out)
@@ -230,11 +246,29 @@ def main():
         roof = {"bound": "mfma", "achieved": gu_flops / (gate_up_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    # the same against what this box measurably reaches: a streaming copy (HBM-bound case) or the
+    # vendor library's dense bf16 GEMM of the same shape (MFMA-bound case)
+    roof["peak_measured"] = copy_gbs if roof["bound"] == "hbm" else dense_tflops
+    roof["peak_measured_source"] = ("1 GiB device-to-device copy (read + write)" if roof["bound"] == "hbm"
+                                    else "dense bf16 GEMM of the gate/up shape via torch.mm (hipBLASLt)")
+    roof["frac_of_measured"] = (roof["achieved"] / roof["peak_measured"]) if roof["peak_measured"] else None
     roof["traffic"] = gate_up_traffic(wl.name)
     roof["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)"
     roof["algorithmic_bytes"] = gu_bytes
     roof["kernel"] = "gate/up grouped GEMM (S4)"
     roof["kernel_us"] = gate_up_ms * 1e3
+
+    # whole layer: flops 2(S+T)*3HI + 2THE (MFMA-bound shapes) or the bytes of every touched
+    # expert, the shared expert, the router weight and the activations (HBM-bound shapes)
+    if roof["bound"] == "hbm":
+        layer_bytes = ((touched * 3 * I + 3 * wl.I_shared) * H * NVFP4_BYTES_PER_WEIGHT + 2 * E * H + 4 * T * H)
+        layer_roof = {"bound": "hbm", "achieved": layer_bytes / (ms_per_step * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                      "unit": "GB/s", "algorithmic_bytes": layer_bytes}
+    else:
+        layer_flops = 2.0 * S * 3 * H * I + 2.0 * T * 3 * H * wl.I_shared + 2.0 * T * H * E
+        layer_roof = {"bound": "mfma", "achieved": layer_flops / (ms_per_step * 1e-3) / 1e12,
+                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "algorithmic_flops": layer_flops}
+    layer_roof["frac"] = layer_roof["achieved"] / layer_roof["peak"]
 
     cpu = None
     if args.cpu_tokens > 0:
@@ -253,6 +287,7 @@ def main():
                                f"NVFP4 W4A16", "tokens": T, "hidden": H, "inter": I, "experts": E, "top_k": k,
                    "weight_copies": copies, "experts_touched": touched},
         "roofline": roof,
+        "layer_roofline": layer_roof,
         "stages_us": stages_us,
         "measured_copy_GBs": copy_gbs,
         "timed_stages_us": {"gate_up": gate_up_ms * 1e3, "down": down_ms * 1e3},
