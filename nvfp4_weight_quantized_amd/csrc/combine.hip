@@ -12,6 +12,7 @@ namespace moe {
 namespace {
 
 constexpr int kCombineThreads = 256;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kCols = kCombineThreads * 8;  // columns per workgroup
 
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t* __restrict__ y,
@@ -38,7 +39,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t
     }
     uint4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const uint4*>(y + (size_t)rows[u] * H + h0);
+    for (int u = 0; u < 8; ++u) {
+      // each expert row is read once: stream it past the caches
+      const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(y + (size_t)rows[u] * H + h0));
+      v[u] = uint4{t[0], t[1], t[2], t[3]};
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (j0 + u < k) {

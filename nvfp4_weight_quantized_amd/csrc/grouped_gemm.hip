@@ -616,7 +616,7 @@ long long avg_rows(const GemmProblem& p) {
 }
 }  // namespace
 
-bool grouped_gemm_uses_tall_tiles(const GemmProblem& p) { return avg_rows(p) > 64; }
+bool grouped_gemm_uses_tall_tiles(const GemmProblem& p) { return avg_rows(p) > 32; }
 
 moe_status_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
   const bool gate_up = p.stage == MOE_GEMM_GATE_UP;
@@ -626,13 +626,13 @@ moe_status_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
   if (p.out_tiled && !gate_up) return MOE_ERR_INVALID_ARGUMENT;
   if (gate_up) {
     if (avg <= 16) return launch_small<true>(p, stream);
-    if (avg <= 64) return launch_cfg<4, 4, 128, true>(p, stream);
+    if (avg <= 32) return launch_cfg<4, 4, 128, true>(p, stream);
     // eight waves (one workgroup per CU) where the width allows: half the A traffic per MFMA
     return (p.N % 256 == 0) ? launch_tall<4, true, 8>(p, stream) : launch_tall<4, true, 4>(p, stream);
   }
   const bool wide = (p.N % 256) == 0;
   if (avg <= 16) return launch_small<false>(p, stream);
-  if (avg <= 64) return wide ? launch_cfg<4, 4, 128, false>(p, stream) : launch_cfg<4, 2, 128, false>(p, stream);
+  if (avg <= 32) return wide ? launch_cfg<4, 4, 128, false>(p, stream) : launch_cfg<4, 2, 128, false>(p, stream);
   if (p.N % 512 == 0) return launch_tall<4, false, 8>(p, stream);
   return wide ? launch_tall<4, false, 4>(p, stream) : launch_tall<2, false, 4>(p, stream);
 }
