@@ -4,9 +4,11 @@
 A step is one pass of the whole layer (router, top-k, permute, gate/up GEMM + SiLU*up, down
 GEMM, combine, shared expert) over one batch of synthetic tokens already resident in HBM.
 The default workload is the decode-shaped layer (T=8, H=4096, I=1536, E=320 top-8 + 1 shared).
-Prints one JSON line with the layer tokens/s, the roofline of the dominant kernel (timed live
-with HIP events recorded by the library at the stage boundaries of every timed step) and the
-CPU oracle timed on a bounded sample of the same workload.
+The K timed steps are launched eagerly, with HIP events recorded by the library at the stage
+boundaries of every step (they time the dominant kernel for the roofline); the same K forwards
+replayed from HIP graphs are reported beside them.
+Prints one JSON line with the layer tokens/s, the roofline of the dominant kernel and the CPU
+oracle timed on a bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -32,8 +34,8 @@ NVFP4_BYTES_PER_WEIGHT = 0.5625
 _GEMM_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "nvfp4_weight_quantized_amd", "csrc",
                          "grouped_gemm.hip")
 _TRAFFIC = {  # workload: (sha256 of grouped_gemm.hip, bytes read, bytes written) per gate/up launch
-    "decode": ("dbda343b4f147041d2ec03c32d4f2fcf0c326f830c47e1da7a0e5ac0a6edf085", 432.52e6, 0.22e6),
-    "prefill": ("dbda343b4f147041d2ec03c32d4f2fcf0c326f830c47e1da7a0e5ac0a6edf085", 2768.74e6, 113.70e6),
+    "decode": ("b429170cc48b38c0902678505cf79ef7d2e741908e03391abb2968af22254596", 432.59e6, 0.22e6),
+    "prefill": ("b429170cc48b38c0902678505cf79ef7d2e741908e03391abb2968af22254596", 2768.90e6, 113.70e6),
 }
 
 
@@ -220,6 +222,36 @@ def main():
     total_ms = start.elapsed_time(end)
     gate_up_ms = float(np.mean([hip.elapsed_ms(e[0], e[1]) for e in evs]))
     down_ms = float(np.mean([hip.elapsed_ms(e[1], e[2]) for e in evs]))
+    # the same forwards replayed from HIP graphs (one captured forward per weight copy): how a
+    # serving loop runs the layer, without per-kernel launch overhead
+    graph_ms = None
+    try:
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for lay in layers:
+                ops.forward(lay, x, ws, out)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for lay in layers:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                ops.forward(lay, x, ws, out)
+            graphs.append(g)
+        for i in range(warmup):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for i in range(steps):
+            graphs[i % copies].replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / steps
+        del graphs
+    except RuntimeError as exc:  # capture unsupported: report the eager timing only
+        print(f"[bench] graph replay unavailable: {exc}", file=sys.stderr, flush=True)
     # per-stage breakdown, outside the timed region: all six stage boundaries
     bevs = [[hip.create() for _ in range(6)] for _ in range(min(steps, 50))]
     torch.cuda.synchronize()
@@ -288,6 +320,7 @@ def main():
                    "weight_copies": copies, "experts_touched": touched},
         "roofline": roof,
         "layer_roofline": layer_roof,
+        "graph_replay_ms_per_step": graph_ms,
         "stages_us": stages_us,
         "measured_copy_GBs": copy_gbs,
         "timed_stages_us": {"gate_up": gate_up_ms * 1e3, "down": down_ms * 1e3},

@@ -29,6 +29,9 @@ SMALL = [
     (50, 256, 128, 6, 2, True, False, 256),
     (1, 256, 128, 4, 4, True, False, None),
     (129, 256, 128, 64, 8, True, True, None),
+    (200, 256, 128, 4, 2, True, False, 256),     # 128-row tiles, shared expert of another width
+    (400, 256, 128, 4, 2, True, False, None),    # 128-row tiles with 2 and 1 K chunks
+    (700, 384, 256, 40, 8, False, True, None),   # 128-row tiles, multi-block permute, no shared
 ]
 
 
@@ -55,6 +58,37 @@ def test_zero_tokens_is_a_no_op():
     glayer = parity.to_gpu_layer(helpers.random_layer(rng, 256, 128, 4, 2))
     out = ops.forward(glayer, torch.zeros(0, 256, dtype=torch.bfloat16, device=DEV))
     assert out.shape == (0, 256)
+
+
+def test_forward_replays_from_a_hip_graph():
+    """The forward only enqueues kernels (no allocation, synchronisation or memset), so it can be
+    captured in a HIP graph: every replay, with eager work between replays, equals the eager output."""
+    rng = np.random.default_rng(11)
+    # 16-row tiles + fused top-k/permute; 128-row tiles + tiled h; multi-block permute
+    for T, H, I, E, k in [(8, 256, 128, 16, 4), (300, 512, 256, 16, 4), (600, 512, 256, 16, 4)]:
+        layer = helpers.random_layer(rng, H, I, E, k)
+        glayer = parity.to_gpu_layer(layer)
+        x = parity.bits_to_bf16(helpers.random_x(rng, T, H))
+        ws = ops.workspace_for(glayer, T, DEV)
+        ref = ops.forward(glayer, x, ws).clone()
+        out = torch.empty_like(x)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            ops.forward(glayer, x, ws, out)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            ops.forward(glayer, x, ws, out)
+        for r in range(3):
+            out.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref), f"T={T}: replay {r} differs from the eager forward"
+            other = ops.forward(glayer, x, ws)
+            torch.cuda.synchronize()
+            assert torch.equal(other, ref)
 
 
 # ----------------------------------------------------------------------------- tiny workload
