@@ -122,7 +122,10 @@ def _offsets(counts):
 
 
 @pytest.mark.parametrize("H,I,counts", [
-    (256, 128, [1, 0, 3, 2]),                      # decode-like: 16-row tiles
+    (256, 128, [1, 0, 3, 2]),                      # decode-like: 8-row skinny tiles, K chunks of 256 / 128
+    (512, 256, [8, 9, 2, 4, 0, 17, 3, 1, 6, 5]),    # skinny: 1, 2 and 4 accumulator registers, 8-row tails
+    (384, 512, [7, 1, 1, 2, 3, 4, 8, 0]),          # skinny: K = 384 (128-wide chunks), narrow down output
+    (256, 128, [12, 0, 9, 16, 20]),                # 16-row tiles
     (512, 256, [0, 17, 16, 15, 1, 33, 0, 64]),      # 64-row tiles, ragged tails
     (384, 256, [129, 0, 128, 127, 300, 5]),         # 128-row tiles; H % 256 != 0 -> narrow down tiles
     (256, 384, [200, 70, 0, 1]),
@@ -178,6 +181,31 @@ def test_grouped_gemm_one_hot_pins_layout():
     y = ops.grouped_gemm(L.MOE_GEMM_DOWN, gbank, torch.from_numpy(a2).to(torch.bfloat16).to(DEV),
                          torch.from_numpy(off2).to(DEV), len(is_))
     ref2 = omoe.grouped_down(a2.astype(np.float64), off2, bank)
+    assert np.all(np.abs(parity.f64(y) - ref2) <= 2.0 ** -8 * np.abs(ref2) + 1e-30)
+
+
+@pytest.mark.parametrize("counts", [[1, 1], [2, 0], [3, 4], [5, 8]])
+def test_skinny_grouped_gemm_one_hot_pins_layout(counts):
+    """The same one-hot pin on the few-rows path (unscaled codes, block scale applied to the sums)."""
+    rng = np.random.default_rng(4 + sum(counts))
+    H, I = 512, 256
+    bank = _random_bank(rng, 2, H, I)
+    gbank = parity.to_gpu_bank(bank)
+    off = _offsets(counts)
+    M = int(off[-1])
+    hs = rng.choice(H, M, replace=False)
+    a = np.zeros((M, H), np.float32)
+    a[np.arange(M), hs] = 1.0
+    h = ops.grouped_gemm(L.MOE_GEMM_GATE_UP, gbank, torch.from_numpy(a).to(torch.bfloat16).to(DEV),
+                         torch.from_numpy(off).to(DEV), M)
+    ref = omoe.grouped_gate_up(a.astype(np.float64), off, bank)
+    assert np.all(np.abs(parity.f64(h) - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)
+    is_ = rng.choice(I, M, replace=False)
+    a2 = np.zeros((M, I), np.float32)
+    a2[np.arange(M), is_] = 1.0
+    y = ops.grouped_gemm(L.MOE_GEMM_DOWN, gbank, torch.from_numpy(a2).to(torch.bfloat16).to(DEV),
+                         torch.from_numpy(off).to(DEV), M)
+    ref2 = omoe.grouped_down(a2.astype(np.float64), off, bank)
     assert np.all(np.abs(parity.f64(y) - ref2) <= 2.0 ** -8 * np.abs(ref2) + 1e-30)
 
 
