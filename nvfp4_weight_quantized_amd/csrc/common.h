@@ -27,15 +27,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 // 16 bytes per lane from global memory straight to LDS (global_load_lds_dwordx4): lane i's bytes
 // land at lds_addr + 16*i.  The global address is a wave-uniform base plus a 32-bit per-lane byte
-// offset; lds_addr must be wave-uniform.  Issued from inline assembly, so the compiler neither
-// orders LDS reads after it nor waits for it: completion is the caller's explicit vmcnt wait.
+// offset; lds_addr must be wave-uniform (it is passed in M0).  Issued from inline assembly, so the
+// compiler does not count it among its outstanding loads and never waits for it: completion is the
+// caller's explicit vmcnt wait, then a barrier before other waves read the data.
 __device__ __forceinline__ void direct_load16(const void* base, uint32_t offset, uint32_t lds_addr) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(offset), "s"(base), "s"(lds_addr)
-      : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(offset), "s"(base), "{m0}"(lds_addr) : "memory");
 }
 
 // Host-side launch helpers -----------------------------------------------------------------

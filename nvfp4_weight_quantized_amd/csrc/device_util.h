@@ -20,32 +20,30 @@ constexpr int kDppRowBcast15 = 0x142;
 constexpr int kDppRowBcast31 = 0x143;
 constexpr int kDppRowShr1 = 0x111;
 
-// (value, index) pair order: larger value first, equal values -> lower index first.
-__device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi) {
-  if (ov > v || (ov == v && oi < i)) {
-    v = ov;
-    i = oi;
-  }
+// Monotone map of a float (not NaN) to uint32: a < b  <=>  key(a) < key(b); -0 and +0 share a key.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  const uint32_t b = __float_as_uint(v + 0.0f);   // -0 + 0 = +0
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-template <int CTRL, int ROW_MASK = 0xF>
-__device__ __forceinline__ void argmax_dpp_step(float& v, int& i) {
-  const float ov = __int_as_float(dpp_i<CTRL, ROW_MASK>(__float_as_int(v), __float_as_int(v)));
-  const int oi = dpp_i<CTRL, ROW_MASK>(i, i);
-  argmax_merge(v, i, ov, oi);
+// Wave-wide max / min of uint32 returned to every lane (DPP row steps, then lane 63).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)dpp_i<kDppQuad1032>((int)x, (int)x));
+  x = max(x, (uint32_t)dpp_i<kDppQuad2301>((int)x, (int)x));
+  x = max(x, (uint32_t)dpp_i<kDppRowHalfMirror>((int)x, (int)x));
+  x = max(x, (uint32_t)dpp_i<kDppRowMirror>((int)x, (int)x));
+  x = max(x, (uint32_t)dpp_i<kDppRowBcast15, 0xA>((int)x, (int)x));
+  x = max(x, (uint32_t)dpp_i<kDppRowBcast31, 0xC>((int)x, (int)x));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
-
-// Wave-wide argmax of (v, i); the result is returned to every lane.  The merge is associative and
-// commutative, so the reduction order does not change the result.
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-  argmax_dpp_step<kDppQuad1032>(v, i);
-  argmax_dpp_step<kDppQuad2301>(v, i);
-  argmax_dpp_step<kDppRowHalfMirror>(v, i);
-  argmax_dpp_step<kDppRowMirror>(v, i);
-  argmax_dpp_step<kDppRowBcast15, 0xA>(v, i);
-  argmax_dpp_step<kDppRowBcast31, 0xC>(v, i);
-  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-  i = __builtin_amdgcn_readlane(i, 63);
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  x = min(x, (uint32_t)dpp_i<kDppQuad1032>((int)x, (int)x));
+  x = min(x, (uint32_t)dpp_i<kDppQuad2301>((int)x, (int)x));
+  x = min(x, (uint32_t)dpp_i<kDppRowHalfMirror>((int)x, (int)x));
+  x = min(x, (uint32_t)dpp_i<kDppRowMirror>((int)x, (int)x));
+  x = min(x, (uint32_t)dpp_i<kDppRowBcast15, 0xA>((int)x, (int)x));
+  x = min(x, (uint32_t)dpp_i<kDppRowBcast31, 0xC>((int)x, (int)x));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
 // Wave-wide sum returned to every lane.
@@ -74,8 +72,9 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
 // the j-th selected expert and its renormalised softmax weight.  Equal logits -> lower index
 // first; NaN ranks lowest.
 // Lane l holds the logits of experts l, l + 64, ..., sorted descending (ties keep expert order);
-// each of the k rounds is one wave-wide argmax over the lanes' heads, after which the winning
-// lane drops its head.
+// each of the k rounds takes the wave-wide maximum of the lanes' heads (as order keys) and, when
+// several heads equal it, the lowest expert index among them; the winning lane (expert index
+// mod 64) drops its head.
 template <int VPL>
 __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E, int k, int* out_id, float* out_w) {
   const int lane = threadIdx.x & 63;
@@ -84,8 +83,8 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E,
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + 64 * i;
-    const float val = (e < E) ? row[e] : -INFINITY;
-    v[i] = (val != val) ? -INFINITY : val;
+    const float val = row[min(e, E - 1)];
+    v[i] = (e < E && val == val) ? val : -INFINITY;
     vi[i] = e;
   }
   // insertion sort, descending; a later slot (higher expert index) moves up only if strictly larger
@@ -104,22 +103,25 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E,
   float my_val = -INFINITY;
   int my_id = 0;
   for (int j = 0; j < k; ++j) {
-    float bv = v[0];
-    int bi = vi[0];
-    wave_argmax(bv, bi);
-    if ((bi & 63) == lane) {   // the winner drops its head
+    const uint32_t key = order_key(v[0]);
+    const uint32_t kmax = wave_max_u32(key);
+    const uint64_t tied = __ballot(key == kmax);
+    int bi;
+    if (__popcll(tied) == 1)
+      bi = __builtin_amdgcn_readlane(vi[0], __ffsll((unsigned long long)tied) - 1);
+    else
+      bi = (int)wave_min_u32(key == kmax ? (uint32_t)vi[0] : 0xFFFFFFFFu);
+    const float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[0]), bi & 63));
+    const bool win = (bi & 63) == lane;   // the winner drops its head
 #pragma unroll
-      for (int i = 0; i + 1 < VPL; ++i) {
-        v[i] = v[i + 1];
-        vi[i] = vi[i + 1];
-      }
-      v[VPL - 1] = -INFINITY;
-      vi[VPL - 1] = 0x7FFFFFFF;
+    for (int i = 0; i + 1 < VPL; ++i) {
+      v[i] = win ? v[i + 1] : v[i];
+      vi[i] = win ? vi[i + 1] : vi[i];
     }
-    if (lane == j) {
-      my_val = bv;
-      my_id = bi;
-    }
+    v[VPL - 1] = win ? -INFINITY : v[VPL - 1];
+    vi[VPL - 1] = win ? 0x7FFFFFFF : vi[VPL - 1];
+    my_val = (lane == j) ? bv : my_val;
+    my_id = (lane == j) ? bi : my_id;
   }
   const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), 0));
   const float z = (lane < k) ? expf(my_val - top) : 0.f;

@@ -3,7 +3,7 @@
 // S1: logits[t][e] = sum_h x[t][h] * Wr[e][h] (+ bias[e]), bf16 inputs, fp32 accumulation.
 //     Few tokens: one workgroup per (expert, 8 tokens) streams the expert's router row once with
 //     every load of a pass in flight together (the router weight is the only real traffic).  Many
-//     tokens: an LDS-tiled bf16 MFMA GEMM (16x16x32 fragments).
+//     tokens: a bf16 MFMA GEMM (16x16x32 fragments) on LDS-staged 64x64 tiles.
 // S2: one wavefront per token: each lane sorts its few logits, then k rounds of a wave-wide
 //     argmax over the lanes' heads (equal logits -> lower index), then the softmax over the k
 //     selected logits (equal to the full softmax renormalised over the selection).
@@ -66,10 +66,19 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
   }
 }
 
-// C[T][E] = X[T][H] . Wr[E][H]^T with bf16 MFMA; 64x64 tile per workgroup, 4 waves of 32x32.
-constexpr int kRB = 64;       // tile rows / cols
-constexpr int kRK = 64;       // K chunk
-constexpr int kRPad = 8;      // bf16 padding per LDS row (16 bytes) against bank conflicts
+// C[T][E] = X[T][H] . Wr[E][H]^T with bf16 MFMA (16x16x32), fp32 accumulation; 64 tokens x 64
+// experts per workgroup, 4 waves of 32x32, K chunks of 128 staged in LDS.  Each chunk is loaded
+// into registers while the previous one is multiplied (one chunk in flight), then written to LDS
+// between two barriers.  Tiles are numbered so that the expert blocks of one token block run on one
+// XCD (workgroup b runs on XCD b % 8) and read its x rows from that XCD's L2.
+constexpr int kRB = 64;                    // tile rows (tokens) and columns (experts)
+constexpr int kRK = 128;                   // K chunk
+constexpr int kRPad = 8;                   // bf16 of padding per LDS row (16 bytes)
+constexpr int kRTpr = kRK / 8;             // threads per tile row per chunk (16 bytes each)
+constexpr int kRRpp = 256 / kRTpr;         // tile rows per pass
+constexpr int kRIt = kRB / kRRpp;          // passes
+constexpr int kRXcds = 8;
+typedef uint32_t u32x4_r __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ wr,
@@ -81,37 +90,55 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int row0 = blockIdx.y * kRB;
-  const int col0 = blockIdx.x * kRB;
+  const int eb = (E + kRB - 1) / kRB;
+  const int total = eb * ((T + kRB - 1) / kRB);
+  const int per_xcd = (total + kRXcds - 1) / kRXcds;
+  const int L = (blockIdx.x % kRXcds) * per_xcd + blockIdx.x / kRXcds;
+  if (L >= total) return;
+  const int row0 = (L / eb) * kRB;
+  const int col0 = (L % eb) * kRB;
+
+  // this thread copies 16 bytes at column lc of tile rows lr + kRRpp*i (rows past T or E repeat
+  // the last valid row; their results are not stored)
+  const int lr = tid / kRTpr, lc = (tid % kRTpr) * 8;
+  const uint16_t* xrow[kRIt];
+  const uint16_t* wrow[kRIt];
+#pragma unroll
+  for (int i = 0; i < kRIt; ++i) {
+    xrow[i] = x + (size_t)min(row0 + lr + kRRpp * i, T - 1) * H + lc;
+    wrow[i] = wr + (size_t)min(col0 + lr + kRRpp * i, E - 1) * H + lc;
+  }
+  u32x4_r av[kRIt], bv[kRIt];
+#pragma unroll
+  for (int i = 0; i < kRIt; ++i) {
+    av[i] = *reinterpret_cast<const u32x4_r*>(xrow[i]);
+    bv[i] = *reinterpret_cast<const u32x4_r*>(wrow[i]);
+  }
   f32x4 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // each thread moves 2 x 16 bytes of A and of B per chunk: row = tid/8 (+32), col8 = tid%8
-  const int lr = tid >> 3, lc = (tid & 7) * 8;
-  for (int k0 = 0; k0 < H; k0 += kRK) {
-    uint4 av[2], bv[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = lr + 32 * i;
-      av[i] = (row0 + r < T) ? *reinterpret_cast<const uint4*>(x + (size_t)(row0 + r) * H + k0 + lc)
-                             : uint4{0, 0, 0, 0};
-      bv[i] = (col0 + r < E) ? *reinterpret_cast<const uint4*>(wr + (size_t)(col0 + r) * H + k0 + lc)
-                             : uint4{0, 0, 0, 0};
-    }
+  const int q = lane >> 4, m = lane & 15;
+  const int nK = H / kRK;
+  for (int c = 0; c < nK; ++c) {
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *reinterpret_cast<uint4*>(&As[lr + 32 * i][lc]) = av[i];
-      *reinterpret_cast<uint4*>(&Bs[lr + 32 * i][lc]) = bv[i];
+    for (int i = 0; i < kRIt; ++i) {
+      *reinterpret_cast<u32x4_r*>(&As[lr + kRRpp * i][lc]) = av[i];
+      *reinterpret_cast<u32x4_r*>(&Bs[lr + kRRpp * i][lc]) = bv[i];
     }
     __syncthreads();
+    if (c + 1 < nK) {
+#pragma unroll
+      for (int i = 0; i < kRIt; ++i) {
+        av[i] = *reinterpret_cast<const u32x4_r*>(xrow[i] + (size_t)(c + 1) * kRK);
+        bv[i] = *reinterpret_cast<const u32x4_r*>(wrow[i] + (size_t)(c + 1) * kRK);
+      }
+    }
 #pragma unroll
     for (int kk = 0; kk < kRK; kk += 32) {
       bf16x8 af[2], bfr[2];
-      const int q = lane >> 4, m = lane & 15;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         af[i] = *reinterpret_cast<const bf16x8*>(&As[wm * 32 + i * 16 + m][kk + 8 * q]);
@@ -124,10 +151,10 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
   }
-  const int q = lane >> 4, n = lane & 15;
+  // lane (q, n) of block (i, j): tokens 4q + r, expert n
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int col = col0 + wn * 32 + j * 16 + n;
+    const int col = col0 + wn * 32 + j * 16 + m;
     if (col >= E) continue;
     const float b = bias ? bias[col] : 0.f;
 #pragma unroll
@@ -164,8 +191,11 @@ moe_status_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, c
     hipLaunchKernelGGL(router_small_kernel, dim3(E, (T + kGemvTokens - 1) / kGemvTokens), dim3(256), 0, stream, x,
                        w_router, bias, (int)T, (int)H, (int)E, logits);
   } else {
-    hipLaunchKernelGGL(router_mfma_kernel, dim3((E + kRB - 1) / kRB, (T + kRB - 1) / kRB), dim3(256), 0, stream, x,
-                       w_router, bias, (int)T, (int)H, (int)E, logits);
+    if (H % kRK != 0) return MOE_ERR_INVALID_ARGUMENT;
+    const long long tiles = (long long)((E + kRB - 1) / kRB) * ((T + kRB - 1) / kRB);
+    const long long grid = (tiles + kRXcds - 1) / kRXcds * kRXcds;
+    hipLaunchKernelGGL(router_mfma_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, w_router, bias, (int)T,
+                       (int)H, (int)E, logits);
   }
   return launch_status();
 }

@@ -62,7 +62,7 @@ def test_pack_tiles_is_the_stated_permutation():
 
 @pytest.mark.parametrize("T,H,E,k,bias", [(1, 128, 8, 1, False), (8, 4096, 320, 8, False), (16, 256, 8, 2, True),
                                           (32, 512, 64, 6, False), (33, 256, 320, 8, True), (200, 384, 256, 8, False),
-                                          (130, 1024, 1024, 64, True)])
+                                          (130, 1024, 1024, 64, True), (100, 256, 72, 4, True)])
 def test_route_matches_oracle(T, H, E, k, bias):
     rng = np.random.default_rng(T * 1000 + E)
     x = helpers.random_x(rng, T, H)
