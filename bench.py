@@ -34,8 +34,8 @@ NVFP4_BYTES_PER_WEIGHT = 0.5625
 _GEMM_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "nvfp4_weight_quantized_amd", "csrc",
                          "grouped_gemm.hip")
 _TRAFFIC = {  # workload: (sha256 of grouped_gemm.hip, bytes read, bytes written) per gate/up launch
-    "decode": ("b429170cc48b38c0902678505cf79ef7d2e741908e03391abb2968af22254596", 432.59e6, 0.22e6),
-    "prefill": ("b429170cc48b38c0902678505cf79ef7d2e741908e03391abb2968af22254596", 2768.90e6, 113.70e6),
+    "decode": ("1ae02b3053f01130dbf21b42da61a2ce7b2f2b1adf699a4af568fab0084f4fe8", 432.58e6, 0.22e6),
+    "prefill": ("1ae02b3053f01130dbf21b42da61a2ce7b2f2b1adf699a4af568fab0084f4fe8", 2746.79e6, 113.70e6),
 }
 
 
