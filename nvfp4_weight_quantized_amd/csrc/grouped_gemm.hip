@@ -573,7 +573,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmProblem p) {
 //    tell that the loads in flight into one buffer leave the other alone and drains them before
 //    every LDS read, which serialises loading and computing.
 //  * B tiles in registers, prefetched one chunk ahead; the end-of-chunk wait names the prefetch
-//    registers, so the compiler waits for them there and nowhere earlier.
+//    registers, so the compiler waits for them there and nowhere earlier.  Within a chunk the
+//    next MFMA step's weight operands are dequantized while the current step's MFMAs run.
 //  * The number of 16-row blocks holding real rows is a template parameter of the main loop (one
 //    instantiation per count): blocks past the group's last row cost nothing and the loop body
 //    has no per-block branches.
@@ -728,19 +729,30 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
         load_b(c + 1);
       }
       const uint8_t* abuf = As + (c & 1) * BUF_BYTES + 16 * lane;
+      // the next step's weight operands are dequantized while this step's MFMAs run
+      bf16x8 wcur[NB];
+#pragma unroll
+      for (int f = 0; f < NB; ++f) wcur[f] = w_operand(bq[f], sc[f], 0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < STEPS; ++j) {
-        bf16x8 wfrag[NB];
+        bf16x8 wnext[NB];
+        if (j + 1 < STEPS) {
 #pragma unroll
-        for (int f = 0; f < NB; ++f) wfrag[f] = w_operand(bq[f], sc[f], j);
+          for (int f = 0; f < NB; ++f) wnext[f] = w_operand(bq[f], sc[f], j + 1);
+        }
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
           const bf16x8 xfrag = *reinterpret_cast<const bf16x8*>(abuf + (STEPS * i + j) * 1024);
 #pragma unroll
-          for (int f = 0; f < NB; ++f) acc[i][f] = mfma(wfrag[f], xfrag, acc[i][f]);
+          for (int f = 0; f < NB; ++f) acc[i][f] = mfma(wcur[f], xfrag, acc[i][f]);
         }
         // keep each step's LDS reads within the step (bounds the live fragment registers)
         __builtin_amdgcn_sched_barrier(0);
+        if (j + 1 < STEPS) {
+#pragma unroll
+          for (int f = 0; f < NB; ++f) wcur[f] = wnext[f];
+        }
       }
       wait_chunk();
       __syncthreads();
