@@ -563,7 +563,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmProblem p) {
 // ------------------------------------------------------------------------------------------
 // Tall tiles (many rows per expert): 128-row workgroup tiles, K chunk 128.
 //  * A chunks go global -> LDS directly (global_load_lds_dwordx4, 16 bytes per lane; lane i of a
-//    wave lands at LDS address M0 + 16*i), double-buffered, one barrier per chunk.  A chunk is
+//    wave lands at LDS address M0 + 16*i), triple-buffered with eight waves (two chunks in
+//    flight) and double-buffered with four, one barrier per chunk.  A chunk is
 //    stored as 32 MFMA fragments of 1 KB: fragment (i, j) holds, at 16*l for lane l = 16q + n, row
 //    16i + n and K [32j + 8q, +8) of the chunk.  Every fragment read is then one contiguous 1 KB
 //    ds_read_b128 (free of bank conflicts), and every direct load reads 64 contiguous bytes from
@@ -604,7 +605,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
   constexpr int BUF_BYTES = FRAGS * 1024;              // 32 KB
   constexpr int A_ITERS = FRAGS / WAVES;               // fragments (direct loads) per wave per chunk
   static_assert(STEPS == 4 && FRAGS % WAVES == 0, "chunk layout");
-  __shared__ __attribute__((aligned(1024))) uint8_t As[2 * BUF_BYTES];
+  constexpr int NBUF = WAVES == 8 ? 3 : 2;              // A chunk buffers (LDS: 96 or 64 KB)
+  constexpr int AHEAD = NBUF - 1;                       // A chunks in flight beyond the current one
+  __shared__ __attribute__((aligned(1024))) uint8_t As[NBUF * BUF_BYTES];
   __shared__ uint32_t s_aoff[BM];
   __shared__ TileInfo tile;
   __shared__ int tile_ok;
@@ -710,11 +713,28 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
                    : "memory");
   };
   // The main loop, for RB 16-row blocks of real rows.
+  // Every load but this wave's last A_ITERS (the A chunk two ahead, issued last) has landed.
+  auto wait_keep_a = [&]() {
+    static_assert(AHEAD == 1 || A_ITERS == 4, "the vmcnt literal below counts one chunk's direct loads");
+#pragma unroll
+    for (int f = 0; f < NB; ++f)
+      asm volatile("s_waitcnt vmcnt(4)" : "+v"(bn[f].x), "+v"(bn[f].y), "+v"(bn[f].z), "+v"(bn[f].w), "+v"(sn[f])
+                   :
+                   : "memory");
+  };
+  // The main loop, for RB 16-row blocks of real rows.  Per chunk c: the B prefetch of c + 1 is
+  // issued, then the A direct loads of c + AHEAD; at the end of the chunk everything but the
+  // newest A loads must have landed (the A chunk c + 1 and B c + 1 are then ready).
   auto run = [&](auto rb_const) {
     constexpr int RB = decltype(rb_const)::value;
     issue_a(0, 0);
     load_b(0);
-    wait_chunk();
+    if (AHEAD == 2 && nK > 1) {
+      issue_a(1, 1);
+      wait_keep_a();
+    } else {
+      wait_chunk();
+    }
     __syncthreads();
     for (int c = 0; c < nK; ++c) {
       uint4 bq[NB];
@@ -724,11 +744,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
         bq[f] = bn[f];
         sc[f] = sn[f];
       }
-      if (c + 1 < nK) {
-        issue_a(c + 1, (c + 1) & 1);
-        load_b(c + 1);
-      }
-      const uint8_t* abuf = As + (c & 1) * BUF_BYTES + 16 * lane;
+      if (c + 1 < nK) load_b(c + 1);
+      if (c + AHEAD < nK) issue_a(c + AHEAD, (c + AHEAD) % NBUF);
+      const uint8_t* abuf = As + (c % NBUF) * BUF_BYTES + 16 * lane;
       // the next step's weight operands are dequantized while this step's MFMAs run
       bf16x8 wcur[NB];
 #pragma unroll
@@ -754,7 +772,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
           for (int f = 0; f < NB; ++f) wcur[f] = wnext[f];
         }
       }
-      wait_chunk();
+      if (AHEAD == 2 && c + 2 < nK)
+        wait_keep_a();
+      else
+        wait_chunk();
       __syncthreads();
     }
   };
