@@ -32,6 +32,7 @@ SMALL = [
     (200, 256, 128, 4, 2, True, False, 256),     # 128-row tiles, shared expert of another width
     (400, 256, 128, 4, 2, True, False, None),    # 128-row tiles with 2 and 1 K chunks
     (700, 384, 256, 40, 8, False, True, None),   # 128-row tiles, multi-block permute, no shared
+    (20, 256, 128, 64, 2, True, False, None),    # 8-row tiles; the shared expert spans 8 + 8 + 4 rows
 ]
 
 

@@ -126,6 +126,8 @@ def _offsets(counts):
     (512, 256, [8, 9, 2, 4, 0, 17, 3, 1, 6, 5]),    # skinny: 1, 2 and 4 accumulator registers, 8-row tails
     (384, 512, [7, 1, 1, 2, 3, 4, 8, 0]),          # skinny: K = 384 (128-wide chunks), narrow down output
     (256, 128, [12, 0, 9, 16, 20]),                # 16-row tiles
+    (256, 128, [0] * 700 + [1, 0, 3] * 100 + [2] * 24),   # 1024 groups: 16 groups per lane in the tile scan
+    (256, 128, [40] * 1000 + [0, 300, 129] * 8),   # 1024 groups, 128-row tiles
     (512, 256, [0, 17, 16, 15, 1, 33, 0, 64]),      # 64-row tiles, ragged tails
     (384, 256, [129, 0, 128, 127, 300, 5]),         # 128-row tiles; H % 256 != 0 -> narrow down tiles
     (256, 384, [200, 70, 0, 1]),
