@@ -9,6 +9,8 @@ binding and imports nothing from them.
 Modules
   nvfp4  -- E2M1 / E4M3 codecs, the NVFP4 quantizer used to build test weights,
             dequantization, and the two global-scale conventions.
+  mxfp4  -- E8M0 block scales per 32 elements: codec, quantizer, dequantization
+            (the second weight format, section 6.4 of the Guide).
   moe    -- router, top-k, permutation, expert FFN, combine, whole-layer forward
             (float64 arithmetic on the exact values of the bf16/NVFP4 inputs).
   brute  -- an independent scalar float64 per-token loop for tiny layers, used to
@@ -33,4 +35,4 @@ printed value on the pages; it is pinned only through ``brute`` (an independent
 scalar implementation of the same definition).
 """
 
-from . import nvfp4, moe, brute  # noqa: F401
+from . import nvfp4, mxfp4, moe, brute  # noqa: F401

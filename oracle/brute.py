@@ -10,7 +10,8 @@ Definitions used (same sources as ``oracle.moe``):
     element 2j in the low nibble of byte j ("vLLM on the NVIDIA DGX Spark: A
     Complete Technical Guide", section 6.1);
   * E4M3 block scale per 16 elements along K; value = element * block scale *
-    global scale (same section);
+    global scale (same section); for MXFP4 one E8M0 scale 2^(b - 127) per 32
+    elements and no global scale (section 6.4, the reading of oracle.mxfp4);
   * top-k on router logits (ties -> lower expert index), softmax renormalised
     over the selected experts; SiLU(gate)*up; down projection; top-k-weighted
     sum; shared expert added with weight 1 (same readings as ``oracle.moe``).
@@ -47,17 +48,26 @@ def fp8_e4m3(byte: int) -> float:
     return sign * math.ldexp(8 + m, e - 10)      # (1 + m/8) * 2^(e-7)
 
 
-def weight(packed, scales, gscale: float, n: int, k: int) -> float:
+def e8m0(byte: int) -> float:
+    byte = int(byte)
+    return math.nan if byte == 255 else math.ldexp(1.0, byte - 127)
+
+
+def weight(packed, scales, gscale: float, n: int, k: int, fmt: str = "nvfp4") -> float:
+    if fmt == "mxfp4":
+        return fp4(packed[n], k) * e8m0(scales[n][k // 32])
     return fp4(packed[n], k) * fp8_e4m3(scales[n][k // 16]) * float(gscale)
 
 
 def dequant_expert(ew):
     """(Wg, Wu, Wd) as lists of float rows, decoded element by element."""
+    fmt = getattr(ew, "fmt", "nvfp4")
     inter = len(ew.w13) // 2
     hdim = 2 * len(ew.w13[0])
-    wg = [[weight(ew.w13, ew.w13_scale, ew.w13_gscale[0], i, h) for h in range(hdim)] for i in range(inter)]
-    wu = [[weight(ew.w13, ew.w13_scale, ew.w13_gscale[1], inter + i, h) for h in range(hdim)] for i in range(inter)]
-    wd = [[weight(ew.w2, ew.w2_scale, ew.w2_gscale, h, i) for i in range(inter)] for h in range(hdim)]
+    wg = [[weight(ew.w13, ew.w13_scale, ew.w13_gscale[0], i, h, fmt) for h in range(hdim)] for i in range(inter)]
+    wu = [[weight(ew.w13, ew.w13_scale, ew.w13_gscale[1], inter + i, h, fmt) for h in range(hdim)]
+          for i in range(inter)]
+    wd = [[weight(ew.w2, ew.w2_scale, ew.w2_gscale, h, i, fmt) for i in range(inter)] for h in range(hdim)]
     return wg, wu, wd
 
 

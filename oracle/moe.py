@@ -23,7 +23,7 @@ Readings where the pages are silent (listed in the design notes):
   * no activation scale exists anywhere: an expert can never be multiplied by 0.
 
 All arithmetic here is float64 on the exact values of the bf16 activations and
-the dequantized NVFP4 weights.  The GPU keeps fp32 accumulators and bf16
+the dequantized NVFP4 (or MXFP4, oracle.mxfp4) weights.  The GPU keeps fp32 accumulators and bf16
 intermediates; the parity tolerances absorb that difference.
 """
 
@@ -34,7 +34,7 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-from . import nvfp4
+from . import mxfp4, nvfp4
 
 
 def bf16_to_float(bits) -> np.ndarray:
@@ -45,38 +45,54 @@ def bf16_to_float(bits) -> np.ndarray:
 
 @dataclass
 class ExpertWeights:
-    """One NVFP4 expert: fused gate/up [2I, H] and down [H, I], packed as the C ABI stores them."""
+    """One expert: fused gate/up [2I, H] and down [H, I], packed as the C ABI stores them.
+
+    fmt "nvfp4": E4M3 block scales per 16 elements along K and fp32 global scales;
+    fmt "mxfp4": E8M0 block scales per 32 elements, no global scale (the gscale
+    fields are ignored).
+    """
     w13: np.ndarray          # uint8 [2I, H/2]
-    w13_scale: np.ndarray    # uint8 [2I, H/16] E4M3
-    w13_gscale: np.ndarray   # fp32 [2]  dequant global scales (gate, up)
+    w13_scale: np.ndarray    # uint8 [2I, H/16] E4M3 (NVFP4) or [2I, H/32] E8M0 (MXFP4)
+    w13_gscale: np.ndarray   # fp32 [2]  dequant global scales (gate, up); NVFP4 only
     w2: np.ndarray           # uint8 [H, I/2]
-    w2_scale: np.ndarray     # uint8 [H, I/16]
-    w2_gscale: float         # fp32 dequant global scale
+    w2_scale: np.ndarray     # uint8 [H, I/16] or [H, I/32]
+    w2_gscale: float         # fp32 dequant global scale; NVFP4 only
+    fmt: str = "nvfp4"
+
+    def _deq(self, packed, scales, gscale) -> np.ndarray:
+        if self.fmt == "mxfp4":
+            return mxfp4.dequantize(packed, scales)
+        return nvfp4.dequantize(packed, scales, gscale)
 
     def dequant_w13(self) -> np.ndarray:
         two_i = self.w13.shape[0]
         i = two_i // 2
-        g = nvfp4.dequantize(self.w13[:i], self.w13_scale[:i], self.w13_gscale[0])
-        u = nvfp4.dequantize(self.w13[i:], self.w13_scale[i:], self.w13_gscale[1])
+        gs = self.w13_gscale if self.fmt == "nvfp4" else (None, None)
+        g = self._deq(self.w13[:i], self.w13_scale[:i], gs[0])
+        u = self._deq(self.w13[i:], self.w13_scale[i:], gs[1])
         return np.concatenate([g, u], axis=0)
 
     def dequant_w2(self) -> np.ndarray:
-        return nvfp4.dequantize(self.w2, self.w2_scale, self.w2_gscale)
+        return self._deq(self.w2, self.w2_scale, self.w2_gscale)
 
 
 class ArrayBank:
     """A bank of experts held as stacked arrays with a leading expert dimension."""
 
-    def __init__(self, w13, w13_scale, w13_gscale, w2, w2_scale, w2_gscale):
-        self.w13, self.w13_scale, self.w13_gscale = w13, w13_scale, np.asarray(w13_gscale, np.float32)
-        self.w2, self.w2_scale, self.w2_gscale = w2, w2_scale, np.asarray(w2_gscale, np.float32)
+    def __init__(self, w13, w13_scale, w13_gscale, w2, w2_scale, w2_gscale, fmt="nvfp4"):
+        self.fmt = fmt
+        self.w13, self.w13_scale = w13, w13_scale
+        self.w2, self.w2_scale = w2, w2_scale
+        e = w13.shape[0]
+        self.w13_gscale = np.asarray(w13_gscale if w13_gscale is not None else np.ones((e, 2)), np.float32)
+        self.w2_gscale = np.asarray(w2_gscale if w2_gscale is not None else np.ones(e), np.float32)
 
     def __len__(self):
         return self.w13.shape[0]
 
     def __getitem__(self, e) -> ExpertWeights:
         return ExpertWeights(self.w13[e], self.w13_scale[e], self.w13_gscale[e],
-                             self.w2[e], self.w2_scale[e], float(self.w2_gscale[e]))
+                             self.w2[e], self.w2_scale[e], float(self.w2_gscale[e]), self.fmt)
 
 
 @dataclass
