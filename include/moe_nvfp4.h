@@ -84,20 +84,32 @@ typedef enum {
 /* Static, human-readable name of a status code (host). */
 const char* moe_status_string(moe_status_t s);
 
-/* One bank of NVFP4 experts (routed: num_experts = E; shared: num_experts = 1), device pointers.
+/* Weight formats of an expert bank.  Both store E2M1 elements two per byte (element 2j in the low
+ * nibble of byte j) and one block scale per group of consecutive elements along K:
+ *   MOE_WEIGHT_NVFP4: E4M3FN scale per 16 elements and an fp32 global scale per tensor
+ *                     ("vLLM on the NVIDIA DGX Spark", section 6.1);
+ *   MOE_WEIGHT_MXFP4: E8M0 scale per 32 elements, value 2^(byte - 127) (0xFF NaN), no global scale
+ *                     (same guide, section 6.4 "NVFP4 vs MXFP4"). */
+#define MOE_WEIGHT_NVFP4 0
+#define MOE_WEIGHT_MXFP4 1
+
+/* One bank of experts (routed: num_experts = E; shared: num_experts = 1), device pointers.
  * The packed weights and block scales are in the MFMA TILE LAYOUT produced by
- * moe_nvfp4_pack_tiles from the canonical layout: per expert, the canonical [2I][H/2] (w13) or
- * [H][I/2] (w2) bytes and their scale bytes, permuted tile by tile (same sizes). */
+ * moe_nvfp4_pack_tiles (NVFP4) or moe_mxfp4_pack_tiles (MXFP4) from the canonical layout: per
+ * expert, the canonical [2I][H/2] (w13) or [H][I/2] (w2) bytes and their scale bytes, permuted
+ * tile by tile (same sizes).  A zero-initialised `format` is NVFP4; the routed and shared banks of
+ * a layer must share one format. */
 typedef struct {
   int32_t num_experts;
   int32_t hidden;            /* H */
   int32_t inter;             /* I */
+  int32_t format;            /* MOE_WEIGHT_NVFP4 or MOE_WEIGHT_MXFP4 */
   const uint8_t* w13;        /* [E] x tiled [2I][H/2]  packed E2M1, gate rows then up rows */
-  const uint8_t* w13_scale;  /* [E] x tiled [2I][H/16] E4M3FN block scales */
-  const float* w13_gscale;   /* [E][2] dequant global scales (gate, up) */
+  const uint8_t* w13_scale;  /* [E] x tiled [2I][H/16] E4M3FN (NVFP4) or [2I][H/32] E8M0 (MXFP4) */
+  const float* w13_gscale;   /* [E][2] dequant global scales (gate, up); NVFP4 only, may be NULL for MXFP4 */
   const uint8_t* w2;         /* [E] x tiled [H][I/2] */
-  const uint8_t* w2_scale;   /* [E] x tiled [H][I/16] */
-  const float* w2_gscale;    /* [E] */
+  const uint8_t* w2_scale;   /* [E] x tiled [H][I/16] (NVFP4) or [H][I/32] (MXFP4) */
+  const float* w2_gscale;    /* [E]; NVFP4 only, may be NULL for MXFP4 */
 } moe_nvfp4_experts_t;
 
 /* The whole layer: router + routed bank + optional shared bank (shared.num_experts == 0: none). */
@@ -234,6 +246,27 @@ moe_status_t moe_nvfp4_pack_tiles(const uint8_t* packed, const uint8_t* scales, 
  * discussion); block scales clamped to 448 ("Serving Solar Open 2 on DGX Spark"). */
 moe_status_t moe_nvfp4_quantize(const float* w, int32_t num_tensors, int32_t rows, int32_t cols,
                                 const float* gscale, uint8_t* packed, uint8_t* scales, void* stream);
+
+/* MXFP4 counterpart of moe_nvfp4_pack_tiles: canonical packed bytes [rows][cols/2] and E8M0 scale
+ * bytes [rows][cols/32] (rows % 16 == 0, cols % 128 == 0) -> tiles of 1024 nibble bytes (the NVFP4
+ * nibble permutation) and 64 scale bytes: bytes [4n, 4n + 4) of tile t are the canonical scale
+ * bytes [4c, 4c + 4) of row 16nb + n, so byte j is the scale of the elements [128c + 32j, +32),
+ * the operand of MFMA step j.  Same sizes as the canonical layout; out of place.
+ * Source: MXFP4 format ("vLLM on the NVIDIA DGX Spark", section 6.4); the one-time swizzle into
+ * the kernel's MMA layout ("Serving Solar Open 2 on DGX Spark", "Supporting real NVFP4
+ * checkpoints"). */
+moe_status_t moe_mxfp4_pack_tiles(const uint8_t* packed, const uint8_t* scales, int32_t num_tensors, int32_t rows,
+                                  int32_t cols, uint8_t* tiled, uint8_t* tiled_scales, void* stream);
+
+/* On-device MXFP4 quantization of fp32 weights (test and checkpoint-conversion data, not part of
+ * the layer pass).  w: num_tensors tensors of [rows][cols] fp32.  Per 32-group along cols:
+ *   e = floor(log2(amax_group)) - 2 clamped to [-127, 127] (-127 when amax == 0), scale byte e + 127;
+ *   code = E2M1_RNE(|w| * 2^-e) saturating at 6, sign bit set for negative w.
+ * Writes packed [num_tensors][rows][cols/2] and scales [num_tensors][rows][cols/32]; cols % 32 == 0.
+ * Source: MXFP4 format (section 6.4 of the guide above); the shared-exponent rule is the OCP
+ * Microscaling conversion (the guide does not state one). */
+moe_status_t moe_mxfp4_quantize(const float* w, int32_t num_tensors, int32_t rows, int32_t cols, uint8_t* packed,
+                                uint8_t* scales, void* stream);
 
 #ifdef __cplusplus
 }

@@ -31,7 +31,7 @@ size_t = ctypes.c_size_t
 class Experts(ctypes.Structure):
     """moe_nvfp4_experts_t"""
     _fields_ = [
-        ("num_experts", i32), ("hidden", i32), ("inter", i32),
+        ("num_experts", i32), ("hidden", i32), ("inter", i32), ("format", i32),
         ("w13", c_void_p), ("w13_scale", c_void_p), ("w13_gscale", c_void_p),
         ("w2", c_void_p), ("w2_scale", c_void_p), ("w2_gscale", c_void_p),
     ]
@@ -73,7 +73,15 @@ SIGNATURES = {
     "moe_gscale_from_quant_scale": (i32, [c_void_p, c_void_p, i32]),
     "moe_nvfp4_pack_tiles": (i32, [c_void_p, c_void_p, i32, i32, i32, c_void_p, c_void_p, c_void_p]),
     "moe_nvfp4_quantize": (i32, [c_void_p, i32, i32, i32, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "moe_mxfp4_pack_tiles": (i32, [c_void_p, c_void_p, i32, i32, i32, c_void_p, c_void_p, c_void_p]),
+    "moe_mxfp4_quantize": (i32, [c_void_p, i32, i32, i32, c_void_p, c_void_p, c_void_p]),
 }
+
+# weight formats of an expert bank (moe_nvfp4_experts_t.format)
+MOE_WEIGHT_NVFP4 = 0
+MOE_WEIGHT_MXFP4 = 1
+FORMATS = {"nvfp4": MOE_WEIGHT_NVFP4, "mxfp4": MOE_WEIGHT_MXFP4}
+SCALE_GROUP = {"nvfp4": 16, "mxfp4": 32}
 
 _lib = None
 

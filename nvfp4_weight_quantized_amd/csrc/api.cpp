@@ -39,7 +39,9 @@ bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 bool valid_bank(const moe_nvfp4_experts_t& b, int32_t H, int32_t expected_experts) {
   if (b.num_experts != expected_experts || b.hidden != H) return false;
   if (b.inter <= 0 || b.inter % 128 != 0) return false;
-  if (!(b.w13 && b.w13_scale && b.w13_gscale && b.w2 && b.w2_scale && b.w2_gscale)) return false;
+  if (b.format != MOE_WEIGHT_NVFP4 && b.format != MOE_WEIGHT_MXFP4) return false;
+  if (!(b.w13 && b.w13_scale && b.w2 && b.w2_scale)) return false;
+  if (b.format == MOE_WEIGHT_NVFP4 && !(b.w13_gscale && b.w2_gscale)) return false;
   return al16(b.w13) && al16(b.w13_scale) && al16(b.w2) && al16(b.w2_scale);
 }
 
@@ -53,8 +55,8 @@ bool valid_route_dims(int32_t T, int32_t H, int32_t E, int32_t k) {
   return (int64_t)T * k < (int64_t)0x7FFFFFFF;
 }
 
-GemmBank bank_w13(const moe_nvfp4_experts_t& b) { return GemmBank{b.w13, b.w13_scale, b.w13_gscale, 2}; }
-GemmBank bank_w2(const moe_nvfp4_experts_t& b) { return GemmBank{b.w2, b.w2_scale, b.w2_gscale, 1}; }
+GemmBank bank_w13(const moe_nvfp4_experts_t& b) { return GemmBank{b.w13, b.w13_scale, b.w13_gscale, 2, b.format}; }
+GemmBank bank_w2(const moe_nvfp4_experts_t& b) { return GemmBank{b.w2, b.w2_scale, b.w2_gscale, 1, b.format}; }
 
 struct ForwardLayout {
   size_t logits, ids, w, counts, offsets, sorted_slot, slot_to_row, block_hist, h, h_shared, y;
@@ -202,6 +204,7 @@ moe_status_t moe_validate_forward(const moe_nvfp4_layer_t* layer, int32_t T, siz
   if (!valid_bank(layer->routed, H, E)) return MOE_ERR_INVALID_ARGUMENT;
   const bool has_shared = layer->shared.num_experts != 0;
   if (has_shared && !valid_bank(layer->shared, H, 1)) return MOE_ERR_INVALID_ARGUMENT;
+  if (has_shared && layer->shared.format != layer->routed.format) return MOE_ERR_INVALID_ARGUMENT;
   const int32_t I = layer->routed.inter, Is = has_shared ? layer->shared.inter : 0;
   if (((int64_t)T * k + T) * std::max(I, Is) * 2 >= kMaxActivationBytes) return MOE_ERR_INVALID_ARGUMENT;
   if (T > 0 && workspace_bytes < moe_nvfp4_forward_workspace_size(T, H, I, Is, E, k))
@@ -369,6 +372,27 @@ moe_status_t moe_nvfp4_quantize(const float* w, int32_t num_tensors, int32_t row
   if (!al16(w) || !al16(packed)) return MOE_ERR_INVALID_ARGUMENT;
   if (moe_status_t st = check_arch(nullptr)) return st;
   return moe::launch_quantize(w, num_tensors, rows, cols, gscale, packed, scales, static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_mxfp4_pack_tiles(const uint8_t* packed, const uint8_t* scales, int32_t num_tensors, int32_t rows,
+                                  int32_t cols, uint8_t* tiled, uint8_t* tiled_scales, void* stream) {
+  if (num_tensors < 0 || rows < 0 || cols < 0 || rows % 16 != 0 || cols % 128 != 0) return MOE_ERR_INVALID_ARGUMENT;
+  if ((int64_t)num_tensors * rows * cols == 0) return MOE_OK;
+  if (!packed || !scales || !tiled || !tiled_scales) return MOE_ERR_INVALID_ARGUMENT;
+  if (!al16(packed) || !al16(scales) || !al16(tiled) || !al16(tiled_scales)) return MOE_ERR_INVALID_ARGUMENT;
+  if (moe_status_t st = check_arch(nullptr)) return st;
+  return moe::launch_pack_tiles_mx(packed, scales, num_tensors, rows, cols, tiled, tiled_scales,
+                                   static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_mxfp4_quantize(const float* w, int32_t num_tensors, int32_t rows, int32_t cols, uint8_t* packed,
+                                uint8_t* scales, void* stream) {
+  if (num_tensors < 0 || rows < 0 || cols < 0 || cols % 32 != 0) return MOE_ERR_INVALID_ARGUMENT;
+  if ((int64_t)num_tensors * rows * cols == 0) return MOE_OK;
+  if (!w || !packed || !scales) return MOE_ERR_INVALID_ARGUMENT;
+  if (!al16(w) || !al16(packed)) return MOE_ERR_INVALID_ARGUMENT;
+  if (moe_status_t st = check_arch(nullptr)) return st;
+  return moe::launch_quantize_mx(w, num_tensors, rows, cols, packed, scales, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

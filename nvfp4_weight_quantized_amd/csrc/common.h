@@ -66,9 +66,11 @@ moe_status_t launch_route(const uint16_t* x, const uint16_t* w_router, const flo
 // Grouped GEMM ------------------------------------------------------------------------------
 struct GemmBank {
   const uint8_t* w;      // packed nibbles, [E][Nrows][K/2] bytes in the MFMA tile layout (layout.hip)
-  const uint8_t* ws;     // E4M3 block scales, [E][Nrows][K/16] bytes in the MFMA tile layout
-  const float* gs;       // dequant global scales, [E][gs_per_expert]
+  const uint8_t* ws;     // block scales in the tile layout: E4M3 [E][Nrows][K/16] (NVFP4) or
+                         // E8M0 [E][Nrows][K/32] (MXFP4)
+  const float* gs;       // dequant global scales, [E][gs_per_expert] (NVFP4; unused for MXFP4)
   int32_t gs_per_expert; // 2 (gate, up) or 1 (down)
+  int32_t format;        // MOE_WEIGHT_NVFP4 or MOE_WEIGHT_MXFP4
 };
 
 struct GemmProblem {
@@ -120,9 +122,13 @@ moe_status_t launch_combine(const uint16_t* y_rows, const int32_t* slot_to_row, 
 // Weight tile layout ------------------------------------------------------------------------
 moe_status_t launch_pack_tiles(const uint8_t* packed, const uint8_t* scales, int32_t num_tensors, int32_t rows,
                                int32_t cols, uint8_t* tiled, uint8_t* tiled_scales, hipStream_t stream);
+moe_status_t launch_pack_tiles_mx(const uint8_t* packed, const uint8_t* scales, int32_t num_tensors, int32_t rows,
+                                  int32_t cols, uint8_t* tiled, uint8_t* tiled_scales, hipStream_t stream);
 
 // Quantize ----------------------------------------------------------------------------------
 moe_status_t launch_quantize(const float* w, int32_t num_tensors, int32_t rows, int32_t cols,
                              const float* gscale, uint8_t* packed, uint8_t* scales, hipStream_t stream);
+moe_status_t launch_quantize_mx(const float* w, int32_t num_tensors, int32_t rows, int32_t cols, uint8_t* packed,
+                                uint8_t* scales, hipStream_t stream);
 
 }  // namespace moe

@@ -95,6 +95,46 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& w, const bf16x8& x, const f3
 __device__ __forceinline__ int w_lane_offset(int lane) { return 16 * lane; }
 __device__ __forceinline__ int s_lane_offset(int lane) { return 8 * (lane & 15) + 4 * ((lane >> 4) >> 1); }
 
+// Weight formats.  NVFP4: E4M3 scale per 16 elements (128 scale bytes per tile) and fp32 global
+// scales applied in the epilogue.  MXFP4 ("vLLM on the NVIDIA DGX Spark", section 6.4): one E8M0
+// exponent-only scale per 32 elements -- exactly one per MFMA step -- so a tile has 64 scale bytes
+// (the dword at 4*(row in tile) holds step j's scale in byte j), there is no global scale, and the
+// conversion applies the scale itself: given the E8M0 byte as an fp32 exponent field,
+// v_cvt_scalef32_pk_bf16_fp4 multiplies by exactly 2^(byte - 127) (byte 0 included; checked on the
+// GPU), one instruction per two codes.
+constexpr int kFmtNvfp4 = MOE_WEIGHT_NVFP4;
+constexpr int kFmtMxfp4 = MOE_WEIGHT_MXFP4;
+
+template <int FMT>
+struct WFmt;
+
+template <>
+struct WFmt<kFmtNvfp4> {
+  static constexpr int kTileScaleBytes = 128;
+  static constexpr int kScaleGroup = 16;
+  static constexpr bool kGlobalScale = true;
+  __device__ static int s_lane(int lane) { return s_lane_offset(lane); }
+  __device__ static bf16x8 operand(const uint4& w, uint32_t sc, int j) { return w_operand(w, sc, j); }
+};
+
+template <>
+struct WFmt<kFmtMxfp4> {
+  static constexpr int kTileScaleBytes = 64;
+  static constexpr int kScaleGroup = 32;
+  static constexpr bool kGlobalScale = false;
+  __device__ static int s_lane(int lane) { return 4 * (lane & 15); }
+  __device__ static bf16x8 operand(const uint4& w, uint32_t sc, int j) {
+    const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+    const float scale = __uint_as_float(((sc >> (8 * j)) & 0xFFu) << 23);
+    const uint32_t q = words[j];
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 0);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 1);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 2);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, scale, 3);
+    return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  }
+};
+
 // Streaming (non-temporal) loads for weight bytes that are read once per pass.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_stream16(const uint8_t* p) {
@@ -201,16 +241,16 @@ __device__ __forceinline__ int frag_row_block(int f, int ntile, int wave, int N)
 // Epilogue: scale the accumulators by the global scale(s), SiLU(gate)*up for gate/up, store bf16.
 // acc[i][f] holds, in lane l = 16q + n, output row 16i + n and the four columns 4q..4q+3 of
 // fragment f's 16 columns.
-template <int MI, int NB, bool GATE_UP, int BN, int COLS_PER_WAVE>
+template <int MI, int NB, bool GATE_UP, int BN, int COLS_PER_WAVE, int FMT = kFmtNvfp4>
 __device__ __forceinline__ void epilogue(const GemmProblem& p, const GemmBank& bank, const TileInfo& ti, int ntile,
                                          const f32x4 (&acc)[MI][NB], int mtile = 0) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int q = lane >> 4, nl = lane & 15;
-  const float* gs = bank.gs + (size_t)ti.group * bank.gs_per_expert;
+  const float* gs = WFmt<FMT>::kGlobalScale ? bank.gs + (size_t)ti.group * bank.gs_per_expert : nullptr;
   const int col0 = ntile * BN + wave * COLS_PER_WAVE + 4 * q;
   if (GATE_UP) {
-    const float dg = gs[0], du = gs[1];
+    const float dg = gs ? gs[0] : 1.f, du = gs ? gs[1] : 1.f;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int row = 16 * i + nl;
@@ -234,7 +274,7 @@ __device__ __forceinline__ void epilogue(const GemmProblem& p, const GemmBank& b
       }
     }
   } else {
-    const float dd = gs[0];
+    const float dd = gs ? gs[0] : 1.f;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int row = 16 * i + nl;
@@ -435,8 +475,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_skinny_kernel(GemmProbl
 // Short and medium tiles.  MI: 16-row A fragments per wave (BM = 16*MI); NB: 16-column B
 // fragments per wave; BK: K chunk staged in LDS per barrier (a multiple of 128: BK/128 weight
 // tiles per fragment per chunk).  A is copied global -> registers -> LDS one chunk ahead.
-template <int MI, int NB, int BK, bool GATE_UP>
+template <int MI, int NB, int BK, bool GATE_UP, int FMT>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmProblem p) {
+  using F = WFmt<FMT>;
   constexpr int BM = 16 * MI;
   constexpr int COLS_PER_WAVE = GATE_UP ? 16 * (NB / 2) : 16 * NB;   // output columns per wave
   constexpr int BN = 4 * COLS_PER_WAVE;                               // output columns per workgroup
@@ -491,14 +532,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmProblem p) {
   const int nl = lane & 15;
   const size_t rows_per_expert = GATE_UP ? 2 * (size_t)p.N : (size_t)p.N;
   const uint8_t* wexp = bank.w + (size_t)ti.group * rows_per_expert * (size_t)(K / 2) + w_lane_offset(lane);
-  const uint8_t* sexp = bank.ws + (size_t)ti.group * rows_per_expert * (size_t)(K / 16) + s_lane_offset(lane);
+  const uint8_t* sexp = bank.ws + (size_t)ti.group * rows_per_expert * (size_t)(K / F::kScaleGroup) + F::s_lane(lane);
   const uint8_t* wptr[NB];
   const uint8_t* sptr[NB];
 #pragma unroll
   for (int f = 0; f < NB; ++f) {
     const size_t t0 = (size_t)frag_row_block<NB, GATE_UP, BN, COLS_PER_WAVE>(f, ntile, wave, p.N) * ktiles;
     wptr[f] = wexp + t0 * 1024;
-    sptr[f] = sexp + t0 * 128;
+    sptr[f] = sexp + t0 * F::kTileScaleBytes;
   }
 
   f32x4 acc[MI][NB];
@@ -520,7 +561,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmProblem p) {
       for (int v = 0; v < NS; ++v) {
         const size_t t = (size_t)c * NS + v;
         b_next[f][v] = load_stream16(wptr[f] + t * 1024);
-        s_next[f][v] = load_stream4(sptr[f] + t * 128);
+        s_next[f][v] = load_stream4(sptr[f] + t * F::kTileScaleBytes);
       }
   };
   load_chunk(0);
@@ -548,7 +589,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmProblem p) {
       for (int j = 0; j < 4; ++j) {
         bf16x8 wfrag[NB];
 #pragma unroll
-        for (int f = 0; f < NB; ++f) wfrag[f] = w_operand(bq[f][v], sc[f][v], j);
+        for (int f = 0; f < NB; ++f) wfrag[f] = F::operand(bq[f][v], sc[f][v], j);
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
           const bf16x8 xfrag = *reinterpret_cast<const bf16x8*>(&As[16 * i + nl][128 * v + 32 * j + 8 * q]);
@@ -557,7 +598,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmProblem p) {
         }
       }
   }
-  epilogue<MI, NB, GATE_UP, BN, COLS_PER_WAVE>(p, bank, ti, ntile, acc);
+  epilogue<MI, NB, GATE_UP, BN, COLS_PER_WAVE, FMT>(p, bank, ti, ntile, acc);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -593,8 +634,9 @@ struct IntC {
   static constexpr int value = N;
 };
 
-template <int NB, bool GATE_UP, int WAVES>
+template <int NB, bool GATE_UP, int WAVES, int FMT>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kernel(GemmProblem p) {
+  using F = WFmt<FMT>;
   constexpr int MI = kTallRows / 16;
   constexpr int BM = kTallRows;
   constexpr int BK = kTallBK;
@@ -673,9 +715,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
   const int ktiles = K / 128;
   const size_t rows_per_expert = GATE_UP ? 2 * (size_t)p.N : (size_t)p.N;
   const uint8_t* wexp = bank.w + (size_t)ti.group * rows_per_expert * (size_t)(K / 2);
-  const uint8_t* sexp = bank.ws + (size_t)ti.group * rows_per_expert * (size_t)(K / 16);
+  const uint8_t* sexp = bank.ws + (size_t)ti.group * rows_per_expert * (size_t)(K / F::kScaleGroup);
   const uint32_t w_lane = (uint32_t)w_lane_offset(lane);
-  const uint32_t s_lane = (uint32_t)s_lane_offset(lane);
+  const uint32_t s_lane = (uint32_t)F::s_lane(lane);
   uint32_t tile0[NB];
 #pragma unroll
   for (int f = 0; f < NB; ++f)
@@ -694,7 +736,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
     for (int f = 0; f < NB; ++f) {
       const size_t t = (size_t)tile0[f] + (size_t)c;
       bn[f] = *reinterpret_cast<const uint4*>(wexp + t * 1024 + w_lane);
-      sn[f] = *reinterpret_cast<const uint32_t*>(sexp + t * 128 + s_lane);
+      sn[f] = *reinterpret_cast<const uint32_t*>(sexp + t * F::kTileScaleBytes + s_lane);
     }
   };
   auto issue_a = [&](int c, int buf) {
@@ -750,14 +792,14 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
       // the next step's weight operands are dequantized while this step's MFMAs run
       bf16x8 wcur[NB];
 #pragma unroll
-      for (int f = 0; f < NB; ++f) wcur[f] = w_operand(bq[f], sc[f], 0);
+      for (int f = 0; f < NB; ++f) wcur[f] = F::operand(bq[f], sc[f], 0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < STEPS; ++j) {
         bf16x8 wnext[NB];
         if (j + 1 < STEPS) {
 #pragma unroll
-          for (int f = 0; f < NB; ++f) wnext[f] = w_operand(bq[f], sc[f], j + 1);
+          for (int f = 0; f < NB; ++f) wnext[f] = F::operand(bq[f], sc[f], j + 1);
         }
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
@@ -789,10 +831,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
     case 7: run(IntC<7>{}); break;
     default: run(IntC<8>{}); break;
   }
-  epilogue<MI, NB, GATE_UP, BN, COLS_PER_WAVE>(p, bank, ti, ntile, acc, mtile);
+  epilogue<MI, NB, GATE_UP, BN, COLS_PER_WAVE, FMT>(p, bank, ti, ntile, acc, mtile);
 }
 
-template <int NB, bool GATE_UP, int WAVES>
+template <int NB, bool GATE_UP, int WAVES, int FMT>
 moe_status_t launch_tall(const GemmProblem& p, hipStream_t stream) {
   constexpr int BN = WAVES * (GATE_UP ? 16 * (NB / 2) : 16 * NB);
   if (p.N % BN != 0 || p.K % kTallBK != 0) return MOE_ERR_INVALID_ARGUMENT;
@@ -803,12 +845,12 @@ moe_status_t launch_tall(const GemmProblem& p, hipStream_t stream) {
   if (grid == 0) return MOE_OK;
   grid = (grid + kXcds - 1) / kXcds * kXcds;
   if (grid > 0x7FFFFFFFLL) return MOE_ERR_INVALID_ARGUMENT;
-  hipLaunchKernelGGL((grouped_gemm_tall_kernel<NB, GATE_UP, WAVES>), dim3((unsigned)grid), dim3(64 * WAVES), 0, stream,
+  hipLaunchKernelGGL((grouped_gemm_tall_kernel<NB, GATE_UP, WAVES, FMT>), dim3((unsigned)grid), dim3(64 * WAVES), 0, stream,
                      p);
   return launch_status();
 }
 
-template <int MI, int NB, int BK, bool GATE_UP>
+template <int MI, int NB, int BK, bool GATE_UP, int FMT>
 moe_status_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
   constexpr int BM = 16 * MI;
   constexpr int BN = GATE_UP ? 4 * 16 * (NB / 2) : 4 * 16 * NB;
@@ -820,7 +862,7 @@ moe_status_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
   const long long grid = mt * NT;
   if (grid == 0) return MOE_OK;
   if (grid > 0x7FFFFFFFLL) return MOE_ERR_INVALID_ARGUMENT;
-  hipLaunchKernelGGL((grouped_gemm_kernel<MI, NB, BK, GATE_UP>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((grouped_gemm_kernel<MI, NB, BK, GATE_UP, FMT>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   return launch_status();
 }
 
@@ -841,11 +883,11 @@ moe_status_t launch_skinny(const GemmProblem& p, hipStream_t stream) {
 
 // Few rows per expert: 16-row tiles; 512-wide K chunks for long reductions, 256-wide for shorter
 // ones (more workgroups in flight; measured on the decode-shaped down GEMM, K = 1536).
-template <bool GATE_UP>
+template <bool GATE_UP, int FMT>
 moe_status_t launch_small(const GemmProblem& p, hipStream_t stream) {
-  if (p.K % 512 == 0 && p.K >= 4096) return launch_cfg<1, 2, 512, GATE_UP>(p, stream);
-  if (p.K % 256 == 0) return launch_cfg<1, 2, 256, GATE_UP>(p, stream);
-  return launch_cfg<1, 2, 128, GATE_UP>(p, stream);
+  if (p.K % 512 == 0 && p.K >= 4096) return launch_cfg<1, 2, 512, GATE_UP, FMT>(p, stream);
+  if (p.K % 256 == 0) return launch_cfg<1, 2, 256, GATE_UP, FMT>(p, stream);
+  return launch_cfg<1, 2, 128, GATE_UP, FMT>(p, stream);
 }
 
 }  // namespace
@@ -859,29 +901,41 @@ long long avg_rows(const GemmProblem& p) {
 }
 }  // namespace
 
-bool grouped_gemm_uses_tall_tiles(const GemmProblem& p) { return avg_rows(p) > 32; }
-
-moe_status_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
+namespace {
+template <int FMT>
+moe_status_t launch_format(const GemmProblem& p, hipStream_t stream) {
   const bool gate_up = p.stage == MOE_GEMM_GATE_UP;
   const long long avg = avg_rows(p);
-  // the tiled activation layouts exist only on the 128-row path
-  if ((p.a_tiled || p.out_tiled) && !grouped_gemm_uses_tall_tiles(p)) return MOE_ERR_INVALID_ARGUMENT;
-  if (p.out_tiled && !gate_up) return MOE_ERR_INVALID_ARGUMENT;
-  if (avg <= kSkinnyRows) {
+  // the skinny kernel applies E4M3 scales to per-group sums; MXFP4 needs no such trick (its scale
+  // is applied by the conversion), so its few-row groups take the 16-row kernel
+  if (FMT == kFmtNvfp4 && avg <= kSkinnyRows) {
     if (p.K % 256 == 0) return gate_up ? launch_skinny<2, 256, true>(p, stream) : launch_skinny<2, 256, false>(p, stream);
     return gate_up ? launch_skinny<2, 128, true>(p, stream) : launch_skinny<2, 128, false>(p, stream);
   }
   if (gate_up) {
-    if (avg <= 16) return launch_small<true>(p, stream);
-    if (avg <= 32) return launch_cfg<4, 4, 128, true>(p, stream);
+    if (avg <= 16) return launch_small<true, FMT>(p, stream);
+    if (avg <= 32) return launch_cfg<4, 4, 128, true, FMT>(p, stream);
     // eight waves (one workgroup per CU) where the width allows: half the A traffic per MFMA
-    return (p.N % 256 == 0) ? launch_tall<4, true, 8>(p, stream) : launch_tall<4, true, 4>(p, stream);
+    return (p.N % 256 == 0) ? launch_tall<4, true, 8, FMT>(p, stream) : launch_tall<4, true, 4, FMT>(p, stream);
   }
   const bool wide = (p.N % 256) == 0;
-  if (avg <= 16) return launch_small<false>(p, stream);
-  if (avg <= 32) return wide ? launch_cfg<4, 4, 128, false>(p, stream) : launch_cfg<4, 2, 128, false>(p, stream);
-  if (p.N % 512 == 0) return launch_tall<4, false, 8>(p, stream);
-  return wide ? launch_tall<4, false, 4>(p, stream) : launch_tall<2, false, 4>(p, stream);
+  if (avg <= 16) return launch_small<false, FMT>(p, stream);
+  if (avg <= 32) return wide ? launch_cfg<4, 4, 128, false, FMT>(p, stream) : launch_cfg<4, 2, 128, false, FMT>(p, stream);
+  if (p.N % 512 == 0) return launch_tall<4, false, 8, FMT>(p, stream);
+  return wide ? launch_tall<4, false, 4, FMT>(p, stream) : launch_tall<2, false, 4, FMT>(p, stream);
+}
+}  // namespace
+
+bool grouped_gemm_uses_tall_tiles(const GemmProblem& p) { return avg_rows(p) > 32; }
+
+moe_status_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
+  // the tiled activation layouts exist only on the 128-row path
+  if ((p.a_tiled || p.out_tiled) && !grouped_gemm_uses_tall_tiles(p)) return MOE_ERR_INVALID_ARGUMENT;
+  if (p.out_tiled && p.stage != MOE_GEMM_GATE_UP) return MOE_ERR_INVALID_ARGUMENT;
+  if (p.has_extra && p.extra.format != p.bank.format) return MOE_ERR_INVALID_ARGUMENT;
+  if (p.bank.format == kFmtMxfp4) return launch_format<kFmtMxfp4>(p, stream);
+  if (p.bank.format == kFmtNvfp4) return launch_format<kFmtNvfp4>(p, stream);
+  return MOE_ERR_INVALID_ARGUMENT;
 }
 
 }  // namespace moe

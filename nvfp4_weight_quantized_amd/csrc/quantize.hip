@@ -78,7 +78,46 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
   scales[g] = (uint8_t)scode;
 }
 
+// MXFP4 ("vLLM on the NVIDIA DGX Spark", section 6.4: E2M1 elements, one E8M0 exponent-only
+// scale per 32 elements, no global scale).  One thread per 32-element group:
+//   e = floor(log2(amax)) - 2 clamped to [-127, 127] (-127 when amax == 0), scale byte e + 127;
+//   code = E2M1_RNE(|w| * 2^-e) saturated at 6 (exact power-of-two scaling), sign bit = (w < 0).
+__global__ __launch_bounds__(256) void quantize_mx_kernel(const float* __restrict__ w, long long total_groups,
+                                                          uint8_t* __restrict__ packed, uint8_t* __restrict__ scales) {
+  const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (g >= total_groups) return;
+  const float4* src = reinterpret_cast<const float4*>(w + g * 32);
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 x = src[i];
+    v[4 * i] = x.x; v[4 * i + 1] = x.y; v[4 * i + 2] = x.z; v[4 * i + 3] = x.w;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int e = amax > 0.f ? min(max(ilogbf(amax) - 2, -127), 127) : -127;
+  uint32_t word[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t c = e2m1_rne(ldexpf(fabsf(v[i]), -e)) | (v[i] < 0.f ? 8u : 0u);
+    word[i >> 3] |= c << (4 * (i & 7));
+  }
+  *reinterpret_cast<uint4*>(packed + g * 16) = uint4{word[0], word[1], word[2], word[3]};
+  scales[g] = (uint8_t)(e + 127);
+}
+
 }  // namespace
+
+moe_status_t launch_quantize_mx(const float* w, int32_t num_tensors, int32_t rows, int32_t cols, uint8_t* packed,
+                                uint8_t* scales, hipStream_t stream) {
+  const long long total = (long long)num_tensors * rows * (cols / 32);
+  if (total == 0) return MOE_OK;
+  const long long blocks = (total + 255) / 256;
+  if (blocks > 0x7FFFFFFFLL) return MOE_ERR_INVALID_ARGUMENT;
+  hipLaunchKernelGGL(quantize_mx_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w, total, packed, scales);
+  return launch_status();
+}
 
 moe_status_t launch_quantize(const float* w, int32_t num_tensors, int32_t rows, int32_t cols,
                              const float* gscale, uint8_t* packed, uint8_t* scales, hipStream_t stream) {

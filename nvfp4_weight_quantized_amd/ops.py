@@ -41,18 +41,20 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: Optional[int] = None):
 
 @dataclass
 class NvFp4Experts:
-    """A bank of NVFP4 experts on the GPU, weights and scales in the MFMA tile layout.
+    """A bank of 4-bit experts on the GPU, weights and scales in the MFMA tile layout.
 
-    Shapes are those of the canonical tensors (include/moe_nvfp4.h); the bytes of each expert's
-    tensors are permuted by ``pack_tiles``.  Use ``NvFp4Experts.from_canonical`` to build one from
-    checkpoint-layout tensors.
+    ``fmt`` "nvfp4": E4M3 scales per 16 elements along K plus fp32 global scales; "mxfp4": E8M0
+    scales per 32 elements and no global scale (the gscale tensors are None).  Shapes are those of
+    the canonical tensors (include/moe_nvfp4.h); the bytes of each expert's tensors are permuted by
+    ``pack_tiles``.  Use ``NvFp4Experts.from_canonical`` to build one from checkpoint-layout tensors.
     """
-    w13: torch.Tensor          # uint8 [E, 2I, H/2]
-    w13_scale: torch.Tensor    # uint8 [E, 2I, H/16]
-    w13_gscale: torch.Tensor   # float32 [E, 2]
-    w2: torch.Tensor           # uint8 [E, H, I/2]
-    w2_scale: torch.Tensor     # uint8 [E, H, I/16]
-    w2_gscale: torch.Tensor    # float32 [E]
+    w13: torch.Tensor                    # uint8 [E, 2I, H/2]
+    w13_scale: torch.Tensor              # uint8 [E, 2I, H/16] (nvfp4) or [E, 2I, H/32] (mxfp4)
+    w13_gscale: Optional[torch.Tensor]   # float32 [E, 2] (nvfp4) or None
+    w2: torch.Tensor                     # uint8 [E, H, I/2]
+    w2_scale: torch.Tensor               # uint8 [E, H, I/16] or [E, H, I/32]
+    w2_gscale: Optional[torch.Tensor]    # float32 [E] (nvfp4) or None
+    fmt: str = "nvfp4"
 
     @property
     def num_experts(self) -> int:
@@ -67,28 +69,36 @@ class NvFp4Experts:
         return self.w13.shape[1] // 2
 
     def check(self) -> None:
-        e, h, i = self.num_experts, self.hidden, self.inter
-        for name, t, dt, shape in [("w13", self.w13, torch.uint8, (e, 2 * i, h // 2)),
-                                   ("w13_scale", self.w13_scale, torch.uint8, (e, 2 * i, h // 16)),
-                                   ("w13_gscale", self.w13_gscale, torch.float32, (e, 2)),
-                                   ("w2", self.w2, torch.uint8, (e, h, i // 2)),
-                                   ("w2_scale", self.w2_scale, torch.uint8, (e, h, i // 16)),
-                                   ("w2_gscale", self.w2_gscale, torch.float32, (e,))]:
+        if self.fmt not in L.FORMATS:
+            raise ValueError(f"unknown weight format {self.fmt!r}")
+        e, h, i, g = self.num_experts, self.hidden, self.inter, L.SCALE_GROUP[self.fmt]
+        specs = [("w13", self.w13, torch.uint8, (e, 2 * i, h // 2)),
+                 ("w13_scale", self.w13_scale, torch.uint8, (e, 2 * i, h // g)),
+                 ("w2", self.w2, torch.uint8, (e, h, i // 2)),
+                 ("w2_scale", self.w2_scale, torch.uint8, (e, h, i // g))]
+        if self.fmt == "nvfp4":
+            specs += [("w13_gscale", self.w13_gscale, torch.float32, (e, 2)),
+                      ("w2_gscale", self.w2_gscale, torch.float32, (e,))]
+        for name, t, dt, shape in specs:
+            if t is None:
+                raise ValueError(f"{name} is required for {self.fmt}")
             _need(t, name, dt)
             if tuple(t.shape) != shape:
                 raise ValueError(f"{name}: expected shape {shape}, got {tuple(t.shape)}")
 
     @classmethod
-    def from_canonical(cls, w13, w13_scale, w13_gscale, w2, w2_scale, w2_gscale) -> "NvFp4Experts":
+    def from_canonical(cls, w13, w13_scale, w13_gscale, w2, w2_scale, w2_gscale, fmt: str = "nvfp4") -> "NvFp4Experts":
         """Repack canonical-layout device tensors into the tile layout (new tensors)."""
-        t13, s13 = pack_tiles(w13, w13_scale)
-        t2, s2 = pack_tiles(w2, w2_scale)
-        return cls(t13, s13, w13_gscale, t2, s2, w2_gscale)
+        t13, s13 = pack_tiles(w13, w13_scale, fmt=fmt)
+        t2, s2 = pack_tiles(w2, w2_scale, fmt=fmt)
+        return cls(t13, s13, w13_gscale, t2, s2, w2_gscale, fmt)
 
     def c_struct(self) -> L.Experts:
-        return L.Experts(self.num_experts, self.hidden, self.inter,
-                         self.w13.data_ptr(), self.w13_scale.data_ptr(), self.w13_gscale.data_ptr(),
-                         self.w2.data_ptr(), self.w2_scale.data_ptr(), self.w2_gscale.data_ptr())
+        def addr(t):
+            return t.data_ptr() if t is not None else None
+        return L.Experts(self.num_experts, self.hidden, self.inter, L.FORMATS[self.fmt],
+                         self.w13.data_ptr(), self.w13_scale.data_ptr(), addr(self.w13_gscale),
+                         self.w2.data_ptr(), self.w2_scale.data_ptr(), addr(self.w2_gscale))
 
 
 @dataclass
@@ -116,17 +126,21 @@ class NvFp4MoELayer:
 
     @classmethod
     def from_tensors(cls, tensors: dict, top_k: int, global_scale_convention: str = "modelopt",
-                     device="cuda") -> "NvFp4MoELayer":
+                     device="cuda", weight_format: str = "nvfp4") -> "NvFp4MoELayer":
         """Build a layer from a checkpoint-like dict.
 
         Keys: router.weight, router.bias (optional), experts.{w13, w13_scale, w13_global_scale,
         w2, w2_scale, w2_global_scale} and the same under shared_expert.* (optional).
         Global scales in the "compressed_tensors" convention are quant scales (448*6)/amax and are
         inverted on load; "modelopt" global scales are dequant scales and are used as stored.
-        Any activation-scale key (``*input_scale*``) is ignored: the layer is weight-only.
+        With ``weight_format="mxfp4"`` the scales are E8M0 per 32 elements and there are no
+        global-scale keys.  Any activation-scale key (``*input_scale*``) is ignored: the layer is
+        weight-only.
         """
         if global_scale_convention not in ("modelopt", "compressed_tensors"):
             raise ValueError(global_scale_convention)
+        if weight_format not in L.FORMATS:
+            raise ValueError(weight_format)
 
         def dev(t, dtype):
             return torch.as_tensor(t).to(device=device, dtype=dtype).contiguous()
@@ -140,11 +154,12 @@ class NvFp4MoELayer:
         def bank(prefix):
             if prefix + "w13" not in tensors:
                 return None
+            nv = weight_format == "nvfp4"
             return NvFp4Experts.from_canonical(
                 dev(tensors[prefix + "w13"], torch.uint8), dev(tensors[prefix + "w13_scale"], torch.uint8),
-                gscale(tensors[prefix + "w13_global_scale"]),
+                gscale(tensors[prefix + "w13_global_scale"]) if nv else None,
                 dev(tensors[prefix + "w2"], torch.uint8), dev(tensors[prefix + "w2_scale"], torch.uint8),
-                gscale(tensors[prefix + "w2_global_scale"]))
+                gscale(tensors[prefix + "w2_global_scale"]) if nv else None, fmt=weight_format)
 
         routed = bank("experts.")
         shared = bank("shared_expert.")
@@ -313,20 +328,21 @@ def gscale_from_quant_scale(q) -> np.ndarray:
 
 
 def pack_tiles(packed: torch.Tensor, scales: torch.Tensor, tiled: Optional[torch.Tensor] = None,
-               tiled_scales: Optional[torch.Tensor] = None):
-    """Canonical [..., rows, cols/2] nibbles + [..., rows, cols/16] scales -> MFMA tile layout (same shapes)."""
+               tiled_scales: Optional[torch.Tensor] = None, fmt: str = "nvfp4"):
+    """Canonical [..., rows, cols/2] nibbles + [..., rows, cols/16] (nvfp4) or [..., rows, cols/32]
+    (mxfp4) scales -> MFMA tile layout (same shapes)."""
     _need(packed, "packed", torch.uint8)
     _need(scales, "scales", torch.uint8)
     rows, half = packed.shape[-2], packed.shape[-1]
     cols = half * 2
     nt = int(np.prod(packed.shape[:-2])) if packed.dim() > 2 else 1
-    if tuple(scales.shape) != tuple(packed.shape[:-1]) + (cols // 16,):
+    if tuple(scales.shape) != tuple(packed.shape[:-1]) + (cols // L.SCALE_GROUP[fmt],):
         raise ValueError("scales shape does not match packed")
     tiled = torch.empty_like(packed) if tiled is None else tiled
     tiled_scales = torch.empty_like(scales) if tiled_scales is None else tiled_scales
-    L.check("moe_nvfp4_pack_tiles", L.lib().moe_nvfp4_pack_tiles(_ptr(packed), _ptr(scales), nt, rows, cols,
-                                                                 _ptr(tiled), _ptr(tiled_scales),
-                                                                 _stream(packed.device)))
+    fn = "moe_nvfp4_pack_tiles" if fmt == "nvfp4" else "moe_mxfp4_pack_tiles"
+    L.check(fn, getattr(L.lib(), fn)(_ptr(packed), _ptr(scales), nt, rows, cols, _ptr(tiled), _ptr(tiled_scales),
+                                     _stream(packed.device)))
     return tiled, tiled_scales
 
 
@@ -348,4 +364,21 @@ def quantize(w: torch.Tensor, gscale: torch.Tensor, packed: Optional[torch.Tenso
     _need(scales, "scales", torch.uint8)
     L.check("moe_nvfp4_quantize", L.lib().moe_nvfp4_quantize(_ptr(w), nt, rows, cols, _ptr(gscale), _ptr(packed),
                                                              _ptr(scales), _stream(w.device)))
+    return packed, scales
+
+
+def quantize_mx(w: torch.Tensor, packed: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None):
+    """On-device MXFP4 quantization of fp32 [..., rows, cols] (E8M0 scale per 32 elements)."""
+    _need(w, "w", torch.float32)
+    rows, cols = w.shape[-2], w.shape[-1]
+    nt = int(np.prod(w.shape[:-2])) if w.dim() > 2 else 1
+    lead = tuple(w.shape[:-2])
+    if packed is None:
+        packed = torch.empty(*lead, rows, cols // 2, dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty(*lead, rows, cols // 32, dtype=torch.uint8, device=w.device)
+    _need(packed, "packed", torch.uint8)
+    _need(scales, "scales", torch.uint8)
+    L.check("moe_mxfp4_quantize", L.lib().moe_mxfp4_quantize(_ptr(w), nt, rows, cols, _ptr(packed), _ptr(scales),
+                                                             _stream(w.device)))
     return packed, scales

@@ -1,6 +1,6 @@
-"""Synthetic NVFP4 MoE layers on the GPU: seeded fp32 weights quantized by the library's own
-on-device quantizer (moe_nvfp4_quantize), global scales in the workload's checkpoint convention
-and converted on load like a real checkpoint."""
+"""Synthetic NVFP4 (or MXFP4) MoE layers on the GPU: seeded fp32 weights quantized by the
+library's own on-device quantizers (moe_nvfp4_quantize / moe_mxfp4_quantize), NVFP4 global scales
+in the workload's checkpoint convention and converted on load like a real checkpoint."""
 
 from __future__ import annotations
 
@@ -16,9 +16,35 @@ def _dequant_scales(amax, convention: str):
     return gs
 
 
-def build_bank(wl: synth.Workload, bank: str, device="cuda") -> ops.NvFp4Experts:
+def build_bank_mx(wl: synth.Workload, bank: str, device="cuda") -> ops.NvFp4Experts:
+    """The same seeded fp32 experts quantized to MXFP4 (E8M0 scales per 32, no global scale)."""
+    count = wl.E if bank == "routed" else 1
+    inter = wl.I if bank == "routed" else wl.I_shared
+    h = wl.H
+    dev = torch.device(device)
+    w13 = torch.empty(count, 2 * inter, h // 2, dtype=torch.uint8, device=dev)
+    w13_s = torch.empty(count, 2 * inter, h // 32, dtype=torch.uint8, device=dev)
+    w2 = torch.empty(count, h, inter // 2, dtype=torch.uint8, device=dev)
+    w2_s = torch.empty(count, h, inter // 32, dtype=torch.uint8, device=dev)
+    c13 = torch.empty(2 * inter, h // 2, dtype=torch.uint8, device=dev)
+    c13_s = torch.empty(2 * inter, h // 32, dtype=torch.uint8, device=dev)
+    c2 = torch.empty(h, inter // 2, dtype=torch.uint8, device=dev)
+    c2_s = torch.empty(h, inter // 32, dtype=torch.uint8, device=dev)
+    for e in range(count):
+        f13, f2 = synth.expert_fp32(wl, bank, e, dev)
+        ops.quantize_mx(f13, packed=c13, scales=c13_s)
+        ops.quantize_mx(f2, packed=c2, scales=c2_s)
+        ops.pack_tiles(c13, c13_s, tiled=w13[e], tiled_scales=w13_s[e], fmt="mxfp4")
+        ops.pack_tiles(c2, c2_s, tiled=w2[e], tiled_scales=w2_s[e], fmt="mxfp4")
+        del f13, f2
+    return ops.NvFp4Experts(w13, w13_s, None, w2, w2_s, None, fmt="mxfp4")
+
+
+def build_bank(wl: synth.Workload, bank: str, device="cuda", fmt: str = "nvfp4") -> ops.NvFp4Experts:
     """Quantize every expert of a bank ("routed": E experts of width I; "shared": 1 of width I_shared)
     on the GPU and repack it into the MFMA tile layout."""
+    if fmt == "mxfp4":
+        return build_bank_mx(wl, bank, device)
     count = wl.E if bank == "routed" else 1
     inter = wl.I if bank == "routed" else wl.I_shared
     h = wl.H
@@ -48,11 +74,11 @@ def build_bank(wl: synth.Workload, bank: str, device="cuda") -> ops.NvFp4Experts
     return ops.NvFp4Experts(w13, w13_s, gs13.to(dev), w2, w2_s, gs2.to(dev))
 
 
-def build_layer(wl: synth.Workload, device="cuda") -> ops.NvFp4MoELayer:
+def build_layer(wl: synth.Workload, device="cuda", fmt: str = "nvfp4") -> ops.NvFp4MoELayer:
     bias = synth.router_bias(wl)
     return ops.NvFp4MoELayer(
         w_router=synth.router_weight(wl, device).contiguous(),
         router_bias=torch.from_numpy(bias).to(device) if bias is not None else None,
-        routed=build_bank(wl, "routed", device),
-        shared=build_bank(wl, "shared", device) if wl.I_shared > 0 else None,
+        routed=build_bank(wl, "routed", device, fmt),
+        shared=build_bank(wl, "shared", device, fmt) if wl.I_shared > 0 else None,
         top_k=wl.k)

@@ -7,6 +7,7 @@ import torch
 
 from nvfp4_weight_quantized_amd import synth
 from oracle import moe as omoe
+from oracle import mxfp4 as omx
 from oracle import nvfp4 as onv
 
 
@@ -23,8 +24,18 @@ def dequant_scale_from_checkpoint(gs: np.ndarray, convention: str) -> np.ndarray
     return onv.gscale_from_quant_scale(gs)
 
 
-def oracle_expert(wl, bank: str, e: int, device="cpu") -> omoe.ExpertWeights:
+def oracle_expert_mx(wl, bank: str, e: int, device="cpu") -> omoe.ExpertWeights:
+    """Quantize one synthetic expert to MXFP4 with the oracle quantizer."""
+    w13, w2 = synth.expert_fp32(wl, bank, e, device)
+    p13, s13 = omx.quantize(w13.cpu().numpy())
+    p2, s2 = omx.quantize(w2.cpu().numpy())
+    return omoe.ExpertWeights(p13, s13, np.ones(2, np.float32), p2, s2, 1.0, fmt="mxfp4")
+
+
+def oracle_expert(wl, bank: str, e: int, device="cpu", fmt: str = "nvfp4") -> omoe.ExpertWeights:
     """Quantize one synthetic expert with the oracle quantizer."""
+    if fmt == "mxfp4":
+        return oracle_expert_mx(wl, bank, e, device)
     w13, w2 = synth.expert_fp32(wl, bank, e, device)
     amax = synth.expert_amax(w13, w2)
     d = dequant_scale_from_checkpoint(synth.checkpoint_global_scales(amax, wl.gscale_convention),
@@ -49,11 +60,11 @@ class LazyBank:
     workloads share one bank.  ``prefetch`` quantizes a set of experts on a thread pool.
     """
 
-    def __init__(self, wl, bank: str, count: int, device="cpu"):
-        self.wl, self.bank, self.count, self.device = wl, bank, count, device
+    def __init__(self, wl, bank: str, count: int, device="cpu", fmt: str = "nvfp4"):
+        self.wl, self.bank, self.count, self.device, self.fmt = wl, bank, count, device, fmt
 
     def _key(self, e):
-        return (self.wl.wseed, self.wl.H, self.wl.I, self.bank, int(e), str(self.device))
+        return (self.wl.wseed, self.wl.H, self.wl.I, self.bank, int(e), str(self.device), self.fmt)
 
     def __len__(self):
         return self.count
@@ -61,20 +72,21 @@ class LazyBank:
     def __getitem__(self, e):
         key = self._key(e)
         if key not in _EXPERT_CACHE:
-            _EXPERT_CACHE[key] = oracle_expert(self.wl, self.bank, int(e), self.device)
+            _EXPERT_CACHE[key] = oracle_expert(self.wl, self.bank, int(e), self.device, self.fmt)
         return _EXPERT_CACHE[key]
 
     def prefetch(self, experts, threads=8):
         from concurrent.futures import ThreadPoolExecutor
         todo = sorted({int(e) for e in experts if self._key(e) not in _EXPERT_CACHE})
         with ThreadPoolExecutor(max_workers=threads) as ex:
-            for e, ew in zip(todo, ex.map(lambda i: oracle_expert(self.wl, self.bank, i, self.device), todo)):
+            for e, ew in zip(todo, ex.map(lambda i: oracle_expert(self.wl, self.bank, i, self.device, self.fmt),
+                                          todo)):
                 _EXPERT_CACHE[self._key(e)] = ew
 
 
-def oracle_layer(wl, device="cpu") -> omoe.Layer:
-    routed = LazyBank(wl, "routed", wl.E, device)
-    shared = LazyBank(wl, "shared", 1, device) if wl.I_shared > 0 else None
+def oracle_layer(wl, device="cpu", fmt: str = "nvfp4") -> omoe.Layer:
+    routed = LazyBank(wl, "routed", wl.E, device, fmt)
+    shared = LazyBank(wl, "shared", 1, device, fmt) if wl.I_shared > 0 else None
     return omoe.Layer(w_router=bf16_bits(synth.router_weight(wl, device)),
                       router_bias=synth.router_bias(wl), routed=routed, shared=shared, top_k=wl.k)
 
@@ -87,11 +99,15 @@ def stack_bank(bank) -> omoe.ArrayBank:
                           np.array([i.w2_gscale for i in items], np.float32))
 
 
-def random_layer(rng, H, I, E, k, shared=True, sigma=0.05, bias=False, i_shared=None) -> omoe.Layer:
+def random_layer(rng, H, I, E, k, shared=True, sigma=0.05, bias=False, i_shared=None, fmt="nvfp4") -> omoe.Layer:
     """A small random layer quantized by the oracle (for brute-force comparisons)."""
     def one(i_dim):
         w13 = rng.normal(0, sigma, (2 * i_dim, H)).astype(np.float32)
         w2 = rng.normal(0, sigma, (H, i_dim)).astype(np.float32)
+        if fmt == "mxfp4":
+            p13, s13 = omx.quantize(w13)
+            p2, s2 = omx.quantize(w2)
+            return omoe.ExpertWeights(p13, s13, np.ones(2, np.float32), p2, s2, 1.0, fmt="mxfp4")
         d = [onv.gscale_modelopt(np.abs(a).max()) for a in (w13[:i_dim], w13[i_dim:], w2)]
         pg, sg = onv.quantize(w13[:i_dim], d[0])
         pu, su = onv.quantize(w13[i_dim:], d[1])

@@ -29,6 +29,10 @@ def to_gpu_bank(bank, device="cuda") -> ops.NvFp4Experts:
     def st(name, dtype):
         return torch.from_numpy(np.ascontiguousarray(np.stack([getattr(i, name) for i in items]))).to(device, dtype)
 
+    fmt = getattr(items[0], "fmt", "nvfp4")
+    if fmt == "mxfp4":
+        return ops.NvFp4Experts.from_canonical(st("w13", torch.uint8), st("w13_scale", torch.uint8), None,
+                                               st("w2", torch.uint8), st("w2_scale", torch.uint8), None, fmt="mxfp4")
     return ops.NvFp4Experts.from_canonical(
         st("w13", torch.uint8), st("w13_scale", torch.uint8),
         torch.tensor(np.stack([i.w13_gscale for i in items]), dtype=torch.float32, device=device),
@@ -49,6 +53,16 @@ def tile_np(packed: np.ndarray, scales: np.ndarray):
     t = packed.reshape(r // 16, 16, k // 128, 4, 4, 4).transpose(0, 2, 4, 1, 3, 5).reshape(r, half)
     # canonical scale byte g = 2jj + parity  ->  tile order (n, parity, jj)
     ts = scales.reshape(r // 16, 16, k // 128, 4, 2).transpose(0, 2, 1, 4, 3).reshape(r, k // 16)
+    return np.ascontiguousarray(t), np.ascontiguousarray(ts)
+
+
+def tile_np_mx(packed: np.ndarray, scales: np.ndarray):
+    """Test-side statement of the MXFP4 tile layout: nibbles as tile_np; scales [R, K/32] -> per tile
+    (nb, c) the 16 rows' 4 scale bytes of the chunk (one per 32-wide MFMA step), row after row."""
+    r, half = packed.shape
+    k = half * 2
+    t = packed.reshape(r // 16, 16, k // 128, 4, 4, 4).transpose(0, 2, 4, 1, 3, 5).reshape(r, half)
+    ts = scales.reshape(r // 16, 16, k // 128, 4).transpose(0, 2, 1, 3).reshape(r, k // 32)
     return np.ascontiguousarray(t), np.ascontiguousarray(ts)
 
 

@@ -45,8 +45,9 @@ def test_gscale_conversion_worked_example_and_errors():
             moe.gscale_from_quant_scale(np.array([1.0, bad], np.float32))
 
 
-def _fake_bank(e, h, i, base=0x1000):
-    return L.Experts(e, h, i, base, base + 0x10, base + 0x20, base + 0x30, base + 0x40, base + 0x50)
+def _fake_bank(e, h, i, base=0x1000, fmt=L.MOE_WEIGHT_NVFP4):
+    return L.Experts(num_experts=e, hidden=h, inter=i, format=fmt, w13=base, w13_scale=base + 0x10,
+                     w13_gscale=base + 0x20, w2=base + 0x30, w2_scale=base + 0x40, w2_gscale=base + 0x50)
 
 
 def _fake_layer(h=4096, e=320, k=8, i=1536, i_sh=1536, shared=True):
@@ -85,6 +86,20 @@ def test_validate_forward_host_only():
     assert moe.validate_forward(_fake_layer(), 1 << 19, 1 << 62) == L.MOE_ERR_INVALID_ARGUMENT
     assert moe.validate_forward(_fake_layer(), (1 << 19) - 1, 1 << 62, arch="gfx950") in (L.MOE_OK,
                                                                                         L.MOE_ERR_INVALID_ARGUMENT)
+    # weight formats: MXFP4 needs no global scales; unknown formats and mixed banks are rejected
+    lay8 = _fake_layer()
+    lay8.routed.format = lay8.shared.format = L.MOE_WEIGHT_MXFP4
+    lay8.routed.w13_gscale = lay8.routed.w2_gscale = lay8.shared.w13_gscale = lay8.shared.w2_gscale = None
+    assert moe.validate_forward(lay8, 8, need) == L.MOE_OK
+    lay9 = _fake_layer()
+    lay9.routed.w2_gscale = None
+    assert moe.validate_forward(lay9, 8, 1 << 40) == L.MOE_ERR_INVALID_ARGUMENT   # NVFP4 needs them
+    lay10 = _fake_layer()
+    lay10.routed.format = L.MOE_WEIGHT_MXFP4
+    assert moe.validate_forward(lay10, 8, 1 << 40) == L.MOE_ERR_INVALID_ARGUMENT  # shared is NVFP4
+    lay11 = _fake_layer()
+    lay11.routed.format = lay11.shared.format = 2
+    assert moe.validate_forward(lay11, 8, 1 << 40) == L.MOE_ERR_INVALID_ARGUMENT
     # no shared expert is valid
     lay5 = _fake_layer(shared=False)
     assert moe.validate_forward(lay5, 8, moe.forward_workspace_size(8, 4096, 1536, 0, 320, 8)) == L.MOE_OK
