@@ -25,7 +25,7 @@ import torch
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-NVFP4_BYTES_PER_WEIGHT = 0.5625
+BYTES_PER_WEIGHT = {"nvfp4": 0.5 + 1 / 16, "mxfp4": 0.5 + 1 / 32}   # nibble + block-scale bytes
 
 # HBM traffic of the gate/up GEMM per launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this
 # script (profiles/traffic_<workload>.md), scaled by what the same counters read for the 1 GiB copy
@@ -87,23 +87,28 @@ class HipEvents:
 
 def clone_layer(layer, ops):
     def bank(b):
-        return ops.NvFp4Experts(*(t.clone() for t in (b.w13, b.w13_scale, b.w13_gscale, b.w2, b.w2_scale,
-                                                     b.w2_gscale)))
+        return ops.NvFp4Experts(*(t.clone() if t is not None else None
+                                  for t in (b.w13, b.w13_scale, b.w13_gscale, b.w2, b.w2_scale, b.w2_gscale)),
+                                fmt=b.fmt)
     return ops.NvFp4MoELayer(layer.w_router.clone(), None if layer.router_bias is None else layer.router_bias.clone(),
                              bank(layer.routed), bank(layer.shared) if layer.shared is not None else None, layer.top_k)
 
 
-def cpu_baseline(wl, x_bits, ids, n_tokens, synth):
+def cpu_baseline(wl, x_bits, ids, n_tokens, synth, fmt="nvfp4"):
     """The oracle as it stands, single-threaded, on the first ``n_tokens`` tokens of the workload."""
     from concurrent.futures import ThreadPoolExecutor
 
     from threadpoolctl import threadpool_limits
 
     from oracle import moe as omoe
+    from oracle import mxfp4 as omx
     from oracle import nvfp4 as onv
 
     def oracle_expert(bank, e):
         w13, w2 = synth.expert_fp32(wl, bank, e, "cuda")
+        if fmt == "mxfp4":
+            (p13, s13), (p2, s2) = omx.quantize(w13.cpu().numpy()), omx.quantize(w2.cpu().numpy())
+            return omoe.ExpertWeights(p13, s13, np.ones(2, np.float32), p2, s2, 1.0, fmt="mxfp4")
         gs = synth.checkpoint_global_scales(synth.expert_amax(w13, w2), wl.gscale_convention)
         d = onv.gscale_from_quant_scale(gs) if wl.gscale_convention == "compressed_tensors" else gs
         w13, w2 = w13.cpu().numpy(), w2.cpu().numpy()
@@ -144,6 +149,8 @@ def main():
     ap.add_argument("--workload", default="decode", choices=sorted(_DEFAULTS))
     ap.add_argument("--copies", type=int, default=None, help="weight copies cycled through")
     ap.add_argument("--cpu-tokens", type=int, default=1, help="tokens in the CPU oracle sample (0: skip)")
+    ap.add_argument("--format", default="nvfp4", choices=["nvfp4", "mxfp4"],
+                    help="weight format of the synthetic experts (the headline metric is NVFP4)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -162,8 +169,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    print(f"[bench] building {wl.name} layer ({copies} weight copies)", file=sys.stderr, flush=True)
-    layer = build_layer(wl, dev)
+    print(f"[bench] building {wl.name} layer ({copies} weight copies, {args.format})", file=sys.stderr, flush=True)
+    layer = build_layer(wl, dev, fmt=args.format)
+    bytes_per_weight = BYTES_PER_WEIGHT[args.format]
     layers = [layer] + [clone_layer(layer, ops) for _ in range(copies - 1)]
     x = synth.activations(wl, dev)
     ws = ops.workspace_for(layer, wl.T, dev)
@@ -268,7 +276,7 @@ def main():
     value = T * steps / (total_ms / 1e3)
     # roofline of the gate/up GEMM, the dominant kernel (2/3 of the weight bytes and flops)
     n_banks = touched + (1 if wl.I_shared > 0 else 0)
-    gu_weight_bytes = n_banks * 2 * I * H * NVFP4_BYTES_PER_WEIGHT
+    gu_weight_bytes = n_banks * 2 * I * H * bytes_per_weight
     gu_bytes = gu_weight_bytes + T * H * 2 + (S + T) * I * 2
     gu_flops = 2.0 * (S + T) * H * 2 * I
     if wl.name in ("tiny", "decode"):
@@ -284,7 +292,7 @@ def main():
     roof["peak_measured_source"] = ("1 GiB device-to-device copy (read + write)" if roof["bound"] == "hbm"
                                     else "dense bf16 GEMM of the gate/up shape via torch.mm (hipBLASLt)")
     roof["frac_of_measured"] = (roof["achieved"] / roof["peak_measured"]) if roof["peak_measured"] else None
-    roof["traffic"] = gate_up_traffic(wl.name)
+    roof["traffic"] = gate_up_traffic(wl.name) if args.format == "nvfp4" else None
     roof["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)"
     roof["algorithmic_bytes"] = gu_bytes
     roof["kernel"] = "gate/up grouped GEMM (S4)"
@@ -293,7 +301,7 @@ def main():
     # whole layer: flops 2(S+T)*3HI + 2THE (MFMA-bound shapes) or the bytes of every touched
     # expert, the shared expert, the router weight and the activations (HBM-bound shapes)
     if roof["bound"] == "hbm":
-        layer_bytes = ((touched * 3 * I + 3 * wl.I_shared) * H * NVFP4_BYTES_PER_WEIGHT + 2 * E * H + 4 * T * H)
+        layer_bytes = ((touched * 3 * I + 3 * wl.I_shared) * H * bytes_per_weight + 2 * E * H + 4 * T * H)
         layer_roof = {"bound": "hbm", "achieved": layer_bytes / (ms_per_step * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                       "unit": "GB/s", "algorithmic_bytes": layer_bytes}
     else:
@@ -309,14 +317,16 @@ def main():
         def bits(t):
             return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
-        cpu = cpu_baseline(wl, {"x": bits(x), "router": bits(layer.w_router)}, ids, args.cpu_tokens, synth)
+        cpu = cpu_baseline(wl, {"x": bits(x), "router": bits(layer.w_router)}, ids, args.cpu_tokens, synth,
+                           args.format)
     line = {
-        "metric": "NVFP4 MoE layer tokens/s; decode HBM GB/s %peak, prefill MFMA %peak",
+        "metric": "NVFP4 MoE layer tokens/s; decode HBM GB/s %peak, prefill MFMA %peak"
+                  + ("" if args.format == "nvfp4" else " (measured here on MXFP4 weights)"),
         "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{wl.name}: T={T} H={H} I={I} E={E} top-{k} + 1 shared (I={wl.I_shared}), "
-                               f"NVFP4 W4A16", "tokens": T, "hidden": H, "inter": I, "experts": E, "top_k": k,
+                               f"{args.format.upper()} W4A16", "tokens": T, "hidden": H, "inter": I, "experts": E, "top_k": k,
                    "weight_copies": copies, "experts_touched": touched},
         "roofline": roof,
         "layer_roofline": layer_roof,
