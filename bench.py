@@ -34,8 +34,8 @@ BYTES_PER_WEIGHT = {"nvfp4": 0.5 + 1 / 16, "mxfp4": 0.5 + 1 / 32}   # nibble + b
 _GEMM_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "nvfp4_weight_quantized_amd", "csrc",
                          "grouped_gemm.hip")
 _TRAFFIC = {  # workload: (sha256 of grouped_gemm.hip, bytes read, bytes written) per gate/up launch
-    "decode": ("1ae02b3053f01130dbf21b42da61a2ce7b2f2b1adf699a4af568fab0084f4fe8", 432.58e6, 0.22e6),
-    "prefill": ("1ae02b3053f01130dbf21b42da61a2ce7b2f2b1adf699a4af568fab0084f4fe8", 2746.79e6, 113.70e6),
+    "decode": ("26e3866d11fd6ee21de50f4460775e72e02553c6254faf743b28f4bbc5b67150", 432.58e6, 0.22e6),
+    "prefill": ("26e3866d11fd6ee21de50f4460775e72e02553c6254faf743b28f4bbc5b67150", 2726.06e6, 113.70e6),
 }
 
 
