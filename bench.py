@@ -29,24 +29,32 @@ BYTES_PER_WEIGHT = {"nvfp4": 0.5 + 1 / 16, "mxfp4": 0.5 + 1 / 32}   # nibble + b
 
 # HBM traffic of the gate/up GEMM per launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this
 # script (profiles/traffic_<workload>.md), scaled by what the same counters read for the 1 GiB copy
-# (FETCH x 2.0, WRITE x 1.0).  Valid only for the kernel source it was measured on: reported as null
-# once grouped_gemm.hip has changed.
+# (FETCH x 2.0, WRITE x 1.0).  Valid only for the kernel code it was measured on: reported as null
+# once the code of grouped_gemm.hip has changed (the fingerprint ignores comments and blank lines).
 _GEMM_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "nvfp4_weight_quantized_amd", "csrc",
                          "grouped_gemm.hip")
-_TRAFFIC = {  # workload: (sha256 of grouped_gemm.hip, bytes read, bytes written) per gate/up launch
-    "decode": ("26e3866d11fd6ee21de50f4460775e72e02553c6254faf743b28f4bbc5b67150", 432.58e6, 0.22e6),
-    "prefill": ("26e3866d11fd6ee21de50f4460775e72e02553c6254faf743b28f4bbc5b67150", 2726.06e6, 113.70e6),
+_TRAFFIC = {  # workload: (code fingerprint of grouped_gemm.hip, bytes read, bytes written) per gate/up launch
+    "decode": ("715d239ae0aa2814bf5db1cb2a315c7aad234e4827511c9402689ed8075368c7", 432.58e6, 0.22e6),
+    "prefill": ("715d239ae0aa2814bf5db1cb2a315c7aad234e4827511c9402689ed8075368c7", 2726.06e6, 113.70e6),
 }
 
 
-def gate_up_traffic(workload: str):
+def code_fingerprint(path: str) -> str:
+    """sha256 of a C++ source without its // comments, trailing spaces and blank lines."""
     import hashlib
+    import re
+    lines = []
+    for line in open(path, encoding="utf-8"):
+        line = re.sub(r"//.*$", "", line.rstrip("\n")).rstrip()
+        if line:
+            lines.append(line)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
+def gate_up_traffic(workload: str):
     rec = _TRAFFIC.get(workload)
-    if rec is None:
+    if rec is None or code_fingerprint(_GEMM_SRC) != rec[0]:
         return None
-    with open(_GEMM_SRC, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != rec[0]:
-            return None
     return rec[1] + rec[2]
 
 

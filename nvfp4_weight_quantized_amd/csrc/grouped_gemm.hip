@@ -1,10 +1,12 @@
-// Grouped NVFP4 x bf16 GEMMs of the MoE layer (S4 gate/up with SiLU(gate)*up, S5 down), gfx950.
+// Grouped NVFP4 (or MXFP4) x bf16 GEMMs of the MoE layer (S4 gate/up with SiLU(gate)*up, S5
+// down), gfx950.
 //
 // Method: weight-only W4A16 -- 16-bit activations times 4-bit weights that are dequantized to
 // 16-bit inside the GEMM ("vLLM on the NVIDIA DGX Spark: A Complete Technical Guide", section 5,
 // Marlin), on the NVFP4 format of section 6.1 (E2M1 pairs per byte, one E4M3 scale per 16
-// elements along K, one fp32 global scale per tensor).  SiLU(gate)*up between the GEMMs as in the
-// fused MoE of section 4.
+// elements along K, one fp32 global scale per tensor) or the MXFP4 format of section 6.4 (one
+// E8M0 scale per 32 elements, no global scale; see WFmt below).  SiLU(gate)*up between the GEMMs
+// as in the fused MoE of section 4.  The notes below describe NVFP4.
 //
 // CDNA4 design:
 //  * Weights are read in the MFMA tile layout (see layout.hip): one 16-row x 128-K tile is 1 KB of
@@ -610,10 +612,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmProblem p) {
 //    16i + n and K [32j + 8q, +8) of the chunk.  Every fragment read is then one contiguous 1 KB
 //    ds_read_b128 (free of bank conflicts), and every direct load reads 64 contiguous bytes from
 //    each of 16 rows.
-//  * The direct loads are issued from inline assembly and waited for explicitly (vmcnt(0) and a
-//    barrier at the end of each chunk).  Issued through the compiler builtin, the compiler cannot
-//    tell that the loads in flight into one buffer leave the other alone and drains them before
-//    every LDS read, which serialises loading and computing.
+//  * The direct loads are issued from inline assembly and waited for explicitly (an s_waitcnt
+//    vmcnt and a barrier at the end of each chunk).  Issued through the compiler builtin, the
+//    compiler cannot tell that the loads in flight into one buffer leave the others alone and
+//    drains them before every LDS read, which serialises loading and computing.
 //  * B tiles in registers, prefetched one chunk ahead; the end-of-chunk wait names the prefetch
 //    registers, so the compiler waits for them there and nowhere earlier.  Within a chunk the
 //    next MFMA step's weight operands are dequantized while the current step's MFMAs run.
@@ -881,8 +883,9 @@ moe_status_t launch_skinny(const GemmProblem& p, hipStream_t stream) {
   return launch_status();
 }
 
-// Few rows per expert: 16-row tiles; 512-wide K chunks for long reductions, 256-wide for shorter
-// ones (more workgroups in flight; measured on the decode-shaped down GEMM, K = 1536).
+// 16-row tiles (up to 16 rows per expert on average; NVFP4 groups of at most 8 take the skinny
+// kernel): 512-wide K chunks for long reductions, 256-wide for shorter ones (more workgroups in
+// flight; measured on the decode-shaped down GEMM, K = 1536).
 template <bool GATE_UP, int FMT>
 moe_status_t launch_small(const GemmProblem& p, hipStream_t stream) {
   if (p.K % 512 == 0 && p.K >= 4096) return launch_cfg<1, 2, 512, GATE_UP, FMT>(p, stream);
