@@ -13,8 +13,10 @@ Modules
             (the second weight format, section 6.4 of the Guide).
   moe    -- router, top-k, permutation, expert FFN, combine, whole-layer forward
             (float64 arithmetic on the exact values of the bf16/NVFP4 inputs).
+  w4a4   -- the W4A4 variant: MXFP4 weights and MXFP4-quantized activations
+            (x before gate/up, bf16-rounded h before down).
   brute  -- an independent scalar float64 per-token loop for tiny layers, used to
-            pin ``moe`` itself.
+            pin ``moe`` and ``w4a4`` themselves.
 
 Sources (the pages these follow):
   * "vLLM on the NVIDIA DGX Spark: A Complete Technical Guide", section 6.1
@@ -35,4 +37,4 @@ printed value on the pages; it is pinned only through ``brute`` (an independent
 scalar implementation of the same definition).
 """
 
-from . import nvfp4, mxfp4, moe, brute  # noqa: F401
+from . import nvfp4, mxfp4, moe, w4a4, brute  # noqa: F401

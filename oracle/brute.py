@@ -14,7 +14,12 @@ Definitions used (same sources as ``oracle.moe``):
     elements and no global scale (section 6.4, the reading of oracle.mxfp4);
   * top-k on router logits (ties -> lower expert index), softmax renormalised
     over the selected experts; SiLU(gate)*up; down projection; top-k-weighted
-    sum; shared expert added with weight 1 (same readings as ``oracle.moe``).
+    sum; shared expert added with weight 1 (same readings as ``oracle.moe``);
+  * W4A4 (``act="mxfp4"``): each GEMM input vector is quantized per 32 elements
+    to an E8M0 shared exponent floor(log2 amax) - 2 (clamped to [-127, 127]) and
+    the nearest E2M1 value, found by searching the value table (ties -> even
+    code, i.e. mantissa bit 0); h is rounded to bf16 first (the readings of
+    ``oracle.w4a4``).
 """
 
 from __future__ import annotations
@@ -71,9 +76,50 @@ def dequant_expert(ew):
     return wg, wu, wd
 
 
-def expert_out(xv, mats) -> list:
-    """y = Wd (silu(Wg x) * (Wu x)) for one token, scalar loops."""
+def bf16_round(v: float) -> float:
+    """Nearest bf16 value of v (8 significant bits, ties to even), via frexp and round()."""
+    if v == 0.0 or math.isnan(v) or math.isinf(v):
+        return v
+    _, e = math.frexp(v)                 # |v| in [2^(e-1), 2^e): spacing 2^(e-8)
+    e = max(e, -125)                     # subnormal bf16 spacing is 2^-133
+    r = math.ldexp(float(round(math.ldexp(v, 8 - e))), e - 8)   # round(): half to even
+    return math.copysign(math.inf, r) if abs(r) > 3.3895313892515355e38 else r
+
+
+def mx_group(vals):
+    """MXFP4 of one 32-element group: (signed E2M1 values, scale exponent)."""
+    amax = max(abs(v) for v in vals)
+    if amax == 0.0:
+        e = -127
+    else:
+        _, ex = math.frexp(amax)         # amax in [2^(ex-1), 2^ex)
+        e = min(max(ex - 1 - 2, -127), 127)
+    out = []
+    for v in vals:
+        t = abs(v) / math.ldexp(1.0, e)
+        best = 0
+        for c in range(8):
+            d, db = abs(t - E2M1_TABLE[c]), abs(t - E2M1_TABLE[best])
+            if d < db or (d == db and c % 2 == 0 and best % 2 == 1):
+                best = c
+        out.append(-E2M1_TABLE[best] if v < 0 else E2M1_TABLE[best])
+    return out, e
+
+
+def mx_fake_quant(vec) -> list:
+    """The values a vector stands for after MXFP4 quantization in groups of 32."""
+    res = []
+    for g0 in range(0, len(vec), 32):
+        vals, e = mx_group(vec[g0:g0 + 32])
+        res.extend(v * math.ldexp(1.0, e) for v in vals)
+    return res
+
+
+def expert_out(xv, mats, act: str = "bf16") -> list:
+    """y = Wd (silu(Wg x) * (Wu x)) for one token, scalar loops (act "mxfp4": W4A4)."""
     wg, wu, wd = mats
+    if act == "mxfp4":
+        xv = mx_fake_quant(xv)
     hvec = []
     for grow, urow in zip(wg, wu):
         g = 0.0
@@ -81,8 +127,10 @@ def expert_out(xv, mats) -> list:
         for xh, a, b in zip(xv, grow, urow):
             g += xh * a
             u += xh * b
-        act = g / (1.0 + math.exp(-g)) if g > -700.0 else 0.0
-        hvec.append(act * u)
+        sg = g / (1.0 + math.exp(-g)) if g > -700.0 else 0.0
+        hvec.append(sg * u)
+    if act == "mxfp4":
+        hvec = mx_fake_quant([bf16_round(v) for v in hvec])
     y = []
     for drow in wd:
         acc = 0.0
@@ -92,8 +140,9 @@ def expert_out(xv, mats) -> list:
     return y
 
 
-def forward(x_bits, layer, tokens=None):
-    """Per-token results [(ids, weights, out row, logits)] for the given token indices."""
+def forward(x_bits, layer, tokens=None, act: str = "bf16"):
+    """Per-token results [(ids, weights, out row, logits)] for the given token indices
+    (act "mxfp4": the W4A4 layer, MXFP4 weights and activations)."""
     cache = {}
 
     def mats(bank, e):
@@ -122,11 +171,11 @@ def forward(x_bits, layer, tokens=None):
         wts = [v / total for v in z]
         out = [0.0] * len(xv)
         for e, w in zip(chosen, wts):
-            y = expert_out(xv, mats(layer.routed, e))
+            y = expert_out(xv, mats(layer.routed, e), act)
             for h in range(len(xv)):
                 out[h] += w * y[h]
         if layer.shared is not None:
-            y = expert_out(xv, mats(layer.shared, 0))
+            y = expert_out(xv, mats(layer.shared, 0), act)
             for h in range(len(xv)):
                 out[h] += y[h]
         results.append((chosen, wts, out, logits))
