@@ -25,35 +25,38 @@ import torch
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-BYTES_PER_WEIGHT = {"nvfp4": 0.5 + 1 / 16, "mxfp4": 0.5 + 1 / 32}   # nibble + block-scale bytes
+FP4_PEAK_TFLOPS = 10100.0      # MI355X dense fp4 MFMA (the W4A4 layer)
+BYTES_PER_WEIGHT = {"nvfp4": 0.5 + 1 / 16, "mxfp4": 0.5 + 1 / 32, "mxfp4_a4": 0.5 + 1 / 32}   # nibble + scale bytes
 
 # HBM traffic of the gate/up GEMM per launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this
 # script (profiles/traffic_<workload>.md), scaled by what the same counters read for the 1 GiB copy
 # (FETCH x 2.0, WRITE x 1.0).  Valid only for the kernel code it was measured on: reported as null
-# once the code of grouped_gemm.hip has changed (the fingerprint ignores comments and blank lines).
-_GEMM_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "nvfp4_weight_quantized_amd", "csrc",
-                         "grouped_gemm.hip")
-_TRAFFIC = {  # workload: (code fingerprint of grouped_gemm.hip, bytes read, bytes written) per gate/up launch
-    "decode": ("715d239ae0aa2814bf5db1cb2a315c7aad234e4827511c9402689ed8075368c7", 432.58e6, 0.22e6),
-    "prefill": ("715d239ae0aa2814bf5db1cb2a315c7aad234e4827511c9402689ed8075368c7", 2726.06e6, 113.70e6),
+# once the code of the W4A16 GEMM sources has changed (the fingerprint ignores comments and blank
+# lines).
+_CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "nvfp4_weight_quantized_amd", "csrc")
+_GEMM_SRCS = [os.path.join(_CSRC, f) for f in ("grouped_gemm.hip", "gemm_tiles.h")]
+_TRAFFIC = {  # workload: (code fingerprint of the GEMM sources, bytes read, bytes written) per gate/up launch
+    "decode": ("d09fe6e77f8541271bb85e69fd86663aca56fad955f8b68668459e84c228c6ad", 432.58e6, 0.22e6),
+    "prefill": ("d09fe6e77f8541271bb85e69fd86663aca56fad955f8b68668459e84c228c6ad", 2726.06e6, 113.70e6),
 }
 
 
-def code_fingerprint(path: str) -> str:
-    """sha256 of a C++ source without its // comments, trailing spaces and blank lines."""
+def code_fingerprint(paths) -> str:
+    """sha256 of C++ sources without their // comments, trailing spaces and blank lines."""
     import hashlib
     import re
     lines = []
-    for line in open(path, encoding="utf-8"):
-        line = re.sub(r"//.*$", "", line.rstrip("\n")).rstrip()
-        if line:
-            lines.append(line)
+    for path in paths:
+        for line in open(path, encoding="utf-8"):
+            line = re.sub(r"//.*$", "", line.rstrip("\n")).rstrip()
+            if line:
+                lines.append(line)
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
 def gate_up_traffic(workload: str):
     rec = _TRAFFIC.get(workload)
-    if rec is None or code_fingerprint(_GEMM_SRC) != rec[0]:
+    if rec is None or code_fingerprint(_GEMM_SRCS) != rec[0]:
         return None
     return rec[1] + rec[2]
 
@@ -111,10 +114,11 @@ def cpu_baseline(wl, x_bits, ids, n_tokens, synth, fmt="nvfp4"):
     from oracle import moe as omoe
     from oracle import mxfp4 as omx
     from oracle import nvfp4 as onv
+    from oracle import w4a4 as oa4
 
     def oracle_expert(bank, e):
         w13, w2 = synth.expert_fp32(wl, bank, e, "cuda")
-        if fmt == "mxfp4":
+        if fmt in ("mxfp4", "mxfp4_a4"):
             (p13, s13), (p2, s2) = omx.quantize(w13.cpu().numpy()), omx.quantize(w2.cpu().numpy())
             return omoe.ExpertWeights(p13, s13, np.ones(2, np.float32), p2, s2, 1.0, fmt="mxfp4")
         gs = synth.checkpoint_global_scales(synth.expert_amax(w13, w2), wl.gscale_convention)
@@ -139,9 +143,10 @@ def cpu_baseline(wl, x_bits, ids, n_tokens, synth, fmt="nvfp4"):
 
     layer = omoe.Layer(w_router=x_bits["router"], router_bias=synth.router_bias(wl), routed=Bank(), shared=shared,
                        top_k=wl.k)
+    forward = oa4.forward if fmt == "mxfp4_a4" else omoe.forward
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        omoe.forward(x_bits["x"][:n_tokens], layer)
+        forward(x_bits["x"][:n_tokens], layer)
         dt = time.perf_counter() - t0
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n_tokens} of {wl.T} tokens of the {wl.name} workload ({len(used)} routed experts + "
@@ -157,8 +162,9 @@ def main():
     ap.add_argument("--workload", default="decode", choices=sorted(_DEFAULTS))
     ap.add_argument("--copies", type=int, default=None, help="weight copies cycled through")
     ap.add_argument("--cpu-tokens", type=int, default=1, help="tokens in the CPU oracle sample (0: skip)")
-    ap.add_argument("--format", default="nvfp4", choices=["nvfp4", "mxfp4"],
-                    help="weight format of the synthetic experts (the headline metric is NVFP4)")
+    ap.add_argument("--format", default="nvfp4", choices=["nvfp4", "mxfp4", "mxfp4_a4"],
+                    help="weight format of the synthetic experts (the headline metric is NVFP4); mxfp4_a4: "
+                         "the W4A4 layer (MXFP4 weights and activations on the FP4 matrix cores)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -205,7 +211,8 @@ def main():
     # dense bf16 GEMM of the gate/up shape through the vendor library (torch.mm -> hipBLASLt): the
     # practical MFMA ceiling of this machine for that shape (context only; not part of the layer)
     dense_tflops = None
-    if wl.name not in ("tiny", "decode"):
+    w4a4 = args.format == "mxfp4_a4"
+    if wl.name not in ("tiny", "decode") and not w4a4:
         m_rows, n_cols = wl.T * wl.k + wl.T, 2 * wl.I
         a_ = torch.randn(m_rows, wl.H, device=dev, dtype=torch.bfloat16)
         b_ = torch.randn(n_cols, wl.H, device=dev, dtype=torch.bfloat16)
@@ -285,13 +292,20 @@ def main():
     # roofline of the gate/up GEMM, the dominant kernel (2/3 of the weight bytes and flops)
     n_banks = touched + (1 if wl.I_shared > 0 else 0)
     gu_weight_bytes = n_banks * 2 * I * H * bytes_per_weight
-    gu_bytes = gu_weight_bytes + T * H * 2 + (S + T) * I * 2
+    # activations in: bf16 x (W4A16); for W4A4 the x read by its quantizer plus the 4-bit copy
+    x_bytes = T * H * 2 + (T * H * bytes_per_weight * 2 if w4a4 else 0)
+    gu_bytes = gu_weight_bytes + x_bytes + (S + T) * I * 2
     gu_flops = 2.0 * (S + T) * H * 2 * I
-    if wl.name in ("tiny", "decode"):
+    mfma_peak = FP4_PEAK_TFLOPS if w4a4 else BF16_PEAK_TFLOPS
+    if w4a4:   # bound by the algorithmic intensity against the fp4 ridge point
+        hbm_bound = gu_bytes / (HBM_PEAK_GBS * 1e9) >= gu_flops / (mfma_peak * 1e12)
+    else:
+        hbm_bound = wl.name in ("tiny", "decode")
+    if hbm_bound:
         roof = {"bound": "hbm", "achieved": gu_bytes / (gate_up_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": gu_flops / (gate_up_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+        roof = {"bound": "mfma", "achieved": gu_flops / (gate_up_ms * 1e-3) / 1e12, "peak": mfma_peak,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     # the same against what this box measurably reaches: a streaming copy (HBM-bound case) or the
@@ -303,7 +317,8 @@ def main():
     roof["traffic"] = gate_up_traffic(wl.name) if args.format == "nvfp4" else None
     roof["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)"
     roof["algorithmic_bytes"] = gu_bytes
-    roof["kernel"] = "gate/up grouped GEMM (S4)"
+    roof["kernel"] = ("gate/up stage (S4): x to MXFP4 + W4A4 grouped GEMM" if w4a4
+                      else "gate/up grouped GEMM (S4)")
     roof["kernel_us"] = gate_up_ms * 1e3
 
     # whole layer: flops 2(S+T)*3HI + 2THE (MFMA-bound shapes) or the bytes of every touched
@@ -315,7 +330,7 @@ def main():
     else:
         layer_flops = 2.0 * S * 3 * H * I + 2.0 * T * 3 * H * wl.I_shared + 2.0 * T * H * E
         layer_roof = {"bound": "mfma", "achieved": layer_flops / (ms_per_step * 1e-3) / 1e12,
-                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "algorithmic_flops": layer_flops}
+                      "peak": mfma_peak, "unit": "TFLOP/s", "algorithmic_flops": layer_flops}
     layer_roof["frac"] = layer_roof["achieved"] / layer_roof["peak"]
 
     cpu = None
@@ -329,12 +344,14 @@ def main():
                            args.format)
     line = {
         "metric": "NVFP4 MoE layer tokens/s; decode HBM GB/s %peak, prefill MFMA %peak"
-                  + ("" if args.format == "nvfp4" else " (measured here on MXFP4 weights)"),
+                  + {"nvfp4": "", "mxfp4": " (measured here on MXFP4 weights)",
+                     "mxfp4_a4": " (measured here on the MXFP4 W4A4 layer)"}[args.format],
         "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
+        "dtype": "fp4" if w4a4 else "bf16", "data": "synthetic",
         "config": {"workload": f"{wl.name}: T={T} H={H} I={I} E={E} top-{k} + 1 shared (I={wl.I_shared}), "
-                               f"{args.format.upper()} W4A16", "tokens": T, "hidden": H, "inter": I, "experts": E, "top_k": k,
+                               + ("MXFP4 W4A4" if w4a4 else f"{args.format.upper()} W4A16"),
+                   "tokens": T, "hidden": H, "inter": I, "experts": E, "top_k": k,
                    "weight_copies": copies, "experts_touched": touched},
         "roofline": roof,
         "layer_roofline": layer_roof,

@@ -268,6 +268,61 @@ moe_status_t moe_mxfp4_pack_tiles(const uint8_t* packed, const uint8_t* scales, 
 moe_status_t moe_mxfp4_quantize(const float* w, int32_t num_tensors, int32_t rows, int32_t cols, uint8_t* packed,
                                 uint8_t* scales, void* stream);
 
+/* ---------------------------------------------------------------- W4A4 (MXFP4 weights and activations)
+ * The W4A4 variant of the layer: the activations entering each GEMM are quantized to 4 bits as
+ * well and the GEMMs run on the FP4 matrix cores (gfx950 v_mfma_scale_f32_16x16x128_f8f6f4), both
+ * operands in the MXFP4 format (E2M1 elements, one E8M0 scale per 32 elements along K).
+ * Source: W4A4 checkpoints carry 4-bit weights and activations and run a native FP4 matmul, whose
+ * gain is in prefill ("vLLM on the DGX Spark, the Hard Way: Seven Months of GB10 Field Notes",
+ * "The one rule that explains all the FP4 confusion" and "Measured: native FP4 + MTP vs the
+ * published Marlin numbers"); the fused MoE kernel quantizes bf16 hidden states to FP4 itself
+ * ("vLLM on the NVIDIA DGX Spark", section 4.3); MXFP4 (same guide, section 6.4).  The pages'
+ * NVFP4 activation format (E4M3 per 16 elements plus a global scale) has no counterpart in the
+ * gfx950 FP4 instruction, whose block scales are E8M0 per 32 elements, so both sides use MXFP4.
+ *
+ * MXFP4 quantization of bf16 rows: a [rows][cols] bf16 -> packed [rows][cols/2] E2M1 codes and
+ * scales [rows][cols/32] E8M0, per 32-group by the rule of moe_mxfp4_quantize (computed exactly on
+ * the bf16 values).  cols % 32 == 0; a and packed 16-byte aligned. */
+moe_status_t moe_mxfp4_quantize_act(const uint16_t* a, int32_t rows, int32_t cols, uint8_t* packed,
+                                    uint8_t* scales, void* stream);
+
+/* Load-time repack of canonical MXFP4 tensors into the W4A4 tile layout the W4A4 GEMMs read:
+ * tile t = (rows/16 block nb) * (cols/128) + (128-column chunk c) holds 1024 nibble bytes and 64
+ * scale bytes; with l = 16q + n, nibble bytes [16l, 16l + 16) are the canonical bytes
+ * [64c + 16q, +16) of row 16nb + n (its elements [128c + 32q, +32), one scale block) and scale
+ * byte l is that row's canonical scale byte 4c + q.  rows % 16 == 0, cols % 128 == 0; out of
+ * place, same sizes.  A bank for the W4A4 entry points has format MOE_WEIGHT_MXFP4 and its
+ * weights in this layout (not the one of moe_mxfp4_pack_tiles). */
+moe_status_t moe_mxfp4_pack_tiles_a4(const uint8_t* packed, const uint8_t* scales, int32_t num_tensors, int32_t rows,
+                                     int32_t cols, uint8_t* tiled, uint8_t* tiled_scales, void* stream);
+
+/* W4A4 grouped GEMM, the counterpart of moe_nvfp4_grouped_gemm: A row r is MXFP4 activation row
+ * a[row_index[r] / row_divisor] (or a[r]) -- codes `a` [rows][K/2], scales `a_scale` [rows][K/32]
+ * from moe_mxfp4_quantize_act -- and every product of a weight and an activation is exact before
+ * the fp32 accumulation.  Gate/up writes h = bf16(silu(A.Qg^T) * (A.Qu^T)) [M_total][I]; down
+ * writes y = bf16(A.Qd^T) [M_total][H].  w->format must be MOE_WEIGHT_MXFP4 (W4A4 tile layout);
+ * a, a_scale and out 16-byte aligned; M_total * K / 2 < 4 GiB. */
+moe_status_t moe_mxfp4_w4a4_grouped_gemm(int32_t stage, const moe_nvfp4_experts_t* w, const uint8_t* a,
+                                         const uint8_t* a_scale, const int32_t* row_index, int32_t row_divisor,
+                                         const int32_t* expert_offsets, int32_t M_total, uint16_t* out,
+                                         void* stream);
+
+/* Workspace bytes of moe_mxfp4_w4a4_forward: the routing buffers, x and h in MXFP4, h in bf16 and
+ * the expert outputs y. */
+size_t moe_mxfp4_w4a4_forward_workspace_size(int32_t T, int32_t H, int32_t I, int32_t I_shared,
+                                             int32_t E, int32_t k);
+
+/* Host validation of moe_mxfp4_w4a4_forward (as moe_validate_forward, plus MXFP4 banks). */
+moe_status_t moe_mxfp4_w4a4_validate_forward(const moe_nvfp4_layer_t* layer, int32_t T, size_t workspace_bytes,
+                                             const char* gfx_arch);
+
+/* The W4A4 layer: S1-S3 and S6 as moe_nvfp4_forward; S4 quantizes x to MXFP4 (once per token) and
+ * runs the W4A4 gate/up GEMM, S5 quantizes the bf16 h rows to MXFP4 and runs the W4A4 down GEMM.
+ * Banks in the W4A4 tile layout; aux and stage events as for moe_nvfp4_forward. */
+moe_status_t moe_mxfp4_w4a4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int32_t T,
+                                    uint16_t* out, void* workspace, size_t workspace_bytes,
+                                    const moe_forward_aux_t* aux, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

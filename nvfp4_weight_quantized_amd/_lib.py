@@ -75,13 +75,23 @@ SIGNATURES = {
     "moe_nvfp4_quantize": (i32, [c_void_p, i32, i32, i32, c_void_p, c_void_p, c_void_p, c_void_p]),
     "moe_mxfp4_pack_tiles": (i32, [c_void_p, c_void_p, i32, i32, i32, c_void_p, c_void_p, c_void_p]),
     "moe_mxfp4_quantize": (i32, [c_void_p, i32, i32, i32, c_void_p, c_void_p, c_void_p]),
+    "moe_mxfp4_quantize_act": (i32, [c_void_p, i32, i32, c_void_p, c_void_p, c_void_p]),
+    "moe_mxfp4_pack_tiles_a4": (i32, [c_void_p, c_void_p, i32, i32, i32, c_void_p, c_void_p, c_void_p]),
+    "moe_mxfp4_w4a4_grouped_gemm": (i32, [i32, ctypes.POINTER(Experts), c_void_p, c_void_p, c_void_p, i32, c_void_p,
+                                          i32, c_void_p, c_void_p]),
+    "moe_mxfp4_w4a4_forward_workspace_size": (size_t, [i32, i32, i32, i32, i32, i32]),
+    "moe_mxfp4_w4a4_validate_forward": (i32, [ctypes.POINTER(Layer), i32, size_t, ctypes.c_char_p]),
+    "moe_mxfp4_w4a4_forward": (i32, [ctypes.POINTER(Layer), c_void_p, i32, c_void_p, c_void_p, size_t,
+                                     ctypes.POINTER(ForwardAux), c_void_p]),
 }
 
 # weight formats of an expert bank (moe_nvfp4_experts_t.format)
 MOE_WEIGHT_NVFP4 = 0
 MOE_WEIGHT_MXFP4 = 1
-FORMATS = {"nvfp4": MOE_WEIGHT_NVFP4, "mxfp4": MOE_WEIGHT_MXFP4}
-SCALE_GROUP = {"nvfp4": 16, "mxfp4": 32}
+# bank layouts of the Python side: "mxfp4_a4" is MXFP4 in the W4A4 tile layout (the W4A4 layer)
+FORMATS = {"nvfp4": MOE_WEIGHT_NVFP4, "mxfp4": MOE_WEIGHT_MXFP4, "mxfp4_a4": MOE_WEIGHT_MXFP4}
+SCALE_GROUP = {"nvfp4": 16, "mxfp4": 32, "mxfp4_a4": 32}
+PACK_FN = {"nvfp4": "moe_nvfp4_pack_tiles", "mxfp4": "moe_mxfp4_pack_tiles", "mxfp4_a4": "moe_mxfp4_pack_tiles_a4"}
 
 _lib = None
 

@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <functional>
 
 #include "common.h"
 
@@ -87,6 +88,42 @@ ForwardLayout forward_layout(int32_t T, int32_t H, int32_t I, int32_t I_shared, 
   const size_t h_tiled_bytes = I_shared == 0 || I_shared == I ? mt_bound * 128 * (size_t)I * 2 : 0;
   L.h = take(std::max(h_rows_bytes, h_tiled_bytes));
   L.h_shared = L.h + align_up(S * I * 2);
+  L.y = take((S + (I_shared > 0 ? (size_t)T : 0)) * H * 2);
+  L.total = off;
+  return L;
+}
+
+// W4A4 forward: routing buffers as above, then the 4-bit activations (x, then h), h in bf16
+// (row-major; the shared expert's rows after the routed ones) and the expert outputs y.
+struct ForwardLayoutA4 {
+  size_t logits, ids, w, counts, offsets, sorted_slot, slot_to_row, block_hist;
+  size_t xq, xs, h, hq, hs, y;
+  size_t total;
+};
+
+ForwardLayoutA4 forward_layout_a4(int32_t T, int32_t H, int32_t I, int32_t I_shared, int32_t E, int32_t k) {
+  ForwardLayoutA4 L{};
+  const size_t S = (size_t)T * k;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  L.logits = take((size_t)T * E * 4);
+  L.ids = take(S * 4);
+  L.w = take(S * 4);
+  L.counts = take((size_t)E * 4);
+  L.offsets = take((size_t)(E + 1) * 4);
+  L.sorted_slot = take(S * 4);
+  L.slot_to_row = take(S * 4);
+  L.block_hist = take(S > (size_t)moe::kPermuteChunk ? (size_t)moe::permute_blocks((int64_t)S) * E * 4 : 0);
+  L.xq = take((size_t)T * H / 2);
+  L.xs = take((size_t)T * H / 32);
+  const size_t h_elems = S * I + (size_t)T * I_shared;   // both parts are multiples of 128 elements
+  L.h = take(h_elems * 2);
+  L.hq = take(h_elems / 2);
+  L.hs = take(h_elems / 32);
   L.y = take((S + (I_shared > 0 ? (size_t)T : 0)) * H * 2);
   L.total = off;
   return L;
@@ -195,8 +232,13 @@ size_t moe_nvfp4_forward_workspace_size(int32_t T, int32_t H, int32_t I, int32_t
   return forward_layout(T, H, I, I_shared, E, k).total;
 }
 
-moe_status_t moe_validate_forward(const moe_nvfp4_layer_t* layer, int32_t T, size_t workspace_bytes,
-                                  const char* gfx_arch) {
+}  // extern "C"
+
+namespace {
+
+// Shapes, pointers and formats of a layer for T tokens (every check of a forward pass but the
+// workspace size and the device).
+moe_status_t validate_layer(const moe_nvfp4_layer_t* layer, int32_t T) {
   if (!layer) return MOE_ERR_INVALID_ARGUMENT;
   const int32_t H = layer->hidden, E = layer->num_experts, k = layer->top_k;
   if (!valid_route_dims(T, H, E, k)) return MOE_ERR_INVALID_ARGUMENT;
@@ -207,10 +249,58 @@ moe_status_t moe_validate_forward(const moe_nvfp4_layer_t* layer, int32_t T, siz
   if (has_shared && layer->shared.format != layer->routed.format) return MOE_ERR_INVALID_ARGUMENT;
   const int32_t I = layer->routed.inter, Is = has_shared ? layer->shared.inter : 0;
   if (((int64_t)T * k + T) * std::max(I, Is) * 2 >= kMaxActivationBytes) return MOE_ERR_INVALID_ARGUMENT;
-  if (T > 0 && workspace_bytes < moe_nvfp4_forward_workspace_size(T, H, I, Is, E, k))
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_validate_forward(const moe_nvfp4_layer_t* layer, int32_t T, size_t workspace_bytes,
+                                  const char* gfx_arch) {
+  if (moe_status_t st = validate_layer(layer, T)) return st;
+  const bool has_shared = layer->shared.num_experts != 0;
+  const int32_t I = layer->routed.inter, Is = has_shared ? layer->shared.inter : 0;
+  if (T > 0 && workspace_bytes < moe_nvfp4_forward_workspace_size(T, layer->hidden, I, Is, layer->num_experts,
+                                                                   layer->top_k))
     return MOE_ERR_WORKSPACE_TOO_SMALL;
   return check_arch(gfx_arch);
 }
+
+moe_status_t moe_mxfp4_w4a4_validate_forward(const moe_nvfp4_layer_t* layer, int32_t T, size_t workspace_bytes,
+                                             const char* gfx_arch) {
+  if (moe_status_t st = validate_layer(layer, T)) return st;
+  if (layer->routed.format != MOE_WEIGHT_MXFP4) return MOE_ERR_INVALID_ARGUMENT;
+  const bool has_shared = layer->shared.num_experts != 0;
+  const int32_t I = layer->routed.inter, Is = has_shared ? layer->shared.inter : 0;
+  if (T > 0 && workspace_bytes < moe_mxfp4_w4a4_forward_workspace_size(T, layer->hidden, I, Is, layer->num_experts,
+                                                                        layer->top_k))
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return check_arch(gfx_arch);
+}
+
+namespace {
+
+// S1-S3 of a forward pass: router logits, top-k, permutation.
+moe_status_t run_routing(const moe_nvfp4_layer_t* layer, const uint16_t* x, int32_t T, float* logits, int32_t* ids,
+                         float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_to_row,
+                         int32_t* block_hist, const std::function<moe_status_t(int)>& mark, hipStream_t stream) {
+  const int32_t H = layer->hidden, E = layer->num_experts, k = layer->top_k;
+  moe_status_t st = moe::launch_router_logits(x, layer->w_router, layer->router_bias, T, H, E, logits, stream);
+  if (st || (st = mark(1))) return st;
+  if ((int64_t)T * k <= moe::kPermuteChunk) {
+    // few tokens: top-k and permutation together in one workgroup
+    st = moe::launch_topk_permute_small(logits, T, E, k, ids, w, counts, offsets, sorted_slot, slot_to_row, stream);
+  } else {
+    st = moe::launch_route(nullptr, nullptr, nullptr, T, H, E, k, true, logits, ids, w, stream);
+    if (st) return st;
+    st = moe::launch_permute(ids, T, k, E, counts, offsets, sorted_slot, slot_to_row, block_hist, stream);
+  }
+  if (st) return st;
+  return mark(2);
+}
+
+}  // namespace
 
 moe_status_t moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int32_t T, uint16_t* out,
                                void* workspace, size_t workspace_bytes, const moe_forward_aux_t* aux,
@@ -238,24 +328,15 @@ moe_status_t moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x
   uint16_t* y = at<uint16_t>(workspace, L.y);
 
   void* const* events = aux ? aux->stage_events : nullptr;
-  auto mark = [&](int i) -> moe_status_t {
+  const std::function<moe_status_t(int)> mark = [&](int i) -> moe_status_t {
     if (!events || !events[i]) return MOE_OK;
     return hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
   };
 
   moe_status_t st = mark(0);
   if (st) return st;
-  st = moe::launch_router_logits(x, layer->w_router, layer->router_bias, T, H, E, logits, stream);
-  if (st || (st = mark(1))) return st;
-  if (S <= moe::kPermuteChunk) {
-    // few tokens: top-k and permutation together in one workgroup
-    st = moe::launch_topk_permute_small(logits, T, E, k, ids, w, counts, offsets, sorted_slot, slot_to_row, stream);
-  } else {
-    st = moe::launch_route(nullptr, nullptr, nullptr, T, H, E, k, true, logits, ids, w, stream);
-    if (st) return st;
-    st = moe::launch_permute(ids, T, k, E, counts, offsets, sorted_slot, slot_to_row, block_hist, stream);
-  }
-  if (st || (st = mark(2))) return st;
+  st = run_routing(layer, x, T, logits, ids, w, counts, offsets, sorted_slot, slot_to_row, block_hist, mark, stream);
+  if (st) return st;
 
   // S4: routed rows gathered through sorted_slot; the shared expert rides in the same launch when
   // its width matches, otherwise it gets a launch of its own.
@@ -393,6 +474,197 @@ moe_status_t moe_mxfp4_quantize(const float* w, int32_t num_tensors, int32_t row
   if (!al16(w) || !al16(packed)) return MOE_ERR_INVALID_ARGUMENT;
   if (moe_status_t st = check_arch(nullptr)) return st;
   return moe::launch_quantize_mx(w, num_tensors, rows, cols, packed, scales, static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_mxfp4_quantize_act(const uint16_t* a, int32_t rows, int32_t cols, uint8_t* packed, uint8_t* scales,
+                                    void* stream) {
+  if (rows < 0 || cols < 0 || cols % 32 != 0) return MOE_ERR_INVALID_ARGUMENT;
+  if ((int64_t)rows * cols == 0) return MOE_OK;
+  if (!a || !packed || !scales || !al16(a) || !al16(packed)) return MOE_ERR_INVALID_ARGUMENT;
+  if (moe_status_t st = check_arch(nullptr)) return st;
+  return moe::launch_quantize_act_mx(a, rows, cols, packed, scales, static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_mxfp4_pack_tiles_a4(const uint8_t* packed, const uint8_t* scales, int32_t num_tensors, int32_t rows,
+                                     int32_t cols, uint8_t* tiled, uint8_t* tiled_scales, void* stream) {
+  if (num_tensors < 0 || rows < 0 || cols < 0 || rows % 16 != 0 || cols % 128 != 0) return MOE_ERR_INVALID_ARGUMENT;
+  if ((int64_t)num_tensors * rows * cols == 0) return MOE_OK;
+  if (!packed || !scales || !tiled || !tiled_scales) return MOE_ERR_INVALID_ARGUMENT;
+  if (!al16(packed) || !al16(scales) || !al16(tiled) || !al16(tiled_scales)) return MOE_ERR_INVALID_ARGUMENT;
+  if (moe_status_t st = check_arch(nullptr)) return st;
+  return moe::launch_pack_tiles_a4(packed, scales, num_tensors, rows, cols, tiled, tiled_scales,
+                                   static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_mxfp4_w4a4_grouped_gemm(int32_t stage, const moe_nvfp4_experts_t* w, const uint8_t* a,
+                                         const uint8_t* a_scale, const int32_t* row_index, int32_t row_divisor,
+                                         const int32_t* expert_offsets, int32_t M_total, uint16_t* out, void* stream) {
+  if (!w || (stage != MOE_GEMM_GATE_UP && stage != MOE_GEMM_DOWN)) return MOE_ERR_INVALID_ARGUMENT;
+  if (w->num_experts < 1 || w->num_experts > 1024) return MOE_ERR_INVALID_ARGUMENT;
+  if (!valid_bank(*w, w->hidden, w->num_experts) || w->format != MOE_WEIGHT_MXFP4) return MOE_ERR_INVALID_ARGUMENT;
+  if (w->hidden <= 0 || w->hidden % 128 != 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (M_total < 0 || row_divisor < 1) return MOE_ERR_INVALID_ARGUMENT;
+  const int64_t K_ = stage == MOE_GEMM_GATE_UP ? w->hidden : w->inter;
+  if ((int64_t)M_total * K_ / 2 >= kMaxActivationBytes) return MOE_ERR_INVALID_ARGUMENT;
+  if (stage == MOE_GEMM_DOWN && row_index) return MOE_ERR_INVALID_ARGUMENT;
+  if (M_total == 0) return MOE_OK;
+  if (!a || !a_scale || !expert_offsets || !out || !al16(a) || !al16(a_scale) || !al16(out))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (moe_status_t st = check_arch(nullptr)) return st;
+  moe::GemmProblemA4 p{};
+  p.stage = stage;
+  const bool gu = stage == MOE_GEMM_GATE_UP;
+  p.N = gu ? w->inter : w->hidden;
+  p.K = gu ? w->hidden : w->inter;
+  p.bank = gu ? bank_w13(*w) : bank_w2(*w);
+  p.offsets = expert_offsets;
+  p.G = w->num_experts;
+  p.M = M_total;
+  p.a = a;
+  p.a_scale = a_scale;
+  p.row_index = row_index;
+  p.row_divisor = row_divisor;
+  p.out = out;
+  return moe::launch_grouped_gemm_a4(p, static_cast<hipStream_t>(stream));
+}
+
+size_t moe_mxfp4_w4a4_forward_workspace_size(int32_t T, int32_t H, int32_t I, int32_t I_shared, int32_t E, int32_t k) {
+  if (T < 0 || H <= 0 || I <= 0 || I_shared < 0 || E < 1 || k < 1) return 0;
+  return forward_layout_a4(T, H, I, I_shared, E, k).total;
+}
+
+moe_status_t moe_mxfp4_w4a4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int32_t T, uint16_t* out,
+                                    void* workspace, size_t workspace_bytes, const moe_forward_aux_t* aux,
+                                    void* stream_) {
+  if (moe_status_t st = moe_mxfp4_w4a4_validate_forward(layer, T, workspace_bytes, nullptr)) return st;
+  if (T == 0) return MOE_OK;
+  const int32_t H = layer->hidden, E = layer->num_experts, k = layer->top_k;
+  const bool has_shared = layer->shared.num_experts != 0;
+  const int32_t I = layer->routed.inter, Is = has_shared ? layer->shared.inter : 0;
+  if (!x || !out || !workspace || !al16(x) || !al16(out) || !al16(workspace)) return MOE_ERR_INVALID_ARGUMENT;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const int32_t S = T * k;
+  const ForwardLayoutA4 L = forward_layout_a4(T, H, I, Is, E, k);
+
+  float* logits = (aux && aux->logits) ? aux->logits : at<float>(workspace, L.logits);
+  int32_t* ids = (aux && aux->topk_ids) ? aux->topk_ids : at<int32_t>(workspace, L.ids);
+  float* w = (aux && aux->topk_w) ? aux->topk_w : at<float>(workspace, L.w);
+  int32_t* counts = (aux && aux->expert_counts) ? aux->expert_counts : at<int32_t>(workspace, L.counts);
+  int32_t* offsets = at<int32_t>(workspace, L.offsets);
+  int32_t* sorted_slot = at<int32_t>(workspace, L.sorted_slot);
+  int32_t* slot_to_row = at<int32_t>(workspace, L.slot_to_row);
+  int32_t* block_hist = at<int32_t>(workspace, L.block_hist);
+  uint8_t* xq = at<uint8_t>(workspace, L.xq);
+  uint8_t* xs = at<uint8_t>(workspace, L.xs);
+  uint16_t* h = at<uint16_t>(workspace, L.h);
+  uint8_t* hq = at<uint8_t>(workspace, L.hq);
+  uint8_t* hs = at<uint8_t>(workspace, L.hs);
+  uint16_t* y = at<uint16_t>(workspace, L.y);
+  // the shared expert's rows follow the routed ones in h and in its 4-bit copy
+  uint16_t* h_sh = h + (size_t)S * I;
+  uint8_t* hq_sh = hq + (size_t)S * I / 2;
+  uint8_t* hs_sh = hs + (size_t)S * I / 32;
+
+  void* const* events = aux ? aux->stage_events : nullptr;
+  const std::function<moe_status_t(int)> mark = [&](int i) -> moe_status_t {
+    if (!events || !events[i]) return MOE_OK;
+    return hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  };
+
+  moe_status_t st = mark(0);
+  if (st) return st;
+  st = run_routing(layer, x, T, logits, ids, w, counts, offsets, sorted_slot, slot_to_row, block_hist, mark, stream);
+  if (st) return st;
+
+  // S4: x to MXFP4 once per token; routed rows gathered through sorted_slot, the shared expert in
+  // the same launch when its width matches
+  if ((st = moe::launch_quantize_act_mx(x, T, H, xq, xs, stream))) return st;
+  const bool fuse_shared = has_shared && Is == I;
+  moe::GemmProblemA4 gu{};
+  gu.stage = MOE_GEMM_GATE_UP;
+  gu.N = I;
+  gu.K = H;
+  gu.bank = bank_w13(layer->routed);
+  gu.offsets = offsets;
+  gu.G = E;
+  gu.M = S;
+  gu.a = xq;
+  gu.a_scale = xs;
+  gu.row_index = sorted_slot;
+  gu.row_divisor = k;
+  gu.out = h;
+  if (fuse_shared) {
+    gu.has_extra = 1;
+    gu.extra = bank_w13(layer->shared);
+    gu.M_extra = T;
+    gu.a_extra = xq;
+    gu.a_extra_scale = xs;
+  }
+  if ((st = moe::launch_grouped_gemm_a4(gu, stream))) return st;
+  if (has_shared && !fuse_shared) {
+    moe::GemmProblemA4 gs{};
+    gs.stage = MOE_GEMM_GATE_UP;
+    gs.N = Is;
+    gs.K = H;
+    gs.bank = bank_w13(layer->shared);
+    gs.out = h_sh;
+    gs.has_extra = 1;
+    gs.extra = gs.bank;
+    gs.M_extra = T;
+    gs.a_extra = xq;
+    gs.a_extra_scale = xs;
+    if ((st = moe::launch_grouped_gemm_a4(gs, stream))) return st;
+  }
+  if ((st = mark(3))) return st;
+
+  // S5: h (bf16) to MXFP4, then the down GEMM
+  if (fuse_shared || !has_shared) {
+    if ((st = moe::launch_quantize_act_mx(h, (int64_t)S + (has_shared ? T : 0), I, hq, hs, stream))) return st;
+  } else {
+    if ((st = moe::launch_quantize_act_mx(h, S, I, hq, hs, stream))) return st;
+    if ((st = moe::launch_quantize_act_mx(h_sh, T, Is, hq_sh, hs_sh, stream))) return st;
+  }
+  moe::GemmProblemA4 dn{};
+  dn.stage = MOE_GEMM_DOWN;
+  dn.N = H;
+  dn.K = I;
+  dn.bank = bank_w2(layer->routed);
+  dn.offsets = offsets;
+  dn.G = E;
+  dn.M = S;
+  dn.a = hq;
+  dn.a_scale = hs;
+  dn.row_divisor = 1;
+  dn.out = y;
+  if (fuse_shared) {
+    dn.has_extra = 1;
+    dn.extra = bank_w2(layer->shared);
+    dn.M_extra = T;
+    dn.a_extra = hq_sh;
+    dn.a_extra_scale = hs_sh;
+  }
+  if ((st = moe::launch_grouped_gemm_a4(dn, stream))) return st;
+  if (has_shared && !fuse_shared) {
+    moe::GemmProblemA4 ds{};
+    ds.stage = MOE_GEMM_DOWN;
+    ds.N = H;
+    ds.K = Is;
+    ds.bank = bank_w2(layer->shared);
+    ds.M = S;  // output rows start after the routed rows
+    ds.out = y;
+    ds.has_extra = 1;
+    ds.extra = ds.bank;
+    ds.M_extra = T;
+    ds.a_extra = hq_sh;
+    ds.a_extra_scale = hs_sh;
+    if ((st = moe::launch_grouped_gemm_a4(ds, stream))) return st;
+  }
+  if ((st = mark(4))) return st;
+
+  // S6
+  st = moe::launch_combine(y, slot_to_row, w, has_shared ? y + (size_t)S * H : nullptr, T, k, H, out, stream);
+  if (st) return st;
+  return mark(5);
 }
 
 }  // extern "C"

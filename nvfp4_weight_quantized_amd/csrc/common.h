@@ -34,6 +34,12 @@ __device__ __forceinline__ void direct_load16(const void* base, uint32_t offset,
   asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(offset), "s"(base), "{m0}"(lds_addr) : "memory");
 }
 
+// 4 bytes per lane from global memory straight to LDS (global_load_lds_dword): lane i's dword lands
+// at lds_addr + 4*i; otherwise as direct_load16.
+__device__ __forceinline__ void direct_load4(const void* base, uint32_t offset, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dword %0, %1" : : "v"(offset), "s"(base), "{m0}"(lds_addr) : "memory");
+}
+
 // Host-side launch helpers -----------------------------------------------------------------
 
 // Status of the last launch on this thread; MOE_ERR_HIP if the launch was rejected.
@@ -114,6 +120,32 @@ bool grouped_gemm_uses_tall_tiles(const GemmProblem& p);
 
 moe_status_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream);
 
+// W4A4 grouped GEMM: MXFP4 weights in the W4A4 tile layout (layout.hip) times MXFP4 activations,
+// on the scaled FP4 matrix cores.  Same grouping and output as GemmProblem; the activations are
+// E2M1 codes [rows][K/2] and E8M0 scales [rows][K/32] (row-major, as quantize.hip writes them).
+struct GemmProblemA4 {
+  int32_t stage;
+  int32_t N;
+  int32_t K;
+  GemmBank bank;          // format MXFP4, w / ws in the W4A4 tile layout
+  const int32_t* offsets;
+  int32_t G;
+  int32_t M;
+  const uint8_t* a;       // activation codes
+  const uint8_t* a_scale; // activation block scales
+  const int32_t* row_index;
+  int32_t row_divisor;
+  uint16_t* out;
+  int32_t has_extra;
+  GemmBank extra;
+  int32_t M_extra;
+  const uint8_t* a_extra;
+  const uint8_t* a_extra_scale;
+  uint16_t* out_tiled;    // always NULL here (the shared epilogue's tiled-h output is W4A16 only)
+};
+
+moe_status_t launch_grouped_gemm_a4(const GemmProblemA4& p, hipStream_t stream);
+
 // Combine -----------------------------------------------------------------------------------
 moe_status_t launch_combine(const uint16_t* y_rows, const int32_t* slot_to_row, const float* w,
                             const uint16_t* y_shared, int32_t T, int32_t k, int32_t H, uint16_t* out,
@@ -124,11 +156,15 @@ moe_status_t launch_pack_tiles(const uint8_t* packed, const uint8_t* scales, int
                                int32_t cols, uint8_t* tiled, uint8_t* tiled_scales, hipStream_t stream);
 moe_status_t launch_pack_tiles_mx(const uint8_t* packed, const uint8_t* scales, int32_t num_tensors, int32_t rows,
                                   int32_t cols, uint8_t* tiled, uint8_t* tiled_scales, hipStream_t stream);
+moe_status_t launch_pack_tiles_a4(const uint8_t* packed, const uint8_t* scales, int32_t num_tensors, int32_t rows,
+                                  int32_t cols, uint8_t* tiled, uint8_t* tiled_scales, hipStream_t stream);
 
 // Quantize ----------------------------------------------------------------------------------
 moe_status_t launch_quantize(const float* w, int32_t num_tensors, int32_t rows, int32_t cols,
                              const float* gscale, uint8_t* packed, uint8_t* scales, hipStream_t stream);
 moe_status_t launch_quantize_mx(const float* w, int32_t num_tensors, int32_t rows, int32_t cols, uint8_t* packed,
                                 uint8_t* scales, hipStream_t stream);
+moe_status_t launch_quantize_act_mx(const uint16_t* a, int64_t rows, int32_t cols, uint8_t* packed, uint8_t* scales,
+                                    hipStream_t stream);
 
 }  // namespace moe

@@ -27,22 +27,13 @@
 //  * Groups (experts) are found on the device from the offsets array: no host synchronisation.
 //    Workgroups beyond the real tile count exit at once; empty experts cost nothing.
 #include "common.h"
+#include "gemm_tiles.h"
 
 namespace moe {
 namespace {
 
 constexpr int kAPad = 8;        // bf16 of padding per LDS row (16 bytes) against bank conflicts
 constexpr int kThreads = 256;   // 4 waves
-
-struct TileInfo {
-  int group;     // expert index in its bank
-  int row0;      // first output row of the tile (global row index in the output)
-  int rows;      // valid rows (<= BM)
-  int a_row0;    // first A row (for extra / identity rows) or first sorted row
-  int extra;     // 1: shared-expert group
-};
-
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // Dequantize 8 packed E2M1 codes (one dword, element order = nibble order) times scale s.
 __device__ __forceinline__ bf16x8 dequant8(uint32_t q, float s) {
@@ -145,148 +136,6 @@ __device__ __forceinline__ uint4 load_stream16(const uint8_t* p) {
 }
 __device__ __forceinline__ uint32_t load_stream4(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
-}
-
-__device__ __forceinline__ void store_bf16x4(uint16_t* dst, float a, float b, float c, float d) {
-  const uint32_t lo = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-  const uint32_t hi = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
-  *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
-}
-
-// Tile `mtile`: the extra group's tiles come first (the shared expert, every token: the longest
-// group, started early), then each group's in order.  Wave 0 only.  Lane i owns the contiguous
-// groups [i*gpl, (i+1)*gpl) (gpl = ceil(G/64) <= 16): one scan of the lanes' tile counts finds the
-// owning lane, which walks its groups.
-template <int BM>
-__device__ bool find_tile(const GemmProblem& p, int mtile, TileInfo* out) {
-  const int lane = threadIdx.x & 63;
-  if (p.has_extra) {
-    const int xt = (p.M_extra + BM - 1) / BM;
-    if (mtile < xt) {
-      if (lane == 0) {
-        out->group = 0;
-        out->row0 = p.M + mtile * BM;
-        out->a_row0 = mtile * BM;
-        out->rows = min(BM, p.M_extra - mtile * BM);
-        out->extra = 1;
-      }
-      return true;
-    }
-    mtile -= xt;
-  }
-  const int gpl = (p.G + 63) >> 6;
-  const int g0 = lane * gpl;
-  int start[17];
-#pragma unroll
-  for (int i = 0; i <= 16; ++i) start[i] = (i <= gpl && g0 + i <= p.G) ? p.offsets[g0 + i] : 0;
-  int t = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-    if (i < gpl && g0 + i < p.G) t += (start[i + 1] - start[i] + BM - 1) / BM;
-  int incl = t;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
-  const int excl = incl - t;
-  const uint64_t m = __ballot(excl <= mtile && mtile < incl);
-  if (!m) return false;
-  if (lane == __ffsll((unsigned long long)m) - 1) {
-    int first = excl;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i >= gpl || g0 + i >= p.G) break;
-      const int cnt = start[i + 1] - start[i];
-      const int ti = (cnt + BM - 1) / BM;
-      if (mtile < first + ti) {
-        const int within = mtile - first;
-        out->group = g0 + i;
-        out->row0 = start[i] + within * BM;
-        out->a_row0 = start[i] + within * BM;
-        out->rows = min(BM, cnt - within * BM);
-        out->extra = 0;
-        break;
-      }
-      first += ti;
-    }
-  }
-  return true;
-}
-
-// Wave 0: number of BM-row tiles over the groups (+ extra group).
-template <int BM>
-__device__ int count_tiles(const GemmProblem& p) {
-  const int lane = threadIdx.x & 63;
-  int t = 0;
-  for (int g = lane; g < p.G; g += 64) t += (p.offsets[g + 1] - p.offsets[g] + BM - 1) / BM;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
-  if (p.has_extra) t += (p.M_extra + BM - 1) / BM;
-  return t;
-}
-
-// Weight-row block (16 rows) of B fragment f of `wave` in output-column tile `ntile`.
-template <int NB, bool GATE_UP, int BN, int COLS_PER_WAVE>
-__device__ __forceinline__ int frag_row_block(int f, int ntile, int wave, int N) {
-  int n;
-  if (GATE_UP) {
-    const int fg = (f < NB / 2) ? f : f - NB / 2;
-    n = ntile * BN + wave * COLS_PER_WAVE + 16 * fg;
-    if (f >= NB / 2) n += N;  // up rows follow the gate rows
-  } else {
-    n = ntile * BN + wave * COLS_PER_WAVE + 16 * f;
-  }
-  return n >> 4;
-}
-
-// Epilogue: scale the accumulators by the global scale(s), SiLU(gate)*up for gate/up, store bf16.
-// acc[i][f] holds, in lane l = 16q + n, output row 16i + n and the four columns 4q..4q+3 of
-// fragment f's 16 columns.
-template <int MI, int NB, bool GATE_UP, int BN, int COLS_PER_WAVE, int FMT = kFmtNvfp4>
-__device__ __forceinline__ void epilogue(const GemmProblem& p, const GemmBank& bank, const TileInfo& ti, int ntile,
-                                         const f32x4 (&acc)[MI][NB], int mtile = 0) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int q = lane >> 4, nl = lane & 15;
-  const float* gs = WFmt<FMT>::kGlobalScale ? bank.gs + (size_t)ti.group * bank.gs_per_expert : nullptr;
-  const int col0 = ntile * BN + wave * COLS_PER_WAVE + 4 * q;
-  if (GATE_UP) {
-    const float dg = gs ? gs[0] : 1.f, du = gs ? gs[1] : 1.f;
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int row = 16 * i + nl;
-      if (row >= ti.rows) continue;
-      uint16_t* orow = p.out + (size_t)(ti.row0 + row) * p.N + col0;
-#pragma unroll
-      for (int f = 0; f < NB / 2; ++f) {
-        float h[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) h[r] = silu(acc[i][f][r] * dg) * (acc[i][f + NB / 2][r] * du);
-        if (p.out_tiled) {
-          // tiled layout: column col -> chunk col/128, step (col%128)/32, lane group (col%32)/8
-          const int col = col0 + 16 * f;
-          const int kk = col & 127;
-          const size_t byte = ((size_t)(mtile * (p.N >> 7) + (col >> 7)) * 32 + 4 * i + (kk >> 5)) * 1024 +
-                              (size_t)(16 * (((kk >> 3) & 3) * 16 + nl) + 2 * (kk & 7));
-          store_bf16x4(p.out_tiled + byte / 2, h[0], h[1], h[2], h[3]);
-        } else {
-          store_bf16x4(orow + 16 * f, h[0], h[1], h[2], h[3]);
-        }
-      }
-    }
-  } else {
-    const float dd = gs ? gs[0] : 1.f;
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int row = 16 * i + nl;
-      if (row >= ti.rows) continue;
-      uint16_t* orow = p.out + (size_t)(ti.row0 + row) * p.N + col0;
-#pragma unroll
-      for (int f = 0; f < NB; ++f)
-        store_bf16x4(orow + 16 * f, acc[i][f][0] * dd, acc[i][f][1] * dd, acc[i][f][2] * dd, acc[i][f][3] * dd);
-    }
-  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -600,7 +449,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmProblem p) {
         }
       }
   }
-  epilogue<MI, NB, GATE_UP, BN, COLS_PER_WAVE, FMT>(p, bank, ti, ntile, acc);
+  epilogue<MI, NB, GATE_UP, BN, COLS_PER_WAVE, WFmt<FMT>::kGlobalScale>(p, bank, ti, ntile, acc);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -629,12 +478,6 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmProblem p) {
 //    registers per lane.
 constexpr int kTallBK = 128;
 constexpr int kTallRows = 128;
-constexpr int kXcds = 8;
-
-template <int N>
-struct IntC {
-  static constexpr int value = N;
-};
 
 template <int NB, bool GATE_UP, int WAVES, int FMT>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kernel(GemmProblem p) {
@@ -833,7 +676,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
     case 7: run(IntC<7>{}); break;
     default: run(IntC<8>{}); break;
   }
-  epilogue<MI, NB, GATE_UP, BN, COLS_PER_WAVE, FMT>(p, bank, ti, ntile, acc, mtile);
+  epilogue<MI, NB, GATE_UP, BN, COLS_PER_WAVE, WFmt<FMT>::kGlobalScale>(p, bank, ti, ntile, acc, mtile);
 }
 
 template <int NB, bool GATE_UP, int WAVES, int FMT>

@@ -79,7 +79,42 @@ __global__ __launch_bounds__(256) void pack_tiles_mx_kernel(const uint8_t* __res
         *reinterpret_cast<const uint32_t*>(scales + row * (cols / 32) + 4 * c);
 }
 
+// W4A4 tiles for the scaled FP4 MFMA (grouped_gemm_a4.hip): lane l = 16*q + n owns row r and the
+// 32 elements K [128c + 32q, +32), one E8M0 block.  Nibble bytes [16*l, 16*l + 16) of tile t are
+// row r's canonical bytes [64*c + 16*q, +16); scale byte l is row r's canonical scale byte 4*c + q.
+__global__ __launch_bounds__(256) void pack_tiles_a4_kernel(const uint8_t* __restrict__ packed,
+                                                            const uint8_t* __restrict__ scales, long long total_lanes,
+                                                            int rows, int cols, uint8_t* __restrict__ tiled,
+                                                            uint8_t* __restrict__ tiled_scales) {
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= total_lanes) return;
+  const long long tile = gid >> 6;
+  const int l = (int)(gid & 63);
+  const int ct = cols / 128;
+  const long long tiles_per_tensor = (long long)(rows / 16) * ct;
+  const long long b = tile / tiles_per_tensor;
+  const long long t = tile - b * tiles_per_tensor;
+  const int nb = (int)(t / ct);
+  const int c = (int)(t - (long long)nb * ct);
+  const int q = l >> 4, n = l & 15;
+  const long long row = b * rows + 16LL * nb + n;
+  *reinterpret_cast<uint4*>(tiled + tile * 1024 + 16 * l) =
+      *reinterpret_cast<const uint4*>(packed + row * (cols / 2) + 64 * c + 16 * q);
+  tiled_scales[tile * 64 + l] = scales[row * (cols / 32) + 4 * c + q];
+}
+
 }  // namespace
+
+moe_status_t launch_pack_tiles_a4(const uint8_t* packed, const uint8_t* scales, int32_t num_tensors, int32_t rows,
+                                  int32_t cols, uint8_t* tiled, uint8_t* tiled_scales, hipStream_t stream) {
+  const long long lanes = (long long)num_tensors * (rows / 16) * (cols / 128) * 64;
+  if (lanes == 0) return MOE_OK;
+  const long long blocks = (lanes + 255) / 256;
+  if (blocks > 0x7FFFFFFFLL) return MOE_ERR_INVALID_ARGUMENT;
+  hipLaunchKernelGGL(pack_tiles_a4_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, packed, scales, lanes,
+                     (int)rows, (int)cols, tiled, tiled_scales);
+  return launch_status();
+}
 
 moe_status_t launch_pack_tiles_mx(const uint8_t* packed, const uint8_t* scales, int32_t num_tensors, int32_t rows,
                                   int32_t cols, uint8_t* tiled, uint8_t* tiled_scales, hipStream_t stream) {

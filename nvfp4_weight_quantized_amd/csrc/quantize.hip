@@ -79,20 +79,43 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
 }
 
 // MXFP4 ("vLLM on the NVIDIA DGX Spark", section 6.4: E2M1 elements, one E8M0 exponent-only
-// scale per 32 elements, no global scale).  One thread per 32-element group:
+// scale per 32 elements, no global scale).  One thread per 32-element group of fp32 weights or
+// bf16 activations:
 //   e = floor(log2(amax)) - 2 clamped to [-127, 127] (-127 when amax == 0), scale byte e + 127;
 //   code = E2M1_RNE(|w| * 2^-e) saturated at 6 (exact power-of-two scaling), sign bit = (w < 0).
-__global__ __launch_bounds__(256) void quantize_mx_kernel(const float* __restrict__ w, long long total_groups,
-                                                          uint8_t* __restrict__ packed, uint8_t* __restrict__ scales) {
-  const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (g >= total_groups) return;
+// The bf16 instantiation quantizes activation rows for the W4A4 GEMMs (W4A4 checkpoints carry
+// 4-bit activations: "vLLM on the DGX Spark, the Hard Way", "The one rule that explains all the FP4
+// confusion"; the fused MoE kernel quantizes bf16 hidden states itself: the guide's section 4.3).
+__device__ __forceinline__ void load_group(const float* w, long long g, float (&v)[32]) {
   const float4* src = reinterpret_cast<const float4*>(w + g * 32);
-  float v[32];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float4 x = src[i];
     v[4 * i] = x.x; v[4 * i + 1] = x.y; v[4 * i + 2] = x.z; v[4 * i + 3] = x.w;
   }
+}
+
+__device__ __forceinline__ void load_group(const uint16_t* a, long long g, float (&v)[32]) {
+  const uint4* src = reinterpret_cast<const uint4*>(a + g * 32);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 x = src[i];
+    const uint32_t u[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * i + 2 * j] = __uint_as_float(u[j] << 16);
+      v[8 * i + 2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
+    }
+  }
+}
+
+template <typename In>
+__global__ __launch_bounds__(256) void quantize_mx_kernel(const In* __restrict__ w, long long total_groups,
+                                                          uint8_t* __restrict__ packed, uint8_t* __restrict__ scales) {
+  const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (g >= total_groups) return;
+  float v[32];
+  load_group(w, g, v);
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
@@ -115,7 +138,18 @@ moe_status_t launch_quantize_mx(const float* w, int32_t num_tensors, int32_t row
   if (total == 0) return MOE_OK;
   const long long blocks = (total + 255) / 256;
   if (blocks > 0x7FFFFFFFLL) return MOE_ERR_INVALID_ARGUMENT;
-  hipLaunchKernelGGL(quantize_mx_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w, total, packed, scales);
+  hipLaunchKernelGGL(quantize_mx_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream, w, total, packed, scales);
+  return launch_status();
+}
+
+moe_status_t launch_quantize_act_mx(const uint16_t* a, int64_t rows, int32_t cols, uint8_t* packed, uint8_t* scales,
+                                    hipStream_t stream) {
+  const long long total = (long long)rows * (cols / 32);
+  if (total == 0) return MOE_OK;
+  const long long blocks = (total + 255) / 256;
+  if (blocks > 0x7FFFFFFFLL) return MOE_ERR_INVALID_ARGUMENT;
+  hipLaunchKernelGGL(quantize_mx_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, stream, a, total, packed,
+                     scales);
   return launch_status();
 }
 

@@ -44,7 +44,8 @@ class NvFp4Experts:
     """A bank of 4-bit experts on the GPU, weights and scales in the MFMA tile layout.
 
     ``fmt`` "nvfp4": E4M3 scales per 16 elements along K plus fp32 global scales; "mxfp4": E8M0
-    scales per 32 elements and no global scale (the gscale tensors are None).  Shapes are those of
+    scales per 32 elements and no global scale (the gscale tensors are None); "mxfp4_a4": MXFP4 in
+    the W4A4 tile layout, which makes a layer run the W4A4 path.  Shapes are those of
     the canonical tensors (include/moe_nvfp4.h); the bytes of each expert's tensors are permuted by
     ``pack_tiles``.  Use ``NvFp4Experts.from_canonical`` to build one from checkpoint-layout tensors.
     """
@@ -117,6 +118,11 @@ class NvFp4MoELayer:
     @property
     def num_experts(self) -> int:
         return self.routed.num_experts
+
+    @property
+    def is_w4a4(self) -> bool:
+        """True for banks in the W4A4 layout: forward() then quantizes the activations too."""
+        return self.routed.fmt == "mxfp4_a4"
 
     def c_struct(self) -> L.Layer:
         empty = L.Experts()
@@ -235,6 +241,43 @@ def grouped_gemm(stage: int, experts: NvFp4Experts, a: torch.Tensor, expert_offs
     return out
 
 
+def quantize_act(a: torch.Tensor, packed: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None):
+    """MXFP4 quantization of bf16 rows [M, K] -> (codes uint8 [M, K/2], E8M0 scales uint8 [M, K/32])."""
+    _need(a, "a", torch.bfloat16, 2)
+    m, k = a.shape
+    if packed is None:
+        packed = torch.empty(m, k // 2, dtype=torch.uint8, device=a.device)
+    if scales is None:
+        scales = torch.empty(m, k // 32, dtype=torch.uint8, device=a.device)
+    _need(packed, "packed", torch.uint8)
+    _need(scales, "scales", torch.uint8)
+    L.check("moe_mxfp4_quantize_act", L.lib().moe_mxfp4_quantize_act(_ptr(a), m, k, _ptr(packed), _ptr(scales),
+                                                                     _stream(a.device)))
+    return packed, scales
+
+
+def grouped_gemm_a4(stage: int, experts: NvFp4Experts, a_codes: torch.Tensor, a_scales: torch.Tensor,
+                    expert_offsets: torch.Tensor, m_total: int, row_index: Optional[torch.Tensor] = None,
+                    row_divisor: int = 1) -> torch.Tensor:
+    """W4A4 S4/S5 on MXFP4 activations (from ``quantize_act``) and an "mxfp4_a4" bank, bf16 out."""
+    if experts.fmt != "mxfp4_a4":
+        raise ValueError("the W4A4 GEMM needs a bank in the mxfp4_a4 layout")
+    experts.check()
+    _need(a_codes, "a_codes", torch.uint8, 2)
+    _need(a_scales, "a_scales", torch.uint8, 2)
+    _need(expert_offsets, "expert_offsets", torch.int32, 1)
+    if row_index is not None:
+        _need(row_index, "row_index", torch.int32, 1)
+    n = experts.inter if stage == L.MOE_GEMM_GATE_UP else experts.hidden
+    out = torch.empty(m_total, n, dtype=torch.bfloat16, device=a_codes.device)
+    st = experts.c_struct()
+    L.check("moe_mxfp4_w4a4_grouped_gemm",
+            L.lib().moe_mxfp4_w4a4_grouped_gemm(stage, ctypes.byref(st), _ptr(a_codes), _ptr(a_scales),
+                                                _ptr(row_index), row_divisor, _ptr(expert_offsets), m_total,
+                                                _ptr(out), _stream(a_codes.device)))
+    return out
+
+
 def combine(y_rows: torch.Tensor, slot_to_row: torch.Tensor, topk_w: torch.Tensor,
             y_shared: Optional[torch.Tensor] = None) -> torch.Tensor:
     """S6: out [T, H] bf16."""
@@ -253,8 +296,9 @@ def combine(y_rows: torch.Tensor, slot_to_row: torch.Tensor, topk_w: torch.Tenso
 
 # ----------------------------------------------------------------------------- whole layer
 
-def forward_workspace_size(T: int, H: int, I: int, I_shared: int, E: int, k: int) -> int:
-    return int(L.lib().moe_nvfp4_forward_workspace_size(T, H, I, I_shared, E, k))
+def forward_workspace_size(T: int, H: int, I: int, I_shared: int, E: int, k: int, w4a4: bool = False) -> int:
+    fn = L.lib().moe_mxfp4_w4a4_forward_workspace_size if w4a4 else L.lib().moe_nvfp4_forward_workspace_size
+    return int(fn(T, H, I, I_shared, E, k))
 
 
 _POOL = {}
@@ -263,7 +307,8 @@ _POOL = {}
 def workspace_for(layer: NvFp4MoELayer, T: int, device) -> torch.Tensor:
     """One module-level workspace per device, grown on demand and shared by every layer."""
     i_sh = layer.shared.inter if layer.shared is not None else 0
-    need = forward_workspace_size(T, layer.hidden, layer.routed.inter, i_sh, layer.num_experts, layer.top_k)
+    need = forward_workspace_size(T, layer.hidden, layer.routed.inter, i_sh, layer.num_experts, layer.top_k,
+                                  layer.is_w4a4)
     dev = torch.device(device)
     cur = _POOL.get(dev)
     if cur is None or cur.numel() < need:
@@ -275,6 +320,8 @@ def workspace_for(layer: NvFp4MoELayer, T: int, device) -> torch.Tensor:
 def forward(layer: NvFp4MoELayer, x: torch.Tensor, workspace: Optional[torch.Tensor] = None,
             out: Optional[torch.Tensor] = None, return_aux: bool = False, stage_events=None):
     """The whole layer on x [T, H] bf16 -> [T, H] bf16 (and, if asked, logits/ids/weights/counts).
+
+    Runs moe_nvfp4_forward, or moe_mxfp4_w4a4_forward when the layer's banks are "mxfp4_a4".
 
     ``stage_events``: optional sequence of 6 raw hipEvent_t handles (ints or None) recorded at the
     stage boundaries (before S1, after S1, after S2+S3, after S4, S5, S6) on the current stream.
@@ -303,16 +350,17 @@ def forward(layer: NvFp4MoELayer, x: torch.Tensor, workspace: Optional[torch.Ten
         arr = (ctypes.c_void_p * L.NUM_STAGE_EVENTS)(*stage_events)
         aux.stage_events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
     st = layer.c_struct()
-    L.check("moe_nvfp4_forward",
-            L.lib().moe_nvfp4_forward(ctypes.byref(st), _ptr(x), t, _ptr(out), _ptr(workspace), workspace.numel(),
-                                      ctypes.byref(aux) if aux is not None else None, _stream(x.device)))
+    fn = "moe_mxfp4_w4a4_forward" if layer.is_w4a4 else "moe_nvfp4_forward"
+    L.check(fn, getattr(L.lib(), fn)(ctypes.byref(st), _ptr(x), t, _ptr(out), _ptr(workspace), workspace.numel(),
+                                     ctypes.byref(aux) if aux is not None else None, _stream(x.device)))
     return (out, aux_t) if return_aux else out
 
 
-def validate_forward(layer_struct: L.Layer, T: int, workspace_bytes: int, arch: Optional[str] = "gfx950") -> int:
+def validate_forward(layer_struct: L.Layer, T: int, workspace_bytes: int, arch: Optional[str] = "gfx950",
+                     w4a4: bool = False) -> int:
     """Pure-host validation status (needs no GPU when ``arch`` is given)."""
-    return int(L.lib().moe_validate_forward(ctypes.byref(layer_struct), T, workspace_bytes,
-                                            arch.encode() if arch is not None else None))
+    fn = L.lib().moe_mxfp4_w4a4_validate_forward if w4a4 else L.lib().moe_validate_forward
+    return int(fn(ctypes.byref(layer_struct), T, workspace_bytes, arch.encode() if arch is not None else None))
 
 
 # ----------------------------------------------------------------------------- weight preparation
@@ -330,7 +378,7 @@ def gscale_from_quant_scale(q) -> np.ndarray:
 def pack_tiles(packed: torch.Tensor, scales: torch.Tensor, tiled: Optional[torch.Tensor] = None,
                tiled_scales: Optional[torch.Tensor] = None, fmt: str = "nvfp4"):
     """Canonical [..., rows, cols/2] nibbles + [..., rows, cols/16] (nvfp4) or [..., rows, cols/32]
-    (mxfp4) scales -> MFMA tile layout (same shapes)."""
+    (mxfp4, mxfp4_a4) scales -> the MFMA tile layout of ``fmt`` (same shapes)."""
     _need(packed, "packed", torch.uint8)
     _need(scales, "scales", torch.uint8)
     rows, half = packed.shape[-2], packed.shape[-1]
@@ -340,7 +388,7 @@ def pack_tiles(packed: torch.Tensor, scales: torch.Tensor, tiled: Optional[torch
         raise ValueError("scales shape does not match packed")
     tiled = torch.empty_like(packed) if tiled is None else tiled
     tiled_scales = torch.empty_like(scales) if tiled_scales is None else tiled_scales
-    fn = "moe_nvfp4_pack_tiles" if fmt == "nvfp4" else "moe_mxfp4_pack_tiles"
+    fn = L.PACK_FN[fmt]
     L.check(fn, getattr(L.lib(), fn)(_ptr(packed), _ptr(scales), nt, rows, cols, _ptr(tiled), _ptr(tiled_scales),
                                      _stream(packed.device)))
     return tiled, tiled_scales

@@ -16,8 +16,9 @@ def _dequant_scales(amax, convention: str):
     return gs
 
 
-def build_bank_mx(wl: synth.Workload, bank: str, device="cuda") -> ops.NvFp4Experts:
-    """The same seeded fp32 experts quantized to MXFP4 (E8M0 scales per 32, no global scale)."""
+def build_bank_mx(wl: synth.Workload, bank: str, device="cuda", fmt: str = "mxfp4") -> ops.NvFp4Experts:
+    """The same seeded fp32 experts quantized to MXFP4 (E8M0 scales per 32, no global scale), in the
+    tile layout of ``fmt`` ("mxfp4": W4A16 kernels, "mxfp4_a4": W4A4 kernels)."""
     count = wl.E if bank == "routed" else 1
     inter = wl.I if bank == "routed" else wl.I_shared
     h = wl.H
@@ -34,17 +35,17 @@ def build_bank_mx(wl: synth.Workload, bank: str, device="cuda") -> ops.NvFp4Expe
         f13, f2 = synth.expert_fp32(wl, bank, e, dev)
         ops.quantize_mx(f13, packed=c13, scales=c13_s)
         ops.quantize_mx(f2, packed=c2, scales=c2_s)
-        ops.pack_tiles(c13, c13_s, tiled=w13[e], tiled_scales=w13_s[e], fmt="mxfp4")
-        ops.pack_tiles(c2, c2_s, tiled=w2[e], tiled_scales=w2_s[e], fmt="mxfp4")
+        ops.pack_tiles(c13, c13_s, tiled=w13[e], tiled_scales=w13_s[e], fmt=fmt)
+        ops.pack_tiles(c2, c2_s, tiled=w2[e], tiled_scales=w2_s[e], fmt=fmt)
         del f13, f2
-    return ops.NvFp4Experts(w13, w13_s, None, w2, w2_s, None, fmt="mxfp4")
+    return ops.NvFp4Experts(w13, w13_s, None, w2, w2_s, None, fmt=fmt)
 
 
 def build_bank(wl: synth.Workload, bank: str, device="cuda", fmt: str = "nvfp4") -> ops.NvFp4Experts:
     """Quantize every expert of a bank ("routed": E experts of width I; "shared": 1 of width I_shared)
     on the GPU and repack it into the MFMA tile layout."""
-    if fmt == "mxfp4":
-        return build_bank_mx(wl, bank, device)
+    if fmt in ("mxfp4", "mxfp4_a4"):
+        return build_bank_mx(wl, bank, device, fmt)
     count = wl.E if bank == "routed" else 1
     inter = wl.I if bank == "routed" else wl.I_shared
     h = wl.H

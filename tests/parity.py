@@ -22,8 +22,9 @@ REL_L2 = 5e-3
 MAX_ABS_FRAC = 2e-2
 
 
-def to_gpu_bank(bank, device="cuda") -> ops.NvFp4Experts:
-    """Upload canonical oracle-side experts and repack them on the GPU into the tile layout."""
+def to_gpu_bank(bank, device="cuda", w4a4: bool = False) -> ops.NvFp4Experts:
+    """Upload canonical oracle-side experts and repack them on the GPU into the tile layout
+    (``w4a4``: MXFP4 experts in the W4A4 tile layout)."""
     items = [bank[e] for e in range(len(bank))]
 
     def st(name, dtype):
@@ -31,8 +32,10 @@ def to_gpu_bank(bank, device="cuda") -> ops.NvFp4Experts:
 
     fmt = getattr(items[0], "fmt", "nvfp4")
     if fmt == "mxfp4":
+        lay = "mxfp4_a4" if w4a4 else "mxfp4"
         return ops.NvFp4Experts.from_canonical(st("w13", torch.uint8), st("w13_scale", torch.uint8), None,
-                                               st("w2", torch.uint8), st("w2_scale", torch.uint8), None, fmt="mxfp4")
+                                               st("w2", torch.uint8), st("w2_scale", torch.uint8), None, fmt=lay)
+    assert not w4a4, "the W4A4 layout holds MXFP4 weights"
     return ops.NvFp4Experts.from_canonical(
         st("w13", torch.uint8), st("w13_scale", torch.uint8),
         torch.tensor(np.stack([i.w13_gscale for i in items]), dtype=torch.float32, device=device),
@@ -66,14 +69,26 @@ def tile_np_mx(packed: np.ndarray, scales: np.ndarray):
     return np.ascontiguousarray(t), np.ascontiguousarray(ts)
 
 
+def tile_np_a4(packed: np.ndarray, scales: np.ndarray):
+    """Test-side statement of the W4A4 tile layout: tile (nb, c), lane l = 16q + n holds canonical
+    row 16nb + n bytes [64c + 16q, +16) (one 32-element block); scale byte l of the tile is that
+    row's canonical scale byte 4c + q."""
+    r, half = packed.shape
+    k = half * 2
+    t = packed.reshape(r // 16, 16, k // 128, 4, 16).transpose(0, 2, 3, 1, 4).reshape(r, half)
+    ts = scales.reshape(r // 16, 16, k // 128, 4).transpose(0, 2, 3, 1).reshape(r, k // 32)
+    return np.ascontiguousarray(t), np.ascontiguousarray(ts)
+
+
 def bits_to_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
 
 
-def to_gpu_layer(layer: omoe.Layer, device="cuda") -> ops.NvFp4MoELayer:
+def to_gpu_layer(layer: omoe.Layer, device="cuda", w4a4: bool = False) -> ops.NvFp4MoELayer:
     bias = None if layer.router_bias is None else torch.from_numpy(layer.router_bias).to(device)
-    return ops.NvFp4MoELayer(bits_to_bf16(layer.w_router, device), bias, to_gpu_bank(layer.routed, device),
-                             to_gpu_bank(layer.shared, device) if layer.shared is not None else None, layer.top_k)
+    return ops.NvFp4MoELayer(bits_to_bf16(layer.w_router, device), bias, to_gpu_bank(layer.routed, device, w4a4),
+                             to_gpu_bank(layer.shared, device, w4a4) if layer.shared is not None else None,
+                             layer.top_k)
 
 
 def f64(t: torch.Tensor) -> np.ndarray:
@@ -126,14 +141,15 @@ def ambiguous(logits_exact, k, margin=1e-3):
     return (s[:, k - 1] - s[:, k]) < margin
 
 
-def reference_for_selection(x_bits, layer, ids_gpu):
-    """Oracle forward where tokens with an ambiguous k-th choice take the GPU's selection."""
-    res = omoe.forward(x_bits, layer)
+def reference_for_selection(x_bits, layer, ids_gpu, forward=omoe.forward):
+    """Oracle forward (``forward``: oracle.moe's or oracle.w4a4's) where tokens with an ambiguous
+    k-th choice take the GPU's selection."""
+    res = forward(x_bits, layer)
     amb = ambiguous(res["logits"], layer.top_k)
     ids = ids_gpu.copy()
     mismatch = np.any(ids != res["ids"], axis=1)
     assert not np.any(mismatch & ~amb), f"unambiguous tokens routed differently: {np.where(mismatch & ~amb)[0][:10]}"
     if np.any(mismatch):
         route = np.where(mismatch[:, None], ids, res["ids"])
-        res = omoe.forward(x_bits, layer, route=route)
+        res = forward(x_bits, layer, route=route)
     return res

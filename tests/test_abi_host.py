@@ -127,3 +127,21 @@ def test_product_path_has_no_oracle_dependency():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
+
+
+def test_w4a4_validation_host_only():
+    """The W4A4 layer needs MXFP4 banks (no global scales) and its own, larger workspace."""
+    lay = _fake_layer()
+    lay.routed.format = lay.shared.format = L.MOE_WEIGHT_MXFP4
+    lay.routed.w13_gscale = lay.routed.w2_gscale = lay.shared.w13_gscale = lay.shared.w2_gscale = None
+    need = moe.forward_workspace_size(8, 4096, 1536, 1536, 320, 8, w4a4=True)
+    assert moe.validate_forward(lay, 8, need, w4a4=True) == L.MOE_OK
+    assert moe.validate_forward(lay, 8, need - 1, w4a4=True) == L.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert moe.validate_forward(lay, 8, need, arch="gfx942", w4a4=True) == L.MOE_ERR_UNSUPPORTED_DEVICE
+    assert moe.validate_forward(_fake_layer(), 8, 1 << 40, w4a4=True) == L.MOE_ERR_INVALID_ARGUMENT  # NVFP4
+    # the 4-bit copies of x and h, bf16 h and the y rows
+    t, h, i, e, k = 4096, 4096, 1536, 320, 8
+    s = t * k
+    big = moe.forward_workspace_size(t, h, i, i, e, k, w4a4=True)
+    floor = (s + t) * i * 2 + (s + t) * i // 2 + (s + t) * i // 32 + t * h // 2 + (s + t) * h * 2
+    assert floor <= big < floor + (64 << 20)
