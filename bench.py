@@ -36,8 +36,8 @@ BYTES_PER_WEIGHT = {"nvfp4": 0.5 + 1 / 16, "mxfp4": 0.5 + 1 / 32, "mxfp4_a4": 0.
 _CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "nvfp4_weight_quantized_amd", "csrc")
 _GEMM_SRCS = [os.path.join(_CSRC, f) for f in ("grouped_gemm.hip", "gemm_tiles.h")]
 _TRAFFIC = {  # workload: (code fingerprint of the GEMM sources, bytes read, bytes written) per gate/up launch
-    "decode": ("d09fe6e77f8541271bb85e69fd86663aca56fad955f8b68668459e84c228c6ad", 432.58e6, 0.22e6),
-    "prefill": ("d09fe6e77f8541271bb85e69fd86663aca56fad955f8b68668459e84c228c6ad", 2726.06e6, 113.70e6),
+    "decode": ("0f9416d502cfea9cffd9558bd6062bac59f45907e97823f8a2847711b5e24fba", 432.58e6, 0.22e6),
+    "prefill": ("0f9416d502cfea9cffd9558bd6062bac59f45907e97823f8a2847711b5e24fba", 2726.06e6, 113.70e6),
 }
 
 

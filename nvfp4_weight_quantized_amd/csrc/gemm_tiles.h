@@ -33,9 +33,10 @@ struct IntC {
 // Tile `mtile`: the extra group's tiles come first (the shared expert, every token: the longest
 // group, started early), then each group's in order.  Wave 0 only.  Lane i owns the contiguous
 // groups [i*gpl, (i+1)*gpl) (gpl = ceil(G/64) <= 16): one scan of the lanes' tile counts finds the
-// owning lane, which walks its groups.
+// owning lane, which walks its groups.  `span` (optional) receives the tile's index within its
+// group and the group's row count.
 template <int BM, class P>
-__device__ bool find_tile(const P& p, int mtile, TileInfo* out) {
+__device__ bool find_tile(const P& p, int mtile, TileInfo* out, int2* span = nullptr) {
   const int lane = threadIdx.x & 63;
   if (p.has_extra) {
     const int xt = (p.M_extra + BM - 1) / BM;
@@ -46,6 +47,7 @@ __device__ bool find_tile(const P& p, int mtile, TileInfo* out) {
         out->a_row0 = mtile * BM;
         out->rows = min(BM, p.M_extra - mtile * BM);
         out->extra = 1;
+        if (span) *span = int2{mtile, p.M_extra};
       }
       return true;
     }
@@ -83,6 +85,7 @@ __device__ bool find_tile(const P& p, int mtile, TileInfo* out) {
         out->a_row0 = start[i] + within * BM;
         out->rows = min(BM, cnt - within * BM);
         out->extra = 0;
+        if (span) *span = int2{within, cnt};
         break;
       }
       first += ti;

@@ -16,16 +16,24 @@
 //    op_sel picks (byte 0 here); lane l, register r of the result is row 4q + r of the first
 //    operand and row n of the second -- the layout of the bf16 16x16 MFMAs, so the W4A16 epilogue
 //    applies unchanged.  The scales are applied inside the instruction: no dequantization at all.
-//  * Weights are the first operand, read in the W4A4 tile layout (layout.hip): one contiguous 1 KB
-//    load per 16-row x 128-K tile and wave, plus one scale byte per lane.
-//  * Activations (codes [rows][K/2], scales [rows][K/32], quantized by quantize.hip) are the second
-//    operand.  Per 128-K chunk the 128-row tile's codes (8 KB, eight 1 KB fragments, one per wave)
-//    and scales (one dword per row: its four blocks of the chunk, 512 B, loaded by waves 0 and 1)
-//    go global -> LDS by direct loads (gathered through the sorted slot list for gate/up) into a
-//    ring of three chunk buffers (two chunks in flight); each wave reads every fragment back with
-//    one ds_read_b128 and its scale dword with one ds_read_b32, shifted to the lane's block.
-//  * 128-row tiles, 8 waves; the same tile list, XCD-aware tile order and per-row-count main-loop
-//    instantiations as the W4A16 tall-tile kernel (grouped_gemm.hip).
+//  * Every operand goes global -> LDS by direct loads (global_load_lds_*), into a ring of three
+//    chunk buffers with two 128-K chunks in flight; nothing is prefetched through registers, so
+//    the bytes in flight per CU (about 84 KB) are set by LDS, not by the register budget -- the
+//    weight stream needs them: at these shapes the kernel streams weights at HBM speed while its
+//    matrix work takes a quarter of the time.  Per chunk and wave: the 1 KB activation fragment
+//    of its 16 rows (codes [rows][K/2] from quantize.hip, gathered through the sorted slot list for
+//    gate/up), its NB 1 KB weight tiles (W4A4 tile layout, layout.hip) and their 64 scale bytes
+//    each (one 4-byte load per lane), and for waves 0 and 1 the activation scale dwords of 64 rows
+//    (the row's four blocks of the chunk).  Each wave then reads its weight tiles once and every
+//    activation fragment with one ds_read_b128 (scale: one ds_read_b32, shifted to the lane's
+//    block).
+//  * Tile order: within an expert the 128-row m-tiles of one output-column tile run next to each
+//    other (blocks of up to 8 m-tiles, n-tiles inside a block), so the expert's weight tile is
+//    fetched from HBM once and shared through L2 by the m-tiles running at the same time, while
+//    the block's activation rows stay in L2 across the n-tiles.  Blocks and groups are spread over
+//    the XCDs in contiguous ranges (workgroup b runs on XCD b mod 8).
+//  * 128-row tiles, 8 waves; the same tile list, per-row-count main-loop instantiations and
+//    epilogue as the W4A16 tall-tile kernel (grouped_gemm.hip).
 #include "common.h"
 #include "gemm_tiles.h"
 
@@ -37,6 +45,7 @@ typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 constexpr int kA4Rows = 128;   // token rows per tile
 constexpr int kA4Waves = 8;
 constexpr int kA4Bufs = 3;     // LDS chunk buffers: the current chunk and two in flight
+constexpr int kA4Block = 8;    // m-tiles per block of the tile order
 
 // acc[first-operand row 4q + r][second-operand row n] += (W * 2^ws) . (X * 2^xs) over 128 K.
 __device__ __forceinline__ f32x4 mfma_fp4(const uint4& w, uint32_t ws, const uint4& x, uint32_t xs, const f32x4& acc) {
@@ -46,10 +55,11 @@ __device__ __forceinline__ f32x4 mfma_fp4(const uint4& w, uint32_t ws, const uin
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 4, 4, 0, (int)ws, 0, (int)xs);
 }
 
-__device__ __forceinline__ uint4 load_weights16(const uint8_t* p) {
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return uint4{v[0], v[1], v[2], v[3]};
+// Wait until at most N of this wave's vector-memory loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
 template <int NB, bool GATE_UP>
@@ -59,17 +69,23 @@ __global__ __launch_bounds__(64 * kA4Waves, 1) void grouped_gemm_a4_kernel(GemmP
   constexpr int BM = kA4Rows;
   constexpr int COLS_PER_WAVE = GATE_UP ? 16 * (NB / 2) : 16 * NB;
   constexpr int BN = WAVES * COLS_PER_WAVE;
-  constexpr int BUF = MI * 1024;                 // one chunk: 8 fragments of 1 KB
-  constexpr int SBUF = BM * 4;                   // one chunk's activation scales: a dword per row
+  // one chunk buffer: activation codes (8 fragments of 1 KB), activation scales (a dword per
+  // row), the waves' weight tiles (NB KB each) and weight scales (256 B each)
+  constexpr int A_OFF = 0;
+  constexpr int S_OFF = A_OFF + MI * 1024;
+  constexpr int W_OFF = S_OFF + BM * 4;
+  constexpr int WS_OFF = W_OFF + WAVES * NB * 1024;
+  constexpr int BUF = WS_OFF + WAVES * 256;
   constexpr int NBUF = kA4Bufs;
-  static_assert(MI == WAVES && BM == 128, "one activation fragment per wave, scales by waves 0 and 1");
-  __shared__ __attribute__((aligned(1024))) uint8_t As[NBUF * BUF];
-  __shared__ __attribute__((aligned(512))) uint8_t Ss[NBUF * SBUF];
+  // direct loads per chunk: codes + NB weight tiles + weight scales (+ activation scales: waves 0, 1)
+  constexpr int LOADS = NB + 2;
+  static_assert(MI == WAVES && BM == 128 && NB <= 4, "one activation fragment per wave, scales by waves 0 and 1");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * BUF];
   __shared__ uint32_t s_arow[BM];
   __shared__ TileInfo tile;
+  __shared__ int2 tile_span;
   __shared__ int tile_ok;
   __shared__ int tile_n;
-  __shared__ int tile_m;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -78,29 +94,45 @@ __global__ __launch_bounds__(64 * kA4Waves, 1) void grouped_gemm_a4_kernel(GemmP
   const int nl = lane & 15;
   const int NT = p.N / BN;
 
+  // tile lookup: L -> the group owning standard m-tile L / NT, then (m, n) inside the group in
+  // the blocked order
   if (wave == 0) {
     const int total = count_tiles<BM>(p) * NT;
     const int per_xcd = (total + kXcds - 1) / kXcds;
     const int slot = blockIdx.x / kXcds;
     const int L = (blockIdx.x % kXcds) * per_xcd + slot;
     bool ok = slot < per_xcd && L < total;
-    if (ok) ok = find_tile<BM>(p, L / NT, &tile);
+    if (ok) ok = find_tile<BM>(p, L / NT, &tile, &tile_span);
     if (lane == 0) {
       tile_ok = ok ? 1 : 0;
-      tile_n = ok ? L % NT : 0;
-      tile_m = ok ? L / NT : 0;
+      tile_n = L;
     }
   }
   __syncthreads();
   if (!tile_ok) return;
   TileInfo ti;
   ti.group = __builtin_amdgcn_readfirstlane(tile.group);
-  ti.row0 = __builtin_amdgcn_readfirstlane(tile.row0);
-  ti.rows = __builtin_amdgcn_readfirstlane(tile.rows);
-  ti.a_row0 = __builtin_amdgcn_readfirstlane(tile.a_row0);
   ti.extra = __builtin_amdgcn_readfirstlane(tile.extra);
-  const int ntile = __builtin_amdgcn_readfirstlane(tile_n);
-  const int mtile = __builtin_amdgcn_readfirstlane(tile_m);
+  int ntile, mtile;
+  {
+    const int L = __builtin_amdgcn_readfirstlane(tile_n);
+    const int within = __builtin_amdgcn_readfirstlane(tile_span.x);
+    const int cnt = __builtin_amdgcn_readfirstlane(tile_span.y);
+    const int mt_g = (cnt + BM - 1) / BM;
+    const int base = L / NT - within;                   // the group's first standard m-tile
+    const int local = L - base * NT;                    // in [0, mt_g * NT)
+    const int blk = local / (kA4Block * NT);
+    const int gm = min(kA4Block, mt_g - blk * kA4Block);
+    const int r = local - blk * kA4Block * NT;
+    const int m = blk * kA4Block + r % gm;
+    ntile = r / gm;
+    mtile = base + m;
+    const int row0 = __builtin_amdgcn_readfirstlane(tile.row0) - within * BM;
+    const int a_row0 = __builtin_amdgcn_readfirstlane(tile.a_row0) - within * BM;
+    ti.row0 = row0 + m * BM;
+    ti.a_row0 = a_row0 + m * BM;
+    ti.rows = min(BM, cnt - m * BM);
+  }
   const GemmBank& bank = ti.extra ? p.extra : p.bank;
   const int K = p.K;
   const int nK = K / 128;
@@ -113,22 +145,25 @@ __global__ __launch_bounds__(64 * kA4Waves, 1) void grouped_gemm_a4_kernel(GemmP
     s_arow[tid] = (uint32_t)((!ti.extra && p.row_index) ? p.row_index[R] / p.row_divisor : R);
   }
   __syncthreads();
-  // this wave's direct loads: fragment `wave` (row 16*wave + n, code bytes [16q, +16) of the chunk)
-  // and, for waves 0 and 1, the scale dwords (blocks [4c, 4c + 4)) of rows 64*wave + lane
-  const uint32_t a_off = s_arow[16 * wave + nl] * (uint32_t)(K / 2) + (uint32_t)(16 * q);
   const bool loads_scales = wave < 2;
+  // per-lane global byte offsets of this wave's direct loads (chunk 0)
+  const uint32_t a_off = s_arow[16 * wave + nl] * (uint32_t)(K / 2) + (uint32_t)(16 * q);
   const uint32_t s_off = loads_scales ? s_arow[64 * wave + lane] * (uint32_t)(K / 32) : 0u;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)As;
-  const uint32_t lds_s0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)Ss;
-
   const int ktiles = K / 128;
   const size_t rows_per_expert = GATE_UP ? 2 * (size_t)p.N : (size_t)p.N;
-  const uint8_t* wexp = bank.w + (size_t)ti.group * rows_per_expert * (size_t)(K / 2) + 16 * lane;
-  const uint8_t* sexp = bank.ws + (size_t)ti.group * rows_per_expert * (size_t)(K / 32) + lane;
-  uint32_t tile0[NB];
+  const uint8_t* wexp = bank.w + (size_t)ti.group * rows_per_expert * (size_t)(K / 2);
+  const uint8_t* sexp = bank.ws + (size_t)ti.group * rows_per_expert * (size_t)(K / 32);
+  uint32_t w_off[NB];
 #pragma unroll
   for (int f = 0; f < NB; ++f)
-    tile0[f] = (uint32_t)(frag_row_block<NB, GATE_UP, BN, COLS_PER_WAVE>(f, ntile, wave, p.N) * ktiles);
+    w_off[f] = (uint32_t)(frag_row_block<NB, GATE_UP, BN, COLS_PER_WAVE>(f, ntile, wave, p.N) * ktiles) * 1024u +
+               (uint32_t)(16 * lane);
+  // weight scales: lane l loads the 4 bytes [4(l%16), +4) of fragment (l/16) % NB's 64-byte tile
+  const int sf = (lane >> 4) % NB;
+  const uint32_t ws_off =
+      (uint32_t)(frag_row_block<NB, GATE_UP, BN, COLS_PER_WAVE>(sf, ntile, wave, p.N) * ktiles) * 64u +
+      (uint32_t)(4 * nl);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
 
   f32x4 acc[MI][NB];
 #pragma unroll
@@ -136,76 +171,54 @@ __global__ __launch_bounds__(64 * kA4Waves, 1) void grouped_gemm_a4_kernel(GemmP
 #pragma unroll
     for (int f = 0; f < NB; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 bn[NB];
-  uint32_t sn[NB];
-  auto load_b = [&](int c) {
+  auto issue = [&](int c) {
+    const uint32_t buf = lds0 + (uint32_t)((c % NBUF) * BUF);
+    const uint32_t cc = (uint32_t)c;
+    direct_load16(acodes, a_off + 64u * cc, buf + A_OFF + wave * 1024);
 #pragma unroll
-    for (int f = 0; f < NB; ++f) {
-      const size_t t = (size_t)tile0[f] + (size_t)c;
-      bn[f] = load_weights16(wexp + t * 1024);
-      sn[f] = sexp[t * 64];
-    }
+    for (int f = 0; f < NB; ++f) direct_load16(wexp, w_off[f] + 1024u * cc, buf + W_OFF + (wave * NB + f) * 1024);
+    direct_load4(sexp, ws_off + 64u * cc, buf + WS_OFF + wave * 256);
+    if (loads_scales) direct_load4(ascale, s_off + 4u * cc, buf + S_OFF + wave * 256);
   };
-  auto issue_a = [&](int c, int buf) {
-    direct_load16(acodes, a_off + 64u * (uint32_t)c, lds0 + (uint32_t)(buf * BUF + wave * 1024));
-    if (loads_scales) direct_load4(ascale, s_off + 4u * (uint32_t)c, lds_s0 + (uint32_t)(buf * SBUF + wave * 256));
-  };
-  // Waits: every load of the chunk in flight has landed (vmcnt 0), or all but this wave's newest
-  // direct loads (the chunk two ahead: one load, two for the waves that also load scales).  The
-  // prefetch registers are operands, so the compiler's own wait for them lands here.
-  auto fence_regs = [&]() {
-#pragma unroll
-    for (int f = 0; f < NB; ++f)
-      asm volatile("" : "+v"(bn[f].x), "+v"(bn[f].y), "+v"(bn[f].z), "+v"(bn[f].w), "+v"(sn[f]) : : "memory");
-  };
-  auto wait_all = [&]() {
-    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
-    fence_regs();
-  };
-  auto wait_keep_ahead = [&]() {
+  // all but the newest chunk's loads have landed (the loads of one chunk are issued together)
+  auto wait_keep_newest = [&]() {
     if (loads_scales)
-      asm volatile("s_waitcnt vmcnt(2)" : : : "memory");
+      wait_vmcnt<LOADS + 1>();
     else
-      asm volatile("s_waitcnt vmcnt(1)" : : : "memory");
-    fence_regs();
+      wait_vmcnt<LOADS>();
   };
 
   auto run = [&](auto rb_const) {
     constexpr int RB = decltype(rb_const)::value;
-    issue_a(0, 0);
-    load_b(0);
+    issue(0);
     if (nK > 1) {
-      issue_a(1, 1);
-      wait_keep_ahead();
+      issue(1);
+      wait_keep_newest();
     } else {
-      wait_all();
+      wait_vmcnt<0>();
     }
     __syncthreads();
     for (int c = 0; c < nK; ++c) {
-      uint4 bq[NB];
-      uint32_t sc[NB];
+      if (c + 2 < nK) issue(c + 2);
+      const uint8_t* buf = lds + (c % NBUF) * BUF;
+      uint4 wq[NB];
+      uint32_t ws[NB];
 #pragma unroll
       for (int f = 0; f < NB; ++f) {
-        bq[f] = bn[f];
-        sc[f] = sn[f];
+        wq[f] = *reinterpret_cast<const uint4*>(buf + W_OFF + (wave * NB + f) * 1024 + 16 * lane);
+        ws[f] = buf[WS_OFF + wave * 256 + f * 64 + lane];
       }
-      if (c + 1 < nK) load_b(c + 1);
-      if (c + 2 < nK) issue_a(c + 2, (c + 2) % NBUF);
-      const uint8_t* abuf = As + (c % NBUF) * BUF + 16 * lane;
-      const uint8_t* sbuf = Ss + (c % NBUF) * SBUF + 4 * nl;
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
-        const uint4 x = *reinterpret_cast<const uint4*>(abuf + i * 1024);
-        const uint32_t xs = *reinterpret_cast<const uint32_t*>(sbuf + 64 * i) >> (8 * q);   // this lane's block
+        const uint4 x = *reinterpret_cast<const uint4*>(buf + A_OFF + i * 1024 + 16 * lane);
+        const uint32_t xs = *reinterpret_cast<const uint32_t*>(buf + S_OFF + 4 * (16 * i + nl)) >> (8 * q);
 #pragma unroll
-        for (int f = 0; f < NB; ++f) acc[i][f] = mfma_fp4(bq[f], sc[f], x, xs, acc[i][f]);
-        // one fragment read per row block in flight (bounds the live registers)
-        __builtin_amdgcn_sched_barrier(0);
+        for (int f = 0; f < NB; ++f) acc[i][f] = mfma_fp4(wq[f], ws[f], x, xs, acc[i][f]);
       }
       if (c + 2 < nK)
-        wait_keep_ahead();
+        wait_keep_newest();
       else
-        wait_all();
+        wait_vmcnt<0>();
       __syncthreads();
     }
   };
