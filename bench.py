@@ -161,7 +161,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode", choices=sorted(_DEFAULTS))
     ap.add_argument("--copies", type=int, default=None, help="weight copies cycled through")
-    ap.add_argument("--cpu-tokens", type=int, default=1, help="tokens in the CPU oracle sample (0: skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=5,
+                    help="tokens in the CPU oracle sample, about 3 s of CPU each (0: skip)")
     ap.add_argument("--format", default="nvfp4", choices=["nvfp4", "mxfp4", "mxfp4_a4"],
                     help="weight format of the synthetic experts (the headline metric is NVFP4); mxfp4_a4: "
                          "the W4A4 layer (MXFP4 weights and activations on the FP4 matrix cores)")
