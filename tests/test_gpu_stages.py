@@ -132,6 +132,9 @@ def _offsets(counts):
     (384, 256, [129, 0, 128, 127, 300, 5]),         # 128-row tiles; H % 256 != 0 -> narrow down tiles
     (256, 384, [200, 70, 0, 1]),
     (512, 256, [100, 0, 200, 77, 129]),            # eight-wave tall tiles for both GEMMs
+    (128, 256, [100, 0, 200, 77, 129]),            # eight-wave gate/up with a single K chunk
+    (512, 128, [100, 0, 200, 77, 129]),            # eight-wave down with a single K chunk
+    (1024, 384, [100, 0, 200, 77, 129]),           # eight-wave down with three K chunks (odd count)
 ])
 def test_grouped_gemm_random_matches_oracle(H, I, counts):
     rng = np.random.default_rng(H + I + sum(counts))
@@ -183,6 +186,35 @@ def test_grouped_gemm_one_hot_pins_layout():
     y = ops.grouped_gemm(L.MOE_GEMM_DOWN, gbank, torch.from_numpy(a2).to(torch.bfloat16).to(DEV),
                          torch.from_numpy(off2).to(DEV), len(is_))
     ref2 = omoe.grouped_down(a2.astype(np.float64), off2, bank)
+    assert np.all(np.abs(parity.f64(y) - ref2) <= 2.0 ** -8 * np.abs(ref2) + 1e-30)
+
+
+@pytest.mark.parametrize("H,I,counts", [
+    (512, 256, [40, 0, 130]),      # 128-row tiles, eight waves for both GEMMs
+    (384, 256, [40, 0, 130]),      # eight-wave gate/up, four-wave down (H % 512 != 0)
+    (256, 128, [40, 0, 130]),      # four waves for both GEMMs
+])
+def test_tall_grouped_gemm_one_hot_pins_layout(H, I, counts):
+    """Unit rows on the 128-row tile paths: each output is one dequantized weight (gate/up: then
+    SiLU(gate)*up), within one bf16 ulp -- pins nibble order, scale index and gate/up order there."""
+    rng = np.random.default_rng(H + I + 7)
+    bank = _random_bank(rng, len(counts), H, I)
+    gbank = parity.to_gpu_bank(bank)
+    off = _offsets(counts)
+    M = int(off[-1])
+    hs = rng.integers(0, H, M)
+    a = np.zeros((M, H), np.float32)
+    a[np.arange(M), hs] = 1.0
+    h = ops.grouped_gemm(L.MOE_GEMM_GATE_UP, gbank, torch.from_numpy(a).to(torch.bfloat16).to(DEV),
+                         torch.from_numpy(off).to(DEV), M)
+    ref = omoe.grouped_gate_up(a.astype(np.float64), off, bank)
+    assert np.all(np.abs(parity.f64(h) - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)
+    is_ = rng.integers(0, I, M)
+    a2 = np.zeros((M, I), np.float32)
+    a2[np.arange(M), is_] = 1.0
+    y = ops.grouped_gemm(L.MOE_GEMM_DOWN, gbank, torch.from_numpy(a2).to(torch.bfloat16).to(DEV),
+                         torch.from_numpy(off).to(DEV), M)
+    ref2 = omoe.grouped_down(a2.astype(np.float64), off, bank)
     assert np.all(np.abs(parity.f64(y) - ref2) <= 2.0 ** -8 * np.abs(ref2) + 1e-30)
 
 
