@@ -690,14 +690,18 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
 // registers by ordinary loads, the compiler's own wait before their first use also drains every
 // direct load issued after them -- loads complete in order and it cannot count the direct loads --
 // so the activation chunk two ahead had to land within one chunk.)
-//  * Per chunk c: read this wave's weights of chunk c from its slot, then issue the weights of
-//    chunk c + 1 into the slot just read (the wave's own region: the read has returned before the
-//    load is issued) and the activations of chunk c + 2 into the buffer freed by chunk c - 1 (all
-//    waves passed the barrier that ended it).
+//  * Per chunk c: issue the activations of chunk c + 2 into the buffer freed by chunk c - 1 (all
+//    waves passed the barrier that ended it).  During the last MFMA step of the chunk, wait for the
+//    weights of chunk c + 1, move them from the slot to registers, issue chunk c + 2's into the
+//    slot just read (the wave's own region: the read has returned before the load is issued) and
+//    dequantize chunk c + 1's first MFMA step, so that no dequantization runs without MFMAs beside
+//    it (the chunk-start dequantization, with both waves of a SIMD in the same phase after the
+//    barrier, cost 4-5% of the gate/up time).
 //  * Weight slot of one wave: NB tiles of 1 KB (lane l's 16 bytes at 16 l) then NB scale blocks of
 //    256 bytes (lane l's dword at 4 l) -- the registers a direct global load would have produced.
-//  * The activation fragments of the next MFMA step are read from LDS while the current step's
-//    MFMAs run (measured: down GEMM 2-3% faster, gate/up unchanged).
+//    The tile bases are wave-uniform (scalar registers); one lane offset serves every tile.
+//  * Activation fragments are read from LDS in the step that uses them (reading them a step ahead
+//    needs 32 more registers, which the pipelined weights now hold).
 template <int NB, bool GATE_UP, int FMT>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProblem p) {
   using F = WFmt<FMT>;
@@ -779,13 +783,14 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
   const size_t rows_per_expert = GATE_UP ? 2 * (size_t)p.N : (size_t)p.N;
   const uint8_t* wexp = bank.w + (size_t)ti.group * rows_per_expert * (size_t)(K / 2);
   const uint8_t* sexp = bank.ws + (size_t)ti.group * rows_per_expert * (size_t)(K / F::kScaleGroup);
-  uint32_t woff[NB], soff[NB];
+  // wave-uniform tile bases (scalar registers) plus one per-lane offset each for nibbles and scales
+  uint32_t t0[NB];
 #pragma unroll
-  for (int f = 0; f < NB; ++f) {
-    const uint32_t t0 = (uint32_t)(frag_row_block<NB, GATE_UP, BN, COLS_PER_WAVE>(f, ntile, wave, p.N) * ktiles);
-    woff[f] = t0 * 1024u + (uint32_t)w_lane_offset(lane);
-    soff[f] = t0 * (uint32_t)F::kTileScaleBytes + (uint32_t)F::s_lane(lane);
-  }
+  for (int f = 0; f < NB; ++f)
+    t0[f] = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(frag_row_block<NB, GATE_UP, BN, COLS_PER_WAVE>(f, ntile, wave, p.N) * ktiles));
+  const uint32_t wlane = (uint32_t)w_lane_offset(lane);
+  const uint32_t slane = (uint32_t)F::s_lane(lane);
   const uint32_t wslot0 = (uint32_t)(NA * A_BYTES + wave * W_WAVE);
 
   f32x4 acc[MI][NB];
@@ -804,8 +809,9 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
     const uint32_t dst = lds0 + wslot0;
 #pragma unroll
     for (int f = 0; f < NB; ++f) {
-      direct_load16(wexp, woff[f] + (uint32_t)c * 1024u, dst + f * 1024);
-      direct_load4(sexp, soff[f] + (uint32_t)c * (uint32_t)F::kTileScaleBytes, dst + NB * 1024 + f * 256);
+      const uint32_t t = t0[f] + (uint32_t)c;
+      direct_load16(wexp + (size_t)t * 1024u, wlane, dst + f * 1024);
+      direct_load4(sexp + (size_t)t * (size_t)F::kTileScaleBytes, slane, dst + NB * 1024 + f * 256);
     }
   };
   auto wait_vm = [](auto n_const) {
@@ -816,7 +822,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
 
   auto run = [&](auto rb_const) {
     constexpr int RB = decltype(rb_const)::value;
-    // prologue: the first chunk's operands, and the next activation chunk in flight
+    // prologue: chunk 0's weights and activations landed, chunk 1's activations in flight
     issue_w(0);
     issue_a(0, 0);
     if (nK > 1) {
@@ -826,10 +832,10 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
       wait_vm(IntC<0>{});
     }
     __syncthreads();
-    for (int c = 0; c < nK; ++c) {
-      const uint8_t* wl = lds + wslot0;
-      uint4 bq[NB];
-      uint32_t sc[NB];
+    const uint8_t* wl = lds + wslot0;
+    uint4 bq[NB];
+    uint32_t sc[NB];
+    auto read_w = [&]() {
 #pragma unroll
       for (int f = 0; f < NB; ++f) {
         bq[f] = *reinterpret_cast<const uint4*>(wl + f * 1024 + 16 * lane);
@@ -839,48 +845,59 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
 #pragma unroll
       for (int f = 0; f < NB; ++f)
         asm volatile("" : "+v"(bq[f].x), "+v"(bq[f].y), "+v"(bq[f].z), "+v"(bq[f].w), "+v"(sc[f]) : : "memory");
-      if (c + 1 < nK) issue_w(c + 1);
-      const bool more = c + 2 < nK;
-      if (more) issue_a(c + 2, (c + 2) % NA);
+    };
+    read_w();
+    if (nK > 1) issue_w(1);
+    bf16x8 wcur[NB];
+#pragma unroll
+    for (int f = 0; f < NB; ++f) wcur[f] = F::operand(bq[f], sc[f], 0);
+    // Invariant at the top of chunk c: bq/sc hold chunk c's weights and wcur its first MFMA step
+    // dequantized; activations of chunk c are in LDS; loads in flight, oldest first: activations
+    // of chunk c + 1, weights of chunk c + 1.  NEXT: chunk c + 1 exists; MORE: chunk c + 2 exists
+    // (compile-time, so the MFMA steps are one branch-free block).
+    auto chunk = [&](int c, auto next_const, auto more_const) {
+      constexpr bool NEXT = decltype(next_const)::value;
+      constexpr bool MORE = decltype(more_const)::value;
+      if (MORE) issue_a(c + 2, (c + 2) % NA);
       const uint8_t* abuf = lds + (c % NA) * A_BYTES + 16 * lane;
-      bf16x8 wcur[NB];
-#pragma unroll
-      for (int f = 0; f < NB; ++f) wcur[f] = F::operand(bq[f], sc[f], 0);
-      // activation fragments read one MFMA step ahead
-      bf16x8 xcur[RB];
-#pragma unroll
-      for (int i = 0; i < RB; ++i) xcur[i] = *reinterpret_cast<const bf16x8*>(abuf + (STEPS * i) * 1024);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < STEPS; ++j) {
         bf16x8 wnext[NB];
-        bf16x8 xnext[RB];
+        bf16x8 xcur[RB];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) xcur[i] = *reinterpret_cast<const bf16x8*>(abuf + (STEPS * i + j) * 1024);
         if (j + 1 < STEPS) {
 #pragma unroll
-          for (int i = 0; i < RB; ++i) xnext[i] = *reinterpret_cast<const bf16x8*>(abuf + (STEPS * i + j + 1) * 1024);
-#pragma unroll
           for (int f = 0; f < NB; ++f) wnext[f] = F::operand(bq[f], sc[f], j + 1);
+        } else if (NEXT) {
+          // the last step dequantizes the next chunk's first step: wait for its weights (only the
+          // activation loads issued at the top of this chunk stay in flight; the activations of
+          // chunk c + 1, issued before those weights, have landed too), move them to registers,
+          // refill the slot with chunk c + 2's
+          wait_vm(IntC<MORE ? A_ITERS : 0>{});
+          read_w();
+          if (MORE) issue_w(c + 2);
+#pragma unroll
+          for (int f = 0; f < NB; ++f) wnext[f] = F::operand(bq[f], sc[f], 0);
         }
 #pragma unroll
         for (int i = 0; i < RB; ++i)
 #pragma unroll
           for (int f = 0; f < NB; ++f) acc[i][f] = mfma(wcur[f], xcur[i], acc[i][f]);
         __builtin_amdgcn_sched_barrier(0);
-        if (j + 1 < STEPS) {
+        if (j + 1 < STEPS || NEXT) {
 #pragma unroll
           for (int f = 0; f < NB; ++f) wcur[f] = wnext[f];
-#pragma unroll
-          for (int i = 0; i < RB; ++i) xcur[i] = xnext[i];
         }
       }
-      // the next chunk's operands have landed; the loads issued last in this chunk stay in flight
-      if (more) {
-        wait_vm(IntC<A_ITERS>{});
-      } else {
-        wait_vm(IntC<0>{});
-      }
+      // every wave's activations of chunk c + 1 have landed (waited for above); chunk c's buffer
+      // is free once all waves pass
       __syncthreads();
-    }
+    };
+    for (int c = 0; c + 2 < nK; ++c) chunk(c, IntC<1>{}, IntC<1>{});
+    if (nK > 1) chunk(nK - 2, IntC<1>{}, IntC<0>{});
+    chunk(nK - 1, IntC<0>{}, IntC<0>{});
   };
   switch ((ti.rows + 15) / 16) {
     case 1: run(IntC<1>{}); break;

@@ -135,6 +135,7 @@ def _offsets(counts):
     (128, 256, [100, 0, 200, 77, 129]),            # eight-wave gate/up with a single K chunk
     (512, 128, [100, 0, 200, 77, 129]),            # eight-wave down with a single K chunk
     (1024, 384, [100, 0, 200, 77, 129]),           # eight-wave down with three K chunks (odd count)
+    (256, 1024, [100, 0, 200, 77, 129]),           # eight-wave gate/up with two K chunks, down with eight
 ])
 def test_grouped_gemm_random_matches_oracle(H, I, counts):
     rng = np.random.default_rng(H + I + sum(counts))
