@@ -36,8 +36,8 @@ BYTES_PER_WEIGHT = {"nvfp4": 0.5 + 1 / 16, "mxfp4": 0.5 + 1 / 32, "mxfp4_a4": 0.
 _CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "nvfp4_weight_quantized_amd", "csrc")
 _GEMM_SRCS = [os.path.join(_CSRC, f) for f in ("grouped_gemm.hip", "gemm_tiles.h")]
 _TRAFFIC = {  # workload: (code fingerprint of the GEMM sources, bytes read, bytes written) per gate/up launch
-    "decode": ("3b87500da7de33313f2b45b26457cd2a2f679767ebc3086357ea89cbff4da827", 432.55e6, 0.22e6),
-    "prefill": ("3b87500da7de33313f2b45b26457cd2a2f679767ebc3086357ea89cbff4da827", 2727.88e6, 113.70e6),
+    "decode": ("7fd9cae9f7ad5cc55afb6badeac7d2334ea1ed82365b72832121b3202a190d74", 432.58e6, 0.22e6),
+    "prefill": ("7fd9cae9f7ad5cc55afb6badeac7d2334ea1ed82365b72832121b3202a190d74", 2755.82e6, 115.81e6),
 }
 
 
