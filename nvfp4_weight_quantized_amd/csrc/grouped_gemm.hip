@@ -474,9 +474,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmProblem p) {
 //  * Tile order is XCD-aware: workgroup b runs on XCD b % 8; each XCD walks a contiguous range of
 //    (m-tile, n-tile) pairs, n fastest, so the A rows of an m-tile are reused from that XCD's L2.
 //  * Launched with WAVES = 4 (two workgroups per CU, two waves per SIMD, at most 256 registers per
-//    lane) for output widths that are not a multiple of 256 (gate/up) or 512 (down); wider outputs
-//    take the eight-wave kernel below (one workgroup per CU).  The WAVES = 8 form of this kernel
-//    (three A buffers) is kept compilable but not launched.
+//    lane) for every down GEMM and for gate/up outputs whose width is not a multiple of 256; wider
+//    gate/up outputs take the eight-wave kernel below (one workgroup per CU).  The WAVES = 8 form
+//    of this kernel (three A buffers) is kept compilable but not launched.
 constexpr int kTallBK = 128;
 constexpr int kTallRows = 128;
 
@@ -680,8 +680,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
   epilogue<MI, NB, GATE_UP, BN, COLS_PER_WAVE, WFmt<FMT>::kGlobalScale>(p, bank, ti, ntile, acc, mtile);
 }
 
-// Tall tiles with eight waves, every operand by direct loads (the kernel for 128-row tiles whenever
-// the output width is a multiple of 256 for gate/up or of 512 for down).  The activation chunks are
+// Tall tiles with eight waves, every operand by direct loads (the gate/up kernel for 128-row tiles
+// whenever the output width is a multiple of 256; it also compiles for down, which the four-wave
+// kernel above runs faster).  The activation chunks are
 // staged as in the kernel above (three buffers, two chunks in flight); the waves' weight tiles (1 KB
 // each) and their scale dwords (one per lane) also go global -> LDS by direct loads, into one slot
 // per wave, and are read back into registers at the start of the chunk that uses them.  No load of
@@ -1004,7 +1005,8 @@ moe_status_t launch_format(const GemmProblem& p, hipStream_t stream) {
   const bool wide = (p.N % 256) == 0;
   if (avg <= 16) return launch_small<false, FMT>(p, stream);
   if (avg <= 32) return wide ? launch_cfg<4, 4, 128, false, FMT>(p, stream) : launch_cfg<4, 2, 128, false, FMT>(p, stream);
-  if (p.N % 512 == 0) return launch_tall<4, false, 8, FMT>(p, stream);
+  // down: four waves, two workgroups per CU (measured 2-6% faster than the eight-wave kernel at
+  // every prefill shape, whose 512-column tiles halve the workgroup count of this short-K GEMM)
   return wide ? launch_tall<4, false, 4, FMT>(p, stream) : launch_tall<2, false, 4, FMT>(p, stream);
 }
 }  // namespace

@@ -54,6 +54,23 @@ def test_small_layer_end_to_end(case):
     assert torch.equal(out, out2), "two runs differ"
 
 
+def test_skewed_routing_on_128_row_tiles():
+    """A few experts take most rows and many take a handful: the XCD ranges of the 128-row GEMMs are
+    cut by cost, so most tiles land on few XCDs' ranges; every token is checked."""
+    T, H, I, E, k = 900, 256, 128, 24, 2
+    rng = np.random.default_rng(4242)
+    layer = helpers.random_layer(rng, H, I, E, k, shared=True, bias=True)
+    layer.router_bias = (-6.0 * np.log(rng.permutation(E) + 1.0)).astype(np.float32)
+    x = helpers.random_x(rng, T, H)
+    glayer = parity.to_gpu_layer(layer)
+    out, aux = ops.forward(glayer, parity.bits_to_bf16(x), return_aux=True)
+    ids = aux["topk_ids"].cpu().numpy()
+    counts = omoe.permute(ids, E)[0]
+    assert counts.max() > 256 and (counts < 32).sum() >= 8, counts
+    res = parity.reference_for_selection(x, layer, ids)
+    parity.assert_close(parity.f64(out), res["out"], "layer")
+
+
 def test_zero_tokens_is_a_no_op():
     rng = np.random.default_rng(1)
     glayer = parity.to_gpu_layer(helpers.random_layer(rng, 256, 128, 4, 2))

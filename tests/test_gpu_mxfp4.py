@@ -78,7 +78,7 @@ def _offsets(counts):
     (256, 128, [1, 0, 3, 2]),                       # 16-row tiles (few rows per expert)
     (512, 256, [0, 17, 16, 15, 1, 33, 0, 64]),       # 64-row tiles, ragged tails
     (384, 256, [129, 0, 128, 127, 300, 5]),          # 128-row tiles; H % 256 != 0 -> narrow down tiles
-    (512, 256, [100, 0, 200, 77, 129]),             # eight-wave 128-row tiles for both GEMMs
+    (512, 256, [100, 0, 200, 77, 129]),             # 128-row tiles: eight-wave gate/up, four-wave down
     (256, 384, [200, 70, 0, 1]),
 ])
 def test_mx_grouped_gemm_random_matches_oracle(H, I, counts):

@@ -131,11 +131,11 @@ def _offsets(counts):
     (512, 256, [0, 17, 16, 15, 1, 33, 0, 64]),      # 64-row tiles, ragged tails
     (384, 256, [129, 0, 128, 127, 300, 5]),         # 128-row tiles; H % 256 != 0 -> narrow down tiles
     (256, 384, [200, 70, 0, 1]),
-    (512, 256, [100, 0, 200, 77, 129]),            # eight-wave tall tiles for both GEMMs
+    (512, 256, [100, 0, 200, 77, 129]),            # eight-wave gate/up, four-wave down (128-row tiles)
     (128, 256, [100, 0, 200, 77, 129]),            # eight-wave gate/up with a single K chunk
-    (512, 128, [100, 0, 200, 77, 129]),            # eight-wave down with a single K chunk
-    (1024, 384, [100, 0, 200, 77, 129]),           # eight-wave down with three K chunks (odd count)
-    (256, 1024, [100, 0, 200, 77, 129]),           # eight-wave gate/up with two K chunks, down with eight
+    (512, 128, [100, 0, 200, 77, 129]),            # four-wave down, 512-column output, a single K chunk
+    (1024, 384, [100, 0, 200, 77, 129]),           # four-wave down with three K chunks (odd count)
+    (256, 1024, [100, 0, 200, 77, 129]),           # eight-wave gate/up with two K chunks, four-wave down with eight
 ])
 def test_grouped_gemm_random_matches_oracle(H, I, counts):
     rng = np.random.default_rng(H + I + sum(counts))
@@ -191,8 +191,8 @@ def test_grouped_gemm_one_hot_pins_layout():
 
 
 @pytest.mark.parametrize("H,I,counts", [
-    (512, 256, [40, 0, 130]),      # 128-row tiles, eight waves for both GEMMs
-    (384, 256, [40, 0, 130]),      # eight-wave gate/up, four-wave down (H % 512 != 0)
+    (512, 256, [40, 0, 130]),      # 128-row tiles: eight-wave gate/up, four-wave down (4 fragments)
+    (384, 256, [40, 0, 130]),      # eight-wave gate/up, four-wave down with 2 fragments per wave
     (256, 128, [40, 0, 130]),      # four waves for both GEMMs
 ])
 def test_tall_grouped_gemm_one_hot_pins_layout(H, I, counts):
