@@ -60,7 +60,7 @@ GemmBank bank_w13(const moe_nvfp4_experts_t& b) { return GemmBank{b.w13, b.w13_s
 GemmBank bank_w2(const moe_nvfp4_experts_t& b) { return GemmBank{b.w2, b.w2_scale, b.w2_gscale, 1, b.format}; }
 
 struct ForwardLayout {
-  size_t logits, ids, w, counts, offsets, sorted_slot, slot_to_row, block_hist, h, h_shared, y;
+  size_t logits, ids, w, counts, offsets, sorted_slot, slot_to_row, block_hist, x16, row_shift, h, h_shared, y;
   size_t total;
 };
 
@@ -81,6 +81,9 @@ ForwardLayout forward_layout(int32_t T, int32_t H, int32_t I, int32_t I_shared, 
   L.sorted_slot = take(S * 4);
   L.slot_to_row = take(S * 4);
   L.block_hist = take(S > (size_t)moe::kPermuteChunk ? (size_t)moe::permute_blocks((int64_t)S) * E * 4 : 0);
+  // x as fp16 rows with per-row power-of-two shifts (the NVFP4 128-row gate/up path)
+  L.x16 = take((size_t)T * H * 2);
+  L.row_shift = take((size_t)T * 4);
   // h rows (row-major, shared-expert rows right after the routed ones), or the same bytes reused
   // for h in the fragment-tiled layout of the 128-row GEMM path (one 128-row block per m-tile)
   const size_t h_rows_bytes = align_up(S * I * 2) + align_up((size_t)T * I_shared * 2);
@@ -364,6 +367,14 @@ moe_status_t moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x
   // layout, so the down GEMM's A tiles are contiguous 1 KB loads
   const bool tiled = (fuse_shared || !has_shared) && moe::grouped_gemm_uses_tall_tiles(gu);
   if (tiled) gu.out_tiled = h;
+  if (moe::grouped_gemm_takes_f16_rows(gu)) {
+    // fp16 operands halve the dequantization work of the NVFP4 weights (exact, see launch_act_to_f16)
+    uint16_t* x16 = at<uint16_t>(workspace, L.x16);
+    int32_t* row_shift = at<int32_t>(workspace, L.row_shift);
+    if ((st = moe::launch_act_to_f16(x, T, H, x16, row_shift, stream))) return st;
+    gu.a16 = x16;
+    gu.row_shift = row_shift;
+  }
   if ((st = moe::launch_grouped_gemm(gu, stream))) return st;
   if (has_shared && !fuse_shared) {
     GemmProblem gs{};

@@ -106,6 +106,11 @@ struct GemmProblem {
   // undefined.
   int32_t a_tiled;        // 1: `a` (and the extra group's rows) are read in that layout
   uint16_t* out_tiled;    // gate/up: write h in that layout (K = N columns) instead of `out`
+  // Gate/up on NVFP4 weights, eight-wave 128-row path only (ignored elsewhere): the activation
+  // rows as fp16, a16[r] = a[r] * 2^row_shift[r] exactly (launch_act_to_f16), for both `a` and
+  // `a_extra` (the same token matrix); the GEMM then runs on fp16 operands.
+  const uint16_t* a16;
+  const int32_t* row_shift;
 };
 
 // Bound on the number of 128-row m-tiles of a problem (every non-empty group adds at most one
@@ -119,6 +124,13 @@ inline long long tall_mtiles_bound(const GemmProblem& p) {
 bool grouped_gemm_uses_tall_tiles(const GemmProblem& p);
 
 moe_status_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream);
+// x16[t][h] = fp16(x[t][h] * 2^shift[t]) with shift[t] = 14 - floor(log2(max_h |x[t][h]|)) (0 for a
+// row of zeros or with a non-finite value): exact for every element within 2^31 of its row's
+// largest magnitude.  One workgroup per row.
+moe_status_t launch_act_to_f16(const uint16_t* x, int32_t T, int32_t H, uint16_t* x16, int32_t* shift,
+                               hipStream_t stream);
+// True if launch_grouped_gemm would read p.a16 / p.row_shift for this problem.
+bool grouped_gemm_takes_f16_rows(const GemmProblem& p);
 
 // W4A4 grouped GEMM: MXFP4 weights in the W4A4 tile layout (layout.hip) times MXFP4 activations,
 // on the scaled FP4 matrix cores.  Same grouping and output as GemmProblem; the activations are

@@ -124,9 +124,12 @@ __device__ __forceinline__ int frag_row_block(int f, int ntile, int wave, int N)
 // acc[i][f] holds, in lane l = 16q + n, output row 16i + n and the four columns 4q..4q+3 of
 // fragment f's 16 columns.
 // GSCALE: the bank carries fp32 global scales (NVFP4); otherwise the scale is 1.
+// rshift (optional, gate/up): per tile row, the power of two the activation row was scaled by
+// (2^rshift[row]); the sums are scaled back by 2^-rshift[row] (exact) before SiLU.
 template <int MI, int NB, bool GATE_UP, int BN, int COLS_PER_WAVE, bool GSCALE, class P>
 __device__ __forceinline__ void epilogue(const P& p, const GemmBank& bank, const TileInfo& ti, int ntile,
-                                         const f32x4 (&acc)[MI][NB], int mtile = 0) {
+                                         const f32x4 (&acc)[MI][NB], int mtile = 0,
+                                         const int* rshift = nullptr) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int q = lane >> 4, nl = lane & 15;
@@ -139,11 +142,19 @@ __device__ __forceinline__ void epilogue(const P& p, const GemmBank& bank, const
       const int row = 16 * i + nl;
       if (row >= ti.rows) continue;
       uint16_t* orow = p.out + (size_t)(ti.row0 + row) * p.N + col0;
+      const int sh = rshift ? -rshift[row] : 0;
 #pragma unroll
       for (int f = 0; f < NB / 2; ++f) {
         float h[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) h[r] = silu(acc[i][f][r] * dg) * (acc[i][f + NB / 2][r] * du);
+        for (int r = 0; r < 4; ++r) {
+          float g = acc[i][f][r] * dg, u = acc[i][f + NB / 2][r] * du;
+          if (rshift) {
+            g = ldexpf(g, sh);
+            u = ldexpf(u, sh);
+          }
+          h[r] = silu(g) * u;
+        }
         if (p.out_tiled) {
           // tiled layout: column col -> chunk col/128, step (col%128)/32, lane group (col%32)/8
           const int col = col0 + 16 * f;

@@ -26,6 +26,8 @@
 //    gate/up workgroups hold matching gate and up columns so h = silu(g)*u is formed in registers.
 //  * Groups (experts) are found on the device from the offsets array: no host synchronisation.
 //    Workgroups beyond the real tile count exit at once; empty experts cost nothing.
+#include <type_traits>
+
 #include "common.h"
 #include "gemm_tiles.h"
 
@@ -82,6 +84,30 @@ __device__ __forceinline__ bf16x8 w_operand(const uint4& w, uint32_t sc, int j) 
 // acc[weight row][token row] += W(16x32) . X(16x32)^T
 __device__ __forceinline__ f32x4 mfma(const bf16x8& w, const bf16x8& x, const f32x4& acc) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, x, acc, 0, 0, 0);
+}
+
+// fp16 operands (NVFP4 gate/up on fp16 activation rows; see grouped_gemm_tall_lds_kernel).
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mfma(const f16x8& w, const f16x8& x, const f32x4& acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(w, x, acc, 0, 0, 0);
+}
+// Weight operand of MFMA step j as fp16: the E2M1 values (v_cvt_scalef32_pk_f16_fp4, scale 1) times
+// the E4M3 block scale as an fp16 pair (v_cvt_scalef32_pk_f16_fp8 converts two scale bytes at
+// once), one packed fp16 multiply per two elements.  Exact: every E4M3 value is an fp16 value, and
+// element * scale has at most 6 significant bits, lies within 6 * 448 and is a multiple of 2^-12.
+__device__ __forceinline__ f16x8 w_operand16(const uint4& w, uint32_t sc, int j) {
+  const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+  const f16x2 sp = j >= 2 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, true)
+                          : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, false);
+  const _Float16 s1 = (j & 1) ? sp[1] : sp[0];
+  const f16x2 ss = {s1, s1};
+  const uint32_t q = words[j];
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 0) * ss;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 1) * ss;
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 2) * ss;
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 3) * ss;
+  return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
 // Byte offsets, within an expert's tiles, of the 16 nibble bytes and the scale dword of this lane.
@@ -703,9 +729,16 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
 //    The tile bases are wave-uniform (scalar registers); one lane offset serves every tile.
 //  * Activation fragments are read from LDS in the step that uses them (reading them a step ahead
 //    needs 32 more registers, which the pipelined weights now hold).
-template <int NB, bool GATE_UP, int FMT>
+template <int NB, bool GATE_UP, int FMT, bool A16>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProblem p) {
   using F = WFmt<FMT>;
+  static_assert(!A16 || (GATE_UP && FMT == kFmtNvfp4), "fp16 rows: NVFP4 gate/up only");
+  // operand type: bf16, or fp16 when the activation rows come as fp16 (p.a16)
+  using OpT = typename std::conditional<A16, f16x8, bf16x8>::type;
+  auto w_op = [](const uint4& w, uint32_t sc, int j) -> OpT {
+    if constexpr (A16) return w_operand16(w, sc, j);
+    else return F::operand(w, sc, j);
+  };
   constexpr int WAVES = 8;
   constexpr int MI = kTallRows / 16;
   constexpr int BM = kTallRows;
@@ -723,6 +756,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
   static_assert(NA * A_BYTES + W_BYTES <= 150 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NA * A_BYTES + W_BYTES];
   __shared__ uint32_t s_aoff[BM];
+  __shared__ int s_shift[A16 ? BM : 1];
   __shared__ TileInfo tile;
   __shared__ int tile_ok;
   __shared__ int tile_n;
@@ -760,12 +794,13 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
   const int K = p.K;
   const int nK = K / BK;
 
-  const uint8_t* abase = reinterpret_cast<const uint8_t*>(p.a_tiled ? p.a : (ti.extra ? p.a_extra : p.a));
+  const uint8_t* abase = reinterpret_cast<const uint8_t*>(A16 ? p.a16 : p.a_tiled ? p.a : (ti.extra ? p.a_extra : p.a));
   if (p.a_tiled) abase += (size_t)mtile * nK * A_BYTES;
   if (tid < BM && !p.a_tiled) {
     const int R = ti.a_row0 + min(tid, ti.rows - 1);
     const int src = (!ti.extra && p.row_index) ? p.row_index[R] / p.row_divisor : R;
     s_aoff[tid] = (uint32_t)src * (uint32_t)K * 2u;
+    if (A16) s_shift[tid] = p.row_shift[src];
   }
   __syncthreads();
   const int q = lane >> 4;
@@ -849,9 +884,9 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
     };
     read_w();
     if (nK > 1) issue_w(1);
-    bf16x8 wcur[NB];
+    OpT wcur[NB];
 #pragma unroll
-    for (int f = 0; f < NB; ++f) wcur[f] = F::operand(bq[f], sc[f], 0);
+    for (int f = 0; f < NB; ++f) wcur[f] = w_op(bq[f], sc[f], 0);
     // Invariant at the top of chunk c: bq/sc hold chunk c's weights and wcur its first MFMA step
     // dequantized; activations of chunk c are in LDS; loads in flight, oldest first: activations
     // of chunk c + 1, weights of chunk c + 1.  NEXT: chunk c + 1 exists; MORE: chunk c + 2 exists
@@ -864,13 +899,13 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < STEPS; ++j) {
-        bf16x8 wnext[NB];
-        bf16x8 xcur[RB];
+        OpT wnext[NB];
+        OpT xcur[RB];
 #pragma unroll
-        for (int i = 0; i < RB; ++i) xcur[i] = *reinterpret_cast<const bf16x8*>(abuf + (STEPS * i + j) * 1024);
+        for (int i = 0; i < RB; ++i) xcur[i] = *reinterpret_cast<const OpT*>(abuf + (STEPS * i + j) * 1024);
         if (j + 1 < STEPS) {
 #pragma unroll
-          for (int f = 0; f < NB; ++f) wnext[f] = F::operand(bq[f], sc[f], j + 1);
+          for (int f = 0; f < NB; ++f) wnext[f] = w_op(bq[f], sc[f], j + 1);
         } else if (NEXT) {
           // the last step dequantizes the next chunk's first step: wait for its weights (only the
           // activation loads issued at the top of this chunk stay in flight; the activations of
@@ -880,7 +915,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
           read_w();
           if (MORE) issue_w(c + 2);
 #pragma unroll
-          for (int f = 0; f < NB; ++f) wnext[f] = F::operand(bq[f], sc[f], 0);
+          for (int f = 0; f < NB; ++f) wnext[f] = w_op(bq[f], sc[f], 0);
         }
 #pragma unroll
         for (int i = 0; i < RB; ++i)
@@ -910,7 +945,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
     case 7: run(IntC<7>{}); break;
     default: run(IntC<8>{}); break;
   }
-  epilogue<MI, NB, GATE_UP, BN, COLS_PER_WAVE, WFmt<FMT>::kGlobalScale>(p, bank, ti, ntile, acc, mtile);
+  epilogue<MI, NB, GATE_UP, BN, COLS_PER_WAVE, WFmt<FMT>::kGlobalScale>(p, bank, ti, ntile, acc, mtile,
+                                                                        A16 ? s_shift : nullptr);
 }
 
 template <int NB, bool GATE_UP, int WAVES, int FMT>
@@ -925,7 +961,15 @@ moe_status_t launch_tall(const GemmProblem& p, hipStream_t stream) {
   grid = (grid + kXcds - 1) / kXcds * kXcds;
   if (grid > 0x7FFFFFFFLL) return MOE_ERR_INVALID_ARGUMENT;
   if constexpr (WAVES == 8) {
-    hipLaunchKernelGGL((grouped_gemm_tall_lds_kernel<NB, GATE_UP, FMT>), dim3((unsigned)grid), dim3(512), 0, stream, p);
+    if constexpr (GATE_UP && FMT == kFmtNvfp4) {
+      if (p.a16) {
+        hipLaunchKernelGGL((grouped_gemm_tall_lds_kernel<NB, GATE_UP, FMT, true>), dim3((unsigned)grid), dim3(512), 0,
+                           stream, p);
+        return launch_status();
+      }
+    }
+    hipLaunchKernelGGL((grouped_gemm_tall_lds_kernel<NB, GATE_UP, FMT, false>), dim3((unsigned)grid), dim3(512), 0,
+                       stream, p);
   } else {
     hipLaunchKernelGGL((grouped_gemm_tall_kernel<NB, GATE_UP, WAVES, FMT>), dim3((unsigned)grid), dim3(64 * WAVES), 0,
                        stream, p);
@@ -1012,6 +1056,63 @@ moe_status_t launch_format(const GemmProblem& p, hipStream_t stream) {
 }  // namespace
 
 bool grouped_gemm_uses_tall_tiles(const GemmProblem& p) { return avg_rows(p) > 32; }
+
+// The eight-wave NVFP4 gate/up path (launch_format) is the one that reads fp16 rows.
+bool grouped_gemm_takes_f16_rows(const GemmProblem& p) {
+  return p.stage == MOE_GEMM_GATE_UP && p.bank.format == kFmtNvfp4 && grouped_gemm_uses_tall_tiles(p) &&
+         p.N % 256 == 0;
+}
+
+namespace {
+// One workgroup per row: the row's largest magnitude (NaN ignored), then the row times 2^shift in
+// fp16 (round to nearest even), shift = 14 - floor(log2(max)) so that the largest magnitude lands
+// in [2^14, 2^15): every bf16 element within 2^31 of it keeps all 8 significant bits (normal fp16
+// down to 2^-14, subnormal steps of 2^-24).  A row of zeros or with an infinity keeps shift 0.
+__global__ __launch_bounds__(256) void act_to_f16_kernel(const uint16_t* __restrict__ x, int H,
+                                                         uint16_t* __restrict__ x16, int32_t* __restrict__ shift) {
+  __shared__ float wmax[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint16_t* row = x + (size_t)blockIdx.x * H;
+  float m = 0.f;
+  for (int h = tid * 8; h < H; h += 256 * 8) {
+    const uint4 v = *reinterpret_cast<const uint4*>(row + h);
+    const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m = fmaxf(m, fabsf(__uint_as_float(q[i] << 16)));
+      m = fmaxf(m, fabsf(__uint_as_float(q[i] & 0xFFFF0000u)));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (lane == 0) wmax[wave] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const int sh = (m > 0.f && m <= 3.4028235e38f) ? 14 - ilogbf(m) : 0;
+  if (tid == 0) shift[blockIdx.x] = sh;
+  uint16_t* orow = x16 + (size_t)blockIdx.x * H;
+  for (int h = tid * 8; h < H; h += 256 * 8) {
+    const uint4 v = *reinterpret_cast<const uint4*>(row + h);
+    const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const _Float16 lo = (_Float16)ldexpf(__uint_as_float(q[i] << 16), sh);
+      const _Float16 hi = (_Float16)ldexpf(__uint_as_float(q[i] & 0xFFFF0000u), sh);
+      o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    *reinterpret_cast<uint4*>(orow + h) = uint4{o[0], o[1], o[2], o[3]};
+  }
+}
+}  // namespace
+
+moe_status_t launch_act_to_f16(const uint16_t* x, int32_t T, int32_t H, uint16_t* x16, int32_t* shift,
+                               hipStream_t stream) {
+  if (T < 0 || H <= 0 || H % 8 != 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (T == 0) return MOE_OK;
+  hipLaunchKernelGGL(act_to_f16_kernel, dim3((unsigned)T), dim3(256), 0, stream, x, (int)H, x16, shift);
+  return launch_status();
+}
 
 moe_status_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
   // the tiled activation layouts exist only on the 128-row path

@@ -71,6 +71,29 @@ def test_skewed_routing_on_128_row_tiles():
     parity.assert_close(parity.f64(out), res["out"], "layer")
 
 
+def test_rows_of_widely_different_magnitude_on_128_row_tiles():
+    """The 128-row NVFP4 gate/up path reads the tokens as fp16 rows scaled by a power of two each:
+    rows from 2^-40 to 2^20, a row whose elements span 2^-30..1, and a row of zeros all match the
+    oracle row by row."""
+    T, H, I, E, k = 300, 256, 256, 8, 2
+    rng = np.random.default_rng(777)
+    layer = helpers.random_layer(rng, H, I, E, k, shared=True)
+    xf = rng.normal(0, 1, (T, H))
+    xf *= 2.0 ** rng.integers(-40, 21, T)[:, None]
+    xf[1] *= 2.0 ** rng.integers(-30, 1, H)
+    xf[2] = 0.0
+    x = helpers.bf16_bits(torch.from_numpy(xf.astype(np.float32)).to(torch.bfloat16))
+    glayer = parity.to_gpu_layer(layer)
+    out, aux = ops.forward(glayer, parity.bits_to_bf16(x), return_aux=True)
+    ids = aux["topk_ids"].cpu().numpy()
+    res = parity.reference_for_selection(x, layer, ids)
+    got = parity.f64(out)
+    assert np.all(got[2] == 0.0)
+    for t in range(T):
+        if t != 2:
+            parity.assert_close(got[t:t + 1], res["out"][t:t + 1], f"token {t}")
+
+
 def test_zero_tokens_is_a_no_op():
     rng = np.random.default_rng(1)
     glayer = parity.to_gpu_layer(helpers.random_layer(rng, 256, 128, 4, 2))
