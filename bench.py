@@ -36,8 +36,8 @@ BYTES_PER_WEIGHT = {"nvfp4": 0.5 + 1 / 16, "mxfp4": 0.5 + 1 / 32, "mxfp4_a4": 0.
 _CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "nvfp4_weight_quantized_amd", "csrc")
 _GEMM_SRCS = [os.path.join(_CSRC, f) for f in ("grouped_gemm.hip", "gemm_tiles.h")]
 _TRAFFIC = {  # workload: (code fingerprint of the GEMM sources, bytes read, bytes written) per gate/up launch
-    "decode": ("bd630153f235c241a85ffd7e08803462ec20142040e22b8f02bf815c411519d9", 432.58e6, 0.22e6),
-    "prefill": ("bd630153f235c241a85ffd7e08803462ec20142040e22b8f02bf815c411519d9", 2783.61e6, 115.81e6),
+    "decode": ("bd630153f235c241a85ffd7e08803462ec20142040e22b8f02bf815c411519d9", 432.57e6, 0.22e6),
+    "prefill": ("bd630153f235c241a85ffd7e08803462ec20142040e22b8f02bf815c411519d9", 2782.99e6, 115.81e6),
 }
 
 

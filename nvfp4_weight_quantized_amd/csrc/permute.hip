@@ -66,6 +66,10 @@ __global__ __launch_bounds__(kPermuteThreads) void permute_hist_kernel(const int
 }
 
 // Step 2 (one workgroup): counts, offsets, and block_hist[b][e] -> first row of block b in group e.
+// Each thread owns experts e; the per-block counts of e are read kScanBatch at a time, all loads of
+// a batch in flight together (in one loop of dependent read-then-write the loads would wait for
+// the stores before them, which may alias).
+constexpr int kScanBatch = 16;
 __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict__ block_hist, int nb, int E,
                                                             int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ offsets) {
@@ -73,10 +77,12 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict_
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += 1024) {
     int run = 0;
-    for (int b = 0; b < nb; ++b) {
-      const int c = block_hist[(size_t)b * E + e];
-      block_hist[(size_t)b * E + e] = run;
-      run += c;
+    for (int b0 = 0; b0 < nb; b0 += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) v[i] = (b0 + i < nb) ? block_hist[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) run += v[i];
     }
     counts[e] = run;
     offs[e] = run;
@@ -89,7 +95,17 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* __restrict_
   __syncthreads();
   for (int e = tid; e < E; e += 1024) {
     offsets[e] = offs[e];
-    for (int b = 0; b < nb; ++b) block_hist[(size_t)b * E + e] += offs[e];
+    int run = offs[e];
+    for (int b0 = 0; b0 < nb; b0 += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) v[i] = (b0 + i < nb) ? block_hist[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) {
+        if (b0 + i < nb) block_hist[(size_t)(b0 + i) * E + e] = run;
+        run += v[i];
+      }
+    }
   }
 }
 
