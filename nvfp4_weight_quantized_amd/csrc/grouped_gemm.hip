@@ -16,7 +16,9 @@
 //  * Those bytes are dequantized in registers straight into the bf16 MFMA operand:
 //    v_cvt_scalef32_pk_f32_fp4 (scale 1) gives the E2M1 values, one fp32 multiply applies the
 //    block scale and v_cvt_pk_bf16_f32 packs the result.  element * block scale has at most 6
-//    significant bits, so the bf16 operand is exact.
+//    significant bits, so the bf16 operand is exact.  The eight-wave gate/up kernel can take the
+//    token rows as fp16 instead (each row scaled by a power of two, an exact re-encoding) and
+//    then builds fp16 weight operands with one packed fp16 multiply per two elements.
 //  * The weights are the MFMA's first operand and the activations its second, so the 16x16
 //    accumulator block is (weight row, token row): lane l = 16q + n holds token row n and four
 //    consecutive output columns 4q..4q+3, stored as one 8-byte write.
