@@ -33,6 +33,7 @@ SMALL = [
     (400, 256, 128, 4, 2, True, False, None),    # 128-row tiles with 2 and 1 K chunks
     (700, 384, 256, 40, 8, False, True, None),   # 128-row tiles, multi-block permute, no shared
     (20, 256, 128, 64, 2, True, False, None),    # 8-row tiles; the shared expert spans 8 + 8 + 4 rows
+    (300, 256, 256, 4, 2, True, False, 512),     # fp16-row gate/up for the routed experts, shared expert of another width on bf16
 ]
 
 
