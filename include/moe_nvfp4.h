@@ -92,18 +92,22 @@ const char* moe_status_string(moe_status_t s);
  *                     (same guide, section 6.4 "NVFP4 vs MXFP4"). */
 #define MOE_WEIGHT_NVFP4 0
 #define MOE_WEIGHT_MXFP4 1
+/* MXFP4 weights in the W4A4 tile layout of moe_mxfp4_pack_tiles_a4: accepted only by the W4A4 entry
+ * points (moe_mxfp4_w4a4_*), which in turn accept no other format, so a bank packed for one kernel
+ * family can never be read by the other. */
+#define MOE_WEIGHT_MXFP4_A4 2
 
 /* One bank of experts (routed: num_experts = E; shared: num_experts = 1), device pointers.
  * The packed weights and block scales are in the MFMA TILE LAYOUT produced by
- * moe_nvfp4_pack_tiles (NVFP4) or moe_mxfp4_pack_tiles (MXFP4) from the canonical layout: per
- * expert, the canonical [2I][H/2] (w13) or [H][I/2] (w2) bytes and their scale bytes, permuted
- * tile by tile (same sizes).  A zero-initialised `format` is NVFP4; the routed and shared banks of
- * a layer must share one format. */
+ * moe_nvfp4_pack_tiles (NVFP4), moe_mxfp4_pack_tiles (MXFP4) or moe_mxfp4_pack_tiles_a4 (MXFP4_A4)
+ * from the canonical layout: per expert, the canonical [2I][H/2] (w13) or [H][I/2] (w2) bytes and
+ * their scale bytes, permuted tile by tile (same sizes).  A zero-initialised `format` is NVFP4; the
+ * routed and shared banks of a layer must share one format. */
 typedef struct {
   int32_t num_experts;
   int32_t hidden;            /* H */
   int32_t inter;             /* I */
-  int32_t format;            /* MOE_WEIGHT_NVFP4 or MOE_WEIGHT_MXFP4 */
+  int32_t format;            /* MOE_WEIGHT_NVFP4, MOE_WEIGHT_MXFP4 or MOE_WEIGHT_MXFP4_A4 */
   const uint8_t* w13;        /* [E] x tiled [2I][H/2]  packed E2M1, gate rows then up rows */
   const uint8_t* w13_scale;  /* [E] x tiled [2I][H/16] E4M3FN (NVFP4) or [2I][H/32] E8M0 (MXFP4) */
   const float* w13_gscale;   /* [E][2] dequant global scales (gate, up); NVFP4 only, may be NULL for MXFP4 */
@@ -140,8 +144,13 @@ moe_status_t moe_route(const uint16_t* x, const uint16_t* w_router, const float*
  * topk_ids [T][k] int32 in [0, E).  Writes expert_counts [E], expert_offsets [E+1] (exclusive
  * prefix sum; offsets[E] = T*k), sorted_slot [T*k] (slot ids t*k+j grouped by expert, ascending
  * inside a group) and slot_to_row [T*k] (inverse permutation).  Bit-exact and atomic-order free.
- * Needs moe_permute_workspace_size(T, k, E) bytes of workspace.  ids outside [0, E) are not
- * checked (the route stage never produces them).
+ * Needs moe_permute_workspace_size(T, k, E) bytes of workspace.
+ * Out-of-range ids (checked on the device; the route stage never produces them): a slot whose id is
+ * outside [0, E) joins no group and nothing is written outside the output buffers.  Its slot_to_row
+ * entry is -1, the counts and offsets leave it out, so expert_offsets[E] < T*k -- the caller's
+ * signal that the ids were bad; sorted_slot entries at and past expert_offsets[E] are unspecified.
+ * moe_combine turns every token holding such a slot into a NaN row.  The GEMM entry points, given
+ * these offsets and M_total = T*k, leave output rows past expert_offsets[E] unwritten.
  * Source: "Permute-Experts-Unpermute" ("vLLM on the NVIDIA DGX Spark", section 7.1). */
 size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E);
 moe_status_t moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
@@ -171,6 +180,8 @@ moe_status_t moe_nvfp4_grouped_gemm(int32_t stage, const moe_nvfp4_experts_t* w 
 /* ---------------------------------------------------------------- S6: combine
  * out[t][:] = bf16( sum_j topk_w[t][j] * y_rows[slot_to_row[t*k+j]][:] + y_shared[t][:] ),
  * accumulated in fp32 in the order j = 0..k-1, then the shared row.  y_shared may be NULL.
+ * A negative slot_to_row entry (a slot moe_permute placed nowhere) is not read: the token's output
+ * row is written as NaN.  Non-negative rows must lie inside y_rows (not checked).
  * Source: top-k-weight reduction of the fused MoE ("vLLM on the NVIDIA DGX Spark", section 4);
  * the shared expert is added with weight 1 ("Serving Solar Open 2 on DGX Spark": one shared
  * expert that every token uses). */
@@ -184,7 +195,11 @@ moe_status_t moe_combine(const uint16_t* y_rows, const int32_t* slot_to_row, con
  * stage_events (host array of MOE_NUM_STAGE_EVENTS hipEvent_t handles, or NULL): when given,
  * event i is recorded on the stream at stage boundary i -- 0 before S1, 1 after S1, 2 after S2+S3,
  * 3 after S4, 4 after S5, 5 after S6 -- so callers can time each stage; NULL entries are skipped.
- * The events are created and owned by the caller. */
+ * The events are created and owned by the caller.
+ * y_rows (device, bf16 [T*k + T_shared][H], T_shared = T with a shared expert, else 0): when given,
+ * the expert outputs of S5 are written there instead of the workspace -- row r < T*k is the routed
+ * expert output of sorted row r (slot sorted_slot[r] of the permutation), row T*k + t the shared
+ * expert's output for token t -- the inputs of the combine, for callers that check the stages. */
 #define MOE_NUM_STAGE_EVENTS 6
 typedef struct {
   float* logits;
@@ -192,6 +207,7 @@ typedef struct {
   float* topk_w;
   int32_t* expert_counts;
   void* const* stage_events;
+  uint16_t* y_rows;
 } moe_forward_aux_t;
 
 /* Workspace bytes moe_nvfp4_forward needs for T tokens (I_shared = 0: no shared expert).  It holds
@@ -293,7 +309,7 @@ moe_status_t moe_mxfp4_quantize_act(const uint16_t* a, int32_t rows, int32_t col
  * scale bytes; with l = 16q + n, nibble bytes [16l, 16l + 16) are the canonical bytes
  * [64c + 16q, +16) of row 16nb + n (its elements [128c + 32q, +32), one scale block) and scale
  * byte l is that row's canonical scale byte 4c + q.  rows % 16 == 0, cols % 128 == 0; out of
- * place, same sizes.  A bank for the W4A4 entry points has format MOE_WEIGHT_MXFP4 and its
+ * place, same sizes.  A bank for the W4A4 entry points has format MOE_WEIGHT_MXFP4_A4 and its
  * weights in this layout (not the one of moe_mxfp4_pack_tiles). */
 moe_status_t moe_mxfp4_pack_tiles_a4(const uint8_t* packed, const uint8_t* scales, int32_t num_tensors, int32_t rows,
                                      int32_t cols, uint8_t* tiled, uint8_t* tiled_scales, void* stream);
@@ -302,7 +318,7 @@ moe_status_t moe_mxfp4_pack_tiles_a4(const uint8_t* packed, const uint8_t* scale
  * a[row_index[r] / row_divisor] (or a[r]) -- codes `a` [rows][K/2], scales `a_scale` [rows][K/32]
  * from moe_mxfp4_quantize_act -- and every product of a weight and an activation is exact before
  * the fp32 accumulation.  Gate/up writes h = bf16(silu(A.Qg^T) * (A.Qu^T)) [M_total][I]; down
- * writes y = bf16(A.Qd^T) [M_total][H].  w->format must be MOE_WEIGHT_MXFP4 (W4A4 tile layout);
+ * writes y = bf16(A.Qd^T) [M_total][H].  w->format must be MOE_WEIGHT_MXFP4_A4 (W4A4 tile layout);
  * a, a_scale and out 16-byte aligned; M_total * K / 2 < 4 GiB. */
 moe_status_t moe_mxfp4_w4a4_grouped_gemm(int32_t stage, const moe_nvfp4_experts_t* w, const uint8_t* a,
                                          const uint8_t* a_scale, const int32_t* row_index, int32_t row_divisor,
@@ -324,6 +340,17 @@ moe_status_t moe_mxfp4_w4a4_validate_forward(const moe_nvfp4_layer_t* layer, int
 moe_status_t moe_mxfp4_w4a4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int32_t T,
                                     uint16_t* out, void* workspace, size_t workspace_bytes,
                                     const moe_forward_aux_t* aux, void* stream);
+
+/* ---------------------------------------------------------------- measurement helper
+ * Not a step of the layer: reads `bytes` bytes of device memory at `buf` once with a plain
+ * streaming-read kernel (16-byte non-temporal loads, at most `workgroups` workgroups of 256 threads
+ * in a grid-stride loop) and writes nothing but, in a case that never arises for real data, one
+ * word to `sink` (device, 4 bytes).  Timed by the caller, it gives the HBM read bandwidth this GPU
+ * reaches, the practical ceiling of the weight-stream-bound decode GEMMs (decode re-reads the active
+ * weights for every token and is memory-bandwidth bound: "vLLM on the DGX Spark, the Hard Way: Seven
+ * Months of GB10 Field Notes", "The five-minute model of what vLLM is doing on this box", item 1).
+ * bytes % 16 == 0, buf 16-byte aligned, 1 <= workgroups <= 2^20. */
+moe_status_t moe_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t workgroups, void* stream);
 
 #ifdef __cplusplus
 }

@@ -49,7 +49,7 @@ class Layer(ctypes.Structure):
 class ForwardAux(ctypes.Structure):
     """moe_forward_aux_t"""
     _fields_ = [("logits", c_void_p), ("topk_ids", c_void_p), ("topk_w", c_void_p), ("expert_counts", c_void_p),
-                ("stage_events", ctypes.POINTER(c_void_p))]
+                ("stage_events", ctypes.POINTER(c_void_p)), ("y_rows", c_void_p)]
 
 
 NUM_STAGE_EVENTS = 6
@@ -83,13 +83,15 @@ SIGNATURES = {
     "moe_mxfp4_w4a4_validate_forward": (i32, [ctypes.POINTER(Layer), i32, size_t, ctypes.c_char_p]),
     "moe_mxfp4_w4a4_forward": (i32, [ctypes.POINTER(Layer), c_void_p, i32, c_void_p, c_void_p, size_t,
                                      ctypes.POINTER(ForwardAux), c_void_p]),
+    "moe_hbm_read_probe": (i32, [c_void_p, size_t, c_void_p, i32, c_void_p]),
 }
 
 # weight formats of an expert bank (moe_nvfp4_experts_t.format)
 MOE_WEIGHT_NVFP4 = 0
 MOE_WEIGHT_MXFP4 = 1
+MOE_WEIGHT_MXFP4_A4 = 2
 # bank layouts of the Python side: "mxfp4_a4" is MXFP4 in the W4A4 tile layout (the W4A4 layer)
-FORMATS = {"nvfp4": MOE_WEIGHT_NVFP4, "mxfp4": MOE_WEIGHT_MXFP4, "mxfp4_a4": MOE_WEIGHT_MXFP4}
+FORMATS = {"nvfp4": MOE_WEIGHT_NVFP4, "mxfp4": MOE_WEIGHT_MXFP4, "mxfp4_a4": MOE_WEIGHT_MXFP4_A4}
 SCALE_GROUP = {"nvfp4": 16, "mxfp4": 32, "mxfp4_a4": 32}
 PACK_FN = {"nvfp4": "moe_nvfp4_pack_tiles", "mxfp4": "moe_mxfp4_pack_tiles", "mxfp4_a4": "moe_mxfp4_pack_tiles_a4"}
 

@@ -40,11 +40,14 @@ bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 bool valid_bank(const moe_nvfp4_experts_t& b, int32_t H, int32_t expected_experts) {
   if (b.num_experts != expected_experts || b.hidden != H) return false;
   if (b.inter <= 0 || b.inter % 128 != 0) return false;
-  if (b.format != MOE_WEIGHT_NVFP4 && b.format != MOE_WEIGHT_MXFP4) return false;
+  if (b.format != MOE_WEIGHT_NVFP4 && b.format != MOE_WEIGHT_MXFP4 && b.format != MOE_WEIGHT_MXFP4_A4) return false;
   if (!(b.w13 && b.w13_scale && b.w2 && b.w2_scale)) return false;
   if (b.format == MOE_WEIGHT_NVFP4 && !(b.w13_gscale && b.w2_gscale)) return false;
   return al16(b.w13) && al16(b.w13_scale) && al16(b.w2) && al16(b.w2_scale);
 }
+
+// Banks the W4A16 kernels read (the W4A4 tile layout is for the W4A4 entry points only).
+bool w4a16_format(int32_t f) { return f == MOE_WEIGHT_NVFP4 || f == MOE_WEIGHT_MXFP4; }
 
 // The LDS-staging kernels address activation rows with 32-bit byte offsets.
 constexpr int64_t kMaxActivationBytes = (int64_t)1 << 32;
@@ -194,7 +197,8 @@ moe_status_t moe_nvfp4_grouped_gemm(int32_t stage, const moe_nvfp4_experts_t* w,
                                     int32_t M_total, uint16_t* out, void* stream) {
   if (!w || (stage != MOE_GEMM_GATE_UP && stage != MOE_GEMM_DOWN)) return MOE_ERR_INVALID_ARGUMENT;
   if (w->num_experts < 1 || w->num_experts > 1024) return MOE_ERR_INVALID_ARGUMENT;
-  if (!valid_bank(*w, w->hidden, w->num_experts) || w->hidden <= 0 || w->hidden % 128 != 0)
+  if (!valid_bank(*w, w->hidden, w->num_experts) || !w4a16_format(w->format) || w->hidden <= 0 ||
+      w->hidden % 128 != 0)
     return MOE_ERR_INVALID_ARGUMENT;
   if (M_total < 0 || row_divisor < 1) return MOE_ERR_INVALID_ARGUMENT;
   const int64_t K_ = stage == MOE_GEMM_GATE_UP ? w->hidden : w->inter;
@@ -262,6 +266,7 @@ extern "C" {
 moe_status_t moe_validate_forward(const moe_nvfp4_layer_t* layer, int32_t T, size_t workspace_bytes,
                                   const char* gfx_arch) {
   if (moe_status_t st = validate_layer(layer, T)) return st;
+  if (!w4a16_format(layer->routed.format)) return MOE_ERR_INVALID_ARGUMENT;
   const bool has_shared = layer->shared.num_experts != 0;
   const int32_t I = layer->routed.inter, Is = has_shared ? layer->shared.inter : 0;
   if (T > 0 && workspace_bytes < moe_nvfp4_forward_workspace_size(T, layer->hidden, I, Is, layer->num_experts,
@@ -273,7 +278,7 @@ moe_status_t moe_validate_forward(const moe_nvfp4_layer_t* layer, int32_t T, siz
 moe_status_t moe_mxfp4_w4a4_validate_forward(const moe_nvfp4_layer_t* layer, int32_t T, size_t workspace_bytes,
                                              const char* gfx_arch) {
   if (moe_status_t st = validate_layer(layer, T)) return st;
-  if (layer->routed.format != MOE_WEIGHT_MXFP4) return MOE_ERR_INVALID_ARGUMENT;
+  if (layer->routed.format != MOE_WEIGHT_MXFP4_A4) return MOE_ERR_INVALID_ARGUMENT;
   const bool has_shared = layer->shared.num_experts != 0;
   const int32_t I = layer->routed.inter, Is = has_shared ? layer->shared.inter : 0;
   if (T > 0 && workspace_bytes < moe_mxfp4_w4a4_forward_workspace_size(T, layer->hidden, I, Is, layer->num_experts,
@@ -328,7 +333,8 @@ moe_status_t moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x
   int32_t* block_hist = at<int32_t>(workspace, L.block_hist);
   uint16_t* h = at<uint16_t>(workspace, L.h);
   uint16_t* h_shared = at<uint16_t>(workspace, L.h_shared);
-  uint16_t* y = at<uint16_t>(workspace, L.y);
+  uint16_t* y = (aux && aux->y_rows) ? aux->y_rows : at<uint16_t>(workspace, L.y);
+  if (!al16(y)) return MOE_ERR_INVALID_ARGUMENT;
 
   void* const* events = aux ? aux->stage_events : nullptr;
   const std::function<moe_status_t(int)> mark = [&](int i) -> moe_status_t {
@@ -512,7 +518,7 @@ moe_status_t moe_mxfp4_w4a4_grouped_gemm(int32_t stage, const moe_nvfp4_experts_
                                          const int32_t* expert_offsets, int32_t M_total, uint16_t* out, void* stream) {
   if (!w || (stage != MOE_GEMM_GATE_UP && stage != MOE_GEMM_DOWN)) return MOE_ERR_INVALID_ARGUMENT;
   if (w->num_experts < 1 || w->num_experts > 1024) return MOE_ERR_INVALID_ARGUMENT;
-  if (!valid_bank(*w, w->hidden, w->num_experts) || w->format != MOE_WEIGHT_MXFP4) return MOE_ERR_INVALID_ARGUMENT;
+  if (!valid_bank(*w, w->hidden, w->num_experts) || w->format != MOE_WEIGHT_MXFP4_A4) return MOE_ERR_INVALID_ARGUMENT;
   if (w->hidden <= 0 || w->hidden % 128 != 0) return MOE_ERR_INVALID_ARGUMENT;
   if (M_total < 0 || row_divisor < 1) return MOE_ERR_INVALID_ARGUMENT;
   const int64_t K_ = stage == MOE_GEMM_GATE_UP ? w->hidden : w->inter;
@@ -570,7 +576,8 @@ moe_status_t moe_mxfp4_w4a4_forward(const moe_nvfp4_layer_t* layer, const uint16
   uint16_t* h = at<uint16_t>(workspace, L.h);
   uint8_t* hq = at<uint8_t>(workspace, L.hq);
   uint8_t* hs = at<uint8_t>(workspace, L.hs);
-  uint16_t* y = at<uint16_t>(workspace, L.y);
+  uint16_t* y = (aux && aux->y_rows) ? aux->y_rows : at<uint16_t>(workspace, L.y);
+  if (!al16(y)) return MOE_ERR_INVALID_ARGUMENT;
   // the shared expert's rows follow the routed ones in h and in its 4-bit copy
   uint16_t* h_sh = h + (size_t)S * I;
   uint8_t* hq_sh = hq + (size_t)S * I / 2;

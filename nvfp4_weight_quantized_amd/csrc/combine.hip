@@ -6,6 +6,8 @@
 // out[t][h] = bf16( sum_{j<k} w[t][j] * y[slot_to_row[t*k+j]][h]  +  y_shared[t][h] ),
 // accumulated in fp32 in that order.  A gather-add: each thread owns 8 consecutive columns and
 // reads 16-byte pieces of the k+1 source rows; no atomics, so the result is deterministic.
+// A negative row (a slot the permutation placed nowhere because its expert id was out of range)
+// is never read: the token's output row becomes NaN instead, a loud result.
 #include "common.h"
 
 namespace moe {
@@ -28,13 +30,16 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   // the k source rows in groups of 8: indices and weights first, then all row loads, then the
   // fma chain in j order (every load of a group in flight together)
+  bool placed = true;
   for (int j0 = 0; j0 < k; j0 += 8) {
     int rows[8];
     float wj[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int j = min(j0 + u, k - 1);
-      rows[u] = slot_to_row[(size_t)t * k + j];
+      const int r = slot_to_row[(size_t)t * k + j];
+      placed = placed && r >= 0;
+      rows[u] = max(r, 0);
       wj[u] = w[(size_t)t * k + j];
     }
     uint4 v[8];
@@ -68,7 +73,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t
   uint32_t o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    o[i] = (uint32_t)f32_to_bf16(acc[2 * i]) | ((uint32_t)f32_to_bf16(acc[2 * i + 1]) << 16);
+    o[i] = placed ? (uint32_t)f32_to_bf16(acc[2 * i]) | ((uint32_t)f32_to_bf16(acc[2 * i + 1]) << 16)
+                  : 0x7FC07FC0u;   // two bf16 quiet NaNs
   *reinterpret_cast<uint4*>(out + (size_t)t * H + h0) = uint4{o[0], o[1], o[2], o[3]};
 }
 

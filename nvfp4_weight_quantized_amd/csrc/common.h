@@ -99,7 +99,8 @@ struct GemmProblem {
   int32_t M_extra;
   const uint16_t* a_extra;
   // Tall-tile path only: activations in the fragment-tiled layout.  Tile m of the problem's
-  // 128-row m-tiles (numbered over the groups in order, then the extra group) holds, for each
+  // 128-row m-tiles (numbered as find_tile does: the extra group's first, then the groups in
+  // order) holds, for each
   // 128-column chunk c of the K dimension, 32 fragments of 1 KB: fragment F = 4*i + j holds at
   // byte 16*l (l = 16*q + n) row 16*i + n, columns [128*c + 32*j + 8*q, +8) of the tile, i.e.
   // byte offset ((m * (K/128) + c) * 32 + F) * 1024 + 16 * l.  Rows past a group's end are

@@ -164,7 +164,8 @@ __device__ __forceinline__ int wave_exclusive_scan(const int* cnt, int* out, int
 // Stable scatter of one wave's slots [s_begin, s_end): position = base[e] + rank among the earlier
 // slots of the same expert in this wave's range; base[e] advances by the wave's count.  The lanes
 // holding the same expert are found with one ballot per bit of the expert index (E <= 1024: at
-// most 10), so no atomic ordering and no loop over distinct experts is involved.
+// most 10), so no atomic ordering and no loop over distinct experts is involved.  A slot whose id
+// lies outside [0, E) is placed nowhere: its slot_to_row entry is -1 (the histograms skip it too).
 __device__ __forceinline__ void wave_stable_scatter(const int32_t* ids, int s_begin, int s_end, int E, int* base,
                                                     int32_t* __restrict__ sorted_slot,
                                                     int32_t* __restrict__ slot_to_row) {
@@ -173,8 +174,11 @@ __device__ __forceinline__ void wave_stable_scatter(const int32_t* ids, int s_be
   const int nbits = E > 1 ? 32 - __builtin_clz((unsigned)(E - 1)) : 0;
   for (int s0 = s_begin; s0 < s_end; s0 += 64) {
     const int s = s0 + lane;
-    const bool valid = s < s_end;
-    const int e = valid ? ids[s] : 0;
+    const bool in_range = s < s_end;
+    const int id = in_range ? ids[s] : 0;
+    const bool valid = in_range && id >= 0 && id < E;
+    const int e = valid ? id : 0;
+    if (in_range && !valid) slot_to_row[s] = -1;
     uint64_t peers = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (e >> b) & 1;
@@ -208,7 +212,10 @@ __device__ __forceinline__ void permute_block(const int32_t* ids, int S, int E, 
   __syncthreads();
   const int s_begin = wave * kPermSlotsPerWave;
   const int s_end = min(S, s_begin + kPermSlotsPerWave);
-  for (int s = s_begin + (tid & 63); s < s_end; s += 64) atomicAdd(&wave_hist[wave][ids[s]], 1);
+  for (int s = s_begin + (tid & 63); s < s_end; s += 64) {
+    const int e = ids[s];
+    if (e >= 0 && e < E) atomicAdd(&wave_hist[wave][e], 1);   // an id outside [0, E) joins no group
+  }
   __syncthreads();
   for (int e = tid; e < E; e += kPermuteThreads) {
     int c = 0;

@@ -253,7 +253,7 @@ moe_status_t launch_a4(const GemmProblemA4& p, hipStream_t stream) {
 }  // namespace
 
 moe_status_t launch_grouped_gemm_a4(const GemmProblemA4& p, hipStream_t stream) {
-  if (p.bank.format != MOE_WEIGHT_MXFP4 || (p.has_extra && p.extra.format != MOE_WEIGHT_MXFP4))
+  if (p.bank.format != MOE_WEIGHT_MXFP4_A4 || (p.has_extra && p.extra.format != MOE_WEIGHT_MXFP4_A4))
     return MOE_ERR_INVALID_ARGUMENT;
   if (p.out_tiled) return MOE_ERR_INVALID_ARGUMENT;
   if (p.stage == MOE_GEMM_GATE_UP) {

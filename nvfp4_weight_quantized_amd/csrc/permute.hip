@@ -60,7 +60,10 @@ __global__ __launch_bounds__(kPermuteThreads) void permute_hist_kernel(const int
   __syncthreads();
   const int s_begin = blockIdx.x * kPermuteChunk;
   const int s_end = min(S, s_begin + kPermuteChunk);
-  for (int s = s_begin + tid; s < s_end; s += kPermuteThreads) atomicAdd(&hist[ids[s]], 1);
+  for (int s = s_begin + tid; s < s_end; s += kPermuteThreads) {
+    const int e = ids[s];
+    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);   // an id outside [0, E) joins no group
+  }
   __syncthreads();
   for (int e = tid; e < E; e += kPermuteThreads) block_hist[(size_t)blockIdx.x * E + e] = hist[e];
 }
@@ -121,7 +124,10 @@ __global__ __launch_bounds__(kPermuteThreads) void permute_scatter_kernel(
   const int blk0 = blockIdx.x * kPermuteChunk;
   const int s_begin = blk0 + wave * kPermSlotsPerWave;
   const int s_end = min(S, s_begin + kPermSlotsPerWave);
-  for (int s = s_begin + (tid & 63); s < s_end; s += 64) atomicAdd(&wave_hist[wave][ids[s]], 1);
+  for (int s = s_begin + (tid & 63); s < s_end; s += 64) {
+    const int e = ids[s];
+    if (e >= 0 && e < E) atomicAdd(&wave_hist[wave][e], 1);
+  }
   __syncthreads();
   for (int e = tid; e < E; e += kPermuteThreads) {
     int run = block_base[(size_t)blockIdx.x * E + e];

@@ -37,6 +37,17 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: Optional[int] = None):
         raise ValueError(f"{name}: expected {ndim} dims, got {tuple(t.shape)}")
 
 
+def _shape(t: torch.Tensor, name: str, shape) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _same_device(ref: torch.Tensor, *named) -> None:
+    for name, t in named:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name}: on {t.device}, expected {ref.device}")
+
+
 # ----------------------------------------------------------------------------- weights
 
 @dataclass
@@ -124,6 +135,43 @@ class NvFp4MoELayer:
         """True for banks in the W4A4 layout: forward() then quantizes the activations too."""
         return self.routed.fmt == "mxfp4_a4"
 
+    def check(self) -> None:
+        """Shapes, dtypes and devices of every tensor of the layer (raises before any launch)."""
+        self.routed.check()
+        e, h = self.routed.num_experts, self.routed.hidden
+        _need(self.w_router, "w_router", torch.bfloat16, 2)
+        _shape(self.w_router, "w_router", (e, h))
+        if self.router_bias is not None:
+            _need(self.router_bias, "router_bias", torch.float32, 1)
+            _shape(self.router_bias, "router_bias", (e,))
+        if self.shared is not None:
+            self.shared.check()
+            if self.shared.num_experts != 1 or self.shared.hidden != h:
+                raise ValueError("shared expert bank: expected one expert of the routed hidden size")
+            if self.shared.fmt != self.routed.fmt:
+                raise ValueError("routed and shared banks must share one weight format")
+        if not 1 <= self.top_k <= e:
+            raise ValueError(f"top_k {self.top_k} outside [1, {e}]")
+        b = self.routed
+        _same_device(self.w_router, ("router_bias", self.router_bias), ("routed.w13", b.w13),
+                     ("routed.w2", b.w2), ("shared.w13", self.shared.w13 if self.shared is not None else None))
+
+    def _key(self):
+        banks = [b for b in (self.routed, self.shared) if b is not None]
+        return (id(self.w_router), id(self.router_bias), self.top_k,
+                *[(id(t), b.fmt) for b in banks for t in (b.w13, b.w13_scale, b.w13_gscale, b.w2, b.w2_scale,
+                                                          b.w2_gscale)])
+
+    def checked_struct(self) -> L.Layer:
+        """check() + c_struct(), cached while the layer holds the same tensors."""
+        key = self._key()
+        cached = self.__dict__.get("_checked")
+        if cached is None or cached[0] != key:
+            self.check()
+            cached = (key, self.c_struct())
+            self.__dict__["_checked"] = cached
+        return cached[1]
+
     def c_struct(self) -> L.Layer:
         empty = L.Experts()
         return L.Layer(self.hidden, self.num_experts, self.top_k, self.w_router.data_ptr(),
@@ -184,10 +232,13 @@ def route(x: torch.Tensor, w_router: torch.Tensor, router_bias: Optional[torch.T
     """S1+S2: (logits fp32 [T, E], topk_ids int32 [T, k], topk_w fp32 [T, k])."""
     _need(x, "x", torch.bfloat16, 2)
     _need(w_router, "w_router", torch.bfloat16, 2)
-    if router_bias is not None:
-        _need(router_bias, "router_bias", torch.float32, 1)
     t, h = x.shape
     e = w_router.shape[0]
+    _shape(w_router, "w_router", (e, h))
+    if router_bias is not None:
+        _need(router_bias, "router_bias", torch.float32, 1)
+        _shape(router_bias, "router_bias", (e,))
+    _same_device(x, ("w_router", w_router), ("router_bias", router_bias))
     logits = torch.empty(t, e, dtype=torch.float32, device=x.device)
     ids = torch.empty(t, k, dtype=torch.int32, device=x.device)
     w = torch.empty(t, k, dtype=torch.float32, device=x.device)
@@ -211,6 +262,8 @@ def permute(topk_ids: torch.Tensor, num_experts: int):
     """S3: (counts [E], offsets [E+1], sorted_slot [S], slot_to_row [S]), all int32."""
     _need(topk_ids, "topk_ids", torch.int32, 2)
     t, k = topk_ids.shape
+    if not 1 <= num_experts <= 1024:
+        raise ValueError(f"num_experts {num_experts} outside [1, 1024]")
     dev = topk_ids.device
     counts = torch.empty(num_experts, dtype=torch.int32, device=dev)
     offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
@@ -227,11 +280,26 @@ def permute(topk_ids: torch.Tensor, num_experts: int):
 def grouped_gemm(stage: int, experts: NvFp4Experts, a: torch.Tensor, expert_offsets: torch.Tensor, m_total: int,
                  row_index: Optional[torch.Tensor] = None, row_divisor: int = 1) -> torch.Tensor:
     """S4 (stage 0: gate/up + SiLU*up -> [M, I]) or S5 (stage 1: down -> [M, H]), bf16."""
+    if experts.fmt == "mxfp4_a4":
+        raise ValueError("a bank in the W4A4 layout runs through grouped_gemm_a4")
     experts.check()
+    if stage not in (L.MOE_GEMM_GATE_UP, L.MOE_GEMM_DOWN):
+        raise ValueError(f"unknown stage {stage}")
     _need(a, "a", torch.bfloat16, 2)
     _need(expert_offsets, "expert_offsets", torch.int32, 1)
+    _shape(expert_offsets, "expert_offsets", (experts.num_experts + 1,))
+    kdim = experts.hidden if stage == L.MOE_GEMM_GATE_UP else experts.inter
+    if a.shape[1] != kdim:
+        raise ValueError(f"a: expected {kdim} columns, got {a.shape[1]}")
     if row_index is not None:
         _need(row_index, "row_index", torch.int32, 1)
+        if stage != L.MOE_GEMM_GATE_UP:
+            raise ValueError("row_index applies to the gate/up stage only")
+        if row_index.numel() < m_total:
+            raise ValueError(f"row_index: {row_index.numel()} entries for {m_total} rows")
+    elif a.shape[0] < m_total:
+        raise ValueError(f"a: {a.shape[0]} rows for {m_total} output rows")
+    _same_device(a, ("expert_offsets", expert_offsets), ("row_index", row_index), ("experts.w13", experts.w13))
     n = experts.inter if stage == L.MOE_GEMM_GATE_UP else experts.hidden
     out = torch.empty(m_total, n, dtype=torch.bfloat16, device=a.device)
     st = experts.c_struct()
@@ -286,8 +354,11 @@ def combine(y_rows: torch.Tensor, slot_to_row: torch.Tensor, topk_w: torch.Tenso
     _need(topk_w, "topk_w", torch.float32, 2)
     t, k = topk_w.shape
     h = y_rows.shape[1]
+    _shape(slot_to_row, "slot_to_row", (t * k,))
     if y_shared is not None:
         _need(y_shared, "y_shared", torch.bfloat16, 2)
+        _shape(y_shared, "y_shared", (t, h))
+    _same_device(y_rows, ("slot_to_row", slot_to_row), ("topk_w", topk_w), ("y_shared", y_shared))
     out = torch.empty(t, h, dtype=torch.bfloat16, device=y_rows.device)
     L.check("moe_combine", L.lib().moe_combine(_ptr(y_rows), _ptr(slot_to_row), _ptr(topk_w), _ptr(y_shared), t, k,
                                                h, _ptr(out), _stream(y_rows.device)))
@@ -318,21 +389,34 @@ def workspace_for(layer: NvFp4MoELayer, T: int, device) -> torch.Tensor:
 
 
 def forward(layer: NvFp4MoELayer, x: torch.Tensor, workspace: Optional[torch.Tensor] = None,
-            out: Optional[torch.Tensor] = None, return_aux: bool = False, stage_events=None):
+            out: Optional[torch.Tensor] = None, return_aux: bool = False, stage_events=None,
+            return_rows: bool = False):
     """The whole layer on x [T, H] bf16 -> [T, H] bf16 (and, if asked, logits/ids/weights/counts).
 
     Runs moe_nvfp4_forward, or moe_mxfp4_w4a4_forward when the layer's banks are "mxfp4_a4".
+    ``return_rows`` (with ``return_aux``): the aux dict also holds "y_rows", the expert outputs the
+    combine reads (bf16 [T*k + T_shared, H], routed rows in expert-sorted order, then the shared
+    expert's row of every token).
 
     ``stage_events``: optional sequence of 6 raw hipEvent_t handles (ints or None) recorded at the
     stage boundaries (before S1, after S1, after S2+S3, after S4, S5, S6) on the current stream.
     """
     _need(x, "x", torch.bfloat16, 2)
+    st = layer.checked_struct()
     t = x.shape[0]
+    if x.shape[1] != layer.hidden:
+        raise ValueError(f"x: expected {layer.hidden} columns, got {x.shape[1]}")
+    _same_device(x, ("w_router", layer.w_router))
     if workspace is None:
         workspace = workspace_for(layer, t, x.device)
     _need(workspace, "workspace", torch.uint8)
+    _same_device(x, ("workspace", workspace))
     if out is None:
         out = torch.empty_like(x)
+    else:
+        _need(out, "out", torch.bfloat16, 2)
+        _shape(out, "out", x.shape)
+        _same_device(x, ("out", out))
     aux = None
     aux_t = None
     if return_aux or stage_events is not None:
@@ -344,12 +428,15 @@ def forward(layer: NvFp4MoELayer, x: torch.Tensor, workspace: Optional[torch.Ten
                      topk_w=torch.empty(t, k, dtype=torch.float32, device=x.device),
                      expert_counts=torch.empty(e, dtype=torch.int32, device=x.device))
         aux.logits, aux.topk_ids, aux.topk_w, aux.expert_counts = (v.data_ptr() for v in aux_t.values())
+        if return_rows:
+            rows = t * k + (t if layer.shared is not None else 0)
+            aux_t["y_rows"] = torch.empty(rows, layer.hidden, dtype=torch.bfloat16, device=x.device)
+            aux.y_rows = aux_t["y_rows"].data_ptr()
     if stage_events is not None:
         if len(stage_events) != L.NUM_STAGE_EVENTS:
             raise ValueError(f"stage_events: {L.NUM_STAGE_EVENTS} entries expected")
         arr = (ctypes.c_void_p * L.NUM_STAGE_EVENTS)(*stage_events)
         aux.stage_events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
-    st = layer.c_struct()
     fn = "moe_mxfp4_w4a4_forward" if layer.is_w4a4 else "moe_nvfp4_forward"
     L.check(fn, getattr(L.lib(), fn)(ctypes.byref(st), _ptr(x), t, _ptr(out), _ptr(workspace), workspace.numel(),
                                      ctypes.byref(aux) if aux is not None else None, _stream(x.device)))

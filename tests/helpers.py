@@ -24,6 +24,18 @@ def dequant_scale_from_checkpoint(gs: np.ndarray, convention: str) -> np.ndarray
     return onv.gscale_from_quant_scale(gs)
 
 
+def oracle_dequant_scales(w13: np.ndarray, w2: np.ndarray, convention: str) -> np.ndarray:
+    """The oracle's own dequant global scales (gate, up, down) of one fp32 expert: amax of each
+    tensor, the checkpoint scale of the convention (oracle.nvfp4), inverted on load for
+    compressed-tensors."""
+    inter = w13.shape[0] // 2
+    amax = [np.abs(a).max() for a in (w13[:inter], w13[inter:], w2)]
+    if convention == "modelopt":
+        return np.array([onv.gscale_modelopt(a) for a in amax], np.float32)
+    q = np.array([onv.gscale_compressed_tensors(a) for a in amax], np.float32)
+    return onv.gscale_from_quant_scale(q)
+
+
 def oracle_expert_mx(wl, bank: str, e: int, device="cpu") -> omoe.ExpertWeights:
     """Quantize one synthetic expert to MXFP4 with the oracle quantizer."""
     w13, w2 = synth.expert_fp32(wl, bank, e, device)
@@ -37,11 +49,9 @@ def oracle_expert(wl, bank: str, e: int, device="cpu", fmt: str = "nvfp4") -> om
     if fmt == "mxfp4":
         return oracle_expert_mx(wl, bank, e, device)
     w13, w2 = synth.expert_fp32(wl, bank, e, device)
-    amax = synth.expert_amax(w13, w2)
-    d = dequant_scale_from_checkpoint(synth.checkpoint_global_scales(amax, wl.gscale_convention),
-                                      wl.gscale_convention)
     w13 = w13.cpu().numpy()
     w2 = w2.cpu().numpy()
+    d = oracle_dequant_scales(w13, w2, wl.gscale_convention)
     inter = w13.shape[0] // 2
     pg, sg = onv.quantize(w13[:inter], d[0])
     pu, su = onv.quantize(w13[inter:], d[1])

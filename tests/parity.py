@@ -109,6 +109,15 @@ def assert_close(got, ref, what=""):
     return rel, mx
 
 
+# margins of the full-size checks, printed in the pytest terminal summary (also under -q)
+MARGINS = []
+
+
+def record_margin(what: str, rel: float, mx: float) -> None:
+    """Keep the worst rel-L2 and max-abs/max|ref| of a check for the end-of-run summary."""
+    MARGINS.append((what, float(rel), float(mx)))
+
+
 def logit_bound(x_bits, wr_bits, bias=None):
     x = np.abs(omoe.bf16_to_float(x_bits))
     w = np.abs(omoe.bf16_to_float(wr_bits))

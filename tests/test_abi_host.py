@@ -98,8 +98,12 @@ def test_validate_forward_host_only():
     lay10.routed.format = L.MOE_WEIGHT_MXFP4
     assert moe.validate_forward(lay10, 8, 1 << 40) == L.MOE_ERR_INVALID_ARGUMENT  # shared is NVFP4
     lay11 = _fake_layer()
-    lay11.routed.format = lay11.shared.format = 2
+    lay11.routed.format = lay11.shared.format = 3
     assert moe.validate_forward(lay11, 8, 1 << 40) == L.MOE_ERR_INVALID_ARGUMENT
+    # a bank in the W4A4 tile layout is not read by the W4A16 layer
+    lay12 = _fake_layer()
+    lay12.routed.format = lay12.shared.format = L.MOE_WEIGHT_MXFP4_A4
+    assert moe.validate_forward(lay12, 8, 1 << 40) == L.MOE_ERR_INVALID_ARGUMENT
     # no shared expert is valid
     lay5 = _fake_layer(shared=False)
     assert moe.validate_forward(lay5, 8, moe.forward_workspace_size(8, 4096, 1536, 0, 320, 8)) == L.MOE_OK
@@ -132,10 +136,14 @@ def test_product_path_has_no_oracle_dependency():
 def test_w4a4_validation_host_only():
     """The W4A4 layer needs MXFP4 banks (no global scales) and its own, larger workspace."""
     lay = _fake_layer()
-    lay.routed.format = lay.shared.format = L.MOE_WEIGHT_MXFP4
+    lay.routed.format = lay.shared.format = L.MOE_WEIGHT_MXFP4_A4
     lay.routed.w13_gscale = lay.routed.w2_gscale = lay.shared.w13_gscale = lay.shared.w2_gscale = None
     need = moe.forward_workspace_size(8, 4096, 1536, 1536, 320, 8, w4a4=True)
     assert moe.validate_forward(lay, 8, need, w4a4=True) == L.MOE_OK
+    # MXFP4 banks in the W4A16 tile layout are not read by the W4A4 layer
+    lay_w16 = _fake_layer()
+    lay_w16.routed.format = lay_w16.shared.format = L.MOE_WEIGHT_MXFP4
+    assert moe.validate_forward(lay_w16, 8, need, w4a4=True) == L.MOE_ERR_INVALID_ARGUMENT
     assert moe.validate_forward(lay, 8, need - 1, w4a4=True) == L.MOE_ERR_WORKSPACE_TOO_SMALL
     assert moe.validate_forward(lay, 8, need, arch="gfx942", w4a4=True) == L.MOE_ERR_UNSUPPORTED_DEVICE
     assert moe.validate_forward(_fake_layer(), 8, 1 << 40, w4a4=True) == L.MOE_ERR_INVALID_ARGUMENT  # NVFP4

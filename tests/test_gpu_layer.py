@@ -222,17 +222,50 @@ def _gpu_layer(wl):
                              torch.from_numpy(bias).to(DEV) if bias is not None else None, routed, shared, wl.k)
 
 
-SAMPLE_TOKENS = {"decode": 2, "prefill": 1, "skewed": 1, "long_prefill": 1}
+def _xcd_sample_tiles(counts, T, has_shared, N, BN=256, BM=128, xcds=8):
+    """The 128-row m-tiles (group, first sorted row, rows; group -1 = the shared expert) that hold
+    the first, middle and last (m-tile, n-tile) pair of each XCD's contiguous range in the prefill
+    GEMMs of output width N (n-tiles of BN columns; the shared expert's m-tiles numbered first)."""
+    tiles = [(-1, r, min(BM, T - r)) for r in range(0, T, BM)] if has_shared else []
+    off = 0
+    for e, c in enumerate(counts):
+        tiles += [(e, off + r, min(BM, int(c) - r)) for r in range(0, int(c), BM)]
+        off += int(c)
+    nt = N // BN
+    total = len(tiles) * nt
+    per = -(-total // xcds)
+    picks = set()
+    for x in range(xcds):
+        lo, hi = x * per, min((x + 1) * per, total) - 1
+        if lo <= hi:
+            picks.update(L // nt for L in (lo, (lo + hi) // 2, hi))
+    return [tiles[m] for m in sorted(picks)]
 
 
-@pytest.mark.timeout(600)
+E2E_TOKENS = {"decode": 8, "prefill": 16, "skewed": 16, "long_prefill": 16}
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["decode", "prefill", "skewed", "long_prefill"])
 def test_full_size_workload(name):
+    """A full-size workload in the launch configuration the bench times (one moe_nvfp4_forward):
+      * selection bit-exact for every token, router logits on a token sample, permutation for every slot;
+      * the expert outputs y the combine reads (returned by the forward itself): every routed row at
+        decode; at the prefill shapes every row of the m-tiles that start, sit in the middle of and end
+        each XCD's tile range in both GEMMs, and the shared expert's row of EVERY token (all of its
+        m-tiles in both GEMMs), each against the oracle's gate/up -> SiLU*up -> down of those rows;
+      * the combine for EVERY token on the forward's own y rows and weights (fp32 summation bound);
+      * the layer output of every decode token and of 16 tokens spread over the sampled tiles at the
+        prefill shapes against the oracle's whole forward;
+      * every token of the forward against the per-stage entry points (bf16, row-major h);
+      * the GPU-quantized bytes of the experts checked against the oracle quantizer's."""
     wl = synth.WORKLOADS[name]
-    _say(f"[full-size {name}] building layer T={wl.T} H={wl.H} I={wl.I} E={wl.E} k={wl.k}")
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
+    S = T * k
+    _say(f"[full-size {name}] building layer T={T} H={H} I={I} E={E} k={k}")
     glayer = _gpu_layer(wl)
     x = synth.activations(wl, DEV)
-    out, aux = ops.forward(glayer, x, return_aux=True)
+    out, aux = ops.forward(glayer, x, return_aux=True, return_rows=True)
     torch.cuda.synchronize()
     _say(f"[full-size {name}] forward done")
     xb = helpers.bf16_bits(x)
@@ -240,37 +273,100 @@ def test_full_size_workload(name):
     bias = synth.router_bias(wl)
     lg = aux["logits"].cpu().numpy().astype(np.float64)
     ids = aux["topk_ids"].cpu().numpy()
+    wts = aux["topk_w"].cpu().numpy()
     # selection: bit-exact for every token on the GPU's logits
-    ids_ref, w_ref = omoe.topk(lg, wl.k)
+    ids_ref, w_ref = omoe.topk(lg, k)
     assert np.array_equal(ids, ids_ref)
-    np.testing.assert_allclose(aux["topk_w"].cpu().numpy(), w_ref, rtol=0, atol=1e-5)
+    np.testing.assert_allclose(wts, w_ref, rtol=0, atol=1e-5)
     # router GEMM: a token sample within the fp32 bound
     rng = np.random.default_rng(7)
-    rows = np.unique(np.concatenate([rng.choice(wl.T, min(wl.T, 48), replace=False), [0, wl.T - 1]]))
+    rows = np.unique(np.concatenate([rng.choice(T, min(T, 48), replace=False), [0, T - 1]]))
     exact = omoe.router_logits(xb[rows], wrb, bias)
     assert np.all(np.abs(lg[rows] - exact) <= parity.logit_bound(xb[rows], wrb, bias))
     # permutation: bit-exact for every slot
-    counts, offsets, sorted_slot, slot_to_row = ops.permute(aux["topk_ids"], wl.E)
-    c, o, s, r = omoe.permute(ids, wl.E)
+    counts, offsets, sorted_slot, slot_to_row = ops.permute(aux["topk_ids"], E)
+    c, o, srt, s2r = omoe.permute(ids, E)
     assert np.array_equal(aux["expert_counts"].cpu().numpy(), c)
     assert np.array_equal(counts.cpu().numpy(), c) and np.array_equal(offsets.cpu().numpy(), o)
-    assert np.array_equal(sorted_slot.cpu().numpy(), s) and np.array_equal(slot_to_row.cpu().numpy(), r)
+    assert np.array_equal(sorted_slot.cpu().numpy(), srt) and np.array_equal(slot_to_row.cpu().numpy(), s2r)
     _say(f"[full-size {name}] route/permute exact; {int((c > 0).sum())} experts used, max count {int(c.max())}")
 
+    y_gpu = aux["y_rows"]
+    decode = (S + T) // (E + 1) <= 32   # the 8-, 16- and 64-row kernels: no XCD tile ranges
+    if decode:
+        sample = [(int(e), int(o[e]), int(c[e])) for e in range(E) if c[e] > 0] + [(-1, 0, T)]
+        tokens = np.arange(T)
+    else:
+        sample = sorted(set(_xcd_sample_tiles(c, T, True, I) + _xcd_sample_tiles(c, T, True, H)))
+        firsts = [srt[r0] // k for g, r0, n in sample if g >= 0] + [srt[r0 + n - 1] // k for g, r0, n in sample
+                                                                      if g >= 0]
+        cand = np.unique(np.concatenate([firsts, [0, T - 1]]))
+        tokens = cand[np.unique(np.linspace(0, len(cand) - 1, E2E_TOKENS[name]).round().astype(int))]
+    experts = sorted({g for g, _, _ in sample if g >= 0} | {int(e) for e in np.unique(ids[tokens])})
     olayer = helpers.oracle_layer(wl, DEV)
-    # gate/up rows of the most loaded expert (all of its tiles), through the per-stage entry point
-    e_max = int(np.argmax(c))
-    olayer.routed.prefetch([e_max])
-    h = ops.grouped_gemm(L.MOE_GEMM_GATE_UP, glayer.routed, x, offsets, wl.T * wl.k, sorted_slot, wl.k)
-    r0, r1 = int(o[e_max]), int(o[e_max + 1])
-    a_rows = omoe.bf16_to_float(xb[s[r0:r1] // wl.k])
-    h_ref = omoe.gate_up(a_rows, olayer.routed[e_max])
-    parity.assert_close(parity.f64(h[r0:r1]), h_ref, f"gate/up rows of expert {e_max}")
-    _oracle_bank_equal(glayer.routed, olayer.routed, [e_max])
-    # whole-layer output on sampled tokens
-    tokens = np.unique(np.concatenate([[wl.T - 1], s[r0:r0 + 1] // wl.k]))[:SAMPLE_TOKENS[name]]
-    olayer.routed.prefetch(np.unique(ids[tokens]))
+    _say(f"[full-size {name}] oracle quantizes {len(experts)} experts")
+    olayer.routed.prefetch(experts, threads=16)
+    _oracle_bank_equal(glayer.routed, olayer.routed, experts[:: max(1, len(experts) // 8)])
+
+    # expert outputs y of the sampled m-tiles (routed) against the oracle, expert by expert
+    worst = (0.0, 0.0)
+    by_expert = {}
+    for g, r0, n in sample:
+        if g >= 0:
+            by_expert.setdefault(g, []).append(np.arange(r0, r0 + n))
+    for e, parts in by_expert.items():
+        r = np.concatenate(parts)
+        a_rows = omoe.bf16_to_float(xb[srt[r] // k])
+        y_ref = omoe.expert_ffn(a_rows, olayer.routed[e])
+        got = parity.f64(y_gpu[torch.from_numpy(r).to(DEV)])
+        rel, mx = parity.assert_close(got, y_ref, f"y rows of expert {e}")
+        worst = (max(worst[0], rel), max(worst[1], mx))
+    parity.record_margin(f"{name}: routed y rows ({len(by_expert)} experts)", *worst)
+    # the shared expert for every token, and tile by tile
+    ys_ref = omoe.expert_ffn(omoe.bf16_to_float(xb), olayer.shared[0])
+    ys_gpu = parity.f64(y_gpu[S:S + T])
+    rel, mx = parity.assert_close(ys_gpu, ys_ref, "shared expert y, all tokens")
+    for r0 in range(0, T, 128):
+        parity.assert_close(ys_gpu[r0:r0 + 128], ys_ref[r0:r0 + 128], f"shared expert y rows {r0}..")
+    parity.record_margin(f"{name}: shared expert y, all {T} tokens", rel, mx)
+    _say(f"[full-size {name}] y rows match ({len(by_expert)} routed experts, shared expert on every token)")
+
+    # the combine of every token on the forward's own y rows
+    w64 = wts.astype(np.float64)
+    worst = 0.0
+    for t0 in range(0, T, 1024):
+        t1 = min(T, t0 + 1024)
+        rsel = s2r.reshape(T, k)[t0:t1]
+        y_routed = parity.f64(y_gpu[torch.from_numpy(np.unique(rsel)).to(DEV)])
+        lut = np.searchsorted(np.unique(rsel), rsel)
+        ysh = ys_gpu[t0:t1]
+        ref = np.einsum("tj,tjh->th", w64[t0:t1], y_routed[lut]) + ysh
+        sabs = np.einsum("tj,tjh->th", np.abs(w64[t0:t1]), np.abs(y_routed[lut])) + np.abs(ysh)
+        got = parity.f64(out[t0:t1])
+        err = np.abs(got - ref)
+        bound = 2.0 ** -8 * np.abs(ref) + 2.0 ** -20 * sabs + 1e-30
+        assert np.all(err <= bound), f"combine tokens {t0}..{t1}: worst ratio {float((err / bound).max()):.3f}"
+        worst = max(worst, float((err / bound).max()))
+    _say(f"[full-size {name}] combine exact within the fp32 bound for all {T} tokens (worst {worst:.3f} of it)")
+
+    # the whole layer on sampled tokens against the oracle's forward
     res = parity.reference_for_selection(xb[tokens], olayer, ids[tokens])
     rel, mx = parity.assert_close(parity.f64(out[torch.from_numpy(tokens).to(DEV)]), res["out"], "sampled tokens")
-    _oracle_bank_equal(glayer.routed, olayer.routed, np.unique(ids[tokens]))
-    _say(f"[full-size {name}] tokens {tokens.tolist()}: rel-L2 {rel:.2e}, max-abs {mx:.2e}")
+    parity.record_margin(f"{name}: layer output, {len(tokens)} tokens", rel, mx)
+    _say(f"[full-size {name}] layer output of tokens {tokens.tolist()}: rel-L2 {rel:.2e}, max-abs {mx:.2e}")
+
+    # every token against the per-stage entry points (bf16 operands, row-major h)
+    h = ops.grouped_gemm(L.MOE_GEMM_GATE_UP, glayer.routed, x, offsets, S, sorted_slot, k)
+    y = ops.grouped_gemm(L.MOE_GEMM_DOWN, glayer.routed, h, offsets, S)
+    one = torch.tensor([0, T], dtype=torch.int32, device=DEV)
+    hs = ops.grouped_gemm(L.MOE_GEMM_GATE_UP, glayer.shared, x, one, T)
+    ys = ops.grouped_gemm(L.MOE_GEMM_DOWN, glayer.shared, hs, one, T)
+    staged = ops.combine(y, slot_to_row, aux["topk_w"], ys)
+    rel, mx = parity.assert_close(parity.f64(out), parity.f64(staged), "forward vs per-stage entry points")
+    parity.record_margin(f"{name}: forward vs staged, all {T} tokens", rel, mx)
+    e_max = int(np.argmax(c))
+    r0, r1 = int(o[e_max]), int(o[e_max + 1])
+    h_ref = omoe.gate_up(omoe.bf16_to_float(xb[srt[r0:r1] // k]), olayer.routed[e_max])
+    parity.assert_close(parity.f64(h[r0:r1]), h_ref, f"staged gate/up rows of expert {e_max}")
+    del h, y, hs, ys, staged, y_gpu
+    torch.cuda.empty_cache()

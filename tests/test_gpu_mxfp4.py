@@ -155,22 +155,23 @@ def test_mx_small_layer_end_to_end(case):
 @pytest.mark.timeout(600)
 def test_mx_decode_workload_full_size():
     """The decode-shaped layer (T=8, H=4096, I=1536, E=320 top-8 + shared) with MXFP4 weights quantized
-    on the GPU: quantized bytes of the experts used equal the oracle quantizer's, selection is exact,
-    and the output of sampled tokens matches the oracle."""
+    on the GPU: quantized bytes of every expert used equal the oracle quantizer's, selection is exact,
+    every expert output row the combine reads matches the oracle, and so does every token's output."""
     wl = synth.WORKLOADS["decode"]
-    _say(f"[mxfp4 decode] building layer E={wl.E} H={wl.H} I={wl.I}")
+    T, k, E = wl.T, wl.k, wl.E
+    S = T * k
+    _say(f"[mxfp4 decode] building layer E={E} H={wl.H} I={wl.I}")
     glayer = build_layer(wl, DEV, fmt="mxfp4")
     x = synth.activations(wl, DEV)
-    out, aux = ops.forward(glayer, x, return_aux=True)
+    out, aux = ops.forward(glayer, x, return_aux=True, return_rows=True)
     torch.cuda.synchronize()
     xb = helpers.bf16_bits(x)
     ids = aux["topk_ids"].cpu().numpy()
-    ids_ref, _ = omoe.topk(aux["logits"].cpu().numpy().astype(np.float64), wl.k)
+    ids_ref, _ = omoe.topk(aux["logits"].cpu().numpy().astype(np.float64), k)
     assert np.array_equal(ids, ids_ref)
     olayer = helpers.oracle_layer(wl, DEV, fmt="mxfp4")
-    tokens = np.array([0, wl.T - 1])
-    used = np.unique(ids[tokens])
-    olayer.routed.prefetch(used)
+    used = np.unique(ids)
+    olayer.routed.prefetch(used, threads=16)
     for e in used:
         ow = olayer.routed[int(e)]
         t13, s13 = parity.tile_np_mx(ow.w13, ow.w13_scale)
@@ -179,6 +180,21 @@ def test_mx_decode_workload_full_size():
         t2, s2 = parity.tile_np_mx(ow.w2, ow.w2_scale)
         assert np.array_equal(glayer.routed.w2[e].cpu().numpy(), t2), e
         assert np.array_equal(glayer.routed.w2_scale[e].cpu().numpy(), s2), e
-    res = parity.reference_for_selection(xb[tokens], olayer, ids[tokens])
-    rel, mx = parity.assert_close(parity.f64(out[torch.from_numpy(tokens).to(DEV)]), res["out"], "sampled tokens")
-    _say(f"[mxfp4 decode] tokens {tokens.tolist()}: rel-L2 {rel:.2e}, max-abs {mx:.2e}")
+    # every expert output row (routed rows in expert order, then the shared expert's)
+    counts, offsets, srt, s2r = omoe.permute(ids, E)
+    y = parity.f64(aux["y_rows"])
+    xf = omoe.bf16_to_float(xb)
+    worst = (0.0, 0.0)
+    for e in used:
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        rel, mx = parity.assert_close(y[r0:r1], omoe.expert_ffn(xf[srt[r0:r1] // k], olayer.routed[int(e)]),
+                                      f"y rows of expert {e}")
+        worst = (max(worst[0], rel), max(worst[1], mx))
+    parity.record_margin(f"mxfp4 decode: routed y rows ({len(used)} experts)", *worst)
+    rel, mx = parity.assert_close(y[S:S + T], omoe.expert_ffn(xf, olayer.shared[0]), "shared expert y")
+    parity.record_margin("mxfp4 decode: shared expert y", rel, mx)
+    # every token's output
+    res = parity.reference_for_selection(xb, olayer, ids)
+    rel, mx = parity.assert_close(parity.f64(out), res["out"], "all tokens")
+    parity.record_margin(f"mxfp4 decode: layer output, all {T} tokens", rel, mx)
+    _say(f"[mxfp4 decode] all {T} tokens: rel-L2 {rel:.2e}, max-abs {mx:.2e}")

@@ -1,5 +1,7 @@
 """GPU parity of each stage of the HIP path against the oracle, through the C ABI."""
 
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -274,3 +276,98 @@ def test_bad_arguments_fail_loudly():
     with pytest.raises(L.MoeError):
         ops.route(torch.zeros(4, 200, dtype=torch.bfloat16, device=DEV),
                   torch.zeros(8, 200, dtype=torch.bfloat16, device=DEV), None, 2)   # H % 128 != 0
+
+
+def test_mismatched_shapes_raise_before_any_launch():
+    """Host-side checks of the binding: every shape, dtype and device mismatch raises ValueError (or
+    TypeError) before the library is called, so a wrong tensor never turns into out-of-bounds access."""
+    rng = np.random.default_rng(5)
+    layer = helpers.random_layer(rng, 256, 128, 8, 2)
+    glayer = parity.to_gpu_layer(layer)
+    x = torch.zeros(4, 256, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        ops.forward(glayer, torch.zeros(4, 384, dtype=torch.bfloat16, device=DEV))     # x width != H
+    with pytest.raises(ValueError):
+        ops.forward(glayer, x, out=torch.empty(5, 256, dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(TypeError):
+        ops.forward(glayer, x, out=torch.empty(4, 256, dtype=torch.float32, device=DEV))
+    with pytest.raises(ValueError):
+        ops.forward(glayer, x, out=torch.empty(4, 256, dtype=torch.bfloat16))           # host tensor
+    bad = ops.NvFp4MoELayer(glayer.w_router[:, :128].contiguous(), None, glayer.routed, glayer.shared, 2)
+    with pytest.raises(ValueError):
+        ops.forward(bad, x)                                                              # router [E, H/2]
+    bad = ops.NvFp4MoELayer(glayer.w_router, torch.zeros(9, device=DEV), glayer.routed, glayer.shared, 2)
+    with pytest.raises(ValueError):
+        ops.forward(bad, x)                                                              # bias [E+1]
+    wr = glayer.w_router
+    with pytest.raises(ValueError):
+        ops.route(x, torch.zeros(8, 384, dtype=torch.bfloat16, device=DEV), None, 2)
+    with pytest.raises(ValueError):
+        ops.route(x, wr, torch.zeros(7, device=DEV), 2)
+    ids = torch.zeros(4, 2, dtype=torch.int32, device=DEV)
+    counts, offsets, sorted_slot, slot_to_row = ops.permute(ids, 8)
+    with pytest.raises(ValueError):
+        ops.grouped_gemm(L.MOE_GEMM_GATE_UP, glayer.routed, torch.zeros(4, 128, dtype=torch.bfloat16, device=DEV),
+                         offsets, 8, sorted_slot, 2)                                     # a width != H
+    with pytest.raises(ValueError):
+        ops.grouped_gemm(L.MOE_GEMM_GATE_UP, glayer.routed, x, offsets[:5].contiguous(), 8, sorted_slot, 2)
+    with pytest.raises(ValueError):
+        ops.grouped_gemm(L.MOE_GEMM_DOWN, glayer.routed, torch.zeros(3, 128, dtype=torch.bfloat16, device=DEV),
+                         offsets, 8)                                                     # fewer rows than M
+    y = torch.zeros(8, 256, dtype=torch.bfloat16, device=DEV)
+    w = torch.full((4, 2), 0.5, device=DEV)
+    with pytest.raises(ValueError):
+        ops.combine(y, slot_to_row[:7].contiguous(), w)
+    with pytest.raises(ValueError):
+        ops.combine(y, slot_to_row, w, torch.zeros(4, 128, dtype=torch.bfloat16, device=DEV))
+    a4 = ops.NvFp4Experts(glayer.routed.w13, glayer.routed.w13_scale[..., :64].contiguous(), None, glayer.routed.w2,
+                          glayer.routed.w2_scale[..., :4].contiguous(), None, fmt="mxfp4_a4")
+    with pytest.raises(ValueError):
+        ops.grouped_gemm(L.MOE_GEMM_GATE_UP, a4, x, offsets, 8, sorted_slot, 2)         # W4A4 bank
+
+
+def test_permute_rejects_out_of_range_ids_without_writing_out_of_bounds():
+    """ids outside [0, E) join no group: their slots get row -1, the offsets end below T*k, nothing is
+    written past the output buffers, and the combine turns a token with such a slot into NaN."""
+    T, k, E = 300, 4, 16
+    rng = np.random.default_rng(9)
+    for S_case in (T, 4000):   # one-workgroup and multi-block permutation
+        t = S_case // k
+        ids = rng.integers(0, E, (t, k)).astype(np.int32)
+        ids[3, 1] = E
+        ids[t - 1, 0] = -1
+        ids[t // 2, k - 1] = 1 << 20
+        guard = 1000
+        dev_ids = torch.from_numpy(ids).to(DEV)
+        counts = torch.empty(E, dtype=torch.int32, device=DEV)
+        offsets = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+        sorted_buf = torch.full((t * k + guard,), -7, dtype=torch.int32, device=DEV)
+        s2r_buf = torch.full((t * k + guard,), -7, dtype=torch.int32, device=DEV)
+        ws_bytes = L.lib().moe_permute_workspace_size(t, k, E)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=DEV)
+        L.check("moe_permute", L.lib().moe_permute(
+            ctypes.c_void_p(dev_ids.data_ptr()), t, k, E, ctypes.c_void_p(counts.data_ptr()),
+            ctypes.c_void_p(offsets.data_ptr()), ctypes.c_void_p(sorted_buf.data_ptr()),
+            ctypes.c_void_p(s2r_buf.data_ptr()), ctypes.c_void_p(ws.data_ptr()), ws_bytes,
+            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)))
+        torch.cuda.synchronize()
+        valid = (ids >= 0) & (ids < E)
+        n_valid = int(valid.sum())
+        flat = ids.reshape(-1)
+        want_counts = np.bincount(flat[valid.reshape(-1)], minlength=E)
+        assert np.array_equal(counts.cpu().numpy(), want_counts)
+        off = offsets.cpu().numpy()
+        assert off[E] == n_valid < t * k
+        srt = sorted_buf.cpu().numpy()
+        s2r = s2r_buf.cpu().numpy()
+        assert np.all(srt[t * k:] == -7) and np.all(s2r[t * k:] == -7), "write past the end"
+        order = np.argsort(np.where(valid.reshape(-1), flat, E), kind="stable")[:n_valid]
+        assert np.array_equal(srt[:n_valid], order)
+        assert np.all(s2r[:t * k][~valid.reshape(-1)] == -1)
+        assert np.array_equal(s2r[order], np.arange(n_valid))
+        # the combine makes the affected tokens NaN (loud), the others finite
+        y = torch.ones(t * k, 128, dtype=torch.bfloat16, device=DEV)
+        w = torch.full((t, k), 1.0 / k, device=DEV)
+        out = ops.combine(y, s2r_buf[:t * k].contiguous(), w).float().cpu().numpy()
+        bad_tok = ~valid.all(axis=1)
+        assert np.all(np.isnan(out[bad_tok])) and np.all(np.isfinite(out[~bad_tok]))
