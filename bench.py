@@ -9,8 +9,9 @@ the configuration the metric's HBM half is quoted on; `configs` holds, in the sa
 prefill-shaped layers the metric's MFMA half is quoted on (prefill T=4096, skewed routing T=2048,
 long prefill T=16384 with H=6144, I=2048, E=256), each timed the same way.  For every layer:
   * K forwards launched eagerly, timed between two synchronisations; the library records HIP events
-    at the stage boundaries of every step on the launch stream, which give the per-step time
-    (median, p10, p90) and the gate/up and down GEMM intervals;
+    at three stage boundaries of every step on the launch stream, which give the step period (median,
+    p10, p90 over the K-1 periods between one step's end of S3 and the next one's) and the gate/up
+    and down GEMM intervals; the per-stage breakdown comes from a separate run with all six events;
   * the roofline of the gate/up GEMM (the dominant kernel: 2/3 of weight bytes and flops) and of
     the whole layer, against the MI355X data-sheet peaks and against what this box measurably
     reaches (a streaming-read kernel of the library for HBM, the vendor dense bf16 GEMM of the same
@@ -304,24 +305,33 @@ def measure(wl, layers, steps, warmup, fmt, ops, lib, dev, copy_gbs, cpu: bool):
     torch.cuda.synchronize()
 
     hip = HipEvents()
-    evs = [[hip.create() for _ in range(6)] for _ in range(steps)]
+    # three events per timed step (after S3, after S4, after S5): the gate/up and down intervals, and
+    # the step period from one step's "after S3" to the next one's (steps run back to back)
+    evs = [[hip.create() for _ in range(3)] for _ in range(steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     log(f"{wl.name}: timing {steps} steps")
     start.record()
     for i in range(steps):
-        ops.forward(layers[i % copies], x, ws, out, stage_events=evs[i])
+        e = evs[i]
+        ops.forward(layers[i % copies], x, ws, out, stage_events=[None, None, e[0], e[1], e[2], None])
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-    step_ms = [hip.elapsed_ms(e[0], e[5]) for e in evs]
-    gate_up = [hip.elapsed_ms(e[2], e[3]) for e in evs]
-    down = [hip.elapsed_ms(e[3], e[4]) for e in evs]
-    names = ["router", "topk_permute", "gate_up", "down", "combine"]
-    stages_us = {n: float(np.mean([hip.elapsed_ms(e[i], e[i + 1]) for e in evs])) * 1e3 for i, n in enumerate(names)}
-    hip.destroy_all()
+    step_ms = [hip.elapsed_ms(evs[i][0], evs[i + 1][0]) for i in range(steps - 1)] or [total_ms / steps]
+    gate_up = [hip.elapsed_ms(e[0], e[1]) for e in evs]
+    down = [hip.elapsed_ms(e[1], e[2]) for e in evs]
     gate_up_ms = float(np.mean(gate_up))
+    # per-stage breakdown, outside the timed region: all six stage boundaries
+    bevs = [[hip.create() for _ in range(6)] for _ in range(min(steps, 50))]
+    torch.cuda.synchronize()
+    for i, e in enumerate(bevs):
+        ops.forward(layers[i % copies], x, ws, out, stage_events=e)
+    torch.cuda.synchronize()
+    names = ["router", "topk_permute", "gate_up", "down", "combine"]
+    stages_us = {n: float(np.mean([hip.elapsed_ms(e[i], e[i + 1]) for e in bevs])) * 1e3 for i, n in enumerate(names)}
+    hip.destroy_all()
 
     # the same forwards replayed from HIP graphs (one captured forward per weight copy)
     graph_ms = None
