@@ -226,6 +226,19 @@ moe_status_t moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x
                                uint16_t* out, void* workspace, size_t workspace_bytes,
                                const moe_forward_aux_t* aux, void* stream);
 
+/* The whole layer for callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, hosts that forbid hipMalloc): moe_nvfp4_forward with its workspace in a device array the
+ * library holds, MOE_NOALLOC_SCRATCH_BYTES on every GPU it runs on, until the process ends.  No
+ * allocation, no free, no memset.  A layer and T whose moe_nvfp4_forward_workspace_size exceeds
+ * the array give MOE_ERR_WORKSPACE_TOO_SMALL before anything is enqueued (64 MiB covers T up to
+ * about 580 tokens at H=4096, I=1536, E=320, k=8 with a shared expert).  All calls on one GPU share
+ * its array and it keeps the last call's contents: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must be serialised by the caller.  Arguments otherwise as for
+ * moe_nvfp4_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status_t moe_nvfp4_forward_noalloc(const moe_nvfp4_layer_t* layer, const uint16_t* x, int32_t T,
+                                       uint16_t* out, const moe_forward_aux_t* aux, void* stream);
+
 /* Pure-host validation used by moe_nvfp4_forward; needs no GPU when gfx_arch is given
  * (e.g. "gfx950"; NULL = query the current device). */
 moe_status_t moe_validate_forward(const moe_nvfp4_layer_t* layer, int32_t T, size_t workspace_bytes,

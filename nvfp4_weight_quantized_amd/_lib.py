@@ -84,7 +84,11 @@ SIGNATURES = {
     "moe_mxfp4_w4a4_forward": (i32, [ctypes.POINTER(Layer), c_void_p, i32, c_void_p, c_void_p, size_t,
                                      ctypes.POINTER(ForwardAux), c_void_p]),
     "moe_hbm_read_probe": (i32, [c_void_p, size_t, c_void_p, i32, c_void_p]),
+    "moe_nvfp4_forward_noalloc": (i32, [ctypes.POINTER(Layer), c_void_p, i32, c_void_p, ctypes.POINTER(ForwardAux),
+                                        c_void_p]),
 }
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 
 # weight formats of an expert bank (moe_nvfp4_experts_t.format)
 MOE_WEIGHT_NVFP4 = 0

@@ -88,10 +88,17 @@ ForwardLayout forward_layout(int32_t T, int32_t H, int32_t I, int32_t I_shared, 
   L.x16 = take((size_t)T * H * 2);
   L.row_shift = take((size_t)T * 4);
   // h rows (row-major, shared-expert rows right after the routed ones), or the same bytes reused
-  // for h in the fragment-tiled layout of the 128-row GEMM path (one 128-row block per m-tile)
+  // for h in the fragment-tiled layout of the 128-row GEMM path (one 128-row block per m-tile),
+  // which the forward takes exactly when its gate/up problem runs on 128-row tiles
   const size_t h_rows_bytes = align_up(S * I * 2) + align_up((size_t)T * I_shared * 2);
+  GemmProblem gu{};
+  gu.G = E;
+  gu.M = (int32_t)std::min<size_t>(S, 0x7FFFFFFF);
+  gu.has_extra = I_shared == I ? 1 : 0;
+  gu.M_extra = I_shared == I ? T : 0;
+  const bool tiled = (I_shared == 0 || I_shared == I) && moe::grouped_gemm_uses_tall_tiles(gu);
   const size_t mt_bound = std::min<size_t>((size_t)E, S) + S / 128 + ((size_t)T + 127) / 128;
-  const size_t h_tiled_bytes = I_shared == 0 || I_shared == I ? mt_bound * 128 * (size_t)I * 2 : 0;
+  const size_t h_tiled_bytes = tiled ? mt_bound * 128 * (size_t)I * 2 : 0;
   L.h = take(std::max(h_rows_bytes, h_tiled_bytes));
   L.h_shared = L.h + align_up(S * I * 2);
   L.y = take((S + (I_shared > 0 ? (size_t)T : 0)) * H * 2);

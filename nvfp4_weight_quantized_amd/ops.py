@@ -517,3 +517,26 @@ def quantize_mx(w: torch.Tensor, packed: Optional[torch.Tensor] = None, scales: 
     L.check("moe_mxfp4_quantize", L.lib().moe_mxfp4_quantize(_ptr(w), nt, rows, cols, _ptr(packed), _ptr(scales),
                                                              _stream(w.device)))
     return packed, scales
+
+
+def forward_noalloc(layer: NvFp4MoELayer, x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The whole layer through moe_nvfp4_forward_noalloc: no workspace argument (the library's own
+    device array of ``_lib.NOALLOC_SCRATCH_BYTES``), for callers that cannot allocate.  Calls that
+    overlap in time on one GPU race."""
+    _need(x, "x", torch.bfloat16, 2)
+    st = layer.checked_struct()
+    if layer.is_w4a4:
+        raise ValueError("the allocation-free entry point runs the W4A16 layer")
+    if x.shape[1] != layer.hidden:
+        raise ValueError(f"x: expected {layer.hidden} columns, got {x.shape[1]}")
+    _same_device(x, ("w_router", layer.w_router))
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _need(out, "out", torch.bfloat16, 2)
+        _shape(out, "out", x.shape)
+        _same_device(x, ("out", out))
+    L.check("moe_nvfp4_forward_noalloc",
+            L.lib().moe_nvfp4_forward_noalloc(ctypes.byref(st), _ptr(x), x.shape[0], _ptr(out), None,
+                                              _stream(x.device)))
+    return out
