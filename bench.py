@@ -289,8 +289,12 @@ def cpu_baseline(wl, x_bits, wr_bits, synth, fmt="nvfp4", n_experts=4, token_blo
 
 # ----------------------------------------------------------------------------- one workload
 
-def measure(wl, layers, steps, warmup, fmt, ops, lib, dev, copy_gbs, cpu: bool):
+def measure(wl, layers, steps, warmup, fmt, ops_mod, lib, dev, copy_gbs, cpu: bool, fused_decode: bool = False):
     """Time one workload; returns its record (the fields of a bench line)."""
+    import functools
+    import types
+    ops = types.SimpleNamespace(forward=functools.partial(ops_mod.forward, fused_decode=fused_decode),
+                                workspace_for=ops_mod.workspace_for)
     w4a4 = fmt == "mxfp4_a4"
     layer = layers[0]
     copies = len(layers)
@@ -305,9 +309,10 @@ def measure(wl, layers, steps, warmup, fmt, ops, lib, dev, copy_gbs, cpu: bool):
     torch.cuda.synchronize()
 
     hip = HipEvents()
-    # three events per timed step (after S3, after S4, after S5): the gate/up and down intervals, and
-    # the step period from one step's "after S3" to the next one's (steps run back to back)
-    evs = [[hip.create() for _ in range(3)] for _ in range(steps)]
+    # four events per timed step (after S1, after S2+S3, after S4, after S5): the gate/up and down
+    # intervals (staged launches) or the fused S2-S6 launch (few tokens: events 2-4 are recorded
+    # after it), and the step period from one step's "after S1" to the next one's
+    evs = [[hip.create() for _ in range(4)] for _ in range(steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -315,22 +320,29 @@ def measure(wl, layers, steps, warmup, fmt, ops, lib, dev, copy_gbs, cpu: bool):
     start.record()
     for i in range(steps):
         e = evs[i]
-        ops.forward(layers[i % copies], x, ws, out, stage_events=[None, None, e[0], e[1], e[2], None])
+        ops.forward(layers[i % copies], x, ws, out, stage_events=[None, e[0], e[1], e[2], e[3], None])
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     step_ms = [hip.elapsed_ms(evs[i][0], evs[i + 1][0]) for i in range(steps - 1)] or [total_ms / steps]
-    gate_up = [hip.elapsed_ms(e[0], e[1]) for e in evs]
-    down = [hip.elapsed_ms(e[1], e[2]) for e in evs]
-    gate_up_ms = float(np.mean(gate_up))
+    gate_up = [hip.elapsed_ms(e[1], e[2]) for e in evs]
+    down = [hip.elapsed_ms(e[2], e[3]) for e in evs]
+    fused_k = [hip.elapsed_ms(e[0], e[3]) for e in evs]
+    # the library runs the fused launch on request for few tokens (NVFP4, T <= 32, T*k <= 256, E <= 320)
+    fused = (fused_decode and fmt == "nvfp4" and wl.T <= 32 and wl.T * wl.k <= 256 and wl.E <= 320
+             and wl.I_shared in (0, wl.I))
+    kernel = fused_k if fused else gate_up
+    kernel_ms = float(np.mean(kernel))
     # per-stage breakdown, outside the timed region: all six stage boundaries
     bevs = [[hip.create() for _ in range(6)] for _ in range(min(steps, 50))]
     torch.cuda.synchronize()
     for i, e in enumerate(bevs):
         ops.forward(layers[i % copies], x, ws, out, stage_events=e)
     torch.cuda.synchronize()
-    names = ["router", "topk_permute", "gate_up", "down", "combine"]
-    stages_us = {n: float(np.mean([hip.elapsed_ms(e[i], e[i + 1]) for e in bevs])) * 1e3 for i, n in enumerate(names)}
+    names = (["router", "fused_topk_permute_gemms_combine", None, None, None] if fused
+             else ["router", "topk_permute", "gate_up", "down", "combine"])
+    stages_us = {n: float(np.mean([hip.elapsed_ms(e[i], e[i + 1]) for e in bevs])) * 1e3
+                 for i, n in enumerate(names) if n}
     hip.destroy_all()
 
     # the same forwards replayed from HIP graphs (one captured forward per weight copy)
@@ -370,18 +382,22 @@ def measure(wl, layers, steps, warmup, fmt, ops, lib, dev, copy_gbs, cpu: bool):
     n_banks = touched + (1 if wl.I_shared > 0 else 0)
     # activations in: bf16 x (W4A16); for W4A4 the x read by its quantizer plus the 4-bit copy
     x_bytes = T * H * 2 + (T * H * bpw * 2 if w4a4 else 0)
-    gu_bytes = n_banks * 2 * I * H * bpw + x_bytes + (S + T) * I * 2
-    gu_flops = 2.0 * (S + T) * H * 2 * I
+    if fused:   # the fused S2-S6 launch: every expert weight, x in and the output out
+        gu_bytes = n_banks * 3 * I * H * bpw + 2 * T * H * 2
+        gu_flops = 2.0 * (S + T) * 3 * H * I
+    else:
+        gu_bytes = n_banks * 2 * I * H * bpw + x_bytes + (S + T) * I * 2
+        gu_flops = 2.0 * (S + T) * H * 2 * I
     mfma_peak = FP4_PEAK_TFLOPS if w4a4 else BF16_PEAK_TFLOPS
     if w4a4:   # bound by the algorithmic intensity against the fp4 ridge point
         hbm_bound = gu_bytes / (HBM_PEAK_GBS * 1e9) >= gu_flops / (mfma_peak * 1e12)
     else:
         hbm_bound = wl.name in ("tiny", "decode")
     if hbm_bound:
-        roof = {"bound": "hbm", "achieved": gu_bytes / (gate_up_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+        roof = {"bound": "hbm", "achieved": gu_bytes / (kernel_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": gu_flops / (gate_up_ms * 1e-3) / 1e12, "peak": mfma_peak,
+        roof = {"bound": "mfma", "achieved": gu_flops / (kernel_ms * 1e-3) / 1e12, "peak": mfma_peak,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     if roof["bound"] == "hbm":
@@ -391,14 +407,17 @@ def measure(wl, layers, steps, warmup, fmt, ops, lib, dev, copy_gbs, cpu: bool):
         roof["peak_measured"] = None if w4a4 else dense_bf16_tflops(wl, dev)
         roof["peak_measured_source"] = "dense bf16 GEMM of the gate/up shape via torch.mm (hipBLASLt)"
     roof["frac_of_measured"] = (roof["achieved"] / roof["peak_measured"]) if roof["peak_measured"] else None
-    roof["traffic"] = gate_up_traffic(wl.name) if fmt == "nvfp4" else None
+    roof["traffic"] = gate_up_traffic(wl.name) if (fmt == "nvfp4" and not fused) else None
     roof["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)"
     roof["algorithmic_bytes"] = gu_bytes
     roof["algorithmic_flops"] = gu_flops
-    roof["kernel"] = ("gate/up stage (S4): x to MXFP4 + W4A4 grouped GEMM" if w4a4
-                      else "gate/up stage (S4): grouped GEMM" + ("" if hbm_bound else " (+ fp16 row pass)"))
-    roof["kernel_us"] = gate_up_ms * 1e3
-    roof["kernel_us_median"] = float(np.median(gate_up)) * 1e3
+    if fused:
+        roof["kernel"] = "fused decode kernel (S2-S6: top-k, permutation, gate/up, down, combine)"
+    else:
+        roof["kernel"] = ("gate/up stage (S4): x to MXFP4 + W4A4 grouped GEMM" if w4a4
+                          else "gate/up stage (S4): grouped GEMM" + ("" if hbm_bound else " (+ fp16 row pass)"))
+    roof["kernel_us"] = kernel_ms * 1e3
+    roof["kernel_us_median"] = float(np.median(kernel)) * 1e3
 
     # whole layer: flops 2(S+T)*3HI + 2THE (MFMA-bound shapes) or the bytes of every touched
     # expert, the shared expert, the router weight and the activations (HBM-bound shapes)
@@ -435,8 +454,9 @@ def measure(wl, layers, steps, warmup, fmt, ops, lib, dev, copy_gbs, cpu: bool):
         "layer_roofline": layer_roof,
         "graph_replay_ms_per_step": graph_ms,
         "stages_us": stages_us,
-        "timed_stages_us": {"gate_up": percentiles([v * 1e3 for v in gate_up]),
-                            "down": percentiles([v * 1e3 for v in down])},
+        "timed_stages_us": ({"fused_S2_S6": percentiles([v * 1e3 for v in fused_k])} if fused else
+                            {"gate_up": percentiles([v * 1e3 for v in gate_up]),
+                             "down": percentiles([v * 1e3 for v in down])}),
         "cpu_baseline": cpu_rec,
     }
 
@@ -456,6 +476,8 @@ def main():
                          "decode workload: prefill,skewed,long_prefill; 'none' for none)")
     ap.add_argument("--copies", type=int, default=None, help="weight copies cycled through (main workload)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
+    ap.add_argument("--fused-decode", action="store_true",
+                    help="run few-token forwards on the two-launch fused decode path (opt-in; slower on MI355X)")
     ap.add_argument("--format", default="nvfp4", choices=["nvfp4", "mxfp4", "mxfp4_a4"],
                     help="weight format of the synthetic experts (the headline metric is NVFP4); mxfp4_a4: "
                          "the W4A4 layer (MXFP4 weights and activations on the FP4 matrix cores)")
@@ -506,7 +528,8 @@ def main():
         warmup = args.warmup if args.warmup is not None else d_warmup
         copies = (args.copies if args.copies is not None else d_copies) if main_line else d_copies
         layers = layer_for(wl, copies)
-        rec = measure(wl, layers, steps, warmup, args.format, ops, lib, dev, copy_gbs, not args.no_cpu)
+        rec = measure(wl, layers, steps, warmup, args.format, ops, lib, dev, copy_gbs, not args.no_cpu,
+                      args.fused_decode)
         del layers
         torch.cuda.empty_cache()
         return rec

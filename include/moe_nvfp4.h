@@ -199,8 +199,23 @@ moe_status_t moe_combine(const uint16_t* y_rows, const int32_t* slot_to_row, con
  * y_rows (device, bf16 [T*k + T_shared][H], T_shared = T with a shared expert, else 0): when given,
  * the expert outputs of S5 are written there instead of the workspace -- row r < T*k is the routed
  * expert output of sorted row r (slot sorted_slot[r] of the permutation), row T*k + t the shared
- * expert's output for token t -- the inputs of the combine, for callers that check the stages. */
+ * expert's output for token t -- the inputs of the combine, for callers that check the stages.
+ * flags: MOE_FORWARD_FUSED_DECODE runs the two-launch fused decode path below where it applies
+ * (elsewhere the flag is ignored); both paths compute bitwise the same output.
+ *
+ * Fused decode path (opt-in): with few tokens (T <= 32, T*k <= 256, E <= 320, NVFP4 banks, a shared
+ * expert of the routed width or none, at most 8 rows per expert on average) the forward is two
+ * launches: the router, then S2-S6 in one kernel whose workgroups hand work on through counters in
+ * the workspace (cleared by the router launch; every wait points at a workgroup of smaller index and
+ * is bounded: past the bound the output rows are NaN).  Its stage events 2, 3 and 4 are recorded
+ * after that second launch, with event 5.  On MI355X it is slower than the staged launches (the
+ * completion counters of the gate/up tiles become visible to the waiting down tiles tens of
+ * microseconds late while the weights stream at full bandwidth), so it is not the default.  Source:
+ * the fused MoE kernel (token dispatch, two GEMMs, SwiGLU, top-k-weight reduction in one launch;
+ * "vLLM on the NVIDIA DGX Spark", section 4) and the separate small-batch micro path ("Serving Solar
+ * Open 2 on DGX Spark", "Adding Expert Parallelism to b12x"). */
 #define MOE_NUM_STAGE_EVENTS 6
+#define MOE_FORWARD_FUSED_DECODE 1u
 typedef struct {
   float* logits;
   int32_t* topk_ids;
@@ -208,6 +223,7 @@ typedef struct {
   int32_t* expert_counts;
   void* const* stage_events;
   uint16_t* y_rows;
+  uint32_t flags;
 } moe_forward_aux_t;
 
 /* Workspace bytes moe_nvfp4_forward needs for T tokens (I_shared = 0: no shared expert).  It holds

@@ -49,7 +49,10 @@ class Layer(ctypes.Structure):
 class ForwardAux(ctypes.Structure):
     """moe_forward_aux_t"""
     _fields_ = [("logits", c_void_p), ("topk_ids", c_void_p), ("topk_w", c_void_p), ("expert_counts", c_void_p),
-                ("stage_events", ctypes.POINTER(c_void_p)), ("y_rows", c_void_p)]
+                ("stage_events", ctypes.POINTER(c_void_p)), ("y_rows", c_void_p), ("flags", u32)]
+
+
+MOE_FORWARD_FUSED_DECODE = 1
 
 
 NUM_STAGE_EVENTS = 6

@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_nvfp4.so")
-SOURCES = ["api.cpp", "route.hip", "permute.hip", "grouped_gemm.hip", "grouped_gemm_a4.hip", "combine.hip", "quantize.hip", "layout.hip", "probe.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "route.hip", "permute.hip", "grouped_gemm.hip", "grouped_gemm_a4.hip", "combine.hip", "quantize.hip", "layout.hip", "probe.hip", "noalloc.hip", "micro.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

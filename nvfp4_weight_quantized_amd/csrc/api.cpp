@@ -63,7 +63,8 @@ GemmBank bank_w13(const moe_nvfp4_experts_t& b) { return GemmBank{b.w13, b.w13_s
 GemmBank bank_w2(const moe_nvfp4_experts_t& b) { return GemmBank{b.w2, b.w2_scale, b.w2_gscale, 1, b.format}; }
 
 struct ForwardLayout {
-  size_t logits, ids, w, counts, offsets, sorted_slot, slot_to_row, block_hist, x16, row_shift, h, h_shared, y;
+  size_t logits, ids, w, counts, offsets, sorted_slot, slot_to_row, block_hist, x16, row_shift, h, h_shared, y,
+      ctr;
   size_t total;
 };
 
@@ -102,6 +103,10 @@ ForwardLayout forward_layout(int32_t T, int32_t H, int32_t I, int32_t I_shared, 
   L.h = take(std::max(h_rows_bytes, h_tiled_bytes));
   L.h_shared = L.h + align_up(S * I * 2);
   L.y = take((S + (I_shared > 0 ? (size_t)T : 0)) * H * 2);
+  // hand-off counters of the fused decode launch (few tokens only)
+  L.ctr = take(T <= moe::kFusedDecodeMaxTokens && S <= (size_t)moe::kFusedDecodeMaxSlots
+                   ? (size_t)moe::fused_decode_counter_words(T, k, E, I_shared > 0) * 4
+                   : 0);
   L.total = off;
   return L;
 }
@@ -351,8 +356,6 @@ moe_status_t moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x
 
   moe_status_t st = mark(0);
   if (st) return st;
-  st = run_routing(layer, x, T, logits, ids, w, counts, offsets, sorted_slot, slot_to_row, block_hist, mark, stream);
-  if (st) return st;
 
   // S4: routed rows gathered through sorted_slot; the shared expert rides in the same launch when
   // its width matches, otherwise it gets a launch of its own.
@@ -376,6 +379,59 @@ moe_status_t moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x
     gu.M_extra = T;
     gu.a_extra = x;
   }
+  // S5 on the same rows (the shared expert's h rows follow the routed ones)
+  GemmProblem dn{};
+  dn.stage = MOE_GEMM_DOWN;
+  dn.N = H;
+  dn.K = I;
+  dn.bank = bank_w2(layer->routed);
+  dn.offsets = offsets;
+  dn.G = E;
+  dn.M = S;
+  dn.a = h;
+  dn.row_index = nullptr;
+  dn.row_divisor = 1;
+  dn.out = y;
+  if (fuse_shared) {
+    dn.has_extra = 1;
+    dn.extra = bank_w2(layer->shared);
+    dn.M_extra = T;
+    dn.a_extra = h + (size_t)S * I;
+  }
+
+  // Few tokens, on request: two launches -- the router (which also clears the hand-off counters),
+  // then S2-S6 fused (micro.hip).  Same tiles and arithmetic as the staged launches below.
+  const bool fused = aux && (aux->flags & MOE_FORWARD_FUSED_DECODE);
+  if (fused && (fuse_shared || !has_shared) && moe::fused_decode_applies(gu, T, k)) {
+    int32_t* ctr = at<int32_t>(workspace, L.ctr);
+    const int n_ctr = moe::fused_decode_counter_words(T, k, E, fuse_shared);
+    st = moe::launch_router_logits(x, layer->w_router, layer->router_bias, T, H, E, logits, stream, ctr, n_ctr);
+    if (st || (st = mark(1))) return st;
+    moe::FusedDecodeProblem fp{};
+    fp.gu = gu;
+    fp.dn = dn;
+    fp.logits = logits;
+    fp.T = T;
+    fp.E = E;
+    fp.k = k;
+    fp.H = H;
+    fp.ids = ids;
+    fp.w = w;
+    fp.counts = counts;
+    fp.offsets = offsets;
+    fp.sorted_slot = sorted_slot;
+    fp.slot_to_row = slot_to_row;
+    fp.out = out;
+    fp.ctr = ctr;
+    if ((st = moe::launch_fused_decode(fp, stream))) return st;
+    for (int i = 2; i <= 5; ++i)
+      if ((st = mark(i))) return st;
+    return MOE_OK;
+  }
+
+  st = run_routing(layer, x, T, logits, ids, w, counts, offsets, sorted_slot, slot_to_row, block_hist, mark, stream);
+  if (st) return st;
+
   // 128-row tiles for both GEMMs (and one m-tile numbering): h goes through the fragment-tiled
   // layout, so the down GEMM's A tiles are contiguous 1 KB loads
   const bool tiled = (fuse_shared || !has_shared) && moe::grouped_gemm_uses_tall_tiles(gu);
@@ -407,24 +463,6 @@ moe_status_t moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x
   if ((st = mark(3))) return st;
 
   // S5
-  GemmProblem dn{};
-  dn.stage = MOE_GEMM_DOWN;
-  dn.N = H;
-  dn.K = I;
-  dn.bank = bank_w2(layer->routed);
-  dn.offsets = offsets;
-  dn.G = E;
-  dn.M = S;
-  dn.a = h;
-  dn.row_index = nullptr;
-  dn.row_divisor = 1;
-  dn.out = y;
-  if (fuse_shared) {
-    dn.has_extra = 1;
-    dn.extra = bank_w2(layer->shared);
-    dn.M_extra = T;
-    dn.a_extra = h + (size_t)S * I;
-  }
   dn.a_tiled = tiled ? 1 : 0;
   if ((st = moe::launch_grouped_gemm(dn, stream))) return st;
   if (has_shared && !fuse_shared) {

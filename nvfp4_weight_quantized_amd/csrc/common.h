@@ -63,8 +63,12 @@ moe_status_t launch_topk_permute_small(const float* logits, int32_t T, int32_t E
                                        int32_t* slot_to_row, hipStream_t stream);
 
 // Route -------------------------------------------------------------------------------------
+// T <= kRouterSmallTokens runs the one-pass few-token kernel, which can also clear `zero` [n_zero]
+// (given only then).
+constexpr int kRouterSmallTokens = 32;
 moe_status_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, const float* bias, int32_t T,
-                                  int32_t H, int32_t E, float* logits, hipStream_t stream);
+                                  int32_t H, int32_t E, float* logits, hipStream_t stream, int32_t* zero = nullptr,
+                                  int32_t n_zero = 0);
 moe_status_t launch_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int32_t T,
                           int32_t H, int32_t E, int32_t k, bool logits_given, float* logits,
                           int32_t* ids, float* w, hipStream_t stream);
@@ -124,6 +128,9 @@ inline long long tall_mtiles_bound(const GemmProblem& p) {
 // writes the tiled layouts).
 bool grouped_gemm_uses_tall_tiles(const GemmProblem& p);
 
+// True if launch_grouped_gemm runs this problem on the skinny (8-row) tiles.
+bool grouped_gemm_uses_skinny_tiles(const GemmProblem& p);
+
 moe_status_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream);
 // x16[t][h] = fp16(x[t][h] * 2^shift[t]) with shift[t] = 14 - floor(log2(max_h |x[t][h]|)) (0 for a
 // row of zeros or with a non-finite value): exact for every element within 2^31 of its row's
@@ -158,6 +165,33 @@ struct GemmProblemA4 {
 };
 
 moe_status_t launch_grouped_gemm_a4(const GemmProblemA4& p, hipStream_t stream);
+
+// Fused decode path --------------------------------------------------------------------------
+// S2..S6 of a few-token forward in one launch (micro.hip): top-k + permutation, gate/up, down and
+// combine on the skinny tiles, handed from workgroup to workgroup through counters in the
+// workspace that the router launch of the same forward clears.
+struct FusedDecodeProblem {
+  GemmProblem gu;          // gate/up: routed bank (+ shared expert as the extra group), h row-major
+  GemmProblem dn;          // down: y row-major, the shared rows after the routed ones
+  const float* logits;     // [T][E], from the router launch
+  int32_t T, E, k, H;
+  int32_t* ids;            // [T][k]
+  float* w;                // [T][k]
+  int32_t* counts;         // [E]
+  int32_t* offsets;        // [E + 1] (also gu.offsets / dn.offsets)
+  int32_t* sorted_slot;    // [T*k]   (also gu.row_index)
+  int32_t* slot_to_row;    // [T*k]
+  uint16_t* out;           // [T][H]
+  int32_t* ctr;            // fused_decode_counter_words(...) words, zero on entry
+};
+constexpr int kFusedDecodeMaxTokens = 32;
+constexpr int kFusedDecodeMaxSlots = 256;
+constexpr int kFusedDecodeMaxExperts = 320;
+// Words of the counter block (ticket, flags, one counter per m-tile).
+int fused_decode_counter_words(int32_t T, int32_t k, int32_t E, bool shared);
+// True if the fused launch can run this forward (few tokens, NVFP4, skinny tiles for both GEMMs).
+bool fused_decode_applies(const GemmProblem& gu, int32_t T, int32_t k);
+moe_status_t launch_fused_decode(const FusedDecodeProblem& p, hipStream_t stream);
 
 // Combine -----------------------------------------------------------------------------------
 moe_status_t launch_combine(const uint16_t* y_rows, const int32_t* slot_to_row, const float* w,

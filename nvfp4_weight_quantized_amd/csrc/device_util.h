@@ -68,22 +68,30 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
   return x;
 }
 
-// Top-k of one token's logits by one wavefront (E <= 64 * VPL, k <= 64).  Returns, in lane j < k,
-// the j-th selected expert and its renormalised softmax weight.  Equal logits -> lower index
-// first; NaN ranks lowest.
+// This lane's logits of one token (experts lane, lane + 64, ...), as topk_select takes them.
+template <int VPL>
+__device__ __forceinline__ void topk_load(const float* __restrict__ row, int E, float (&v)[VPL]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) v[i] = row[min(lane + 64 * i, E - 1)];
+}
+
+// Top-k of one token's logits by one wavefront (E <= 64 * VPL, k <= 64), from the values topk_load
+// gave this lane.  Returns, in lane j < k, the j-th selected expert and its renormalised softmax
+// weight.  Equal logits -> lower index first; NaN ranks lowest.
 // Lane l holds the logits of experts l, l + 64, ..., sorted descending (ties keep expert order);
 // each of the k rounds takes the wave-wide maximum of the lanes' heads (as order keys) and, when
 // several heads equal it, the lowest expert index among them; the winning lane (expert index
 // mod 64) drops its head.
 template <int VPL>
-__device__ __forceinline__ void topk_token(const float* __restrict__ row, int E, int k, int* out_id, float* out_w) {
+__device__ __forceinline__ void topk_select(const float (&raw)[VPL], int E, int k, int* out_id, float* out_w) {
   const int lane = threadIdx.x & 63;
   float v[VPL];
   int vi[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + 64 * i;
-    const float val = row[min(e, E - 1)];
+    const float val = raw[i];
     v[i] = (e < E && val == val) ? val : -INFINITY;
     vi[i] = e;
   }
@@ -128,6 +136,14 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E,
   const float s = wave_sum(z);
   *out_id = my_id;
   *out_w = z / s;
+}
+
+// Top-k of one token's logits row (topk_load, then topk_select).
+template <int VPL>
+__device__ __forceinline__ void topk_token(const float* __restrict__ row, int E, int k, int* out_id, float* out_w) {
+  float raw[VPL];
+  topk_load<VPL>(row, E, raw);
+  topk_select<VPL>(raw, E, k, out_id, out_w);
 }
 
 // Calls f(IntC-like tag) with the smallest supported logits-per-lane count covering E (<= 1024).

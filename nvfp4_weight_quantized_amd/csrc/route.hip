@@ -15,18 +15,23 @@
 namespace moe {
 namespace {
 
-constexpr int kGemvMaxTokens = 32;
+constexpr int kGemvMaxTokens = kRouterSmallTokens;
 constexpr int kGemvTokens = 8;     // tokens per workgroup
 
 // Few tokens: one workgroup per (expert, group of up to 8 tokens).  Each thread takes 8
 // consecutive h of the expert's router row per 2048-wide pass and dots them with the same h of
 // every token, all loads of a pass issued together; the per-token sums are then reduced across
 // the workgroup (wave sums, then the four waves in order).
+// `zero` (optional): n_zero words the first workgroup clears (the hand-off counters of the fused
+// decode kernel that follows in the same stream).
 __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ wr,
                                                            const float* __restrict__ bias, int T, int H, int E,
-                                                           float* __restrict__ logits) {
+                                                           float* __restrict__ logits, int32_t* __restrict__ zero,
+                                                           int n_zero) {
   __shared__ float part[4][kGemvTokens];
+  if (zero && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < n_zero; i += 256) zero[i] = 0;
   const int e = blockIdx.x;
   const int t0 = blockIdx.y * kGemvTokens;
   const int tn = min(kGemvTokens, T - t0);
@@ -185,12 +190,14 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 }  // namespace
 
 moe_status_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, const float* bias, int32_t T,
-                                  int32_t H, int32_t E, float* logits, hipStream_t stream) {
+                                  int32_t H, int32_t E, float* logits, hipStream_t stream, int32_t* zero,
+                                  int32_t n_zero) {
   if (T == 0) return MOE_OK;
   if (T <= kGemvMaxTokens) {
     hipLaunchKernelGGL(router_small_kernel, dim3(E, (T + kGemvTokens - 1) / kGemvTokens), dim3(256), 0, stream, x,
-                       w_router, bias, (int)T, (int)H, (int)E, logits);
+                       w_router, bias, (int)T, (int)H, (int)E, logits, zero, (int)n_zero);
   } else {
+    if (zero) return MOE_ERR_INVALID_ARGUMENT;   // the clearing rides on the few-token kernel only
     if (H % kRK != 0) return MOE_ERR_INVALID_ARGUMENT;
     const long long tiles = (long long)((E + kRB - 1) / kRB) * ((T + kRB - 1) / kRB);
     const long long grid = (tiles + kRXcds - 1) / kRXcds * kRXcds;

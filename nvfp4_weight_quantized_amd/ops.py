@@ -390,13 +390,14 @@ def workspace_for(layer: NvFp4MoELayer, T: int, device) -> torch.Tensor:
 
 def forward(layer: NvFp4MoELayer, x: torch.Tensor, workspace: Optional[torch.Tensor] = None,
             out: Optional[torch.Tensor] = None, return_aux: bool = False, stage_events=None,
-            return_rows: bool = False):
+            return_rows: bool = False, fused_decode: bool = False):
     """The whole layer on x [T, H] bf16 -> [T, H] bf16 (and, if asked, logits/ids/weights/counts).
 
     Runs moe_nvfp4_forward, or moe_mxfp4_w4a4_forward when the layer's banks are "mxfp4_a4".
     ``return_rows`` (with ``return_aux``): the aux dict also holds "y_rows", the expert outputs the
     combine reads (bf16 [T*k + T_shared, H], routed rows in expert-sorted order, then the shared
     expert's row of every token).
+    ``fused_decode``: run the two-launch fused decode path where it applies (few tokens).
 
     ``stage_events``: optional sequence of 6 raw hipEvent_t handles (ints or None) recorded at the
     stage boundaries (before S1, after S1, after S2+S3, after S4, S5, S6) on the current stream.
@@ -419,8 +420,9 @@ def forward(layer: NvFp4MoELayer, x: torch.Tensor, workspace: Optional[torch.Ten
         _same_device(x, ("out", out))
     aux = None
     aux_t = None
-    if return_aux or stage_events is not None:
+    if return_aux or stage_events is not None or fused_decode:
         aux = L.ForwardAux()
+        aux.flags = L.MOE_FORWARD_FUSED_DECODE if fused_decode else 0
     if return_aux:
         e, k = layer.num_experts, layer.top_k
         aux_t = dict(logits=torch.empty(t, e, dtype=torch.float32, device=x.device),

@@ -370,3 +370,75 @@ def test_full_size_workload(name):
     parity.assert_close(parity.f64(h[r0:r1]), h_ref, f"staged gate/up rows of expert {e_max}")
     del h, y, hs, ys, staged, y_gpu
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------- fused decode path
+
+FUSED = [
+    # T, H, I, E, k, shared, bias: few tokens, where the forward runs as two launches
+    (8, 256, 128, 16, 4, True, False),
+    (1, 512, 256, 64, 8, True, True),
+    (32, 256, 128, 320, 8, True, False),     # T*k = 256 slots, E = 320
+    (5, 384, 256, 12, 3, False, True),       # no shared expert
+    (16, 256, 128, 8, 2, True, False),       # the tiny workload's shape
+    (3, 512, 384, 40, 40, True, False),      # k = E
+    (4, 384, 128, 16, 2, True, False),       # 128-wide K chunks in both GEMMs
+]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=[f"T{c[0]}_H{c[1]}_I{c[2]}_E{c[3]}_k{c[4]}" for c in FUSED])
+def test_fused_decode_path_equals_staged_launches_and_the_oracle(case):
+    """The two-launch fused decode path (router, then top-k + permutation + both GEMMs + combine in
+    one kernel with counter hand-offs) gives bitwise the output, selection, counts and expert rows of
+    the staged launches, matches the oracle, and repeats bitwise."""
+    T, H, I, E, k, shared, bias = case
+    rng = np.random.default_rng(sum(case[:5]) + 99)
+    layer = helpers.random_layer(rng, H, I, E, k, shared=shared, bias=bias)
+    x = helpers.random_x(rng, T, H)
+    glayer = parity.to_gpu_layer(layer)
+    xg = parity.bits_to_bf16(x)
+    out_f, aux_f = ops.forward(glayer, xg, return_aux=True, return_rows=True, fused_decode=True)
+    out_s, aux_s = ops.forward(glayer, xg, return_aux=True, return_rows=True)
+    torch.cuda.synchronize()
+    for key in ("logits", "topk_ids", "topk_w", "expert_counts", "y_rows"):
+        assert torch.equal(aux_f[key], aux_s[key]), key
+    assert torch.equal(out_f, out_s), "fused decode path differs from the staged launches"
+    assert not torch.isnan(out_f.float()).any()
+    ids = aux_f["topk_ids"].cpu().numpy()
+    parity.check_route(aux_f["logits"], aux_f["topk_ids"], aux_f["topk_w"], x, layer.w_router, layer.router_bias, k)
+    res = parity.reference_for_selection(x, layer, ids)
+    parity.assert_close(parity.f64(out_f), res["out"], "fused decode path")
+    for _ in range(3):
+        assert torch.equal(ops.forward(glayer, xg, fused_decode=True), out_f), "repeated fused forward differs"
+
+
+def test_fused_decode_path_replays_from_a_hip_graph_with_other_work_between():
+    """Both launches of the fused decode path captured in a HIP graph: its hand-off counters are
+    cleared by the captured router launch, so every replay, with eager forwards of other sizes on the
+    same workspace between replays, equals the eager output."""
+    rng = np.random.default_rng(21)
+    T, H, I, E, k = 8, 512, 256, 64, 8
+    layer = helpers.random_layer(rng, H, I, E, k, bias=True)
+    glayer = parity.to_gpu_layer(layer)
+    x = parity.bits_to_bf16(helpers.random_x(rng, T, H))
+    x2 = parity.bits_to_bf16(helpers.random_x(rng, 24, H))
+    ws = ops.workspace_for(glayer, 24, DEV)
+    ref = ops.forward(glayer, x, ws).clone()
+    ref2 = ops.forward(glayer, x2, ws).clone()
+    out = torch.empty_like(x)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ops.forward(glayer, x, ws, out, fused_decode=True)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ops.forward(glayer, x, ws, out, fused_decode=True)
+    for r in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {r} differs from the eager forward"
+        assert torch.equal(ops.forward(glayer, x2, ws, fused_decode=True), ref2)
+        torch.cuda.synchronize()
