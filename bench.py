@@ -8,10 +8,11 @@ The JSON line's top level is the decode-shaped layer (T=8, H=4096, I=1536, E=320
 the configuration the metric's HBM half is quoted on; `configs` holds, in the same line, the
 prefill-shaped layers the metric's MFMA half is quoted on (prefill T=4096, skewed routing T=2048,
 long prefill T=16384 with H=6144, I=2048, E=256), each timed the same way.  For every layer:
-  * K forwards launched eagerly, timed between two synchronisations; the library records HIP events
-    at three stage boundaries of every step on the launch stream, which give the step period (median,
-    p10, p90 over the K-1 periods between one step's end of S3 and the next one's) and the gate/up
-    and down GEMM intervals; the per-stage breakdown comes from a separate run with all six events;
+  * K forwards launched eagerly, timed between two synchronisations with nothing else in between
+    (the value and ms_per_step); then the same K forwards with one HIP event per step (the step
+    periods: median, p10, p90), and again with events at the stage boundaries, which the library
+    records on its launch stream (the gate/up and down GEMM intervals of the roofline); the
+    per-stage breakdown comes from a run with all six events;
   * the roofline of the gate/up GEMM (the dominant kernel: 2/3 of weight bytes and flops) and of
     the whole layer, against the MI355X data-sheet peaks and against what this box measurably
     reaches (a streaming-read kernel of the library for HBM, the vendor dense bf16 GEMM of the same
@@ -309,22 +310,33 @@ def measure(wl, layers, steps, warmup, fmt, ops_mod, lib, dev, copy_gbs, cpu: bo
     torch.cuda.synchronize()
 
     hip = HipEvents()
-    # four events per timed step (after S1, after S2+S3, after S4, after S5): the gate/up and down
-    # intervals (staged launches) or the fused S2-S6 launch (few tokens: events 2-4 are recorded
-    # after it), and the step period from one step's "after S1" to the next one's
-    evs = [[hip.create() for _ in range(4)] for _ in range(steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    # (1) the K timed steps, nothing but the forwards between the two synchronisations
     torch.cuda.synchronize()
     log(f"{wl.name}: timing {steps} steps")
     start.record()
     for i in range(steps):
-        e = evs[i]
-        ops.forward(layers[i % copies], x, ws, out, stage_events=[None, e[0], e[1], e[2], e[3], None])
+        ops.forward(layers[i % copies], x, ws, out)
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-    step_ms = [hip.elapsed_ms(evs[i][0], evs[i + 1][0]) for i in range(steps - 1)] or [total_ms / steps]
+    # (2) the same K steps with one event per step (before S1): the step periods, for the spread
+    pev = [hip.create() for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ops.forward(layers[i % copies], x, ws, out, stage_events=[pev[i], None, None, None, None, None])
+    ops.forward(layers[steps % copies], x, ws, out, stage_events=[pev[steps], None, None, None, None, None])
+    torch.cuda.synchronize()
+    step_ms = [hip.elapsed_ms(pev[i], pev[i + 1]) for i in range(steps)]
+    # (3) the same K steps with events at the stage boundaries after S1, S3, S4 and S5 (HIP events on
+    # the launch stream): the gate/up and down intervals (staged launches) or the fused S2-S6 launch
+    evs = [[hip.create() for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        e = evs[i]
+        ops.forward(layers[i % copies], x, ws, out, stage_events=[None, e[0], e[1], e[2], e[3], None])
+    torch.cuda.synchronize()
     gate_up = [hip.elapsed_ms(e[1], e[2]) for e in evs]
     down = [hip.elapsed_ms(e[2], e[3]) for e in evs]
     fused_k = [hip.elapsed_ms(e[0], e[3]) for e in evs]
