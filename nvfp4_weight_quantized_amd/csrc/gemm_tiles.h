@@ -126,10 +126,12 @@ __device__ __forceinline__ int frag_row_block(int f, int ntile, int wave, int N)
 // GSCALE: the bank carries fp32 global scales (NVFP4); otherwise the scale is 1.
 // rshift (optional, gate/up): per tile row, the power of two the activation row was scaled by
 // (2^rshift[row]); the sums are scaled back by 2^-rshift[row] (exact) before SiLU.
-template <int MI, int NB, bool GATE_UP, int BN, int COLS_PER_WAVE, bool GSCALE, class P>
+// RBE (default MI): the 16-row blocks that can hold rows of the tile; blocks past it are not read,
+// so a caller that never touched their accumulators need not keep them.
+template <int MI, int NB, bool GATE_UP, int BN, int COLS_PER_WAVE, bool GSCALE, class P, int RBE = MI>
 __device__ __forceinline__ void epilogue(const P& p, const GemmBank& bank, const TileInfo& ti, int ntile,
                                          const f32x4 (&acc)[MI][NB], int mtile = 0,
-                                         const int* rshift = nullptr) {
+                                         const int* rshift = nullptr, IntC<RBE> = {}) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int q = lane >> 4, nl = lane & 15;
@@ -138,7 +140,7 @@ __device__ __forceinline__ void epilogue(const P& p, const GemmBank& bank, const
   if (GATE_UP) {
     const float dg = gs ? gs[0] : 1.f, du = gs ? gs[1] : 1.f;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
+    for (int i = 0; i < RBE; ++i) {
       const int row = 16 * i + nl;
       if (row >= ti.rows) continue;
       uint16_t* orow = p.out + (size_t)(ti.row0 + row) * p.N + col0;
@@ -170,7 +172,7 @@ __device__ __forceinline__ void epilogue(const P& p, const GemmBank& bank, const
   } else {
     const float dd = gs ? gs[0] : 1.f;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
+    for (int i = 0; i < RBE; ++i) {
       const int row = 16 * i + nl;
       if (row >= ti.rows) continue;
       uint16_t* orow = p.out + (size_t)(ti.row0 + row) * p.N + col0;

@@ -294,9 +294,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmProblem p) {
 //  * Tile order is XCD-aware: workgroup b runs on XCD b % 8; each XCD walks a contiguous range of
 //    (m-tile, n-tile) pairs, n fastest, so the A rows of an m-tile are reused from that XCD's L2.
 //  * Launched with WAVES = 4 (two workgroups per CU, two waves per SIMD, at most 256 registers per
-//    lane) for every down GEMM and for gate/up outputs whose width is not a multiple of 256; wider
-//    gate/up outputs take the eight-wave kernel below (one workgroup per CU).  The WAVES = 8 form
-//    of this kernel (three A buffers) is kept compilable but not launched.
+//    lane) for the NVFP4 down GEMM (measured as fast as the eight-wave kernel below or 1% faster),
+//    the MXFP4 down GEMM when its width is not a multiple of 512, and gate/up outputs whose width is
+//    not a multiple of 256; the rest takes the eight-wave kernel below (one workgroup per CU).  The
+//    WAVES = 8 form of this kernel (three A buffers) is kept compilable but not launched.
 constexpr int kTallBK = 128;
 constexpr int kTallRows = 128;
 
@@ -500,34 +501,42 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
   epilogue<MI, NB, GATE_UP, BN, COLS_PER_WAVE, WFmt<FMT>::kGlobalScale>(p, bank, ti, ntile, acc, mtile);
 }
 
-// Tall tiles with eight waves, every operand by direct loads (the gate/up kernel for 128-row tiles
-// whenever the output width is a multiple of 256; it also compiles for down, which the four-wave
-// kernel above runs faster).  The activation chunks are
-// staged as in the kernel above (three buffers, two chunks in flight); the waves' weight tiles (1 KB
-// each) and their scale dwords (one per lane) also go global -> LDS by direct loads, into one slot
-// per wave, and are read back into registers at the start of the chunk that uses them.  No load of
-// the main loop is visible to the compiler, so the only wait is the explicit one at the end of a
-// chunk, which leaves the newest activation loads in flight.  (With the weights loaded into
-// registers by ordinary loads, the compiler's own wait before their first use also drains every
-// direct load issued after them -- loads complete in order and it cannot count the direct loads --
-// so the activation chunk two ahead had to land within one chunk.)
-//  * Per chunk c: issue the activations of chunk c + 2 into the buffer freed by chunk c - 1 (all
-//    waves passed the barrier that ended it).  During the last MFMA step of the chunk, wait for the
-//    weights of chunk c + 1, move them from the slot to registers, issue chunk c + 2's into the
-//    slot just read (the wave's own region: the read has returned before the load is issued) and
-//    dequantize chunk c + 1's first MFMA step, so that no dequantization runs without MFMAs beside
-//    it (the chunk-start dequantization, with both waves of a SIMD in the same phase after the
-//    barrier, cost 4-5% of the gate/up time).
-//  * Weight slot of one wave: NB tiles of 1 KB (lane l's 16 bytes at 16 l) then NB scale blocks of
-//    256 bytes (lane l's dword at 4 l) -- the registers a direct global load would have produced.
-//    The tile bases are wave-uniform (scalar registers); one lane offset serves every tile.
-//  * Activation fragments are read from LDS in the step that uses them (reading them a step ahead
-//    needs 32 more registers, which the pipelined weights now hold).
+// ------------------------------------------------------------------------------------------
+// Tall tiles with eight waves (two per SIMD, one workgroup per CU), every operand by direct loads:
+// the gate/up kernel for 128-row tiles whenever the output width is a multiple of 256 (and the MXFP4
+// down kernel when it is a multiple of 512).  Each wave holds all 128 rows of the tile and NB weight
+// fragments; the workgroup covers 8 * 16 * NB weight rows.
+//  * Staging: activation chunks (32 KB, fragment order as above) by direct loads into three LDS
+//    buffers, two chunks ahead; each wave's weight tiles (1 KB each) and their scale dwords (one per
+//    lane) by direct loads into the wave's own LDS slot, one chunk ahead, read back into registers
+//    during the last MFMA step of the chunk before the one that uses them.  No load of the main loop
+//    is visible to the compiler, so the only waits are the explicit ones.  (With the weights loaded
+//    into registers by ordinary loads, the compiler's own wait before their first use also drains
+//    every direct load issued after them -- loads complete in order and it cannot count the direct
+//    loads.)
+//  * Software pipeline inside the wave: while the MFMAs of step j run, the same wave dequantizes the
+//    weight operands of step j + 1, and each activation fragment is read from LDS two row blocks
+//    before the MFMAs that use it.  The instruction order interleaves them (sched_group_barrier: per
+//    row block one LDS read, then NB times an MFMA followed by up to VPM VALU instructions), so the
+//    dequantization issues while the matrix core works instead of in a burst beside it (measured:
+//    4-6% off the NVFP4 gate/up time against the same kernel with the dequantization of a step done
+//    before its MFMAs, and 5% off the MXFP4 down GEMM against the four-wave kernel).
+//  * Chunk c, in order: the activations of chunk c + 2 into the buffer chunk c - 1 used; MFMA steps
+//    0..2; in step 3 the wait for this wave's activations and weights of chunk c + 1, the slot's read
+//    into registers and the first RB - 2 row blocks of MFMAs beside the next chunk's first
+//    dequantization; then the weights of chunk c + 2 into the slot and the chunk's one barrier (after
+//    it every wave's share of chunk c + 1 has landed, and every read of chunk c's buffer has
+//    returned), and the last two row blocks beside the reads of chunk c + 1's first fragments.
+//  * The 16-row blocks of the tile beyond the group's rows are neither computed nor stored (a
+//    template parameter counts the blocks with real rows; their accumulators are never live).
+//  * Accumulators stay in the ordinary registers (128 per lane at NB = 4): with 512 registers for a
+//    single wave per SIMD, the compiler keeps 16x16x32 accumulators in the accumulation registers but
+//    does not tie each MFMA's result to its accumulator input, and copies every accumulator through
+//    ordinary registers once per loop iteration (seen in the generated code of a four-wave form).
 template <int NB, bool GATE_UP, int FMT, bool A16>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProblem p) {
   using F = WFmt<FMT>;
   static_assert(!A16 || (GATE_UP && FMT == kFmtNvfp4), "fp16 rows: NVFP4 gate/up only");
-  // operand type: bf16, or fp16 when the activation rows come as fp16 (p.a16)
   using OpT = typename std::conditional<A16, f16x8, bf16x8>::type;
   auto w_op = [](const uint4& w, uint32_t sc, int j) -> OpT {
     if constexpr (A16) return w_operand16(w, sc, j);
@@ -544,9 +553,9 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
   constexpr int A_BYTES = FRAGS * 1024;                // 32 KB per activation chunk
   constexpr int A_ITERS = FRAGS / WAVES;               // direct loads per wave per activation chunk
   constexpr int NA = 3;                                // activation chunk buffers
-  constexpr int W_WAVE = NB * (1024 + 256);            // one wave's region of a weight slot
+  constexpr int W_WAVE = NB * (1024 + 256);            // one wave's weight slot
   constexpr int W_BYTES = WAVES * W_WAVE;
-  static_assert(STEPS == 4 && FRAGS % WAVES == 0 && A_ITERS == 4, "chunk layout");
+  static_assert(STEPS == 4 && FRAGS % WAVES == 0 && A_ITERS * WAVES == FRAGS, "chunk layout");
   static_assert(NA * A_BYTES + W_BYTES <= 150 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NA * A_BYTES + W_BYTES];
   __shared__ uint32_t s_aoff[BM];
@@ -588,7 +597,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
   const int K = p.K;
   const int nK = K / BK;
 
-  const uint8_t* abase = reinterpret_cast<const uint8_t*>(A16 ? p.a16 : p.a_tiled ? p.a : (ti.extra ? p.a_extra : p.a));
+  const uint8_t* abase =
+      reinterpret_cast<const uint8_t*>(A16 ? p.a16 : p.a_tiled ? p.a : (ti.extra ? p.a_extra : p.a));
   if (p.a_tiled) abase += (size_t)mtile * nK * A_BYTES;
   if (tid < BM && !p.a_tiled) {
     const int R = ti.a_row0 + min(tid, ti.rows - 1);
@@ -599,6 +609,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
   __syncthreads();
   const int q = lane >> 4;
   const int nl = lane & 15;
+  // direct load `it` of this wave fills fragment Fi = wave + WAVES*it: row block Fi/4, MFMA step Fi%4
   uint32_t aoff[A_ITERS];
 #pragma unroll
   for (int it = 0; it < A_ITERS; ++it) {
@@ -608,12 +619,10 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
 
-  // this wave's weight tiles: wave-uniform expert bases, per-lane 32-bit offsets
   const int ktiles = K / 128;
   const size_t rows_per_expert = GATE_UP ? 2 * (size_t)p.N : (size_t)p.N;
   const uint8_t* wexp = bank.w + (size_t)ti.group * rows_per_expert * (size_t)(K / 2);
   const uint8_t* sexp = bank.ws + (size_t)ti.group * rows_per_expert * (size_t)(K / F::kScaleGroup);
-  // wave-uniform tile bases (scalar registers) plus one per-lane offset each for nibbles and scales
   uint32_t t0[NB];
 #pragma unroll
   for (int f = 0; f < NB; ++f)
@@ -649,19 +658,21 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
     static_assert(N >= 0 && N < 64, "vmcnt immediate");
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
   };
+  // every LDS read this wave issued has returned (before a direct load may overwrite what it read)
+  auto wait_lds_reads = []() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); };
 
   auto run = [&](auto rb_const) {
     constexpr int RB = decltype(rb_const)::value;
-    // prologue: chunk 0's weights and activations landed, chunk 1's activations in flight
-    issue_w(0);
-    issue_a(0, 0);
-    if (nK > 1) {
-      issue_a(1, 1);
-      wait_vm(IntC<A_ITERS>{});
-    } else {
-      wait_vm(IntC<0>{});
-    }
-    __syncthreads();
+    // activation fragments are read from LDS D row blocks ahead of the MFMAs that use them
+    constexpr int D = RB < 2 ? RB : 2;
+    // row blocks of a chunk's last step before the chunk's barrier (the next chunk's first
+    // fragments are read after it)
+    constexpr int H1 = RB - D;
+    // VALU instructions after each MFMA: one step's dequantization (per fragment about 9.5
+    // instructions on fp16 operands, 16.5 on bf16, 5.5 for MXFP4) spread over the step's MFMAs
+    constexpr int VALU_STEP = NB * (A16 ? 19 : (FMT == kFmtMxfp4 ? 11 : 33)) / 2;
+    constexpr int VPM = (VALU_STEP + NB * RB - 1) / (NB * RB);
+    constexpr int VPM_A = H1 > 1 ? (VALU_STEP + NB * (H1 - 1) - 1) / (NB * (H1 - 1)) : VALU_STEP;
     const uint8_t* wl = lds + wslot0;
     uint4 bq[NB];
     uint32_t sc[NB];
@@ -671,63 +682,141 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
         bq[f] = *reinterpret_cast<const uint4*>(wl + f * 1024 + 16 * lane);
         sc[f] = *reinterpret_cast<const uint32_t*>(wl + NB * 1024 + f * 256 + 4 * lane);
       }
-      // the slot's bytes are in registers before a load may overwrite it
-#pragma unroll
-      for (int f = 0; f < NB; ++f)
-        asm volatile("" : "+v"(bq[f].x), "+v"(bq[f].y), "+v"(bq[f].z), "+v"(bq[f].w), "+v"(sc[f]) : : "memory");
     };
-    read_w();
-    if (nK > 1) issue_w(1);
+    auto frag = [&](const uint8_t* buf, int j, int i) -> OpT {
+      return *reinterpret_cast<const OpT*>(buf + (STEPS * i + j) * 1024 + 16 * lane);
+    };
     OpT wcur[NB];
+    // The values exist at this point of the program: code generation may otherwise compute the
+    // next step's weight operands next to their first use, after the step's scheduling region,
+    // instead of in it between the MFMAs.
+    auto pin = [](OpT (&v)[NB]) {
+#pragma unroll
+      for (int f = 0; f < NB; ++f) asm volatile("" : "+v"(v[f]));
+    };
+    // Row blocks [I0, I1) of MFMA step j (fragments in x[i], x[0..D) read before); before block i
+    // the fragment D blocks ahead is read: block i + D of this step, or past the step's end, block
+    // i + D - RB of the next step (buffer nbuf, step nj) when NXT.
+    auto blocks = [&](auto i0_const, auto i1_const, OpT (&x)[RB + D], const uint8_t* buf, int j, const uint8_t* nbuf,
+                      int nj, auto nxt_const) {
+      constexpr int I0 = decltype(i0_const)::value;
+      constexpr int I1 = decltype(i1_const)::value;
+      constexpr bool NXT = decltype(nxt_const)::value;
+#pragma unroll
+      for (int i = I0; i < I1; ++i) {
+        if (i + D < RB) x[i + D] = frag(buf, j, i + D);
+        else if (NXT) x[i + D] = frag(nbuf, nj, i + D - RB);
+#pragma unroll
+        for (int f = 0; f < NB; ++f) acc[i][f] = mfma(wcur[f], x[i], acc[i][f]);
+      }
+    };
+    // instruction order of a region: NDS0 LDS reads first, then per row block one LDS read and
+    // eight times (an MFMA, then up to V VALU instructions; none in the first block if V0 is 0)
+    auto interleave = [](auto nb_const, auto nds0_const, auto v_const, auto v0_const) {
+      constexpr int NBLK = decltype(nb_const)::value;
+      constexpr int NDS0 = decltype(nds0_const)::value;
+      constexpr int V = decltype(v_const)::value;
+      constexpr int V0 = decltype(v0_const)::value;
+      if (NDS0 > 0) __builtin_amdgcn_sched_group_barrier(0x100, NDS0, 0);
+      if (NBLK > 0) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int m = 0; m < NB; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, V0, 0);
+        }
+      }
+#pragma unroll
+      for (int b = 1; b < NBLK; ++b) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int m = 0; m < NB; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+        }
+      }
+    };
+
+    // prologue: chunk 0's weights and activations landed and in registers, chunk 1's weights and
+    // activations in flight
+    issue_w(0);
+    issue_a(0, 0);
+    if (nK > 1) {
+      issue_a(1, 1);
+      wait_vm(IntC<A_ITERS>{});
+    } else {
+      wait_vm(IntC<0>{});
+    }
+    __syncthreads();
+    read_w();
+    wait_lds_reads();
+    if (nK > 1) issue_w(1);
+    OpT xs[D];
 #pragma unroll
     for (int f = 0; f < NB; ++f) wcur[f] = w_op(bq[f], sc[f], 0);
-    // Invariant at the top of chunk c: bq/sc hold chunk c's weights and wcur its first MFMA step
-    // dequantized; activations of chunk c are in LDS; loads in flight, oldest first: activations
-    // of chunk c + 1, weights of chunk c + 1.  NEXT: chunk c + 1 exists; MORE: chunk c + 2 exists
-    // (compile-time, so the MFMA steps are one branch-free block).
+#pragma unroll
+    for (int d = 0; d < D; ++d) xs[d] = frag(lds, 0, d);
+    // Invariant at the top of chunk c: bq/sc hold chunk c's weights, wcur the operands of its
+    // first MFMA step and xs that step's first D activation fragments; loads in flight, oldest
+    // first: the activations, then the weights, of chunk c + 1.
     auto chunk = [&](int c, auto next_const, auto more_const) {
       constexpr bool NEXT = decltype(next_const)::value;
       constexpr bool MORE = decltype(more_const)::value;
       if (MORE) issue_a(c + 2, (c + 2) % NA);
-      const uint8_t* abuf = lds + (c % NA) * A_BYTES + 16 * lane;
+      const uint8_t* abuf = lds + (c % NA) * A_BYTES;
+      const uint8_t* anext = lds + ((c + 1) % NA) * A_BYTES;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < STEPS; ++j) {
+        OpT x[RB + D];
         OpT wnext[NB];
-        OpT xcur[RB];
 #pragma unroll
-        for (int i = 0; i < RB; ++i) xcur[i] = *reinterpret_cast<const OpT*>(abuf + (STEPS * i + j) * 1024);
+        for (int d = 0; d < D; ++d) x[d] = xs[d];
         if (j + 1 < STEPS) {
 #pragma unroll
           for (int f = 0; f < NB; ++f) wnext[f] = w_op(bq[f], sc[f], j + 1);
+          blocks(IntC<0>{}, IntC<RB>{}, x, abuf, j, abuf, j + 1, IntC<1>{});
+          pin(wnext);
+          interleave(IntC<RB>{}, IntC<0>{}, IntC<VPM>{}, IntC<VPM>{});
+          __builtin_amdgcn_sched_barrier(0);
         } else if (NEXT) {
-          // the last step dequantizes the next chunk's first step: wait for its weights (only the
-          // activation loads issued at the top of this chunk stay in flight; the activations of
-          // chunk c + 1, issued before those weights, have landed too), move them to registers,
-          // refill the slot with chunk c + 2's
+          // this wave's activations and weights of chunk c + 1 have landed (only the activations
+          // of chunk c + 2, issued last, may be in flight); the weights go from the wave's own
+          // slot to registers and are dequantized for the next chunk's first step
           wait_vm(IntC<MORE ? A_ITERS : 0>{});
           read_w();
-          if (MORE) issue_w(c + 2);
 #pragma unroll
           for (int f = 0; f < NB; ++f) wnext[f] = w_op(bq[f], sc[f], 0);
+          blocks(IntC<0>{}, IntC<H1>{}, x, abuf, j, anext, 0, IntC<0>{});
+          pin(wnext);
+          interleave(IntC<H1>{}, IntC<2 * NB>{}, IntC<VPM_A>{}, IntC<0>{});
+          __builtin_amdgcn_sched_barrier(0);
+          // the slot is free again: the weights of chunk c + 2 go into it; after the barrier every
+          // wave's activations of chunk c + 1 are in LDS and every read of chunk c's buffer has
+          // returned
+          wait_lds_reads();
+          if (MORE) issue_w(c + 2);
+          __syncthreads();
+          blocks(IntC<H1>{}, IntC<RB>{}, x, abuf, j, anext, 0, IntC<1>{});
+          interleave(IntC<RB - H1>{}, IntC<0>{}, IntC<VPM>{}, IntC<VPM>{});
+          __builtin_amdgcn_sched_barrier(0);
+        } else {
+          blocks(IntC<0>{}, IntC<RB>{}, x, abuf, j, abuf, j, IntC<0>{});
         }
-#pragma unroll
-        for (int i = 0; i < RB; ++i)
-#pragma unroll
-          for (int f = 0; f < NB; ++f) acc[i][f] = mfma(wcur[f], xcur[i], acc[i][f]);
-        __builtin_amdgcn_sched_barrier(0);
         if (j + 1 < STEPS || NEXT) {
 #pragma unroll
           for (int f = 0; f < NB; ++f) wcur[f] = wnext[f];
+#pragma unroll
+          for (int d = 0; d < D; ++d) xs[d] = x[RB + d];
         }
       }
-      // every wave's activations of chunk c + 1 have landed (waited for above); chunk c's buffer
-      // is free once all waves pass
-      __syncthreads();
     };
     for (int c = 0; c + 2 < nK; ++c) chunk(c, IntC<1>{}, IntC<1>{});
     if (nK > 1) chunk(nK - 2, IntC<1>{}, IntC<0>{});
     chunk(nK - 1, IntC<0>{}, IntC<0>{});
+    // only the RB blocks with real rows are stored: the other accumulators are never live
+    epilogue<MI, NB, GATE_UP, BN, COLS_PER_WAVE, WFmt<FMT>::kGlobalScale>(p, bank, ti, ntile, acc, mtile,
+                                                                          A16 ? s_shift : nullptr, IntC<RB>{});
   };
   switch ((ti.rows + 15) / 16) {
     case 1: run(IntC<1>{}); break;
@@ -739,8 +828,6 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
     case 7: run(IntC<7>{}); break;
     default: run(IntC<8>{}); break;
   }
-  epilogue<MI, NB, GATE_UP, BN, COLS_PER_WAVE, WFmt<FMT>::kGlobalScale>(p, bank, ti, ntile, acc, mtile,
-                                                                        A16 ? s_shift : nullptr);
 }
 
 template <int NB, bool GATE_UP, int WAVES, int FMT>
@@ -845,6 +932,9 @@ moe_status_t launch_format(const GemmProblem& p, hipStream_t stream) {
   if (avg <= 32) return wide ? launch_cfg<4, 4, 128, false, FMT>(p, stream) : launch_cfg<4, 2, 128, false, FMT>(p, stream);
   // down: four waves, two workgroups per CU (measured 2-6% faster than the eight-wave kernel at
   // every prefill shape, whose 512-column tiles halve the workgroup count of this short-K GEMM)
+  // MXFP4 (0.7 VALU instructions of dequantization per weight element) on the eight-wave kernel's
+  // 512-column tiles: 5% faster than the four-wave kernel at the prefill shape
+  if (FMT == kFmtMxfp4 && p.N % 512 == 0) return launch_tall<4, false, 8, FMT>(p, stream);
   return wide ? launch_tall<4, false, 4, FMT>(p, stream) : launch_tall<2, false, 4, FMT>(p, stream);
 }
 }  // namespace
