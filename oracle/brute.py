@@ -19,7 +19,13 @@ Definitions used (same sources as ``oracle.moe``):
     to an E8M0 shared exponent floor(log2 amax) - 2 (clamped to [-127, 127]) and
     the nearest E2M1 value, found by searching the value table (ties -> even
     code, i.e. mantissa bit 0); h is rounded to bf16 first (the readings of
-    ``oracle.w4a4``).
+    ``oracle.w4a4``);
+  * W4A4 in NVFP4 (``act="nvfp4"``, activation dequant global scales d_x, d_h): per
+    16 elements, t = amax / (6 d) rounded to fp32 (6 d rounded first), capped at
+    448, the nearest E4M3 value s by searching all 127 finite codes (ties -> even
+    code); each element v / (s d) (s d and the quotient rounded to fp32) to the
+    nearest E2M1 value; fp32 rounding emulated through ``struct`` (the readings
+    of ``oracle.nvfp4_w4a4``).
 """
 
 from __future__ import annotations
@@ -115,11 +121,55 @@ def mx_fake_quant(vec) -> list:
     return res
 
 
-def expert_out(xv, mats, act: str = "bf16") -> list:
-    """y = Wd (silu(Wg x) * (Wu x)) for one token, scalar loops (act "mxfp4": W4A4)."""
+def f32(v: float) -> float:
+    """v rounded to the nearest fp32 value (ties to even), by packing it as a C float."""
+    return struct.unpack("<f", struct.pack("<f", v))[0]
+
+
+E4M3_VALUES = tuple(fp8_e4m3(b) for b in range(0x7F))   # finite non-negative codes, increasing
+
+
+def nearest_index(t: float, table) -> int:
+    """Index of the table value nearest to t; on a tie the even index (mantissa bit 0)."""
+    best = 0
+    for c, v in enumerate(table):
+        d, db = abs(t - v), abs(t - table[best])
+        if d < db or (d == db and c % 2 == 0 and best % 2 == 1):
+            best = c
+    return best
+
+
+def nv_group(vals, d: float):
+    """NVFP4 of one 16-element group with dequant global scale d: (signed E2M1 values, E4M3 scale)."""
+    amax = max(abs(v) for v in vals)
+    t = min(f32(amax / f32(6.0 * d)), 448.0)
+    s = E4M3_VALUES[nearest_index(t, E4M3_VALUES)]
+    sd = f32(s * d)
+    out = []
+    for v in vals:
+        q = f32(v / sd) if sd > 0.0 else 0.0
+        mag = E2M1_TABLE[nearest_index(abs(q), E2M1_TABLE)]
+        out.append(-mag if q < 0 else mag)
+    return out, s
+
+
+def nv_fake_quant(vec, d: float) -> list:
+    """The values a vector stands for after NVFP4 quantization in groups of 16 (global scale d)."""
+    res = []
+    for g0 in range(0, len(vec), 16):
+        vals, s = nv_group(vec[g0:g0 + 16], d)
+        res.extend(v * s * d for v in vals)
+    return res
+
+
+def expert_out(xv, mats, act: str = "bf16", act_gscales=(1.0, 1.0)) -> list:
+    """y = Wd (silu(Wg x) * (Wu x)) for one token, scalar loops (act "mxfp4" or "nvfp4": W4A4;
+    act_gscales = (d_x, d_h) for "nvfp4")."""
     wg, wu, wd = mats
     if act == "mxfp4":
         xv = mx_fake_quant(xv)
+    elif act == "nvfp4":
+        xv = nv_fake_quant(xv, act_gscales[0])
     hvec = []
     for grow, urow in zip(wg, wu):
         g = 0.0
@@ -131,6 +181,8 @@ def expert_out(xv, mats, act: str = "bf16") -> list:
         hvec.append(sg * u)
     if act == "mxfp4":
         hvec = mx_fake_quant([bf16_round(v) for v in hvec])
+    elif act == "nvfp4":
+        hvec = nv_fake_quant([bf16_round(v) for v in hvec], act_gscales[1])
     y = []
     for drow in wd:
         acc = 0.0
@@ -140,9 +192,10 @@ def expert_out(xv, mats, act: str = "bf16") -> list:
     return y
 
 
-def forward(x_bits, layer, tokens=None, act: str = "bf16"):
+def forward(x_bits, layer, tokens=None, act: str = "bf16", act_gscales=(1.0, 1.0)):
     """Per-token results [(ids, weights, out row, logits)] for the given token indices
-    (act "mxfp4": the W4A4 layer, MXFP4 weights and activations)."""
+    (act "mxfp4": the W4A4 layer, MXFP4 weights and activations; act "nvfp4": NVFP4 weights
+    and activations with activation dequant global scales act_gscales = (d_x, d_h))."""
     cache = {}
 
     def mats(bank, e):
@@ -171,11 +224,11 @@ def forward(x_bits, layer, tokens=None, act: str = "bf16"):
         wts = [v / total for v in z]
         out = [0.0] * len(xv)
         for e, w in zip(chosen, wts):
-            y = expert_out(xv, mats(layer.routed, e), act)
+            y = expert_out(xv, mats(layer.routed, e), act, act_gscales)
             for h in range(len(xv)):
                 out[h] += w * y[h]
         if layer.shared is not None:
-            y = expert_out(xv, mats(layer.shared, 0), act)
+            y = expert_out(xv, mats(layer.shared, 0), act, act_gscales)
             for h in range(len(xv)):
                 out[h] += y[h]
         results.append((chosen, wts, out, logits))
