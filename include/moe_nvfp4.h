@@ -370,6 +370,61 @@ moe_status_t moe_mxfp4_w4a4_forward(const moe_nvfp4_layer_t* layer, const uint16
                                     uint16_t* out, void* workspace, size_t workspace_bytes,
                                     const moe_forward_aux_t* aux, void* stream);
 
+/* ---------------------------------------------------------------- W4A4 in NVFP4 (numerics)
+ * The pages' own W4A4 method: NVFP4 weights (the W4A16 banks: format MOE_WEIGHT_NVFP4, tile layout
+ * of moe_nvfp4_pack_tiles) times NVFP4 activations -- E2M1 elements, one E4M3 block scale per 16
+ * elements along K and one fp32 global scale per GEMM input -- the two global scales combined as
+ * alpha = 1 / (input_global_scale * weight_global_scale) in the GEMM epilogue ("vLLM on the NVIDIA
+ * DGX Spark: A Complete Technical Guide", section 6.1; the fused MoE quantizes its bf16 inputs to
+ * FP4 itself, section 4.3 and the table of section 4.5).  Global scales are taken in dequant form
+ * d (the ModelOpt convention; a compressed-tensors quant scale is 1 / d), so alpha = d_act * d_w.
+ * One static (calibrated) activation scale per GEMM input, shared by every expert: act_gscale_x
+ * for the gate/up input x, act_gscale_h for the down input h, which is rounded to bf16 first.
+ * A zero, negative or non-finite activation scale gives MOE_ERR_INVALID_ARGUMENT before anything
+ * is enqueued: a missing activation scale folded into the alphas multiplies every expert by zero
+ * ("GLM-5.3-Flash-NVFP4 deployment blocked on SM121" discussion).
+ * The gfx950 FP4 matrix instruction takes E8M0 scales per 32 elements only, so this path forms the
+ * products exactly on 16-bit operands instead: the quantizer writes each activation as the bf16
+ * value e2m1(code) * e4m3(block scale) -- at most 6 significant bits within [2^-10, 2688], exact --
+ * and the W4A16 GEMMs run on those rows with alpha in their epilogue.  It is for numerics, not
+ * speed: the W4A16 layer's time plus the two quantization passes.
+ *
+ * NVFP4 quantization of bf16 rows: a [rows][cols] -> packed [rows][cols/2] E2M1 codes (element 2j
+ * in the low nibble of byte j), scales [rows][cols/16] E4M3 bytes and values [rows][cols] bf16
+ * (e2m1 * e4m3, without the global scale), per 16-group by the rule of moe_nvfp4_quantize with the
+ * dequant global scale `gscale` (every decision in fp32).  Each output may be NULL, not all
+ * three; values may be a itself (in place).  cols % 16 == 0; a, packed and values 16-byte aligned;
+ * gscale finite and positive. */
+moe_status_t moe_nvfp4_quantize_act(const uint16_t* a, int32_t rows, int32_t cols, float gscale, uint8_t* packed,
+                                    uint8_t* scales, uint16_t* values, void* stream);
+
+/* W4A4 grouped GEMM in NVFP4: moe_nvfp4_grouped_gemm on A rows that hold the `values` of
+ * moe_nvfp4_quantize_act, whose dequant global scale act_gscale the epilogue applies together
+ * with the weight's (h or y = bf16 of the sums times d_act * d_w).  w->format must be
+ * MOE_WEIGHT_NVFP4; act_gscale finite and positive; otherwise as moe_nvfp4_grouped_gemm. */
+moe_status_t moe_nvfp4_w4a4_grouped_gemm(int32_t stage, const moe_nvfp4_experts_t* w, const uint16_t* a,
+                                         float act_gscale, const int32_t* row_index, int32_t row_divisor,
+                                         const int32_t* expert_offsets, int32_t M_total, uint16_t* out,
+                                         void* stream);
+
+/* Workspace bytes of moe_nvfp4_w4a4_forward: those of moe_nvfp4_forward plus x's 4-bit values
+ * as bf16 rows [T][H]. */
+size_t moe_nvfp4_w4a4_forward_workspace_size(int32_t T, int32_t H, int32_t I, int32_t I_shared,
+                                             int32_t E, int32_t k);
+
+/* Host validation of moe_nvfp4_w4a4_forward: as moe_validate_forward, plus NVFP4 banks and usable
+ * activation scales. */
+moe_status_t moe_nvfp4_w4a4_validate_forward(const moe_nvfp4_layer_t* layer, int32_t T, size_t workspace_bytes,
+                                             float act_gscale_x, float act_gscale_h, const char* gfx_arch);
+
+/* The NVFP4 W4A4 layer: S1-S3 and S6 as moe_nvfp4_forward (routing on the bf16 tokens); S4
+ * quantizes x (once per token) and runs the gate/up GEMM on its 4-bit values, S5 quantizes the
+ * bf16 h rows in place and runs the down GEMM on theirs.  aux and stage events as for
+ * moe_nvfp4_forward (the fused-decode flag is ignored). */
+moe_status_t moe_nvfp4_w4a4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int32_t T,
+                                    float act_gscale_x, float act_gscale_h, uint16_t* out, void* workspace,
+                                    size_t workspace_bytes, const moe_forward_aux_t* aux, void* stream);
+
 /* ---------------------------------------------------------------- measurement helper
  * Not a step of the layer: reads `bytes` bytes of device memory at `buf` once with a plain
  * streaming-read kernel (16-byte non-temporal loads, at most `workgroups` workgroups of 256 threads

@@ -7,11 +7,11 @@ The layer's steps run in hand-written HIP kernels behind the C ABI of libmoe_nvf
 from . import synth
 from ._lib import LIB_PATH, MoeError
 from .ops import (NvFp4Experts, NvFp4MoELayer, combine, forward, forward_workspace_size, gscale_from_quant_scale,
-                  grouped_gemm, pack_tiles, permute, quantize, route, route_from_logits, validate_forward,
-                  workspace_for)
+                  grouped_gemm, grouped_gemm_w4a4, pack_tiles, permute, quantize, quantize_act_nv, route,
+                  route_from_logits, validate_forward, workspace_for)
 from .workloads import build_bank, build_layer
 
 __all__ = ["synth", "LIB_PATH", "MoeError", "NvFp4Experts", "NvFp4MoELayer", "combine", "forward",
-           "forward_workspace_size", "gscale_from_quant_scale", "grouped_gemm", "pack_tiles", "permute", "quantize",
-           "route",
-           "route_from_logits", "validate_forward", "workspace_for", "build_bank", "build_layer"]
+           "forward_workspace_size", "gscale_from_quant_scale", "grouped_gemm", "grouped_gemm_w4a4", "pack_tiles",
+           "permute", "quantize", "quantize_act_nv", "route", "route_from_logits", "validate_forward",
+           "workspace_for", "build_bank", "build_layer"]

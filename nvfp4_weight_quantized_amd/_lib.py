@@ -86,6 +86,14 @@ SIGNATURES = {
     "moe_mxfp4_w4a4_validate_forward": (i32, [ctypes.POINTER(Layer), i32, size_t, ctypes.c_char_p]),
     "moe_mxfp4_w4a4_forward": (i32, [ctypes.POINTER(Layer), c_void_p, i32, c_void_p, c_void_p, size_t,
                                      ctypes.POINTER(ForwardAux), c_void_p]),
+    "moe_nvfp4_quantize_act": (i32, [c_void_p, i32, i32, ctypes.c_float, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "moe_nvfp4_w4a4_grouped_gemm": (i32, [i32, ctypes.POINTER(Experts), c_void_p, ctypes.c_float, c_void_p, i32,
+                                          c_void_p, i32, c_void_p, c_void_p]),
+    "moe_nvfp4_w4a4_forward_workspace_size": (size_t, [i32, i32, i32, i32, i32, i32]),
+    "moe_nvfp4_w4a4_validate_forward": (i32, [ctypes.POINTER(Layer), i32, size_t, ctypes.c_float, ctypes.c_float,
+                                              ctypes.c_char_p]),
+    "moe_nvfp4_w4a4_forward": (i32, [ctypes.POINTER(Layer), c_void_p, i32, ctypes.c_float, ctypes.c_float, c_void_p,
+                                     c_void_p, size_t, ctypes.POINTER(ForwardAux), c_void_p]),
     "moe_hbm_read_probe": (i32, [c_void_p, size_t, c_void_p, i32, c_void_p]),
     "moe_nvfp4_forward_noalloc": (i32, [ctypes.POINTER(Layer), c_void_p, i32, c_void_p, ctypes.POINTER(ForwardAux),
                                         c_void_p]),

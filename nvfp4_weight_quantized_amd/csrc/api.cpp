@@ -64,11 +64,14 @@ GemmBank bank_w2(const moe_nvfp4_experts_t& b) { return GemmBank{b.w2, b.w2_scal
 
 struct ForwardLayout {
   size_t logits, ids, w, counts, offsets, sorted_slot, slot_to_row, block_hist, x16, row_shift, h, h_shared, y,
-      ctr;
+      ctr, xa;
   size_t total;
 };
 
-ForwardLayout forward_layout(int32_t T, int32_t H, int32_t I, int32_t I_shared, int32_t E, int32_t k) {
+// a4: the NVFP4 W4A4 forward, which also holds x's 4-bit values as bf16 rows (xa) and keeps h
+// row-major.
+ForwardLayout forward_layout(int32_t T, int32_t H, int32_t I, int32_t I_shared, int32_t E, int32_t k,
+                             bool a4 = false) {
   ForwardLayout L{};
   const size_t S = (size_t)T * k;
   size_t off = 0;
@@ -107,6 +110,7 @@ ForwardLayout forward_layout(int32_t T, int32_t H, int32_t I, int32_t I_shared, 
   L.ctr = take(T <= moe::kFusedDecodeMaxTokens && S <= (size_t)moe::kFusedDecodeMaxSlots
                    ? (size_t)moe::fused_decode_counter_words(T, k, E, I_shared > 0) * 4
                    : 0);
+  L.xa = take(a4 ? (size_t)T * H * 2 : 0);
   L.total = off;
   return L;
 }
@@ -204,9 +208,18 @@ moe_status_t moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t 
                              static_cast<int32_t*>(workspace), static_cast<hipStream_t>(stream));
 }
 
-moe_status_t moe_nvfp4_grouped_gemm(int32_t stage, const moe_nvfp4_experts_t* w, const uint16_t* a,
-                                    const int32_t* row_index, int32_t row_divisor, const int32_t* expert_offsets,
-                                    int32_t M_total, uint16_t* out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// A usable activation dequant global scale: finite and positive (a zero would silently zero every
+// expert).
+bool valid_act_gscale(float d) { return std::isfinite(d) && d > 0.f; }
+
+// moe_nvfp4_grouped_gemm, with the activation global scale of NVFP4 W4A4 rows (0: W4A16).
+moe_status_t grouped_gemm_entry(int32_t stage, const moe_nvfp4_experts_t* w, const uint16_t* a, float a_gscale,
+                                const int32_t* row_index, int32_t row_divisor, const int32_t* expert_offsets,
+                                int32_t M_total, uint16_t* out, void* stream) {
   if (!w || (stage != MOE_GEMM_GATE_UP && stage != MOE_GEMM_DOWN)) return MOE_ERR_INVALID_ARGUMENT;
   if (w->num_experts < 1 || w->num_experts > 1024) return MOE_ERR_INVALID_ARGUMENT;
   if (!valid_bank(*w, w->hidden, w->num_experts) || !w4a16_format(w->format) || w->hidden <= 0 ||
@@ -233,7 +246,26 @@ moe_status_t moe_nvfp4_grouped_gemm(int32_t stage, const moe_nvfp4_experts_t* w,
   p.row_divisor = row_divisor;
   p.out = out;
   p.has_extra = 0;
+  p.a_gscale = a_gscale;
   return moe::launch_grouped_gemm(p, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_nvfp4_grouped_gemm(int32_t stage, const moe_nvfp4_experts_t* w, const uint16_t* a,
+                                    const int32_t* row_index, int32_t row_divisor, const int32_t* expert_offsets,
+                                    int32_t M_total, uint16_t* out, void* stream) {
+  return grouped_gemm_entry(stage, w, a, 0.f, row_index, row_divisor, expert_offsets, M_total, out, stream);
+}
+
+moe_status_t moe_nvfp4_w4a4_grouped_gemm(int32_t stage, const moe_nvfp4_experts_t* w, const uint16_t* a,
+                                         float act_gscale, const int32_t* row_index, int32_t row_divisor,
+                                         const int32_t* expert_offsets, int32_t M_total, uint16_t* out,
+                                         void* stream) {
+  if (!valid_act_gscale(act_gscale) || !w || w->format != MOE_WEIGHT_NVFP4) return MOE_ERR_INVALID_ARGUMENT;
+  return grouped_gemm_entry(stage, w, a, act_gscale, row_index, row_divisor, expert_offsets, M_total, out, stream);
 }
 
 moe_status_t moe_combine(const uint16_t* y_rows, const int32_t* slot_to_row, const float* topk_w,
@@ -322,10 +354,12 @@ moe_status_t run_routing(const moe_nvfp4_layer_t* layer, const uint16_t* x, int3
 
 }  // namespace
 
-moe_status_t moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int32_t T, uint16_t* out,
-                               void* workspace, size_t workspace_bytes, const moe_forward_aux_t* aux,
-                               void* stream_) {
-  if (moe_status_t st = moe_validate_forward(layer, T, workspace_bytes, nullptr)) return st;
+namespace {
+
+// The W4A16 forward (a4 == nullptr) or the NVFP4 W4A4 forward (a4 = {d_x, d_h}: the activation
+// dequant global scales of the gate/up and down inputs).  Arguments validated by the caller.
+moe_status_t forward_impl(const moe_nvfp4_layer_t* layer, const uint16_t* x, int32_t T, uint16_t* out,
+                          void* workspace, const moe_forward_aux_t* aux, void* stream_, const float* a4) {
   if (T == 0) return MOE_OK;
   if (!x || !out || !workspace || !al16(x) || !al16(out) || !al16(workspace)) return MOE_ERR_INVALID_ARGUMENT;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
@@ -333,7 +367,7 @@ moe_status_t moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x
   const bool has_shared = layer->shared.num_experts != 0;
   const int32_t I = layer->routed.inter, Is = has_shared ? layer->shared.inter : 0;
   const int32_t S = T * k;
-  const ForwardLayout L = forward_layout(T, H, I, Is, E, k);
+  const ForwardLayout L = forward_layout(T, H, I, Is, E, k, a4 != nullptr);
 
   float* logits = (aux && aux->logits) ? aux->logits : at<float>(workspace, L.logits);
   int32_t* ids = (aux && aux->topk_ids) ? aux->topk_ids : at<int32_t>(workspace, L.ids);
@@ -401,7 +435,7 @@ moe_status_t moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x
 
   // Few tokens, on request: two launches -- the router (which also clears the hand-off counters),
   // then S2-S6 fused (micro.hip).  Same tiles and arithmetic as the staged launches below.
-  const bool fused = aux && (aux->flags & MOE_FORWARD_FUSED_DECODE);
+  const bool fused = !a4 && aux && (aux->flags & MOE_FORWARD_FUSED_DECODE);
   if (fused && (fuse_shared || !has_shared) && moe::fused_decode_applies(gu, T, k)) {
     int32_t* ctr = at<int32_t>(workspace, L.ctr);
     const int n_ctr = moe::fused_decode_counter_words(T, k, E, fuse_shared);
@@ -432,15 +466,28 @@ moe_status_t moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x
   st = run_routing(layer, x, T, logits, ids, w, counts, offsets, sorted_slot, slot_to_row, block_hist, mark, stream);
   if (st) return st;
 
+  // W4A4: the gate/up GEMMs read x's 4-bit values (e2m1 * block scale, exact in bf16) instead of x,
+  // with d_x applied in their epilogues
+  const uint16_t* xg = x;
+  if (a4) {
+    uint16_t* xa = at<uint16_t>(workspace, L.xa);
+    if ((st = moe::launch_quantize_act_nv(x, T, H, a4[0], nullptr, nullptr, xa, stream))) return st;
+    xg = xa;
+    gu.a = xa;
+    gu.a_extra = fuse_shared ? xa : nullptr;
+    gu.a_gscale = a4[0];
+  }
+
   // 128-row tiles for both GEMMs (and one m-tile numbering): h goes through the fragment-tiled
-  // layout, so the down GEMM's A tiles are contiguous 1 KB loads
-  const bool tiled = (fuse_shared || !has_shared) && moe::grouped_gemm_uses_tall_tiles(gu);
+  // layout, so the down GEMM's A tiles are contiguous 1 KB loads (W4A16 only: the W4A4 forward
+  // quantizes the row-major h between the GEMMs)
+  const bool tiled = !a4 && (fuse_shared || !has_shared) && moe::grouped_gemm_uses_tall_tiles(gu);
   if (tiled) gu.out_tiled = h;
   if (moe::grouped_gemm_takes_f16_rows(gu)) {
     // fp16 operands halve the dequantization work of the NVFP4 weights (exact, see launch_act_to_f16)
     uint16_t* x16 = at<uint16_t>(workspace, L.x16);
     int32_t* row_shift = at<int32_t>(workspace, L.row_shift);
-    if ((st = moe::launch_act_to_f16(x, T, H, x16, row_shift, stream))) return st;
+    if ((st = moe::launch_act_to_f16(xg, T, H, x16, row_shift, stream))) return st;
     gu.a16 = x16;
     gu.row_shift = row_shift;
   }
@@ -457,12 +504,24 @@ moe_status_t moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x
     gs.has_extra = 1;
     gs.extra = gs.bank;
     gs.M_extra = T;
-    gs.a_extra = x;
+    gs.a_extra = xg;
+    gs.a_gscale = a4 ? a4[0] : 0.f;
     if ((st = moe::launch_grouped_gemm(gs, stream))) return st;
   }
   if ((st = mark(3))) return st;
 
-  // S5
+  // S5 (W4A4: h to its 4-bit values in place first, d_h in the epilogues)
+  if (a4) {
+    if (fuse_shared || !has_shared) {
+      if ((st = moe::launch_quantize_act_nv(h, (int64_t)S + (has_shared ? T : 0), I, a4[1], nullptr, nullptr, h,
+                                            stream)))
+        return st;
+    } else {
+      if ((st = moe::launch_quantize_act_nv(h, S, I, a4[1], nullptr, nullptr, h, stream))) return st;
+      if ((st = moe::launch_quantize_act_nv(h_shared, T, Is, a4[1], nullptr, nullptr, h_shared, stream))) return st;
+    }
+    dn.a_gscale = a4[1];
+  }
   dn.a_tiled = tiled ? 1 : 0;
   if ((st = moe::launch_grouped_gemm(dn, stream))) return st;
   if (has_shared && !fuse_shared) {
@@ -478,6 +537,7 @@ moe_status_t moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x
     ds.extra = ds.bank;
     ds.M_extra = T;
     ds.a_extra = h_shared;
+    ds.a_gscale = a4 ? a4[1] : 0.f;
     if ((st = moe::launch_grouped_gemm(ds, stream))) return st;
   }
   if ((st = mark(4))) return st;
@@ -486,6 +546,53 @@ moe_status_t moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x
   st = moe::launch_combine(y, slot_to_row, w, has_shared ? y + (size_t)S * H : nullptr, T, k, H, out, stream);
   if (st) return st;
   return mark(5);
+}
+
+}  // namespace
+
+moe_status_t moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int32_t T, uint16_t* out,
+                               void* workspace, size_t workspace_bytes, const moe_forward_aux_t* aux,
+                               void* stream) {
+  if (moe_status_t st = moe_validate_forward(layer, T, workspace_bytes, nullptr)) return st;
+  return forward_impl(layer, x, T, out, workspace, aux, stream, nullptr);
+}
+
+size_t moe_nvfp4_w4a4_forward_workspace_size(int32_t T, int32_t H, int32_t I, int32_t I_shared, int32_t E, int32_t k) {
+  if (T < 0 || H <= 0 || I <= 0 || I_shared < 0 || E < 1 || k < 1) return 0;
+  return forward_layout(T, H, I, I_shared, E, k, true).total;
+}
+
+moe_status_t moe_nvfp4_w4a4_validate_forward(const moe_nvfp4_layer_t* layer, int32_t T, size_t workspace_bytes,
+                                             float act_gscale_x, float act_gscale_h, const char* gfx_arch) {
+  if (!valid_act_gscale(act_gscale_x) || !valid_act_gscale(act_gscale_h)) return MOE_ERR_INVALID_ARGUMENT;
+  if (moe_status_t st = validate_layer(layer, T)) return st;
+  if (layer->routed.format != MOE_WEIGHT_NVFP4) return MOE_ERR_INVALID_ARGUMENT;
+  const bool has_shared = layer->shared.num_experts != 0;
+  const int32_t I = layer->routed.inter, Is = has_shared ? layer->shared.inter : 0;
+  if (T > 0 && workspace_bytes < moe_nvfp4_w4a4_forward_workspace_size(T, layer->hidden, I, Is, layer->num_experts,
+                                                                        layer->top_k))
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return check_arch(gfx_arch);
+}
+
+moe_status_t moe_nvfp4_w4a4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int32_t T,
+                                    float act_gscale_x, float act_gscale_h, uint16_t* out, void* workspace,
+                                    size_t workspace_bytes, const moe_forward_aux_t* aux, void* stream) {
+  if (moe_status_t st = moe_nvfp4_w4a4_validate_forward(layer, T, workspace_bytes, act_gscale_x, act_gscale_h,
+                                                        nullptr))
+    return st;
+  const float a4[2] = {act_gscale_x, act_gscale_h};
+  return forward_impl(layer, x, T, out, workspace, aux, stream, a4);
+}
+
+moe_status_t moe_nvfp4_quantize_act(const uint16_t* a, int32_t rows, int32_t cols, float gscale, uint8_t* packed,
+                                    uint8_t* scales, uint16_t* values, void* stream) {
+  if (rows < 0 || cols < 0 || cols % 16 != 0 || !valid_act_gscale(gscale)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!packed && !scales && !values) return MOE_ERR_INVALID_ARGUMENT;
+  if ((int64_t)rows * cols == 0) return MOE_OK;
+  if (!a || !al16(a) || (packed && !al16(packed)) || (values && !al16(values))) return MOE_ERR_INVALID_ARGUMENT;
+  if (moe_status_t st = check_arch(nullptr)) return st;
+  return moe::launch_quantize_act_nv(a, rows, cols, gscale, packed, scales, values, static_cast<hipStream_t>(stream));
 }
 
 moe_status_t moe_gscale_from_quant_scale(const float* q_host, float* d_host, int32_t n) {

@@ -116,7 +116,16 @@ struct GemmProblem {
   // `a_extra` (the same token matrix); the GEMM then runs on fp16 operands.
   const uint16_t* a16;
   const int32_t* row_shift;
+  // W4A4 on NVFP4 activations: the dequant global scale of the activation rows, which then hold
+  // the exact values e2m1(code) * e4m3(block scale) (launch_quantize_act_nv); the epilogue scales
+  // the sums by it and the weight's global scale (alpha = 1 / (input_global_scale *
+  // weight_global_scale) in the guide's section 6.1).  0: the rows are plain bf16 activations
+  // (W4A16) and nothing is applied.
+  float a_gscale;
 };
+
+// The activation global scale the epilogues apply (1 for W4A16 problems).
+__host__ __device__ inline float act_gscale(const GemmProblem& p) { return p.a_gscale != 0.f ? p.a_gscale : 1.f; }
 
 // Bound on the number of 128-row m-tiles of a problem (every non-empty group adds at most one
 // partial tile), the size of the tiled layouts above.
@@ -213,5 +222,9 @@ moe_status_t launch_quantize_mx(const float* w, int32_t num_tensors, int32_t row
                                 uint8_t* scales, hipStream_t stream);
 moe_status_t launch_quantize_act_mx(const uint16_t* a, int64_t rows, int32_t cols, uint8_t* packed, uint8_t* scales,
                                     hipStream_t stream);
+// NVFP4 activation rows (dequant global scale d); packed, scales and values each optional, values
+// may alias a.
+moe_status_t launch_quantize_act_nv(const uint16_t* a, int64_t rows, int32_t cols, float d, uint8_t* packed,
+                                    uint8_t* scales, uint16_t* values, hipStream_t stream);
 
 }  // namespace moe

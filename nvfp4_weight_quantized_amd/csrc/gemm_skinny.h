@@ -240,12 +240,12 @@ __device__ __forceinline__ bool skinny_tile(const GemmProblem& p, int mtile, int
     if (t >= ti.rows) continue;
     uint16_t* orow = p.out + (size_t)(ti.row0 + t) * p.N + col;
     if (GATE_UP) {
-      const float dg = gs[0], du = gs[1];
+      const float dg = gs[0] * act_gscale(p), du = gs[1] * act_gscale(p);
 #pragma unroll
       for (int f = 0; f < NB / 2; ++f)
         store_out<DEVICE_COHERENT>(orow + 16 * f, f32_to_bf16(silu(acc[f][r] * dg) * (acc[f + NB / 2][r] * du)));
     } else {
-      const float dd = gs[0];
+      const float dd = gs[0] * act_gscale(p);
 #pragma unroll
       for (int f = 0; f < NB; ++f) store_out<DEVICE_COHERENT>(orow + 16 * f, f32_to_bf16(acc[f][r] * dd));
     }

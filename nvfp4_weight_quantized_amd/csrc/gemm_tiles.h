@@ -128,6 +128,11 @@ __device__ __forceinline__ int frag_row_block(int f, int ntile, int wave, int N)
   return n >> 4;
 }
 
+// Activation global scale of a problem: the W4A16 problems' (act_gscale), 1 for the MX W4A4 one.
+__device__ __forceinline__ float epilogue_act_gscale(const GemmProblem& p) { return act_gscale(p); }
+template <class P>
+__device__ __forceinline__ float epilogue_act_gscale(const P&) { return 1.f; }
+
 // Epilogue: scale the accumulators by the global scale(s), SiLU(gate)*up for gate/up, store bf16.
 // acc[i][f] holds, in lane l = 16q + n, output row 16i + n and the four columns 4q..4q+3 of
 // fragment f's 16 columns.
@@ -144,9 +149,10 @@ __device__ __forceinline__ void epilogue(const P& p, const GemmBank& bank, const
   const int wave = threadIdx.x >> 6;
   const int q = lane >> 4, nl = lane & 15;
   const float* gs = GSCALE ? bank.gs + (size_t)ti.group * bank.gs_per_expert : nullptr;
+  const float da = epilogue_act_gscale(p);
   const int col0 = ntile * BN + wave * COLS_PER_WAVE + 4 * q;
   if (GATE_UP) {
-    const float dg = gs ? gs[0] : 1.f, du = gs ? gs[1] : 1.f;
+    const float dg = (gs ? gs[0] : 1.f) * da, du = (gs ? gs[1] : 1.f) * da;
 #pragma unroll
     for (int i = 0; i < RBE; ++i) {
       const int row = 16 * i + nl;
@@ -178,7 +184,7 @@ __device__ __forceinline__ void epilogue(const P& p, const GemmBank& bank, const
       }
     }
   } else {
-    const float dd = gs ? gs[0] : 1.f;
+    const float dd = (gs ? gs[0] : 1.f) * da;
 #pragma unroll
     for (int i = 0; i < RBE; ++i) {
       const int row = 16 * i + nl;

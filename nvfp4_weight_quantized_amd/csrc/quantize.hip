@@ -1,4 +1,5 @@
-// On-device NVFP4 quantization of fp32 weights (weight preparation, not part of the layer pass).
+// On-device NVFP4 quantization of fp32 weights (weight preparation, not part of the layer pass),
+// and of bf16 activation rows for the W4A4 variants.
 //
 // Recipe: group 16 along K, symmetric, FP8 E4M3 block scales, one fp32 global scale per tensor
 // ("GLM-5.3-Flash-NVFP4 deployment blocked on SM121" discussion, compressed-tensors follow-up);
@@ -32,16 +33,45 @@ __device__ __forceinline__ float e4m3_rne(float t, uint32_t* code) {
   return v;
 }
 
-__device__ __forceinline__ uint32_t e2m1_rne(float q) {
+// E2M1 code of q (nearest value, ties to even mantissa, saturating at 6); *mag receives the
+// magnitude of the value it stands for.
+__device__ __forceinline__ uint32_t e2m1_rne(float q, float* mag_out = nullptr) {
   const float mag = fabsf(q);
   const float step_inv = mag < 2.f ? 2.f : (mag < 4.f ? 1.f : 0.5f);
   const float v = fminf(rintf(mag * step_inv) / step_inv, 6.f);
+  if (mag_out) *mag_out = v;
   uint32_t c;
   if (v <= 2.f) c = (uint32_t)(v * 2.f);        // 0, .5, 1, 1.5, 2 -> 0..4
   else if (v == 3.f) c = 5u;
   else if (v == 4.f) c = 6u;
   else c = 7u;
   return c | (q < 0.f ? 8u : 0u);
+}
+
+// One 16-element group with dequant global scale d: the packed codes (elements 0..7 in `lo`,
+// low nibble first), the E4M3 byte of the block scale and (optionally) the values e2m1 * scale the
+// codes stand for without the global scale -- at most 6 significant bits, so exact in fp32 and in
+// any 16-bit float.
+__device__ __forceinline__ void quantize_group16(const float (&v)[16], float d, uint32_t* lo, uint32_t* hi,
+                                                 uint32_t* scode, float (*vals)[16] = nullptr) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  float t = __fdiv_rn(amax, __fmul_rn(6.0f, d));
+  t = fminf(t, 448.0f);
+  const float s = e4m3_rne(t, scode);
+  const float sd = __fmul_rn(s, d);
+  *lo = 0;
+  *hi = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float qv = (sd > 0.f) ? __fdiv_rn(v[i], sd) : 0.f;
+    float mag;
+    const uint32_t c = e2m1_rne(qv, &mag);
+    if (i < 8) *lo |= c << (4 * i);
+    else *hi |= c << (4 * (i - 8));
+    if (vals) (*vals)[i] = (c & 8u) ? -(mag * s) : mag * s;
+  }
 }
 
 // One thread per 16-element group.
@@ -58,24 +88,50 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
     const float4 x = src[i];
     v[4 * i] = x.x; v[4 * i + 1] = x.y; v[4 * i + 2] = x.z; v[4 * i + 3] = x.w;
   }
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  float t = __fdiv_rn(amax, __fmul_rn(6.0f, d));
-  t = fminf(t, 448.0f);
-  uint32_t scode;
-  const float s = e4m3_rne(t, &scode);
-  const float sd = __fmul_rn(s, d);
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float qv = (sd > 0.f) ? __fdiv_rn(v[i], sd) : 0.f;
-    const uint32_t c = e2m1_rne(qv);
-    if (i < 8) lo |= c << (4 * i);
-    else hi |= c << (4 * (i - 8));
-  }
+  uint32_t lo, hi, scode;
+  quantize_group16(v, d, &lo, &hi, &scode);
   *reinterpret_cast<uint2*>(packed + g * 8) = uint2{lo, hi};
   scales[g] = (uint8_t)scode;
+}
+
+// NVFP4 activations (W4A4): bf16 rows quantized with the same rule and one dequant global scale d
+// for the whole tensor (a static activation scale: "vLLM on the NVIDIA DGX Spark", section 6.1,
+// one fp32 global scale for the activations; the fused MoE quantizes its bf16 inputs itself,
+// section 4.3).  One thread per 16-element group; each output is optional: the packed codes, the
+// E4M3 scale bytes, and the values e2m1 * block scale as bf16 (exact), which the W4A16 GEMMs take
+// as their activation rows with the global scale applied in the epilogue.  `values` may be `a`
+// itself: every thread reads its group before it writes it.
+__global__ __launch_bounds__(256) void quantize_act_nv_kernel(const uint16_t* a, long long total_groups, float d,
+                                                              uint8_t* __restrict__ packed,
+                                                              uint8_t* __restrict__ scales, uint16_t* values) {
+  const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (g >= total_groups) return;
+  const uint4* src = reinterpret_cast<const uint4*>(a + g * 16);
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint4 x = src[i];
+    const uint32_t u[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * i + 2 * j] = __uint_as_float(u[j] << 16);
+      v[8 * i + 2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
+    }
+  }
+  uint32_t lo, hi, scode;
+  float vals[16];
+  quantize_group16(v, d, &lo, &hi, &scode, &vals);
+  if (packed) *reinterpret_cast<uint2*>(packed + g * 8) = uint2{lo, hi};
+  if (scales) scales[g] = (uint8_t)scode;
+  if (values) {
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      o[i] = (uint32_t)f32_to_bf16(vals[2 * i]) | ((uint32_t)f32_to_bf16(vals[2 * i + 1]) << 16);
+    uint4* dst = reinterpret_cast<uint4*>(values + g * 16);
+    dst[0] = uint4{o[0], o[1], o[2], o[3]};
+    dst[1] = uint4{o[4], o[5], o[6], o[7]};
+  }
 }
 
 // MXFP4 ("vLLM on the NVIDIA DGX Spark", section 6.4: E2M1 elements, one E8M0 exponent-only
@@ -150,6 +206,18 @@ moe_status_t launch_quantize_act_mx(const uint16_t* a, int64_t rows, int32_t col
   if (blocks > 0x7FFFFFFFLL) return MOE_ERR_INVALID_ARGUMENT;
   hipLaunchKernelGGL(quantize_mx_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, stream, a, total, packed,
                      scales);
+  return launch_status();
+}
+
+moe_status_t launch_quantize_act_nv(const uint16_t* a, int64_t rows, int32_t cols, float d, uint8_t* packed,
+                                    uint8_t* scales, uint16_t* values, hipStream_t stream) {
+  if (rows < 0 || cols < 0 || cols % 16 != 0) return MOE_ERR_INVALID_ARGUMENT;
+  const long long total = (long long)rows * (cols / 16);
+  if (total == 0) return MOE_OK;
+  const long long blocks = (total + 255) / 256;
+  if (blocks > 0x7FFFFFFFLL) return MOE_ERR_INVALID_ARGUMENT;
+  hipLaunchKernelGGL(quantize_act_nv_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, total, d, packed, scales,
+                     values);
   return launch_status();
 }
 

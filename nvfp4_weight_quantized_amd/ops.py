@@ -7,6 +7,7 @@ HIP kernels of libmoe_nvfp4.so.  There is no fallback path.
 from __future__ import annotations
 
 import ctypes
+import math
 from dataclasses import dataclass
 from typing import Optional
 
@@ -324,6 +325,70 @@ def quantize_act(a: torch.Tensor, packed: Optional[torch.Tensor] = None, scales:
     return packed, scales
 
 
+def _act_gscale(d, name: str) -> float:
+    d = float(np.float32(d))
+    if not (math.isfinite(d) and d > 0.0):
+        raise ValueError(f"{name}: an activation global scale must be finite and positive, got {d!r}")
+    return d
+
+
+def quantize_act_nv(a: torch.Tensor, gscale: float, packed: bool = True, scales: bool = True,
+                    values: bool = True, in_place: bool = False):
+    """NVFP4 quantization of bf16 rows [M, K] with dequant global scale ``gscale``.
+
+    Returns (codes uint8 [M, K/2] or None, E4M3 scales uint8 [M, K/16] or None, values bf16 [M, K] or
+    None): ``values`` are e2m1(code) * e4m3(scale) without the global scale, the rows the NVFP4 W4A4
+    GEMMs take.  ``in_place``: the values overwrite ``a``.
+    """
+    _need(a, "a", torch.bfloat16, 2)
+    d = _act_gscale(gscale, "gscale")
+    m, k = a.shape
+    if k % 16:
+        raise ValueError(f"a: {k} columns, not a multiple of 16")
+    pk = torch.empty(m, k // 2, dtype=torch.uint8, device=a.device) if packed else None
+    sc = torch.empty(m, k // 16, dtype=torch.uint8, device=a.device) if scales else None
+    vals = (a if in_place else torch.empty_like(a)) if (values or in_place) else None
+    L.check("moe_nvfp4_quantize_act", L.lib().moe_nvfp4_quantize_act(_ptr(a), m, k, d, _ptr(pk), _ptr(sc), _ptr(vals),
+                                                                     _stream(a.device)))
+    return pk, sc, vals
+
+
+def grouped_gemm_w4a4(stage: int, experts: NvFp4Experts, a_values: torch.Tensor, act_gscale: float,
+                      expert_offsets: torch.Tensor, m_total: int, row_index: Optional[torch.Tensor] = None,
+                      row_divisor: int = 1) -> torch.Tensor:
+    """NVFP4 W4A4 S4/S5: ``a_values`` from ``quantize_act_nv`` with dequant global scale ``act_gscale``,
+    an "nvfp4" bank; shapes and checks as ``grouped_gemm``, bf16 out."""
+    if experts.fmt != "nvfp4":
+        raise ValueError("the NVFP4 W4A4 GEMM needs an nvfp4 bank")
+    d = _act_gscale(act_gscale, "act_gscale")
+    experts.check()
+    if stage not in (L.MOE_GEMM_GATE_UP, L.MOE_GEMM_DOWN):
+        raise ValueError(f"unknown stage {stage}")
+    _need(a_values, "a_values", torch.bfloat16, 2)
+    _need(expert_offsets, "expert_offsets", torch.int32, 1)
+    _shape(expert_offsets, "expert_offsets", (experts.num_experts + 1,))
+    kdim = experts.hidden if stage == L.MOE_GEMM_GATE_UP else experts.inter
+    if a_values.shape[1] != kdim:
+        raise ValueError(f"a_values: expected {kdim} columns, got {a_values.shape[1]}")
+    if row_index is not None:
+        _need(row_index, "row_index", torch.int32, 1)
+        if stage != L.MOE_GEMM_GATE_UP:
+            raise ValueError("row_index applies to the gate/up stage only")
+        if row_index.numel() < m_total:
+            raise ValueError(f"row_index: {row_index.numel()} entries for {m_total} rows")
+    elif a_values.shape[0] < m_total:
+        raise ValueError(f"a_values: {a_values.shape[0]} rows for {m_total} output rows")
+    _same_device(a_values, ("expert_offsets", expert_offsets), ("row_index", row_index), ("experts.w13", experts.w13))
+    n = experts.inter if stage == L.MOE_GEMM_GATE_UP else experts.hidden
+    out = torch.empty(m_total, n, dtype=torch.bfloat16, device=a_values.device)
+    st = experts.c_struct()
+    L.check("moe_nvfp4_w4a4_grouped_gemm",
+            L.lib().moe_nvfp4_w4a4_grouped_gemm(stage, ctypes.byref(st), _ptr(a_values), d, _ptr(row_index),
+                                                row_divisor, _ptr(expert_offsets), m_total, _ptr(out),
+                                                _stream(a_values.device)))
+    return out
+
+
 def grouped_gemm_a4(stage: int, experts: NvFp4Experts, a_codes: torch.Tensor, a_scales: torch.Tensor,
                     expert_offsets: torch.Tensor, m_total: int, row_index: Optional[torch.Tensor] = None,
                     row_divisor: int = 1) -> torch.Tensor:
@@ -367,19 +432,24 @@ def combine(y_rows: torch.Tensor, slot_to_row: torch.Tensor, topk_w: torch.Tenso
 
 # ----------------------------------------------------------------------------- whole layer
 
-def forward_workspace_size(T: int, H: int, I: int, I_shared: int, E: int, k: int, w4a4: bool = False) -> int:
-    fn = L.lib().moe_mxfp4_w4a4_forward_workspace_size if w4a4 else L.lib().moe_nvfp4_forward_workspace_size
+def forward_workspace_size(T: int, H: int, I: int, I_shared: int, E: int, k: int, w4a4: bool = False,
+                           nvfp4_a4: bool = False) -> int:
+    """Workspace bytes of the W4A16 forward, the MXFP4 W4A4 one (``w4a4``) or the NVFP4 W4A4 one."""
+    if nvfp4_a4:
+        fn = L.lib().moe_nvfp4_w4a4_forward_workspace_size
+    else:
+        fn = L.lib().moe_mxfp4_w4a4_forward_workspace_size if w4a4 else L.lib().moe_nvfp4_forward_workspace_size
     return int(fn(T, H, I, I_shared, E, k))
 
 
 _POOL = {}
 
 
-def workspace_for(layer: NvFp4MoELayer, T: int, device) -> torch.Tensor:
+def workspace_for(layer: NvFp4MoELayer, T: int, device, nvfp4_a4: bool = False) -> torch.Tensor:
     """One module-level workspace per device, grown on demand and shared by every layer."""
     i_sh = layer.shared.inter if layer.shared is not None else 0
     need = forward_workspace_size(T, layer.hidden, layer.routed.inter, i_sh, layer.num_experts, layer.top_k,
-                                  layer.is_w4a4)
+                                  layer.is_w4a4, nvfp4_a4)
     dev = torch.device(device)
     cur = _POOL.get(dev)
     if cur is None or cur.numel() < need:
@@ -390,10 +460,12 @@ def workspace_for(layer: NvFp4MoELayer, T: int, device) -> torch.Tensor:
 
 def forward(layer: NvFp4MoELayer, x: torch.Tensor, workspace: Optional[torch.Tensor] = None,
             out: Optional[torch.Tensor] = None, return_aux: bool = False, stage_events=None,
-            return_rows: bool = False, fused_decode: bool = False):
+            return_rows: bool = False, fused_decode: bool = False, act_gscales=None):
     """The whole layer on x [T, H] bf16 -> [T, H] bf16 (and, if asked, logits/ids/weights/counts).
 
-    Runs moe_nvfp4_forward, or moe_mxfp4_w4a4_forward when the layer's banks are "mxfp4_a4".
+    Runs moe_nvfp4_forward, or moe_mxfp4_w4a4_forward when the layer's banks are "mxfp4_a4", or
+    moe_nvfp4_w4a4_forward when ``act_gscales`` = (d_x, d_h) is given (NVFP4 banks; the dequant
+    global scales of the gate/up and down activations, W4A4 in NVFP4).
     ``return_rows`` (with ``return_aux``): the aux dict also holds "y_rows", the expert outputs the
     combine reads (bf16 [T*k + T_shared, H], routed rows in expert-sorted order, then the shared
     expert's row of every token).
@@ -408,8 +480,15 @@ def forward(layer: NvFp4MoELayer, x: torch.Tensor, workspace: Optional[torch.Ten
     if x.shape[1] != layer.hidden:
         raise ValueError(f"x: expected {layer.hidden} columns, got {x.shape[1]}")
     _same_device(x, ("w_router", layer.w_router))
+    a4 = None
+    if act_gscales is not None:
+        if layer.routed.fmt != "nvfp4":
+            raise ValueError("act_gscales (NVFP4 W4A4) needs nvfp4 banks")
+        if len(act_gscales) != 2:
+            raise ValueError("act_gscales: (d_x, d_h) expected")
+        a4 = (_act_gscale(act_gscales[0], "act_gscales[0]"), _act_gscale(act_gscales[1], "act_gscales[1]"))
     if workspace is None:
-        workspace = workspace_for(layer, t, x.device)
+        workspace = workspace_for(layer, t, x.device, nvfp4_a4=a4 is not None)
     _need(workspace, "workspace", torch.uint8)
     _same_device(x, ("workspace", workspace))
     if out is None:
@@ -439,17 +518,28 @@ def forward(layer: NvFp4MoELayer, x: torch.Tensor, workspace: Optional[torch.Ten
             raise ValueError(f"stage_events: {L.NUM_STAGE_EVENTS} entries expected")
         arr = (ctypes.c_void_p * L.NUM_STAGE_EVENTS)(*stage_events)
         aux.stage_events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    aux_p = ctypes.byref(aux) if aux is not None else None
+    if a4 is not None:
+        L.check("moe_nvfp4_w4a4_forward",
+                L.lib().moe_nvfp4_w4a4_forward(ctypes.byref(st), _ptr(x), t, a4[0], a4[1], _ptr(out), _ptr(workspace),
+                                               workspace.numel(), aux_p, _stream(x.device)))
+        return (out, aux_t) if return_aux else out
     fn = "moe_mxfp4_w4a4_forward" if layer.is_w4a4 else "moe_nvfp4_forward"
     L.check(fn, getattr(L.lib(), fn)(ctypes.byref(st), _ptr(x), t, _ptr(out), _ptr(workspace), workspace.numel(),
-                                     ctypes.byref(aux) if aux is not None else None, _stream(x.device)))
+                                     aux_p, _stream(x.device)))
     return (out, aux_t) if return_aux else out
 
 
 def validate_forward(layer_struct: L.Layer, T: int, workspace_bytes: int, arch: Optional[str] = "gfx950",
-                     w4a4: bool = False) -> int:
-    """Pure-host validation status (needs no GPU when ``arch`` is given)."""
+                     w4a4: bool = False, act_gscales=None) -> int:
+    """Pure-host validation status (needs no GPU when ``arch`` is given).  ``act_gscales`` = (d_x, d_h):
+    the NVFP4 W4A4 forward's validation (the scales are passed through unchecked)."""
+    a = arch.encode() if arch is not None else None
+    if act_gscales is not None:
+        return int(L.lib().moe_nvfp4_w4a4_validate_forward(ctypes.byref(layer_struct), T, workspace_bytes,
+                                                            float(act_gscales[0]), float(act_gscales[1]), a))
     fn = L.lib().moe_mxfp4_w4a4_validate_forward if w4a4 else L.lib().moe_validate_forward
-    return int(fn(ctypes.byref(layer_struct), T, workspace_bytes, arch.encode() if arch is not None else None))
+    return int(fn(ctypes.byref(layer_struct), T, workspace_bytes, a))
 
 
 # ----------------------------------------------------------------------------- weight preparation

@@ -153,3 +153,26 @@ def test_w4a4_validation_host_only():
     big = moe.forward_workspace_size(t, h, i, i, e, k, w4a4=True)
     floor = (s + t) * i * 2 + (s + t) * i // 2 + (s + t) * i // 32 + t * h // 2 + (s + t) * h * 2
     assert floor <= big < floor + (64 << 20)
+
+
+def test_nvfp4_w4a4_validation_host_only():
+    """The NVFP4 W4A4 layer takes the NVFP4 banks, a larger workspace, and refuses an activation
+    scale that is zero, negative or not finite (a missing scale would zero every expert)."""
+    lay = _fake_layer()
+    need = moe.forward_workspace_size(8, 4096, 1536, 1536, 320, 8, nvfp4_a4=True)
+    base = moe.forward_workspace_size(8, 4096, 1536, 1536, 320, 8)
+    assert need >= base + 8 * 4096 * 2            # plus x's 4-bit values as bf16 rows
+    good = (1.6e-3, 2.5e-4)
+    assert moe.validate_forward(lay, 8, need, act_gscales=good) == L.MOE_OK
+    assert moe.validate_forward(lay, 8, need - 1, act_gscales=good) == L.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert moe.validate_forward(lay, 8, need, arch="gfx942", act_gscales=good) == L.MOE_ERR_UNSUPPORTED_DEVICE
+    for bad in (0.0, -1e-3, float("nan"), float("inf")):
+        assert moe.validate_forward(lay, 8, need, act_gscales=(bad, 1.0)) == L.MOE_ERR_INVALID_ARGUMENT
+        assert moe.validate_forward(lay, 8, need, act_gscales=(1.0, bad)) == L.MOE_ERR_INVALID_ARGUMENT
+    # MXFP4 banks are not NVFP4 weights
+    lay_mx = _fake_layer()
+    lay_mx.routed.format = lay_mx.shared.format = L.MOE_WEIGHT_MXFP4
+    assert moe.validate_forward(lay_mx, 8, need, act_gscales=good) == L.MOE_ERR_INVALID_ARGUMENT
+    # the Python wrapper refuses a missing scale before anything reaches the library
+    with pytest.raises(ValueError):
+        moe.ops._act_gscale(0.0, "d_x")
