@@ -8,6 +8,7 @@ The JSON line's top level is the decode-shaped layer (T=8, H=4096, I=1536, E=320
 the configuration the metric's HBM half is quoted on; `configs` holds, in the same line, the
 prefill-shaped layers the metric's MFMA half is quoted on (prefill T=4096, skewed routing T=2048,
 long prefill T=16384 with H=6144, I=2048, E=256), each timed the same way.  For every layer:
+  * forwards of the layer for 150 ms (the clock settles under load), then the W warm-up forwards;
   * K forwards launched eagerly, timed between two synchronisations with nothing else in between
     (the value and ms_per_step); then the same K forwards with one HIP event per step (the step
     periods: median, p10, p90), and again with events at the stage boundaries, which the library
@@ -39,7 +40,8 @@ import torch
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP4_PEAK_TFLOPS = 10100.0      # MI355X dense fp4 MFMA (the W4A4 layer)
-BYTES_PER_WEIGHT = {"nvfp4": 0.5 + 1 / 16, "mxfp4": 0.5 + 1 / 32, "mxfp4_a4": 0.5 + 1 / 32}   # nibble + scale bytes
+BYTES_PER_WEIGHT = {"nvfp4": 0.5 + 1 / 16, "mxfp4": 0.5 + 1 / 32, "mxfp4_a4": 0.5 + 1 / 32,
+                    "nvfp4_a4": 0.5 + 1 / 16}   # nibble + scale bytes
 
 # HBM traffic of the gate/up GEMM per launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this
 # script (profiles/traffic_<workload>.md), scaled by what the same counters read for a copy of known
@@ -54,10 +56,15 @@ _TRAFFIC = {  # workload: (code fingerprint of the GEMM sources, bytes read, byt
 }
 
 PREFILL_CONFIGS = ["prefill", "skewed", "long_prefill"]
-_DEFAULTS = {  # steps, warmup, weight copies cycled through (decode: defeat the 256 MB last-level cache)
-    "tiny": (200, 20, 1), "decode": (200, 20, 4), "prefill": (20, 3, 1), "skewed": (20, 3, 1),
+# steps, warmup, weight copies cycled through (decode: defeat the 256 MB last-level cache)
+_DEFAULTS = {
+    "tiny": (200, 50, 1), "decode": (200, 50, 4), "prefill": (20, 5, 1), "skewed": (20, 5, 1),
     "long_prefill": (5, 2, 1),
 }
+# Before the counted warm-up steps, forwards of the same workload run until this much wall time has
+# passed: the first tens of milliseconds of full load run at a lower clock (measured: the first 20
+# prefill forwards of a process 6% slower than later ones), whatever the warm-up count.
+SETTLE_S = 0.15
 
 
 def code_fingerprint(paths) -> str:
@@ -197,7 +204,7 @@ def host_info() -> dict:
             "numpy": np.__version__, "blas": blas}
 
 
-def cpu_baseline(wl, x_bits, wr_bits, synth, fmt="nvfp4", n_experts=4, token_block=1024, runs=3):
+def cpu_baseline(wl, x_bits, wr_bits, synth, fmt="nvfp4", n_experts=4, token_block=1024, runs=3, act_gscales=None):
     """The oracle as it stands, on the host's cores, on a bounded sample of the whole job, scaled to it.
 
     Parts, each timed with 1 warm-up + ``runs`` runs (median): routing of every token (router GEMM,
@@ -212,6 +219,7 @@ def cpu_baseline(wl, x_bits, wr_bits, synth, fmt="nvfp4", n_experts=4, token_blo
     from oracle import moe as omoe
     from oracle import mxfp4 as omx
     from oracle import nvfp4 as onv
+    from oracle import nvfp4_w4a4 as onw
     from oracle import w4a4 as oa4
 
     def oracle_expert(bank, e):
@@ -234,6 +242,9 @@ def cpu_baseline(wl, x_bits, wr_bits, synth, fmt="nvfp4", n_experts=4, token_blo
     bias = synth.router_bias(wl)
     w4a4 = fmt == "mxfp4_a4"
     ffn = oa4.expert_ffn_a4 if w4a4 else omoe.expert_ffn
+    if fmt == "nvfp4_a4":
+        def ffn(a, ew):
+            return onw.expert_ffn_a4(a, ew, act_gscales[0], act_gscales[1])
     cores = len(os.sched_getaffinity(0))
     with threadpool_limits(limits=cores):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -290,21 +301,45 @@ def cpu_baseline(wl, x_bits, wr_bits, synth, fmt="nvfp4", n_experts=4, token_blo
 
 # ----------------------------------------------------------------------------- one workload
 
+def calibrate_nvfp4_a4(wl, layer, x, ops_mod, dev):
+    """Static activation scales of the NVFP4 W4A4 layer, as a caller calibrates them once: d_x =
+    amax(x) / (448 * 6) over the batch, d_h the same over the W4A4 gate/up output of the shared
+    expert (or of routed expert 0) on every token.  Not timed."""
+    from nvfp4_weight_quantized_amd import _lib as L
+    d_x = float(np.float32(float(x.abs().max()) / 2688.0))
+    _, _, xa = ops_mod.quantize_act_nv(x, d_x, packed=False, scales=False)
+    bank = layer.shared if layer.shared is not None else layer.routed
+    offs = torch.zeros(bank.num_experts + 1, dtype=torch.int32, device=dev)
+    offs[1:] = wl.T
+    h = ops_mod.grouped_gemm_w4a4(L.MOE_GEMM_GATE_UP, bank, xa, d_x, offs, wl.T)
+    d_h = float(np.float32(max(float(h.abs().max()), 1e-30) / 2688.0))
+    log(f"{wl.name}: NVFP4 W4A4 activation scales d_x={d_x:.4g} d_h={d_h:.4g}")
+    return (d_x, d_h)
+
+
 def measure(wl, layers, steps, warmup, fmt, ops_mod, lib, dev, copy_gbs, cpu: bool, fused_decode: bool = False):
     """Time one workload; returns its record (the fields of a bench line)."""
     import functools
     import types
-    ops = types.SimpleNamespace(forward=functools.partial(ops_mod.forward, fused_decode=fused_decode),
-                                workspace_for=ops_mod.workspace_for)
     w4a4 = fmt == "mxfp4_a4"
     layer = layers[0]
     copies = len(layers)
     x = synth_mod.activations(wl, dev)
-    ws = ops.workspace_for(layer, wl.T, dev)
+    a4 = calibrate_nvfp4_a4(wl, layer, x, ops_mod, dev) if fmt == "nvfp4_a4" else None
+    ops = types.SimpleNamespace(forward=functools.partial(ops_mod.forward, fused_decode=fused_decode,
+                                                          act_gscales=a4),
+                                workspace_for=ops_mod.workspace_for)
+    ws = ops.workspace_for(layer, wl.T, dev, nvfp4_a4=a4 is not None)
     out = torch.empty_like(x)
     _, aux = ops.forward(layer, x, ws, out, return_aux=True)
     counts = aux["expert_counts"].cpu().numpy()
     touched = int((counts > 0).sum())
+    settle, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_S:
+        for _ in range(8):
+            ops.forward(layers[settle % copies], x, ws, out)
+            settle += 1
+        torch.cuda.synchronize()
     for i in range(warmup):
         ops.forward(layers[i % copies], x, ws, out)
     torch.cuda.synchronize()
@@ -427,6 +462,8 @@ def measure(wl, layers, steps, warmup, fmt, ops_mod, lib, dev, copy_gbs, cpu: bo
         roof["kernel"] = "fused decode kernel (S2-S6: top-k, permutation, gate/up, down, combine)"
     else:
         roof["kernel"] = ("gate/up stage (S4): x to MXFP4 + W4A4 grouped GEMM" if w4a4
+                          else "gate/up stage (S4): x to NVFP4 values + grouped GEMM (alpha = d_x * d_w)"
+                          + ("" if hbm_bound else " (+ fp16 row pass)") if a4 is not None
                           else "gate/up stage (S4): grouped GEMM" + ("" if hbm_bound else " (+ fp16 row pass)"))
     roof["kernel_us"] = kernel_ms * 1e3
     roof["kernel_us_median"] = float(np.median(kernel)) * 1e3
@@ -453,15 +490,18 @@ def measure(wl, layers, steps, warmup, fmt, ops_mod, lib, dev, copy_gbs, cpu: bo
         def bits(t):
             return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
-        cpu_rec = cpu_baseline(wl, bits(x), bits(layer.w_router), synth_mod, fmt)
+        cpu_rec = cpu_baseline(wl, bits(x), bits(layer.w_router), synth_mod, fmt, act_gscales=a4)
     return {
         "value": T * steps / (total_ms / 1e3), "unit": "tokens/s", "steps": steps, "warmup": warmup,
+        "settle_forwards": settle,
         "ms_per_step": ms_per_step,
         "step_ms": percentiles(step_ms),
         "config": {"workload": f"{wl.name}: T={T} H={H} I={I} E={E} top-{k} + 1 shared (I={wl.I_shared}), "
-                               + ("MXFP4 W4A4" if w4a4 else f"{fmt.upper()} W4A16"),
+                               + ("MXFP4 W4A4" if w4a4 else "NVFP4 W4A4 (static activation scales)" if a4
+                                  else f"{fmt.upper()} W4A16"),
                    "tokens": T, "hidden": H, "inter": I, "experts": E, "top_k": k,
-                   "weight_copies": copies, "experts_touched": touched},
+                   "weight_copies": copies, "experts_touched": touched,
+                   **({"activation_gscales": {"d_x": a4[0], "d_h": a4[1]}} if a4 else {})},
         "roofline": roof,
         "layer_roofline": layer_roof,
         "graph_replay_ms_per_step": graph_ms,
@@ -490,9 +530,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
     ap.add_argument("--fused-decode", action="store_true",
                     help="run few-token forwards on the two-launch fused decode path (opt-in; slower on MI355X)")
-    ap.add_argument("--format", default="nvfp4", choices=["nvfp4", "mxfp4", "mxfp4_a4"],
+    ap.add_argument("--format", default="nvfp4", choices=["nvfp4", "mxfp4", "mxfp4_a4", "nvfp4_a4"],
                     help="weight format of the synthetic experts (the headline metric is NVFP4); mxfp4_a4: "
-                         "the W4A4 layer (MXFP4 weights and activations on the FP4 matrix cores)")
+                         "the W4A4 layer (MXFP4 weights and activations on the FP4 matrix cores); nvfp4_a4: "
+                         "the NVFP4 W4A4 layer (NVFP4 weights and activations, a numerics path)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -525,8 +566,9 @@ def main():
             banks.clear()
             torch.cuda.empty_cache()
             log(f"building the {wl.name} expert bank ({args.format})")
-            banks[key] = (build_bank(wl, "routed", dev, args.format),
-                          build_bank(wl, "shared", dev, args.format) if wl.I_shared > 0 else None)
+            bfmt = "nvfp4" if args.format == "nvfp4_a4" else args.format
+            banks[key] = (build_bank(wl, "routed", dev, bfmt),
+                          build_bank(wl, "shared", dev, bfmt) if wl.I_shared > 0 else None)
         routed, shared = banks[key]
         bias = synth.router_bias(wl)
         lay = ops.NvFp4MoELayer(synth.router_weight(wl, dev).contiguous(),
@@ -553,7 +595,8 @@ def main():
     line = {
         "metric": "NVFP4 MoE layer tokens/s; decode HBM GB/s %peak, prefill MFMA %peak"
                   + {"nvfp4": "", "mxfp4": " (measured here on MXFP4 weights)",
-                     "mxfp4_a4": " (measured here on the MXFP4 W4A4 layer)"}[args.format],
+                     "mxfp4_a4": " (measured here on the MXFP4 W4A4 layer)",
+                     "nvfp4_a4": " (measured here on the NVFP4 W4A4 layer)"}[args.format],
         "value": main_rec["value"], "unit": "tokens/s", "n_gpus": 1, "steps": main_rec["steps"],
         "warmup": main_rec["warmup"], "ms_per_step": main_rec["ms_per_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp4" if w4a4 else "bf16", "data": "synthetic",
