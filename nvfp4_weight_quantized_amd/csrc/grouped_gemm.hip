@@ -456,29 +456,58 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
       if (c + 1 < nK) load_b(c + 1);
       if (c + AHEAD < nK) issue_a(c + AHEAD, (c + AHEAD) % NBUF);
       const uint8_t* abuf = As + (c % NBUF) * BUF_BYTES + 16 * lane;
-      // the next step's weight operands are dequantized while this step's MFMAs run
+      auto frag = [&](int j, int i) { return *reinterpret_cast<const bf16x8*>(abuf + (STEPS * i + j) * 1024); };
+      // The next step's weight operands are dequantized while this step's MFMAs run, and each
+      // activation fragment is read D row blocks before its MFMAs (within the chunk: the next
+      // chunk's buffer is complete only after the barrier that ends this one).  Instruction order
+      // per row block: one LDS read, then NB times an MFMA and up to VPM VALU instructions.
+      constexpr int D = RB < 2 ? RB : 2;
+      constexpr int VPM = (NB * (FMT == kFmtMxfp4 ? 11 : 33) / 2 + NB * RB - 1) / (NB * RB);
       bf16x8 wcur[NB];
 #pragma unroll
       for (int f = 0; f < NB; ++f) wcur[f] = F::operand(bq[f], sc[f], 0);
+      bf16x8 xs[D];
+#pragma unroll
+      for (int d = 0; d < D; ++d) xs[d] = frag(0, d);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < STEPS; ++j) {
         bf16x8 wnext[NB];
+        bf16x8 x[RB + D];
+#pragma unroll
+        for (int d = 0; d < D; ++d) x[d] = xs[d];
         if (j + 1 < STEPS) {
 #pragma unroll
           for (int f = 0; f < NB; ++f) wnext[f] = F::operand(bq[f], sc[f], j + 1);
         }
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
-          const bf16x8 xfrag = *reinterpret_cast<const bf16x8*>(abuf + (STEPS * i + j) * 1024);
+          if (i + D < RB) x[i + D] = frag(j, i + D);
+          else if (j + 1 < STEPS) x[i + D] = frag(j + 1, i + D - RB);
 #pragma unroll
-          for (int f = 0; f < NB; ++f) acc[i][f] = mfma(wcur[f], xfrag, acc[i][f]);
+          for (int f = 0; f < NB; ++f) acc[i][f] = mfma(wcur[f], x[i], acc[i][f]);
         }
-        // keep each step's LDS reads within the step (bounds the live fragment registers)
+        if (j + 1 < STEPS) {
+          // the dequantized operands exist inside this region (code generation may otherwise
+          // compute them next to their first use, after it)
+#pragma unroll
+          for (int f = 0; f < NB; ++f) asm volatile("" : "+v"(wnext[f]));
+#pragma unroll
+          for (int b = 0; b < RB; ++b) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+            for (int m = 0; m < NB; ++m) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+            }
+          }
+        }
         __builtin_amdgcn_sched_barrier(0);
         if (j + 1 < STEPS) {
 #pragma unroll
           for (int f = 0; f < NB; ++f) wcur[f] = wnext[f];
+#pragma unroll
+          for (int d = 0; d < D; ++d) xs[d] = x[RB + d];
         }
       }
       if (AHEAD == 2 && c + 2 < nK)
@@ -487,6 +516,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
         wait_chunk();
       __syncthreads();
     }
+    // only the RB blocks with real rows are stored: the other accumulators are never live
+    epilogue<MI, NB, GATE_UP, BN, COLS_PER_WAVE, WFmt<FMT>::kGlobalScale>(p, bank, ti, ntile, acc, mtile, nullptr,
+                                                                          IntC<RB>{});
   };
   switch ((ti.rows + 15) / 16) {
     case 1: run(IntC<1>{}); break;
@@ -498,7 +530,6 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
     case 7: run(IntC<7>{}); break;
     default: run(IntC<8>{}); break;
   }
-  epilogue<MI, NB, GATE_UP, BN, COLS_PER_WAVE, WFmt<FMT>::kGlobalScale>(p, bank, ti, ntile, acc, mtile);
 }
 
 // ------------------------------------------------------------------------------------------
