@@ -49,10 +49,10 @@ BYTES_PER_WEIGHT = {"nvfp4": 0.5 + 1 / 16, "mxfp4": 0.5 + 1 / 32, "mxfp4_a4": 0.
 # null once the code of the W4A16 GEMM sources has changed (the fingerprint ignores comments and
 # blank lines).
 _CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "nvfp4_weight_quantized_amd", "csrc")
-_GEMM_SRCS = [os.path.join(_CSRC, f) for f in ("grouped_gemm.hip", "gemm_tiles.h")]
+_GEMM_SRCS = [os.path.join(_CSRC, f) for f in ("grouped_gemm.hip", "gemm_tiles.h", "gemm_skinny.h")]
 _TRAFFIC = {  # workload: (code fingerprint of the GEMM sources, bytes read, bytes written) per gate/up launch
-    "decode": ("bd630153f235c241a85ffd7e08803462ec20142040e22b8f02bf815c411519d9", 432.57e6, 0.22e6),
-    "prefill": ("bd630153f235c241a85ffd7e08803462ec20142040e22b8f02bf815c411519d9", 2782.99e6, 115.81e6),
+    "decode": ("7402057d5af490ed978546fd91dd86eb9f93d3680149897d120f7b26ed1db030", 432.49e6, 0.22e6),
+    "prefill": ("7402057d5af490ed978546fd91dd86eb9f93d3680149897d120f7b26ed1db030", 2762.37e6, 113.70e6),
 }
 
 PREFILL_CONFIGS = ["prefill", "skewed", "long_prefill"]
@@ -530,6 +530,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
     ap.add_argument("--fused-decode", action="store_true",
                     help="run few-token forwards on the two-launch fused decode path (opt-in; slower on MI355X)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first copy 1 GiB device to device three times (a kernel of known traffic, for "
+                         "calibrating HBM byte counters)")
     ap.add_argument("--format", default="nvfp4", choices=["nvfp4", "mxfp4", "mxfp4_a4", "nvfp4_a4"],
                     help="weight format of the synthetic experts (the headline metric is NVFP4); mxfp4_a4: "
                          "the W4A4 layer (MXFP4 weights and activations on the FP4 matrix cores); nvfp4_a4: "
@@ -555,6 +558,13 @@ def main():
         if c not in _DEFAULTS:
             raise SystemExit(f"unknown workload {c}")
 
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     copy_gbs = hbm_read_ceiling(lib, dev)
     log(f"streaming-read ceiling {copy_gbs:.0f} GB/s")
 
