@@ -64,7 +64,7 @@ GemmBank bank_w2(const moe_nvfp4_experts_t& b) { return GemmBank{b.w2, b.w2_scal
 
 struct ForwardLayout {
   size_t logits, ids, w, counts, offsets, sorted_slot, slot_to_row, block_hist, x16, row_shift, h, h_shared, y,
-      ctr, xa;
+      ctr, xa, tiles;
   size_t total;
 };
 
@@ -111,6 +111,8 @@ ForwardLayout forward_layout(int32_t T, int32_t H, int32_t I, int32_t I_shared, 
                    ? (size_t)moe::fused_decode_counter_words(T, k, E, I_shared > 0) * 4
                    : 0);
   L.xa = take(a4 ? (size_t)T * H * 2 : 0);
+  // tile counters of the gate/up and down launches (cleared by the router launch of the forward)
+  L.tiles = take(2 * moe::kTileCounterWords * 4);
   L.total = off;
   return L;
 }
@@ -336,9 +338,11 @@ namespace {
 // S1-S3 of a forward pass: router logits, top-k, permutation.
 moe_status_t run_routing(const moe_nvfp4_layer_t* layer, const uint16_t* x, int32_t T, float* logits, int32_t* ids,
                          float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_to_row,
-                         int32_t* block_hist, const std::function<moe_status_t(int)>& mark, hipStream_t stream) {
+                         int32_t* block_hist, const std::function<moe_status_t(int)>& mark, hipStream_t stream,
+                         int32_t* zero = nullptr, int32_t n_zero = 0) {
   const int32_t H = layer->hidden, E = layer->num_experts, k = layer->top_k;
-  moe_status_t st = moe::launch_router_logits(x, layer->w_router, layer->router_bias, T, H, E, logits, stream);
+  moe_status_t st =
+      moe::launch_router_logits(x, layer->w_router, layer->router_bias, T, H, E, logits, stream, zero, n_zero);
   if (st || (st = mark(1))) return st;
   if ((int64_t)T * k <= moe::kPermuteChunk) {
     // few tokens: top-k and permutation together in one workgroup
@@ -463,8 +467,13 @@ moe_status_t forward_impl(const moe_nvfp4_layer_t* layer, const uint16_t* x, int
     return MOE_OK;
   }
 
-  st = run_routing(layer, x, T, logits, ids, w, counts, offsets, sorted_slot, slot_to_row, block_hist, mark, stream);
+  // the router launch clears the tile counters of the two GEMM launches
+  int32_t* tile_ctr = at<int32_t>(workspace, L.tiles);
+  st = run_routing(layer, x, T, logits, ids, w, counts, offsets, sorted_slot, slot_to_row, block_hist, mark, stream,
+                   tile_ctr, 2 * moe::kTileCounterWords);
   if (st) return st;
+  gu.tile_ctr = tile_ctr;
+  dn.tile_ctr = tile_ctr + moe::kTileCounterWords;
 
   // W4A4: the gate/up GEMMs read x's 4-bit values (e2m1 * block scale, exact in bf16) instead of x,
   // with d_x applied in their epilogues

@@ -63,8 +63,8 @@ moe_status_t launch_topk_permute_small(const float* logits, int32_t T, int32_t E
                                        int32_t* slot_to_row, hipStream_t stream);
 
 // Route -------------------------------------------------------------------------------------
-// T <= kRouterSmallTokens runs the one-pass few-token kernel, which can also clear `zero` [n_zero]
-// (given only then).
+// T <= kRouterSmallTokens runs the one-pass few-token kernel, larger T the MFMA kernel; either
+// also clears `zero` [n_zero] (counters of the kernels that follow in the same stream).
 constexpr int kRouterSmallTokens = 32;
 moe_status_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, const float* bias, int32_t T,
                                   int32_t H, int32_t E, float* logits, hipStream_t stream, int32_t* zero = nullptr,
@@ -122,7 +122,12 @@ struct GemmProblem {
   // weight_global_scale) in the guide's section 6.1).  0: the rows are plain bf16 activations
   // (W4A16) and nothing is applied.
   float a_gscale;
+  // Eight-wave 128-row path only (ignored elsewhere): kTileCounterWords words, zero on entry, from which the
+  // workgroups draw their tiles after the first (one counter per XCD's share of the tile list).
+  // NULL: each workgroup takes a fixed share of the tiles.
+  int32_t* tile_ctr;
 };
+constexpr int kTileCounterWords = 8;   // words of GemmProblem::tile_ctr
 
 // The activation global scale the epilogues apply (1 for W4A16 problems).
 __host__ __device__ inline float act_gscale(const GemmProblem& p) { return p.a_gscale != 0.f ? p.a_gscale : 1.f; }

@@ -33,6 +33,14 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* dst, float a, float b, fl
 
 constexpr int kXcds = 8;
 
+// This lane's index in its wave, computed where it is used (the mask count is opaque to the
+// optimizer, so no register holds it, or values derived from it, across the code in between).
+__device__ __forceinline__ int lane_now() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 template <int N>
 struct IntC {
   static constexpr int value = N;
@@ -141,12 +149,11 @@ __device__ __forceinline__ float epilogue_act_gscale(const P&) { return 1.f; }
 // (2^rshift[row]); the sums are scaled back by 2^-rshift[row] (exact) before SiLU.
 // RBE (default MI): the 16-row blocks that can hold rows of the tile; blocks past it are not read,
 // so a caller that never touched their accumulators need not keep them.
+// epilogue_at takes the lane and wave indices from the caller.
 template <int MI, int NB, bool GATE_UP, int BN, int COLS_PER_WAVE, bool GSCALE, class P, int RBE = MI>
-__device__ __forceinline__ void epilogue(const P& p, const GemmBank& bank, const TileInfo& ti, int ntile,
-                                         const f32x4 (&acc)[MI][NB], int mtile = 0,
-                                         const int* rshift = nullptr, IntC<RBE> = {}) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+__device__ __forceinline__ void epilogue_at(const P& p, const GemmBank& bank, const TileInfo& ti, int ntile,
+                                            const f32x4 (&acc)[MI][NB], int mtile, const int* rshift, IntC<RBE>,
+                                            int lane, int wave) {
   const int q = lane >> 4, nl = lane & 15;
   const float* gs = GSCALE ? bank.gs + (size_t)ti.group * bank.gs_per_expert : nullptr;
   const float da = epilogue_act_gscale(p);
@@ -195,6 +202,14 @@ __device__ __forceinline__ void epilogue(const P& p, const GemmBank& bank, const
         store_bf16x4(orow + 16 * f, acc[i][f][0] * dd, acc[i][f][1] * dd, acc[i][f][2] * dd, acc[i][f][3] * dd);
     }
   }
+}
+
+template <int MI, int NB, bool GATE_UP, int BN, int COLS_PER_WAVE, bool GSCALE, class P, int RBE = MI>
+__device__ __forceinline__ void epilogue(const P& p, const GemmBank& bank, const TileInfo& ti, int ntile,
+                                         const f32x4 (&acc)[MI][NB], int mtile = 0,
+                                         const int* rshift = nullptr, IntC<RBE> = {}) {
+  epilogue_at<MI, NB, GATE_UP, BN, COLS_PER_WAVE, GSCALE>(p, bank, ti, ntile, acc, mtile, rshift, IntC<RBE>{},
+                                                         (int)(threadIdx.x & 63), (int)(threadIdx.x >> 6));
 }
 
 }  // namespace

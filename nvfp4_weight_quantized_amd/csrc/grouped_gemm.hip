@@ -28,6 +28,7 @@
 //    gate/up workgroups hold matching gate and up columns so h = silu(g)*u is formed in registers.
 //  * Groups (experts) are found on the device from the offsets array: no host synchronisation.
 //    Workgroups beyond the real tile count exit at once; empty experts cost nothing.
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -300,6 +301,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmProblem p) {
 //    WAVES = 8 form of this kernel (three A buffers) is kept compilable but not launched.
 constexpr int kTallBK = 128;
 constexpr int kTallRows = 128;
+// groups the eight-wave kernel keeps in LDS (its tile list)
+constexpr int kTallMaxGroups = 1024;
 
 template <int NB, bool GATE_UP, int WAVES, int FMT>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kernel(GemmProblem p) {
@@ -587,101 +590,238 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
   constexpr int W_WAVE = NB * (1024 + 256);            // one wave's weight slot
   constexpr int W_BYTES = WAVES * W_WAVE;
   static_assert(STEPS == 4 && FRAGS % WAVES == 0 && A_ITERS * WAVES == FRAGS, "chunk layout");
-  static_assert(NA * A_BYTES + W_BYTES <= 150 * 1024, "LDS budget");
+  static_assert(BM == 2 * 64, "the first two waves gather the tile's rows");
+  static_assert(NA * A_BYTES + W_BYTES <= 140 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NA * A_BYTES + W_BYTES];
-  __shared__ uint32_t s_aoff[BM];
-  __shared__ int s_shift[A16 ? BM : 1];
-  __shared__ TileInfo tile;
-  __shared__ int tile_ok;
-  __shared__ int tile_n;
-  __shared__ int tile_m;
+  __shared__ uint32_t s_aoff[BM];                      // byte offset of each A row of a tile
+  __shared__ uint32_t s_ridx[BM];                      // row_index entries of the next tile's rows
+  __shared__ int s_shift[2][A16 ? BM : 1];             // fp16 row shifts, per tile slot
+  __shared__ int s_off[kTallMaxGroups + 1];            // group row offsets
+  __shared__ int s_tstart[kTallMaxGroups + 1];         // first m-tile of each group
+  __shared__ int s_tile[2][8];                         // tile slots: index (-1: none), then its Tile
 
+  // The argument block through a pointer the optimizer cannot follow: a field read through it is a
+  // scalar load from the argument segment where it is read, so the fields that only the per-tile
+  // paths need hold no scalar registers through the main loop.
+  auto args = []() {
+    auto ptr = (const __attribute__((address_space(4))) GemmProblem*)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(ptr));
+    return ptr;
+  };
+  // a pointer every lane holds alike, in scalar registers (the direct loads take their base there)
+  auto uniform = [](const void* ptr) {
+    const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
+  };
+
+  // lane indices are taken afresh (lane_now) wherever a per-tile path needs them, so that none is
+  // held in a register through the main loop
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
+  const int lane = lane_now();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int NT = p.N / BN;
+  const int nK = p.K / BK;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+  const uint32_t ridx0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)s_ridx;
+  const uint32_t shift0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int*)&s_shift[0][0];
 
+  // The tile list: m-tiles of the extra group first, then each group's (the numbering of the tiled
+  // activation layouts), p.N / BN column tiles each; tile L = m-tile * (p.N / BN) + column tile.
+  if (p.G > 0)
+    for (int g = tid; g <= p.G; g += 512) s_off[g] = p.offsets[g];
+  __syncthreads();
   if (wave == 0) {
-    const int total = count_tiles<BM>(p) * NT;
-    const int per_xcd = (total + kXcds - 1) / kXcds;
-    const int slot = blockIdx.x / kXcds;
-    const int L = (blockIdx.x % kXcds) * per_xcd + slot;
-    bool ok = slot < per_xcd && L < total;
-    if (ok) ok = find_tile<BM>(p, L / NT, &tile);
-    if (lane == 0) {
-      tile_ok = ok ? 1 : 0;
-      tile_n = ok ? L % NT : 0;
-      tile_m = ok ? L / NT : 0;
+    int carry = p.has_extra ? (p.M_extra + BM - 1) / BM : 0;
+    for (int g0 = 0; g0 < p.G; g0 += 64) {
+      const int g = g0 + lane;
+      const int cnt = g < p.G ? (s_off[g + 1] - s_off[g] + BM - 1) / BM : 0;
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      if (g < p.G) s_tstart[g] = carry + incl - cnt;
+      carry += __shfl(incl, 63);
+    }
+    if (lane == 0) s_tstart[p.G] = carry;
+  }
+  __syncthreads();
+  const int total = __builtin_amdgcn_readfirstlane(s_tstart[p.G]) * (p.N / BN);
+
+  // Work split: XCD X (blockIdx % 8) owns the window [X * pxd, X * pxd + wsize(X)) of the list, so
+  // the tiles that share activation rows or an expert's weights run on one L2.  Workgroup `slot`
+  // of the XCD starts on tile X * pxd + slot; with counters, each further tile is a ticket drawn
+  // from the window's counter (tile X * pxd + spx + ticket), and once the window is spent, from
+  // the other XCDs' windows in turn; without, the workgroup takes every spx-th tile of its window.
+  const int X = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int spx = gridDim.x / kXcds;
+  const int pxd = (total + kXcds - 1) / kXcds;
+  auto wsize = [&](int y) { return max(0, min(total, (y + 1) * pxd) - y * pxd); };
+  // the next tile is found during the current one, which takes six chunks at least
+  const bool chain = nK >= 6;
+  const bool dyn = chain && p.tile_ctr != nullptr;
+  int ywin = 0;       // wave 0: windows X .. X + ywin - 1 (mod 8) hand out no more tickets
+  int tpend = 0;      // wave 0, lane 0: a ticket drawn on window X + ywin and not looked at yet
+  bool pend = false;
+  // wave 0: the next tile from the counters (the pending ticket first), -1 when all are spent
+  auto draw = [&]() -> int {
+    int32_t* const ctr = args()->tile_ctr;
+#pragma nounroll
+    for (; ywin < kXcds; ++ywin) {
+      const int y = (X + ywin) % kXcds;
+      const int n = wsize(y) - spx;
+      int t;
+      if (pend) {
+        pend = false;
+        t = __builtin_amdgcn_readfirstlane(tpend);
+      } else {
+        if (n <= 0) continue;
+        t = 0;
+        if (lane_now() == 0) t = __hip_atomic_fetch_add(ctr + y, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        t = __builtin_amdgcn_readfirstlane(t);
+      }
+      if (t < n) return y * pxd + spx + t;
+    }
+    return -1;
+  };
+  struct Tile {
+    int L, group, row0, rows, a_row0, extra, ntile, mtile;
+  };
+  // wave 0: tile L of the list (-1: none) into slot sl
+  auto publish = [&](int L, int sl) {
+    const auto* a = args();
+    Tile t{L, 0, 0, 0, 0, 0, 0, 0};
+    if (L >= 0) {
+      const int NT = a->N / BN;
+      const int xt = a->has_extra ? (a->M_extra + BM - 1) / BM : 0;
+      t.mtile = L / NT;
+      t.ntile = L - t.mtile * NT;
+      if (t.mtile < xt) {
+        t.extra = 1;
+        t.a_row0 = t.mtile * BM;
+        t.row0 = a->M + t.a_row0;
+        t.rows = min(BM, a->M_extra - t.a_row0);
+      } else {
+        // the last group whose first m-tile is at most mtile (empty groups share their start)
+        int lo = 0, hi = a->G - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (__builtin_amdgcn_readfirstlane(s_tstart[mid]) <= t.mtile) lo = mid;
+          else hi = mid - 1;
+        }
+        t.group = lo;
+        t.row0 = __builtin_amdgcn_readfirstlane(s_off[lo]) +
+                 (t.mtile - __builtin_amdgcn_readfirstlane(s_tstart[lo])) * BM;
+        t.a_row0 = t.row0;
+        t.rows = min(BM, __builtin_amdgcn_readfirstlane(s_off[lo + 1]) - t.row0);
+      }
+    }
+    if (lane_now() == 0) {
+      s_tile[sl][0] = t.L;
+      s_tile[sl][1] = t.group;
+      s_tile[sl][2] = t.row0;
+      s_tile[sl][3] = t.rows;
+      s_tile[sl][4] = t.a_row0;
+      s_tile[sl][5] = t.extra;
+      s_tile[sl][6] = t.ntile;
+      s_tile[sl][7] = t.mtile;
+    }
+    return t;
+  };
+  // the tile in slot sl (read where needed rather than kept in scalar registers)
+  auto fetch = [&](int sl) {
+    Tile t;
+    t.L = __builtin_amdgcn_readfirstlane(s_tile[sl][0]);
+    t.group = __builtin_amdgcn_readfirstlane(s_tile[sl][1]);
+    t.row0 = __builtin_amdgcn_readfirstlane(s_tile[sl][2]);
+    t.rows = __builtin_amdgcn_readfirstlane(s_tile[sl][3]);
+    t.a_row0 = __builtin_amdgcn_readfirstlane(s_tile[sl][4]);
+    t.extra = __builtin_amdgcn_readfirstlane(s_tile[sl][5]);
+    t.ntile = __builtin_amdgcn_readfirstlane(s_tile[sl][6]);
+    t.mtile = __builtin_amdgcn_readfirstlane(s_tile[sl][7]);
+    return t;
+  };
+
+  if (wave == 0) publish(slot < wsize(X) ? X * pxd + slot : dyn ? draw() : -1, 0);
+  __syncthreads();
+  if (__builtin_amdgcn_readfirstlane(s_tile[0][0]) < 0) return;
+  // the first tile's rows (ordinary loads: no direct load is in flight yet)
+  {
+    const Tile t = fetch(0);
+    if (tid < BM && !p.a_tiled) {
+      const int R = t.a_row0 + min(tid, t.rows - 1);
+      const int src = (!t.extra && p.row_index) ? p.row_index[R] / p.row_divisor : R;
+      s_aoff[tid] = (uint32_t)src * (uint32_t)p.K * 2u;
+      if (A16) s_shift[0][tid] = p.row_shift[src];
     }
   }
   __syncthreads();
-  if (!tile_ok) return;
-  TileInfo ti;
-  ti.group = __builtin_amdgcn_readfirstlane(tile.group);
-  ti.row0 = __builtin_amdgcn_readfirstlane(tile.row0);
-  ti.rows = __builtin_amdgcn_readfirstlane(tile.rows);
-  ti.a_row0 = __builtin_amdgcn_readfirstlane(tile.a_row0);
-  ti.extra = __builtin_amdgcn_readfirstlane(tile.extra);
-  const int ntile = __builtin_amdgcn_readfirstlane(tile_n);
-  const int mtile = __builtin_amdgcn_readfirstlane(tile_m);
-  const GemmBank& bank = ti.extra ? p.extra : p.bank;
-  const int K = p.K;
-  const int nK = K / BK;
 
-  const uint8_t* abase =
-      reinterpret_cast<const uint8_t*>(A16 ? p.a16 : p.a_tiled ? p.a : (ti.extra ? p.a_extra : p.a));
-  if (p.a_tiled) abase += (size_t)mtile * nK * A_BYTES;
-  if (tid < BM && !p.a_tiled) {
-    const int R = ti.a_row0 + min(tid, ti.rows - 1);
-    const int src = (!ti.extra && p.row_index) ? p.row_index[R] / p.row_divisor : R;
-    s_aoff[tid] = (uint32_t)src * (uint32_t)K * 2u;
-    if (A16) s_shift[tid] = p.row_shift[src];
-  }
-  __syncthreads();
-  const int q = lane >> 4;
-  const int nl = lane & 15;
-  // direct load `it` of this wave fills fragment Fi = wave + WAVES*it: row block Fi/4, MFMA step Fi%4
-  uint32_t aoff[A_ITERS];
+  // Per-tile operand bases (uniform).
+  struct Ctx {
+    const uint8_t* abase;
+    const uint8_t* wexp;
+    const uint8_t* sexp;
+    uint32_t t0[NB];
+    uint32_t astride;
+  };
+  auto make_ctx = [&](const Tile& t) {
+    const auto* a = args();
+    Ctx c;
+    const int K = a->K;
+    const size_t rows_per_expert = GATE_UP ? 2 * (size_t)a->N : (size_t)a->N;
+    const uint8_t* w = t.extra ? a->extra.w : a->bank.w;
+    const uint8_t* ws = t.extra ? a->extra.ws : a->bank.ws;
+    const uint16_t* ab = A16 ? a->a16 : a->a_tiled ? a->a : (t.extra ? a->a_extra : a->a);
+    c.abase = reinterpret_cast<const uint8_t*>(ab);
+    if (a->a_tiled) c.abase += (size_t)t.mtile * nK * A_BYTES;
+    c.astride = a->a_tiled ? A_BYTES : BK * 2;
+    c.wexp = w + (size_t)t.group * rows_per_expert * (size_t)(K / 2);
+    c.sexp = ws + (size_t)t.group * rows_per_expert * (size_t)(K / F::kScaleGroup);
 #pragma unroll
-  for (int it = 0; it < A_ITERS; ++it) {
-    const int Fi = wave + WAVES * it;
-    aoff[it] = p.a_tiled ? (uint32_t)(Fi * 1024 + 16 * lane)
-                         : s_aoff[16 * (Fi >> 2) + nl] + (uint32_t)(64 * (Fi & 3) + 16 * q);
-  }
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
-
-  const int ktiles = K / 128;
-  const size_t rows_per_expert = GATE_UP ? 2 * (size_t)p.N : (size_t)p.N;
-  const uint8_t* wexp = bank.w + (size_t)ti.group * rows_per_expert * (size_t)(K / 2);
-  const uint8_t* sexp = bank.ws + (size_t)ti.group * rows_per_expert * (size_t)(K / F::kScaleGroup);
-  uint32_t t0[NB];
+    for (int f = 0; f < NB; ++f)
+      c.t0[f] = __builtin_amdgcn_readfirstlane(
+          (uint32_t)(frag_row_block<NB, GATE_UP, BN, COLS_PER_WAVE>(f, t.ntile, wave, a->N) * (K / 128)));
+    return c;
+  };
+  // direct load `it` of this wave fills fragment Fi = wave + WAVES*it: row block Fi/4, MFMA step
+  // Fi%4 (row offsets from s_aoff, which holds the rows of the tile about to be loaded)
+  auto row_offsets = [&](uint32_t (&ao)[A_ITERS]) {
+    const bool tiled = args()->a_tiled;
+    const int l = lane_now();
 #pragma unroll
-  for (int f = 0; f < NB; ++f)
-    t0[f] = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(frag_row_block<NB, GATE_UP, BN, COLS_PER_WAVE>(f, ntile, wave, p.N) * ktiles));
+    for (int it = 0; it < A_ITERS; ++it) {
+      const int Fi = wave + WAVES * it;
+      ao[it] = tiled ? (uint32_t)(Fi * 1024 + 16 * l)
+                     : s_aoff[16 * (Fi >> 2) + (l & 15)] + (uint32_t)(64 * (Fi & 3) + 16 * (l >> 4));
+    }
+  };
   const uint32_t wlane = (uint32_t)w_lane_offset(lane);
   const uint32_t slane = (uint32_t)F::s_lane(lane);
   const uint32_t wslot0 = (uint32_t)(NA * A_BYTES + wave * W_WAVE);
+  // this lane's bytes of the wave's weight slot: tiles at wq + 1024 f, scale dwords at wsc + 256 f
+  // (two bases; read_w hides them from loop-invariant code motion, which would otherwise hoist
+  // every tile's and every scale's full address into a register of its own)
+  using lds_ptr = const __attribute__((address_space(3))) uint8_t*;
+  lds_ptr wq = (lds_ptr)(__attribute__((address_space(3))) uint8_t*)lds + wslot0 + 16 * lane;
+  lds_ptr wsc = (lds_ptr)(__attribute__((address_space(3))) uint8_t*)lds + wslot0 + NB * 1024 + 4 * lane;
 
-  f32x4 acc[MI][NB];
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int f = 0; f < NB; ++f) acc[i][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto issue_a = [&](int c, int buf) {
-    const uint8_t* src = abase + (size_t)c * (p.a_tiled ? A_BYTES : BK * 2);
+  auto issue_a = [&](const Ctx& t, const uint32_t (&ao)[A_ITERS], int c, int buf) {
+    const uint8_t* src = uniform(t.abase + (size_t)c * t.astride);
 #pragma unroll
     for (int it = 0; it < A_ITERS; ++it)
-      direct_load16(src, aoff[it], lds0 + (uint32_t)(buf * A_BYTES + (wave + WAVES * it) * 1024));
+      direct_load16(src, ao[it], lds0 + (uint32_t)(buf * A_BYTES + (wave + WAVES * it) * 1024));
   };
-  auto issue_w = [&](int c) {
+  auto issue_w = [&](const Ctx& t, int c) {
     const uint32_t dst = lds0 + wslot0;
 #pragma unroll
     for (int f = 0; f < NB; ++f) {
-      const uint32_t t = t0[f] + (uint32_t)c;
-      direct_load16(wexp + (size_t)t * 1024u, wlane, dst + f * 1024);
-      direct_load4(sexp + (size_t)t * (size_t)F::kTileScaleBytes, slane, dst + NB * 1024 + f * 256);
+      const uint32_t tt = t.t0[f] + (uint32_t)c;
+      direct_load16(uniform(t.wexp + (size_t)tt * 1024u), wlane, dst + f * 1024);
+      direct_load4(uniform(t.sexp + (size_t)tt * (size_t)F::kTileScaleBytes), slane, dst + NB * 1024 + f * 256);
     }
   };
   auto wait_vm = [](auto n_const) {
@@ -691,6 +831,109 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
   };
   // every LDS read this wave issued has returned (before a direct load may overwrite what it read)
   auto wait_lds_reads = []() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); };
+  // this wave's weights of one chunk, from its slot to registers
+  auto read_w = [&](uint4 (&bq)[NB], uint32_t (&sc)[NB]) {
+    asm volatile("" : "+v"(wq), "+v"(wsc));
+#pragma unroll
+    for (int f = 0; f < NB; ++f) {
+      typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+      const u32x4_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(wq + f * 1024);
+      bq[f] = uint4{v.x, v.y, v.z, v.w};
+      sc[f] = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(wsc + f * 256);
+    }
+  };
+  auto frag = [&](const uint8_t* buf, int j, int i) -> OpT {
+    return *reinterpret_cast<const OpT*>(buf + (STEPS * i + j) * 1024 + 16 * lane);
+  };
+  // The values exist at this point of the program: code generation may otherwise compute the
+  // next step's weight operands next to their first use, after the step's scheduling region,
+  // instead of in it between the MFMAs.
+  auto pin = [](OpT (&v)[NB]) {
+#pragma unroll
+    for (int f = 0; f < NB; ++f) asm volatile("" : "+v"(v[f]));
+  };
+
+  int par = 0;   // tile slot (s_tile, s_shift) of the current tile
+  int cb = 0;    // LDS buffer of the current tile's first chunk
+  bool has_next = false;
+
+  // First tile: its chunk 0 (weights into the slot, activations into buffer 0) landed and visible,
+  // its chunk 1 activations in flight.  Every later tile starts in the same state, its first two
+  // chunks loaded during the last two chunks of the tile before; no register carries over from
+  // tile to tile (the row-count variants below do not share registers well).
+  {
+    const Ctx c0 = make_ctx(fetch(0));
+    uint32_t ao[A_ITERS];
+    row_offsets(ao);
+    issue_w(c0, 0);
+    issue_a(c0, ao, 0, 0);
+    if (nK > 1) {
+      issue_a(c0, ao, 1, 1);
+      wait_vm(IntC<A_ITERS>{});
+    } else {
+      wait_vm(IntC<0>{});
+    }
+    __syncthreads();
+  }
+
+  // Bookkeeping of the next tile, spread over the current tile's first chunks so that each step's
+  // loads are covered by a wait the main loop does anyway (none of them is visible to the
+  // compiler, except the counter's atomic, whose result wave 0 reads one chunk later):
+  //   chunk 0, step 3, wave 0: draw a ticket (counters);
+  //   chunk 1, step 3, wave 0: the next tile into the other slot, its row_index entries into
+  //   s_ridx;
+  //   chunk 2, top: every wave reads whether there is one;
+  //   chunk 3, top: the next tile's row offsets into s_aoff (and its fp16 row shifts, by direct
+  //   loads, into the other s_shift slot);
+  //   chunk nK - 2, top: its activations of chunk 0 are issued.
+  auto hook_top = [&](int c) {
+    if (c == 2) {
+      has_next = __builtin_amdgcn_readfirstlane(s_tile[par ^ 1][0]) >= 0;
+    } else if (c == 3 && has_next) {
+      const auto* a = args();
+      if (!a->a_tiled && wave < BM / 64) {
+        const int r = wave * 64 + lane_now();
+        const Tile nt = fetch(par ^ 1);
+        const int R = nt.a_row0 + min(r, nt.rows - 1);
+        const int src = (!nt.extra && a->row_index) ? (int)(s_ridx[r] / (uint32_t)a->row_divisor) : R;
+        s_aoff[r] = (uint32_t)src * (uint32_t)a->K * 2u;
+        if (A16)
+          direct_load4(uniform(a->row_shift), 4u * (uint32_t)src, shift0 + (uint32_t)((par ^ 1) * BM * 4 + wave * 256));
+      }
+    }
+  };
+  auto hook_mid = [&](int c) {
+    if (wave != 0) return;
+    if (c == 0) {
+      if (dyn && ywin < kXcds && wsize((X + ywin) % kXcds) > spx) {
+        int32_t* const ctr = args()->tile_ctr;
+        if (lane_now() == 0)
+          tpend = __hip_atomic_fetch_add(ctr + (X + ywin) % kXcds, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        pend = true;
+      }
+    } else if (c == 1) {
+      int Ln;
+      if (dyn) {
+        Ln = draw();
+      } else {
+        Ln = __builtin_amdgcn_readfirstlane(s_tile[par][0]) + spx;
+        if (Ln - X * pxd >= wsize(X)) Ln = -1;
+      }
+      const Tile t = publish(Ln, par ^ 1);
+      const auto* a = args();
+      if (Ln >= 0 && !t.extra && a->row_index && !a->a_tiled) {
+        const uint8_t* ri = uniform(a->row_index);
+        const int l = lane_now();
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          direct_load4(ri, 4u * (uint32_t)(t.a_row0 + min(64 * h + l, t.rows - 1)), ridx0 + 256 * h);
+      }
+    }
+  };
+
+  // chunk modes: this tile's loads two ahead (MID), and the last two chunks, which load the next
+  // tile's first two chunks if there is one (PEN, LAST)
+  constexpr int MID = 0, PEN = 1, LAST = 2;
 
   auto run = [&](auto rb_const) {
     constexpr int RB = decltype(rb_const)::value;
@@ -704,27 +947,10 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
     constexpr int VALU_STEP = NB * (A16 ? 19 : (FMT == kFmtMxfp4 ? 11 : 33)) / 2;
     constexpr int VPM = (VALU_STEP + NB * RB - 1) / (NB * RB);
     constexpr int VPM_A = H1 > 1 ? (VALU_STEP + NB * (H1 - 1) - 1) / (NB * (H1 - 1)) : VALU_STEP;
-    const uint8_t* wl = lds + wslot0;
-    uint4 bq[NB];
-    uint32_t sc[NB];
-    auto read_w = [&]() {
-#pragma unroll
-      for (int f = 0; f < NB; ++f) {
-        bq[f] = *reinterpret_cast<const uint4*>(wl + f * 1024 + 16 * lane);
-        sc[f] = *reinterpret_cast<const uint32_t*>(wl + NB * 1024 + f * 256 + 4 * lane);
-      }
-    };
-    auto frag = [&](const uint8_t* buf, int j, int i) -> OpT {
-      return *reinterpret_cast<const OpT*>(buf + (STEPS * i + j) * 1024 + 16 * lane);
-    };
+    // accumulators of the tile's row blocks (blocks past RB are never touched)
+    f32x4 acc[MI][NB];
+    // weight operands of the current MFMA step
     OpT wcur[NB];
-    // The values exist at this point of the program: code generation may otherwise compute the
-    // next step's weight operands next to their first use, after the step's scheduling region,
-    // instead of in it between the MFMAs.
-    auto pin = [](OpT (&v)[NB]) {
-#pragma unroll
-      for (int f = 0; f < NB; ++f) asm volatile("" : "+v"(v[f]));
-    };
     // Row blocks [I0, I1) of MFMA step j (fragments in x[i], x[0..D) read before); before block i
     // the fragment D blocks ahead is read: block i + D of this step, or past the step's end, block
     // i + D - RB of the next step (buffer nbuf, step nj) when NXT.
@@ -768,34 +994,59 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
       }
     };
 
-    // prologue: chunk 0's weights and activations landed and in registers, chunk 1's weights and
-    // activations in flight
-    issue_w(0);
-    issue_a(0, 0);
-    if (nK > 1) {
-      issue_a(1, 1);
-      wait_vm(IntC<A_ITERS>{});
-    } else {
-      wait_vm(IntC<0>{});
-    }
-    __syncthreads();
-    read_w();
+    // tile start: chunk 0 landed (weights in the slot, activations in buffer cb) and chunk 1's
+    // activations in flight; the weights of chunk 0 go to registers, those of chunk 1 into the slot
+    const Ctx cur = make_ctx(fetch(par));
+    uint32_t aoff[A_ITERS];
+    row_offsets(aoff);
+    uint4 bq[NB];
+    uint32_t sc[NB];
+    read_w(bq, sc);
     wait_lds_reads();
-    if (nK > 1) issue_w(1);
-    OpT xs[D];
+    if (nK > 1) issue_w(cur, 1);
 #pragma unroll
     for (int f = 0; f < NB; ++f) wcur[f] = w_op(bq[f], sc[f], 0);
-#pragma unroll
-    for (int d = 0; d < D; ++d) xs[d] = frag(lds, 0, d);
     // Invariant at the top of chunk c: bq/sc hold chunk c's weights, wcur the operands of its
     // first MFMA step and xs that step's first D activation fragments; loads in flight, oldest
-    // first: the activations, then the weights, of chunk c + 1.
-    auto chunk = [&](int c, auto next_const, auto more_const) {
-      constexpr bool NEXT = decltype(next_const)::value;
-      constexpr bool MORE = decltype(more_const)::value;
-      if (MORE) issue_a(c + 2, (c + 2) % NA);
-      const uint8_t* abuf = lds + (c % NA) * A_BYTES;
-      const uint8_t* anext = lds + ((c + 1) % NA) * A_BYTES;
+    // first: the activations, then the weights, of chunk c + 1 (of this tile or, past its end, the
+    // next tile's activations of its chunk 0, then its weights of chunk 0).
+    OpT xs[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) xs[d] = frag(lds + cb * A_BYTES, 0, d);
+    // zero, opaque and distinct per RB: otherwise code generation merges the identical clearing of
+    // every variant into one place and holds a second set of accumulators beside the previous
+    // tile's, which do not fit in the registers
+    f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    asm volatile("; zero rb %1" : "+v"(zero) : "n"(RB));
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int f = 0; f < NB; ++f) acc[i][f] = zero;
+    has_next = false;
+
+    auto chunk = [&](int c, auto mode_const) {
+      constexpr int MODE = decltype(mode_const)::value;
+      // loads this chunk issues: this tile's chunk c + 2 (MID), the next tile's chunk c + 2 - nK
+      // (PEN, LAST, when there is a next tile)
+      const bool loads = MODE == MID || has_next;
+      // step 3 reads the following chunk's weights and first activation fragments (this tile's)
+      constexpr bool NEXT = MODE != LAST;
+      int bc = cb + c % NA;
+      if (bc >= NA) bc -= NA;
+      const uint8_t* abuf = lds + bc * A_BYTES;
+      const uint8_t* anext = lds + (bc == NA - 1 ? 0 : bc + 1) * A_BYTES;
+      const int b2 = bc == 0 ? NA - 1 : bc - 1;   // (bc + 2) % 3: the buffer chunk c - 1 used
+      if constexpr (MODE == MID) {
+        if (chain) hook_top(c);
+        issue_a(cur, aoff, c + 2, b2);
+      }
+      // the next tile's operand bases (PEN, LAST)
+      const Ctx nxt = MODE == MID ? cur : make_ctx(fetch(par ^ 1));
+      if (MODE != MID && loads) {
+        uint32_t ao[A_ITERS];
+        row_offsets(ao);
+        issue_a(nxt, ao, c + 2 - nK, b2);
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < STEPS; ++j) {
@@ -810,29 +1061,40 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
           pin(wnext);
           interleave(IntC<RB>{}, IntC<0>{}, IntC<VPM>{}, IntC<VPM>{});
           __builtin_amdgcn_sched_barrier(0);
-        } else if (NEXT) {
-          // this wave's activations and weights of chunk c + 1 have landed (only the activations
-          // of chunk c + 2, issued last, may be in flight); the weights go from the wave's own
-          // slot to registers and are dequantized for the next chunk's first step
-          wait_vm(IntC<MORE ? A_ITERS : 0>{});
-          read_w();
+        } else if constexpr (NEXT) {
+          // this wave's activations and weights of the following chunk have landed (only the
+          // activations issued at the top of this chunk may be in flight); the weights go from the
+          // wave's own slot to registers and are dequantized for the following chunk's first step
+          if (loads) wait_vm(IntC<A_ITERS>{});
+          else wait_vm(IntC<0>{});
+          read_w(bq, sc);
 #pragma unroll
           for (int f = 0; f < NB; ++f) wnext[f] = w_op(bq[f], sc[f], 0);
           blocks(IntC<0>{}, IntC<H1>{}, x, abuf, j, anext, 0, IntC<0>{});
           pin(wnext);
           interleave(IntC<H1>{}, IntC<2 * NB>{}, IntC<VPM_A>{}, IntC<0>{});
           __builtin_amdgcn_sched_barrier(0);
-          // the slot is free again: the weights of chunk c + 2 go into it; after the barrier every
-          // wave's activations of chunk c + 1 are in LDS and every read of chunk c's buffer has
-          // returned
+          if constexpr (MODE == MID) {
+            if (chain) hook_mid(c);
+          }
+          // the slot is free again: the weights two chunks ahead go into it; after the barrier
+          // every wave's activations of the following chunk are in LDS and every read of this
+          // chunk's buffer has returned
           wait_lds_reads();
-          if (MORE) issue_w(c + 2);
+          if constexpr (MODE == MID) issue_w(cur, c + 2);
+          else if (loads) issue_w(nxt, c + 2 - nK);
           __syncthreads();
           blocks(IntC<H1>{}, IntC<RB>{}, x, abuf, j, anext, 0, IntC<1>{});
           interleave(IntC<RB - H1>{}, IntC<0>{}, IntC<VPM>{}, IntC<VPM>{});
           __builtin_amdgcn_sched_barrier(0);
         } else {
           blocks(IntC<0>{}, IntC<RB>{}, x, abuf, j, abuf, j, IntC<0>{});
+          // the next tile's chunk 0 has landed (this wave's share; its activations of chunk 1 may
+          // be in flight); after the barrier every wave's share is in LDS and every read of this
+          // chunk's buffer has returned
+          if (loads) wait_vm(IntC<A_ITERS>{});
+          wait_lds_reads();
+          __syncthreads();
         }
         if (j + 1 < STEPS || NEXT) {
 #pragma unroll
@@ -842,23 +1104,55 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
         }
       }
     };
-    for (int c = 0; c + 2 < nK; ++c) chunk(c, IntC<1>{}, IntC<1>{});
-    if (nK > 1) chunk(nK - 2, IntC<1>{}, IntC<0>{});
-    chunk(nK - 1, IntC<0>{}, IntC<0>{});
+    for (int c = 0; c + 2 < nK; ++c) chunk(c, IntC<MID>{});
+    if (nK > 1) chunk(nK - 2, IntC<PEN>{});
+    chunk(nK - 1, IntC<LAST>{});
     // only the RB blocks with real rows are stored: the other accumulators are never live
-    epilogue<MI, NB, GATE_UP, BN, COLS_PER_WAVE, WFmt<FMT>::kGlobalScale>(p, bank, ti, ntile, acc, mtile,
-                                                                          A16 ? s_shift : nullptr, IntC<RB>{});
+    const Tile t = fetch(par);
+    const auto* a = args();
+    GemmProblem pe{};
+    pe.N = a->N;
+    pe.out = a->out;
+    pe.out_tiled = a->out_tiled;
+    pe.a_gscale = a->a_gscale;
+    GemmBank be{};
+    be.gs = t.extra ? a->extra.gs : a->bank.gs;
+    be.gs_per_expert = t.extra ? a->extra.gs_per_expert : a->bank.gs_per_expert;
+    const TileInfo ti{t.group, t.row0, t.rows, t.a_row0, t.extra};
+    epilogue_at<MI, NB, GATE_UP, BN, COLS_PER_WAVE, WFmt<FMT>::kGlobalScale>(
+        pe, be, ti, t.ntile, acc, t.mtile, A16 ? s_shift[par] : nullptr, IntC<RB>{}, lane_now(), wave);
   };
-  switch ((ti.rows + 15) / 16) {
-    case 1: run(IntC<1>{}); break;
-    case 2: run(IntC<2>{}); break;
-    case 3: run(IntC<3>{}); break;
-    case 4: run(IntC<4>{}); break;
-    case 5: run(IntC<5>{}); break;
-    case 6: run(IntC<6>{}); break;
-    case 7: run(IntC<7>{}); break;
-    default: run(IntC<8>{}); break;
+  for (;;) {
+    switch ((__builtin_amdgcn_readfirstlane(s_tile[par][3]) + 15) / 16) {
+      case 1: run(IntC<1>{}); break;
+      case 2: run(IntC<2>{}); break;
+      case 3: run(IntC<3>{}); break;
+      case 4: run(IntC<4>{}); break;
+      case 5: run(IntC<5>{}); break;
+      case 6: run(IntC<6>{}); break;
+      case 7: run(IntC<7>{}); break;
+      default: run(IntC<8>{}); break;
+    }
+    if (!has_next) break;
+    // the next tile: its chunk 0 landed (buffer cb + nK), chunk 1's activations in flight; s_aoff
+    // holds its rows
+    par ^= 1;
+    cb = (cb + nK) % NA;
   }
+}
+
+// Compute units of the current device (looked up once per device; 0 if the query fails).
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cus[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 template <int NB, bool GATE_UP, int WAVES, int FMT>
@@ -873,6 +1167,14 @@ moe_status_t launch_tall(const GemmProblem& p, hipStream_t stream) {
   grid = (grid + kXcds - 1) / kXcds * kXcds;
   if (grid > 0x7FFFFFFFLL) return MOE_ERR_INVALID_ARGUMENT;
   if constexpr (WAVES == 8) {
+    if (p.G > kTallMaxGroups) return MOE_ERR_INVALID_ARGUMENT;
+    // six K chunks or more: one workgroup per compute unit walks its tiles (shorter K: one tile per
+    // workgroup, the kernel never chains)
+    if (p.K / kTallBK >= 6) {
+      const int cus = device_cus();
+      if (cus <= 0) return MOE_ERR_HIP;
+      grid = std::min(grid, (long long)std::max(kXcds, cus / kXcds * kXcds));
+    }
     if constexpr (GATE_UP && FMT == kFmtNvfp4) {
       if (p.a16) {
         hipLaunchKernelGGL((grouped_gemm_tall_lds_kernel<NB, GATE_UP, FMT, true>), dim3((unsigned)grid), dim3(512), 0,

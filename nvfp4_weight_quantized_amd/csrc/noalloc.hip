@@ -8,7 +8,8 @@
 // looked up once per device with hipGetSymbolAddress, with that device current, and only that
 // address is ever passed to a kernel.  Each device holds its own copy of the array at its own
 // address.  The forward needs no part of its workspace to start at zero (every buffer is written
-// before it is read), so nothing is cleared between calls.  Calls on one device share the array:
+// before it is read, and its counters are cleared by its own first kernel), so nothing is cleared
+// between calls.  Calls on one device share the array:
 // two calls that overlap in time on one device race.
 #include <mutex>
 

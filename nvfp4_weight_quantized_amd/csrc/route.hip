@@ -22,8 +22,8 @@ constexpr int kGemvTokens = 8;     // tokens per workgroup
 // consecutive h of the expert's router row per 2048-wide pass and dots them with the same h of
 // every token, all loads of a pass issued together; the per-token sums are then reduced across
 // the workgroup (wave sums, then the four waves in order).
-// `zero` (optional): n_zero words the first workgroup clears (the hand-off counters of the fused
-// decode kernel that follows in the same stream).
+// `zero` (optional): n_zero words the first workgroup clears (counters of the kernels that follow
+// in the same stream: the fused decode kernel's hand-offs, the grouped GEMMs' tile counters).
 __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ wr,
                                                            const float* __restrict__ bias, int T, int H, int E,
@@ -88,10 +88,13 @@ typedef uint32_t u32x4_r __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ wr,
                                                           const float* __restrict__ bias, int T, int H,
-                                                          int E, float* __restrict__ logits) {
+                                                          int E, float* __restrict__ logits,
+                                                          int32_t* __restrict__ zero, int n_zero) {
   __shared__ __attribute__((aligned(16))) uint16_t As[kRB][kRK + kRPad];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[kRB][kRK + kRPad];
   const int tid = threadIdx.x;
+  if (zero && blockIdx.x == 0)
+    for (int i = tid; i < n_zero; i += 256) zero[i] = 0;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -197,12 +200,11 @@ moe_status_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, c
     hipLaunchKernelGGL(router_small_kernel, dim3(E, (T + kGemvTokens - 1) / kGemvTokens), dim3(256), 0, stream, x,
                        w_router, bias, (int)T, (int)H, (int)E, logits, zero, (int)n_zero);
   } else {
-    if (zero) return MOE_ERR_INVALID_ARGUMENT;   // the clearing rides on the few-token kernel only
     if (H % kRK != 0) return MOE_ERR_INVALID_ARGUMENT;
     const long long tiles = (long long)((E + kRB - 1) / kRB) * ((T + kRB - 1) / kRB);
     const long long grid = (tiles + kRXcds - 1) / kRXcds * kRXcds;
     hipLaunchKernelGGL(router_mfma_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, w_router, bias, (int)T,
-                       (int)H, (int)E, logits);
+                       (int)H, (int)E, logits, zero, (int)n_zero);
   }
   return launch_status();
 }
