@@ -25,12 +25,6 @@ __device__ __forceinline__ float silu(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.44269504088896341f));
 }
 
-__device__ __forceinline__ void store_bf16x4(uint16_t* dst, float a, float b, float c, float d) {
-  const uint32_t lo = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-  const uint32_t hi = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
-  *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
-}
-
 constexpr int kXcds = 8;
 
 // This lane's index in its wave, computed where it is used (the mask count is opaque to the
@@ -143,64 +137,82 @@ __device__ __forceinline__ float epilogue_act_gscale(const P&) { return 1.f; }
 
 // Epilogue: scale the accumulators by the global scale(s), SiLU(gate)*up for gate/up, store bf16.
 // acc[i][f] holds, in lane l = 16q + n, output row 16i + n and the four columns 4q..4q+3 of
-// fragment f's 16 columns.
+// fragment f's 16 columns (gate/up: fragments NB/2.. hold the up columns of fragments 0..).
 // GSCALE: the bank carries fp32 global scales (NVFP4); otherwise the scale is 1.
 // rshift (optional, gate/up): per tile row, the power of two the activation row was scaled by
 // (2^rshift[row]); the sums are scaled back by 2^-rshift[row] (exact) before SiLU.
 // RBE (default MI): the 16-row blocks that can hold rows of the tile; blocks past it are not read,
 // so a caller that never touched their accumulators need not keep them.
-// epilogue_at takes the lane and wave indices from the caller.
-template <int MI, int NB, bool GATE_UP, int BN, int COLS_PER_WAVE, bool GSCALE, class P, int RBE = MI>
-__device__ __forceinline__ void epilogue_at(const P& p, const GemmBank& bank, const TileInfo& ti, int ntile,
+// epilogue_at takes the weight global scales of the tile's expert (g0: gate or down, g1: up; 1
+// without) and the lane and wave indices from the caller.
+template <int MI, int NB, bool GATE_UP, int BN, int COLS_PER_WAVE, class P, int RBE = MI>
+__device__ __forceinline__ void epilogue_at(const P& p, float g0, float g1, const TileInfo& ti, int ntile,
                                             const f32x4 (&acc)[MI][NB], int mtile, const int* rshift, IntC<RBE>,
                                             int lane, int wave) {
   const int q = lane >> 4, nl = lane & 15;
-  const float* gs = GSCALE ? bank.gs + (size_t)ti.group * bank.gs_per_expert : nullptr;
   const float da = epilogue_act_gscale(p);
-  const int col0 = ntile * BN + wave * COLS_PER_WAVE + 4 * q;
-  if (GATE_UP) {
-    const float dg = (gs ? gs[0] : 1.f) * da, du = (gs ? gs[1] : 1.f) * da;
+  // output fragments per wave (16 columns each) and their first column
+  constexpr int NF = GATE_UP ? NB / 2 : NB;
+  const int colw = ntile * BN + wave * COLS_PER_WAVE;
+  // Fragments are stored in pairs (f, f + 1), 16 bytes per lane: v_permlane16_swap exchanges the
+  // pair's packed values between the quarters q and q ^ 1 of the wave (lanes 16 apart), after which
+  // lane (q, n) holds the eight consecutive columns of row n starting pc columns after the pair's
+  // first: quarter 0 the first fragment's columns 0..7, quarter 2 its 8..15, quarters 1 and 3 the
+  // second fragment's 0..7 and 8..15.  The four lanes of a row then write its 64 bytes with one
+  // store instruction (the tiled layout's 16-byte lane slots, whole), instead of two with 8 bytes
+  // per lane and 32 per row; fewer, wider stores retire sooner, and the direct loads of the next
+  // chunks wait behind them (the memory counter counts stores).  An odd last fragment is stored
+  // 8 bytes per lane as before.  The swap runs in every lane, rows past the tile's included.
+  const int pc = 16 * (q & 1) + 8 * (q >> 1);
+  auto pack4 = [](float a, float b, float c, float d) {
+    return uint2{(uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16),
+                 (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16)};
+  };
+  // address of column col (of this lane's row) in block i
+  auto dst = [&](int i, int row, int col) -> uint16_t* {
+    if (GATE_UP && p.out_tiled) {
+      // tiled layout: column col -> chunk col/128, step (col%128)/32, lane slot (col%32)/8
+      const int kk = col & 127;
+      const size_t byte = ((size_t)(mtile * (p.N >> 7) + (col >> 7)) * 32 + 4 * i + (kk >> 5)) * 1024 +
+                          (size_t)(16 * (((kk >> 3) & 3) * 16 + nl) + 2 * (kk & 7));
+      return p.out_tiled + byte / 2;
+    }
+    return p.out + (size_t)(ti.row0 + row) * p.N + col;
+  };
 #pragma unroll
-    for (int i = 0; i < RBE; ++i) {
-      const int row = 16 * i + nl;
-      if (row >= ti.rows) continue;
-      uint16_t* orow = p.out + (size_t)(ti.row0 + row) * p.N + col0;
+  for (int i = 0; i < RBE; ++i) {
+    const int row = 16 * i + nl;
+    const bool valid = row < ti.rows;
+    uint2 v[NF];
+    if (GATE_UP) {
+      const float dg = g0 * da, du = g1 * da;
       const int sh = rshift ? -rshift[row] : 0;
 #pragma unroll
-      for (int f = 0; f < NB / 2; ++f) {
+      for (int f = 0; f < NF; ++f) {
         float h[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float g = acc[i][f][r] * dg, u = acc[i][f + NB / 2][r] * du;
+          float g = acc[i][f][r] * dg, u = acc[i][f + NF][r] * du;
           if (rshift) {
             g = ldexpf(g, sh);
             u = ldexpf(u, sh);
           }
           h[r] = silu(g) * u;
         }
-        if (p.out_tiled) {
-          // tiled layout: column col -> chunk col/128, step (col%128)/32, lane group (col%32)/8
-          const int col = col0 + 16 * f;
-          const int kk = col & 127;
-          const size_t byte = ((size_t)(mtile * (p.N >> 7) + (col >> 7)) * 32 + 4 * i + (kk >> 5)) * 1024 +
-                              (size_t)(16 * (((kk >> 3) & 3) * 16 + nl) + 2 * (kk & 7));
-          store_bf16x4(p.out_tiled + byte / 2, h[0], h[1], h[2], h[3]);
-        } else {
-          store_bf16x4(orow + 16 * f, h[0], h[1], h[2], h[3]);
-        }
+        v[f] = pack4(h[0], h[1], h[2], h[3]);
       }
-    }
-  } else {
-    const float dd = (gs ? gs[0] : 1.f) * da;
+    } else {
+      const float dd = g0 * da;
 #pragma unroll
-    for (int i = 0; i < RBE; ++i) {
-      const int row = 16 * i + nl;
-      if (row >= ti.rows) continue;
-      uint16_t* orow = p.out + (size_t)(ti.row0 + row) * p.N + col0;
-#pragma unroll
-      for (int f = 0; f < NB; ++f)
-        store_bf16x4(orow + 16 * f, acc[i][f][0] * dd, acc[i][f][1] * dd, acc[i][f][2] * dd, acc[i][f][3] * dd);
+      for (int f = 0; f < NF; ++f) v[f] = pack4(acc[i][f][0] * dd, acc[i][f][1] * dd, acc[i][f][2] * dd, acc[i][f][3] * dd);
     }
+#pragma unroll
+    for (int f = 0; f + 1 < NF; f += 2) {
+      const auto lo = __builtin_amdgcn_permlane16_swap(v[f].x, v[f + 1].x, false, false);
+      const auto hi = __builtin_amdgcn_permlane16_swap(v[f].y, v[f + 1].y, false, false);
+      if (valid) *reinterpret_cast<uint4*>(dst(i, row, colw + 16 * f + pc)) = uint4{lo[0], hi[0], lo[1], hi[1]};
+    }
+    if (NF % 2 && valid) *reinterpret_cast<uint2*>(dst(i, row, colw + 16 * (NF - 1) + 4 * q)) = v[NF - 1];
   }
 }
 
@@ -208,8 +220,10 @@ template <int MI, int NB, bool GATE_UP, int BN, int COLS_PER_WAVE, bool GSCALE, 
 __device__ __forceinline__ void epilogue(const P& p, const GemmBank& bank, const TileInfo& ti, int ntile,
                                          const f32x4 (&acc)[MI][NB], int mtile = 0,
                                          const int* rshift = nullptr, IntC<RBE> = {}) {
-  epilogue_at<MI, NB, GATE_UP, BN, COLS_PER_WAVE, GSCALE>(p, bank, ti, ntile, acc, mtile, rshift, IntC<RBE>{},
-                                                         (int)(threadIdx.x & 63), (int)(threadIdx.x >> 6));
+  const float* gs = GSCALE ? bank.gs + (size_t)ti.group * bank.gs_per_expert : nullptr;
+  epilogue_at<MI, NB, GATE_UP, BN, COLS_PER_WAVE>(p, gs ? gs[0] : 1.f, (GATE_UP && gs) ? gs[1] : 1.f, ti, ntile, acc,
+                                                  mtile, rshift, IntC<RBE>{}, (int)(threadIdx.x & 63),
+                                                  (int)(threadIdx.x >> 6));
 }
 
 }  // namespace

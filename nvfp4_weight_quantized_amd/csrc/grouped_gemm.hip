@@ -295,8 +295,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmProblem p) {
 //  * Tile order is XCD-aware: workgroup b runs on XCD b % 8; each XCD walks a contiguous range of
 //    (m-tile, n-tile) pairs, n fastest, so the A rows of an m-tile are reused from that XCD's L2.
 //  * Launched with WAVES = 4 (two workgroups per CU, two waves per SIMD, at most 256 registers per
-//    lane) for the NVFP4 down GEMM (measured as fast as the eight-wave kernel below or 1% faster),
-//    the MXFP4 down GEMM when its width is not a multiple of 512, and gate/up outputs whose width is
+//    lane) for down GEMMs whose width is not a multiple of 512 and gate/up outputs whose width is
 //    not a multiple of 256; the rest takes the eight-wave kernel below (one workgroup per CU).  The
 //    WAVES = 8 form of this kernel (three A buffers) is kept compilable but not launched.
 constexpr int kTallBK = 128;
@@ -537,9 +536,18 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
 
 // ------------------------------------------------------------------------------------------
 // Tall tiles with eight waves (two per SIMD, one workgroup per CU), every operand by direct loads:
-// the gate/up kernel for 128-row tiles whenever the output width is a multiple of 256 (and the MXFP4
-// down kernel when it is a multiple of 512).  Each wave holds all 128 rows of the tile and NB weight
+// the gate/up kernel for 128-row tiles whenever the output width is a multiple of 256, and the
+// down kernel when it is a multiple of 512.  Each wave holds all 128 rows of the tile and NB weight
 // fragments; the workgroup covers 8 * 16 * NB weight rows.
+//  * Persistent (K of six chunks or more): one workgroup per compute unit walks its tiles.  Tiles
+//    come from per-XCD counters (the forward's workspace), each XCD drawing from its own window of
+//    the tile list and then from the others'; without counters a workgroup takes every spx-th tile
+//    of its XCD's window.  The next tile is found during the current one's first chunks (tile list
+//    and group offsets in LDS), its rows gathered, and its first two chunks loaded during the
+//    current one's last two, so consecutive tiles run back to back (measured: 5% off the prefill
+//    gate/up time, 4% off the long prefill's, against one workgroup per tile).  Nothing crosses
+//    from tile to tile in registers: the main loop's row-count variants do not share registers
+//    well, and state passed between them spilled.
 //  * Staging: activation chunks (32 KB, fragment order as above) by direct loads into three LDS
 //    buffers, two chunks ahead; each wave's weight tiles (1 KB each) and their scale dwords (one per
 //    lane) by direct loads into the wave's own LDS slot, one chunk ahead, read back into registers
@@ -731,17 +739,20 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
     }
     return t;
   };
-  // the tile in slot sl (read where needed rather than kept in scalar registers)
+  // the tile in slot sl, read where needed (the address is hidden from the optimizer, which would
+  // otherwise keep an earlier read of the slot in registers instead)
   auto fetch = [&](int sl) {
+    const __attribute__((address_space(3))) int* v = (__attribute__((address_space(3))) int*)&s_tile[sl][0];
+    asm volatile("" : "+v"(v));
     Tile t;
-    t.L = __builtin_amdgcn_readfirstlane(s_tile[sl][0]);
-    t.group = __builtin_amdgcn_readfirstlane(s_tile[sl][1]);
-    t.row0 = __builtin_amdgcn_readfirstlane(s_tile[sl][2]);
-    t.rows = __builtin_amdgcn_readfirstlane(s_tile[sl][3]);
-    t.a_row0 = __builtin_amdgcn_readfirstlane(s_tile[sl][4]);
-    t.extra = __builtin_amdgcn_readfirstlane(s_tile[sl][5]);
-    t.ntile = __builtin_amdgcn_readfirstlane(s_tile[sl][6]);
-    t.mtile = __builtin_amdgcn_readfirstlane(s_tile[sl][7]);
+    t.L = __builtin_amdgcn_readfirstlane(v[0]);
+    t.group = __builtin_amdgcn_readfirstlane(v[1]);
+    t.row0 = __builtin_amdgcn_readfirstlane(v[2]);
+    t.rows = __builtin_amdgcn_readfirstlane(v[3]);
+    t.a_row0 = __builtin_amdgcn_readfirstlane(v[4]);
+    t.extra = __builtin_amdgcn_readfirstlane(v[5]);
+    t.ntile = __builtin_amdgcn_readfirstlane(v[6]);
+    t.mtile = __builtin_amdgcn_readfirstlane(v[7]);
     return t;
   };
 
@@ -1115,12 +1126,19 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
     pe.out = a->out;
     pe.out_tiled = a->out_tiled;
     pe.a_gscale = a->a_gscale;
-    GemmBank be{};
-    be.gs = t.extra ? a->extra.gs : a->bank.gs;
-    be.gs_per_expert = t.extra ? a->extra.gs_per_expert : a->bank.gs_per_expert;
+    // the expert's global scales by scalar loads (through the constant address space: they are not
+    // written while the kernel runs), which leave the direct loads in flight alone
+    float g0 = 1.f, g1 = 1.f;
+    if constexpr (WFmt<FMT>::kGlobalScale) {
+      const float* gs = t.extra ? a->extra.gs : a->bank.gs;
+      const int per = t.extra ? a->extra.gs_per_expert : a->bank.gs_per_expert;
+      const auto* gk = (const __attribute__((address_space(4))) float*)(gs + (size_t)t.group * per);
+      g0 = gk[0];
+      if (GATE_UP) g1 = gk[1];
+    }
     const TileInfo ti{t.group, t.row0, t.rows, t.a_row0, t.extra};
-    epilogue_at<MI, NB, GATE_UP, BN, COLS_PER_WAVE, WFmt<FMT>::kGlobalScale>(
-        pe, be, ti, t.ntile, acc, t.mtile, A16 ? s_shift[par] : nullptr, IntC<RB>{}, lane_now(), wave);
+    epilogue_at<MI, NB, GATE_UP, BN, COLS_PER_WAVE>(pe, g0, g1, ti, t.ntile, acc, t.mtile,
+                                                    A16 ? s_shift[par] : nullptr, IntC<RB>{}, lane_now(), wave);
   };
   for (;;) {
     switch ((__builtin_amdgcn_readfirstlane(s_tile[par][3]) + 15) / 16) {
@@ -1263,11 +1281,10 @@ moe_status_t launch_format(const GemmProblem& p, hipStream_t stream) {
   const bool wide = (p.N % 256) == 0;
   if (avg <= 16) return launch_small<false, FMT>(p, stream);
   if (avg <= 32) return wide ? launch_cfg<4, 4, 128, false, FMT>(p, stream) : launch_cfg<4, 2, 128, false, FMT>(p, stream);
-  // down: four waves, two workgroups per CU (measured 2-6% faster than the eight-wave kernel at
-  // every prefill shape, whose 512-column tiles halve the workgroup count of this short-K GEMM)
-  // MXFP4 (0.7 VALU instructions of dequantization per weight element) on the eight-wave kernel's
-  // 512-column tiles: 5% faster than the four-wave kernel at the prefill shape
-  if (FMT == kFmtMxfp4 && p.N % 512 == 0) return launch_tall<4, false, 8, FMT>(p, stream);
+  // down: the eight-wave kernel's 512-column tiles where the width allows (one workgroup per CU
+  // walking its tiles: 6% faster than the four-wave kernel with two workgroups per CU at both
+  // prefill shapes, NVFP4; 5% for MXFP4), else four waves
+  if (p.N % 512 == 0) return launch_tall<4, false, 8, FMT>(p, stream);
   return wide ? launch_tall<4, false, 4, FMT>(p, stream) : launch_tall<2, false, 4, FMT>(p, stream);
 }
 }  // namespace
