@@ -95,6 +95,45 @@ def test_rows_of_widely_different_magnitude_on_128_row_tiles():
             parity.assert_close(got[t:t + 1], res["out"][t:t + 1], f"token {t}")
 
 
+def test_persistent_gemm_tiles_chain_and_steal():
+    """More 128-row tiles than workgroups, down K at the six-chunk minimum for chaining, routing
+    skewed so that the XCD windows hold very different work: the forward (tiles drawn from the
+    workspace counters, stolen across windows) matches the per-stage entry points (fixed share per
+    workgroup) on every token, two forwards in a row agree bitwise (the counters start at zero each
+    time), and sampled tokens match the oracle."""
+    T, H, I, E, k = 8192, 1024, 768, 16, 2
+    rng = np.random.default_rng(8086)
+    layer = helpers.random_layer(rng, H, I, E, k, shared=True, bias=True)
+    layer.router_bias = (-4.0 * np.log(rng.permutation(E) + 1.0)).astype(np.float32)
+    x = helpers.random_x(rng, T, H)
+    glayer = parity.to_gpu_layer(layer)
+    xg = parity.bits_to_bf16(x)
+    out, aux = ops.forward(glayer, xg, return_aux=True)
+    ids = aux["topk_ids"].cpu().numpy()
+    counts = omoe.permute(ids, E)[0]
+    # gate/up: 3 column tiles per m-tile, down: 2; both well past 256 tiles
+    m_tiles = int(np.sum((counts + 127) // 128)) + (T + 127) // 128
+    assert 2 * m_tiles > 256 and counts.max() > 4 * counts.min(), (m_tiles, counts)
+    out2 = ops.forward(glayer, xg)
+    assert torch.equal(out, out2), "two forwards differ"
+    offsets = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(DEV)
+    _, offs2, sorted_slot, slot_to_row = ops.permute(aux["topk_ids"], E)
+    assert torch.equal(offs2, offsets)
+    S = T * k
+    h = ops.grouped_gemm(L.MOE_GEMM_GATE_UP, glayer.routed, xg, offsets, S, sorted_slot, k)
+    y = ops.grouped_gemm(L.MOE_GEMM_DOWN, glayer.routed, h, offsets, S)
+    one = torch.tensor([0, T], dtype=torch.int32, device=DEV)
+    hs = ops.grouped_gemm(L.MOE_GEMM_GATE_UP, glayer.shared, xg, one, T)
+    ys = ops.grouped_gemm(L.MOE_GEMM_DOWN, glayer.shared, hs, one, T)
+    staged = ops.combine(y, slot_to_row, aux["topk_w"], ys)
+    rel, mx = parity.assert_close(parity.f64(out), parity.f64(staged), "forward vs per-stage entry points")
+    parity.record_margin(f"persistent tiles: forward vs staged, all {T} tokens", rel, mx)
+    tokens = np.unique(np.concatenate([rng.choice(T, 24, replace=False), [0, T - 1]]))
+    res = parity.reference_for_selection(x[tokens], layer, ids[tokens])
+    rel, mx = parity.assert_close(parity.f64(out[torch.from_numpy(tokens).to(DEV)]), res["out"], "sampled tokens")
+    parity.record_margin(f"persistent tiles: layer output, {len(tokens)} tokens", rel, mx)
+
+
 def test_zero_tokens_is_a_no_op():
     rng = np.random.default_rng(1)
     glayer = parity.to_gpu_layer(helpers.random_layer(rng, 256, 128, 4, 2))
