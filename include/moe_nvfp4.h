@@ -116,7 +116,15 @@ typedef struct {
   const float* w2_gscale;    /* [E]; NVFP4 only, may be NULL for MXFP4 */
 } moe_nvfp4_experts_t;
 
-/* The whole layer: router + routed bank + optional shared bank (shared.num_experts == 0: none). */
+/* The whole layer: router + routed bank + optional shared bank (shared.num_experts == 0: none).
+ * h16_norm (host values, NVFP4): bounds on the Euclidean norm of every dequantized gate row
+ * (h16_norm[0]) and up row (h16_norm[1]) of both banks, global scales included, as
+ * moe_nvfp4_h16_bound computes them.  Given (both finite and > 0), the W4A16 forward on 128-row
+ * tiles holds h as fp16 rows scaled by a power of two per token chosen from these bounds, and runs
+ * the down GEMM on fp16 operands too; zero (a zero-initialised struct): h stays bf16.  The result
+ * is the same (bitwise, in practice) as long as the bounds hold; values below the true norms can
+ * make h overflow fp16.  Larger values are safe: they only narrow the range below the bound in
+ * which h is exact (2^31, see moe_nvfp4_forward). */
 typedef struct {
   int32_t hidden;            /* H */
   int32_t num_experts;       /* E (routed) */
@@ -125,6 +133,7 @@ typedef struct {
   const float* router_bias;  /* [E] fp32 added to the logits, or NULL */
   moe_nvfp4_experts_t routed;
   moe_nvfp4_experts_t shared;
+  float h16_norm[2];         /* gate, up; {0, 0}: off */
 } moe_nvfp4_layer_t;
 
 /* ---------------------------------------------------------------- S1 + S2: route
@@ -231,13 +240,18 @@ typedef struct {
  * per row ([T][H] fp16 + [T] int32; read by the NVFP4 gate/up GEMM on prefill shapes, an exact
  * re-encoding of the bf16 values), the intermediate h (row-major, or in the 128-row-tile fragment
  * order the prefill-shaped GEMMs exchange it in: up to (min(E, T*k) + T*k/128 + ceil(T/128)) * 128
- * rows) and the expert outputs y [(T*k + T)][H]. */
+ * rows), one int32 power of two per h row ((T*k + T) when h takes the tile order) and the expert
+ * outputs y [(T*k + T)][H]. */
 size_t moe_nvfp4_forward_workspace_size(int32_t T, int32_t H, int32_t I, int32_t I_shared,
                                         int32_t E, int32_t k);
 
 /* S1..S6 for x [T][H] bf16 -> out [T][H] bf16.  `layer` and `aux` are host pointers to structs
  * holding device pointers.  The workspace may be shared by every layer of a model that runs on
- * the same stream (one pool instead of per-layer scratch). */
+ * the same stream (one pool instead of per-layer scratch).  On 128-row tiles with layer->h16_norm
+ * given, h = bf16(silu(g) * u) enters the down GEMM as fp16 after scaling by 2^hs per token, with
+ * hs chosen so that the bound ||x||^2 h16_norm[0] h16_norm[1] on |h| (|silu(g)| <= |g|) lands below
+ * 2^14: every h within 2^31 of that bound is carried exactly (the down sums are then those of the
+ * bf16 h), smaller ones round to the fp16 subnormal grid (absolute error below 2^-38 of the bound). */
 moe_status_t moe_nvfp4_forward(const moe_nvfp4_layer_t* layer, const uint16_t* x, int32_t T,
                                uint16_t* out, void* workspace, size_t workspace_bytes,
                                const moe_forward_aux_t* aux, void* stream);
@@ -281,6 +295,18 @@ moe_status_t moe_gscale_from_quant_scale(const float* q_host, float* d_host, int
  * ("Serving Solar Open 2 on DGX Spark", "Supporting real NVFP4 checkpoints"). */
 moe_status_t moe_nvfp4_pack_tiles(const uint8_t* packed, const uint8_t* scales, int32_t num_tensors, int32_t rows,
                                   int32_t cols, uint8_t* tiled, uint8_t* tiled_scales, void* stream);
+
+/* Load time, NVFP4: the bounds of moe_nvfp4_layer_t::h16_norm for one tiled bank.  For every expert e
+ * and every gate row j (rows [0, I) of w13) the Euclidean norm of d_g[e] * e2m1(code) * e4m3(scale)
+ * over the row's H elements (fp64, then rounded up to fp32), likewise for the up rows with d_u[e];
+ * the largest gate-row norm and the largest up-row norm are folded into bound[0] and bound[1] with a
+ * maximum.  bound: device, two floats, zero-filled by the caller once; call for the routed and the
+ * shared bank of a layer, then copy bound to h16_norm.  An E4M3 NaN scale leaves a NaN bound (the
+ * fp16 h path then stays off).  Errors: MOE_ERR_INVALID_ARGUMENT for a non-NVFP4 bank, a NULL
+ * tensor, I % 16 or H % 128 nonzero.  Enqueued on `stream`.
+ * Source: the fp32 global scale of each NVFP4 tensor and the E2M1 x E4M3 dequantization
+ * ("vLLM on the NVIDIA DGX Spark", section 6.1). */
+moe_status_t moe_nvfp4_h16_bound(const moe_nvfp4_experts_t* bank /* host */, float* bound, void* stream);
 
 /* On-device NVFP4 quantization of fp32 weights (the on-the-fly quantization path a checkpoint
  * without pre-quantized weights needs).  w: num_tensors tensors of [rows][cols] fp32, contiguous;

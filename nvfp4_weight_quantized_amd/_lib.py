@@ -43,6 +43,7 @@ class Layer(ctypes.Structure):
         ("hidden", i32), ("num_experts", i32), ("top_k", i32),
         ("w_router", c_void_p), ("router_bias", c_void_p),
         ("routed", Experts), ("shared", Experts),
+        ("h16_norm", ctypes.c_float * 2),
     ]
 
 
@@ -95,6 +96,7 @@ SIGNATURES = {
     "moe_nvfp4_w4a4_forward": (i32, [ctypes.POINTER(Layer), c_void_p, i32, ctypes.c_float, ctypes.c_float, c_void_p,
                                      c_void_p, size_t, ctypes.POINTER(ForwardAux), c_void_p]),
     "moe_hbm_read_probe": (i32, [c_void_p, size_t, c_void_p, i32, c_void_p]),
+    "moe_nvfp4_h16_bound": (i32, [ctypes.POINTER(Experts), c_void_p, c_void_p]),
     "moe_nvfp4_forward_noalloc": (i32, [ctypes.POINTER(Layer), c_void_p, i32, c_void_p, ctypes.POINTER(ForwardAux),
                                         c_void_p]),
 }

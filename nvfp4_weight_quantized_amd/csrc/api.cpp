@@ -64,7 +64,7 @@ GemmBank bank_w2(const moe_nvfp4_experts_t& b) { return GemmBank{b.w2, b.w2_scal
 
 struct ForwardLayout {
   size_t logits, ids, w, counts, offsets, sorted_slot, slot_to_row, block_hist, x16, row_shift, h, h_shared, y,
-      ctr, xa, tiles;
+      ctr, xa, tiles, hshift;
   size_t total;
 };
 
@@ -113,6 +113,8 @@ ForwardLayout forward_layout(int32_t T, int32_t H, int32_t I, int32_t I_shared, 
   L.xa = take(a4 ? (size_t)T * H * 2 : 0);
   // tile counters of the gate/up and down launches (cleared by the router launch of the forward)
   L.tiles = take(2 * moe::kTileCounterWords * 4);
+  // the power of two of each h row when h is held as fp16 (tiled h only)
+  L.hshift = take(tiled && !a4 ? (S + (size_t)T) * 4 : 0);
   L.total = off;
   return L;
 }
@@ -492,13 +494,28 @@ moe_status_t forward_impl(const moe_nvfp4_layer_t* layer, const uint16_t* x, int
   // quantizes the row-major h between the GEMMs)
   const bool tiled = !a4 && (fuse_shared || !has_shared) && moe::grouped_gemm_uses_tall_tiles(gu);
   if (tiled) gu.out_tiled = h;
+  // h as fp16 too (the down GEMM then also runs on fp16 operands): NVFP4 on both 128-row eight-wave
+  // GEMMs, and the layer's bounds on the gate and up weight row norms given
+  const bool h16 = tiled && !a4 && layer->h16_norm[0] > 0.f && layer->h16_norm[1] > 0.f &&
+                   std::isfinite(layer->h16_norm[0]) && std::isfinite(layer->h16_norm[1]) &&
+                   moe::grouped_gemm_takes_f16_rows(gu) && moe::grouped_gemm_takes_f16_rows(dn);
   if (moe::grouped_gemm_takes_f16_rows(gu)) {
     // fp16 operands halve the dequantization work of the NVFP4 weights (exact, see launch_act_to_f16)
     uint16_t* x16 = at<uint16_t>(workspace, L.x16);
     int32_t* row_shift = at<int32_t>(workspace, L.row_shift);
-    if ((st = moe::launch_act_to_f16(xg, T, H, x16, row_shift, stream))) return st;
+    if ((st = moe::launch_act_to_f16(xg, T, H, x16, row_shift, h16 ? layer->h16_norm[0] : 0.f,
+                                     h16 ? layer->h16_norm[1] : 0.f, stream)))
+      return st;
     gu.a16 = x16;
     gu.row_shift = row_shift;
+  }
+  if (h16) {
+    int32_t* hshift = at<int32_t>(workspace, L.hshift);
+    gu.h16 = 1;
+    gu.hshift_out = hshift;
+    dn.h16 = 1;
+    dn.a16 = h;
+    dn.row_shift = hshift;
   }
   if ((st = moe::launch_grouped_gemm(gu, stream))) return st;
   if (has_shared && !fuse_shared) {
@@ -631,6 +648,19 @@ moe_status_t moe_nvfp4_quantize(const float* w, int32_t num_tensors, int32_t row
   if (!al16(w) || !al16(packed)) return MOE_ERR_INVALID_ARGUMENT;
   if (moe_status_t st = check_arch(nullptr)) return st;
   return moe::launch_quantize(w, num_tensors, rows, cols, gscale, packed, scales, static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_nvfp4_h16_bound(const moe_nvfp4_experts_t* bank, float* bound, void* stream) {
+  if (!bank || !bound) return MOE_ERR_INVALID_ARGUMENT;
+  if (bank->format != MOE_WEIGHT_NVFP4 || bank->num_experts < 0 || bank->inter <= 0 || bank->inter % 16 != 0 ||
+      bank->hidden <= 0 || bank->hidden % 128 != 0)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (bank->num_experts == 0) return MOE_OK;
+  if (!bank->w13 || !bank->w13_scale || !bank->w13_gscale || !al16(bank->w13) || (reinterpret_cast<uintptr_t>(bound) & 3))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (moe_status_t st = check_arch(nullptr)) return st;
+  return moe::launch_h16_bound(bank->w13, bank->w13_scale, bank->w13_gscale, bank->num_experts, bank->inter,
+                               bank->hidden, bound, static_cast<hipStream_t>(stream));
 }
 
 moe_status_t moe_mxfp4_pack_tiles(const uint8_t* packed, const uint8_t* scales, int32_t num_tensors, int32_t rows,

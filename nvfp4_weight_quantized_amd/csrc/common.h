@@ -111,11 +111,21 @@ struct GemmProblem {
   // undefined.
   int32_t a_tiled;        // 1: `a` (and the extra group's rows) are read in that layout
   uint16_t* out_tiled;    // gate/up: write h in that layout (K = N columns) instead of `out`
-  // Gate/up on NVFP4 weights, eight-wave 128-row path only (ignored elsewhere): the activation
-  // rows as fp16, a16[r] = a[r] * 2^row_shift[r] exactly (launch_act_to_f16), for both `a` and
-  // `a_extra` (the same token matrix); the GEMM then runs on fp16 operands.
+  // NVFP4 weights, eight-wave 128-row path only (ignored elsewhere): fp16 operand rows.
+  //  Gate/up: the token rows as fp16, a16[t] = a[t] * 2^xs exactly with xs = (int16_t)row_shift[t]
+  //  (launch_act_to_f16), for both `a` and `a_extra` (the same token matrix).
+  //  Down (h16 set): a16 is h in the tiled layout as the gate/up launch with h16 wrote it, and
+  //  row_shift[r] the power of two of h row r (the row numbering of `out`: the groups' rows, then
+  //  the extra group's).
   const uint16_t* a16;
   const int32_t* row_shift;
+  // h as fp16 (eight-wave 128-row path on fp16 rows, tiled output): gate/up writes each h row as
+  // fp16(bf16(h) * 2^hs) with hs = row_shift[t] >> 16 of the row's token (chosen by
+  // launch_act_to_f16 from a bound on |h|, exact for every element within 2^31 of the bound), and
+  // the column tile 0 workgroups store hs in hshift_out[row]; down takes such h (a16, row_shift
+  // above) and scales its sums back by 2^-hs.
+  int32_t h16;
+  int32_t* hshift_out;
   // W4A4 on NVFP4 activations: the dequant global scale of the activation rows, which then hold
   // the exact values e2m1(code) * e4m3(block scale) (launch_quantize_act_nv); the epilogue scales
   // the sums by it and the weight's global scale (alpha = 1 / (input_global_scale *
@@ -146,12 +156,18 @@ bool grouped_gemm_uses_tall_tiles(const GemmProblem& p);
 bool grouped_gemm_uses_skinny_tiles(const GemmProblem& p);
 
 moe_status_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream);
-// x16[t][h] = fp16(x[t][h] * 2^shift[t]) with shift[t] = 14 - floor(log2(max_h |x[t][h]|)) (0 for a
-// row of zeros or with a non-finite value): exact for every element within 2^31 of its row's
-// largest magnitude.  One workgroup per row.
-moe_status_t launch_act_to_f16(const uint16_t* x, int32_t T, int32_t H, uint16_t* x16, int32_t* shift,
-                               hipStream_t stream);
-// True if launch_grouped_gemm would read p.a16 / p.row_shift for this problem.
+// x16[t][h] = fp16(x[t][h] * 2^xs) with xs = 14 - floor(log2(max_h |x[t][h]|)) (0 for a row of
+// zeros or with a non-finite value): exact for every element within 2^31 of its row's largest
+// magnitude.  shift[t] = (xs & 0xFFFF) | (hs << 16), where hs is the power of two of the row's h
+// in the fp16 h path: with ng, nu bounds on the Euclidean norms of every gate and up weight row
+// (dequantized, global scale included; 0: no fp16 h, hs = 0), |g| <= ||x|| ng and |u| <= ||x|| nu,
+// so |h| = |silu(g) u| <= |g| |u| <= ||x||^2 ng nu < 2^e, and hs = 13 - e puts every h of the
+// token below 2^13 (a binade of margin for the rounding of the sums and of h).  One workgroup per
+// row.
+moe_status_t launch_act_to_f16(const uint16_t* x, int32_t T, int32_t H, uint16_t* x16, int32_t* shift, float ng,
+                               float nu, hipStream_t stream);
+// True if launch_grouped_gemm would read p.a16 / p.row_shift for this problem (the gate/up one, or
+// the down one when it reads fp16 h).
 bool grouped_gemm_takes_f16_rows(const GemmProblem& p);
 
 // W4A4 grouped GEMM: MXFP4 weights in the W4A4 tile layout (layout.hip) times MXFP4 activations,
@@ -221,6 +237,11 @@ moe_status_t launch_pack_tiles_a4(const uint8_t* packed, const uint8_t* scales, 
                                   int32_t cols, uint8_t* tiled, uint8_t* tiled_scales, hipStream_t stream);
 
 // Quantize ----------------------------------------------------------------------------------
+// Largest Euclidean norm of the dequantized gate rows / up rows of a tiled NVFP4 w13 bank (E
+// experts, global scales gs [E][2]), each rounded up to fp32 and folded into bound[0] / bound[1]
+// by a maximum (bound: device, two floats).
+moe_status_t launch_h16_bound(const uint8_t* w13, const uint8_t* s13, const float* gs, int32_t E, int32_t I,
+                              int32_t H, float* bound, hipStream_t stream);
 moe_status_t launch_quantize(const float* w, int32_t num_tensors, int32_t rows, int32_t cols,
                              const float* gscale, uint8_t* packed, uint8_t* scales, hipStream_t stream);
 moe_status_t launch_quantize_mx(const float* w, int32_t num_tensors, int32_t rows, int32_t cols, uint8_t* packed,

@@ -134,13 +134,24 @@ __device__ __forceinline__ int frag_row_block(int f, int ntile, int wave, int N)
 __device__ __forceinline__ float epilogue_act_gscale(const GemmProblem& p) { return act_gscale(p); }
 template <class P>
 __device__ __forceinline__ float epilogue_act_gscale(const P&) { return 1.f; }
+// The fp16 h path of a problem (GemmProblem::h16; never for the MX W4A4 one).
+__device__ __forceinline__ bool epilogue_h16(const GemmProblem& p) { return p.h16 != 0; }
+template <class P>
+__device__ __forceinline__ bool epilogue_h16(const P&) { return false; }
+__device__ __forceinline__ int32_t* epilogue_hshift_out(const GemmProblem& p) { return p.hshift_out; }
+template <class P>
+__device__ __forceinline__ int32_t* epilogue_hshift_out(const P&) { return nullptr; }
 
 // Epilogue: scale the accumulators by the global scale(s), SiLU(gate)*up for gate/up, store bf16.
 // acc[i][f] holds, in lane l = 16q + n, output row 16i + n and the four columns 4q..4q+3 of
 // fragment f's 16 columns (gate/up: fragments NB/2.. hold the up columns of fragments 0..).
 // GSCALE: the bank carries fp32 global scales (NVFP4); otherwise the scale is 1.
-// rshift (optional, gate/up): per tile row, the power of two the activation row was scaled by
-// (2^rshift[row]); the sums are scaled back by 2^-rshift[row] (exact) before SiLU.
+// rshift (optional): per tile row, the powers of two of the fp16 operand rows.  Gate/up: the
+// token row was scaled by 2^xs, xs = (int16_t)rshift[row], and the sums are scaled back by 2^-xs
+// (exact) before SiLU; with the fp16 h path (p.h16), h = bf16(silu(g) u) is stored as fp16 after
+// scaling by 2^hs, hs = rshift[row] >> 16 (folded into u's scale: power-of-two scaling commutes with
+// the bf16 rounding), and the column-tile-0 workgroup records hs in p.hshift_out[row of h].  Down
+// (fp16 h): h row `row` was scaled by 2^rshift[row]; the sums are scaled back by 2^-rshift[row].
 // RBE (default MI): the 16-row blocks that can hold rows of the tile; blocks past it are not read,
 // so a caller that never touched their accumulators need not keep them.
 // epilogue_at takes the weight global scales of the tile's expert (g0: gate or down, g1: up; 1
@@ -168,6 +179,20 @@ __device__ __forceinline__ void epilogue_at(const P& p, float g0, float g1, cons
     return uint2{(uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16),
                  (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16)};
   };
+  // the bf16 rounding of each value, as fp16 (exact for every value of at least 2^-17 and below 2^16;
+  // smaller ones round to nearest even on the fp16 subnormal grid): per pair one bf16 pair
+  // conversion, the two halves back to fp32, one fp16 pair conversion (v_cvt_pk_f16_f32)
+  auto pack4h = [](float a, float b, float c, float d) {
+    auto pair = [](float x, float y) {
+      const uint32_t bb = (uint32_t)f32_to_bf16(x) | ((uint32_t)f32_to_bf16(y) << 16);
+      typedef float f32x2_t __attribute__((ext_vector_type(2)));
+      typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+      const f32x2_t v = {__uint_as_float(bb << 16), __uint_as_float(bb & 0xFFFF0000u)};
+      return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+    };
+    return uint2{pair(a, b), pair(c, d)};
+  };
+  const bool h16 = epilogue_h16(p) && rshift != nullptr;
   // address of column col (of this lane's row) in block i
   auto dst = [&](int i, int row, int col) -> uint16_t* {
     if (GATE_UP && p.out_tiled) {
@@ -186,7 +211,9 @@ __device__ __forceinline__ void epilogue_at(const P& p, float g0, float g1, cons
     uint2 v[NF];
     if (GATE_UP) {
       const float dg = g0 * da, du = g1 * da;
-      const int sh = rshift ? -rshift[row] : 0;
+      const int rs = rshift ? rshift[row] : 0;
+      const int xs = (int)(int16_t)rs;
+      const int hs = h16 ? rs >> 16 : 0;
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         float h[4];
@@ -194,17 +221,27 @@ __device__ __forceinline__ void epilogue_at(const P& p, float g0, float g1, cons
         for (int r = 0; r < 4; ++r) {
           float g = acc[i][f][r] * dg, u = acc[i][f + NF][r] * du;
           if (rshift) {
-            g = ldexpf(g, sh);
-            u = ldexpf(u, sh);
+            g = ldexpf(g, -xs);
+            u = ldexpf(u, hs - xs);
           }
           h[r] = silu(g) * u;
         }
-        v[f] = pack4(h[0], h[1], h[2], h[3]);
+        v[f] = h16 ? pack4h(h[0], h[1], h[2], h[3]) : pack4(h[0], h[1], h[2], h[3]);
       }
+      if (h16 && ntile == 0 && wave == 0 && q == 0 && valid) epilogue_hshift_out(p)[ti.row0 + row] = hs;
     } else {
       const float dd = g0 * da;
+      if (rshift) {
+        const int hs = rshift[row];
 #pragma unroll
-      for (int f = 0; f < NF; ++f) v[f] = pack4(acc[i][f][0] * dd, acc[i][f][1] * dd, acc[i][f][2] * dd, acc[i][f][3] * dd);
+        for (int f = 0; f < NF; ++f)
+          v[f] = pack4(ldexpf(acc[i][f][0] * dd, -hs), ldexpf(acc[i][f][1] * dd, -hs), ldexpf(acc[i][f][2] * dd, -hs),
+                       ldexpf(acc[i][f][3] * dd, -hs));
+      } else {
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+          v[f] = pack4(acc[i][f][0] * dd, acc[i][f][1] * dd, acc[i][f][2] * dd, acc[i][f][3] * dd);
+      }
     }
 #pragma unroll
     for (int f = 0; f + 1 < NF; f += 2) {

@@ -575,10 +575,13 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
 //    single wave per SIMD, the compiler keeps 16x16x32 accumulators in the accumulation registers but
 //    does not tie each MFMA's result to its accumulator input, and copies every accumulator through
 //    ordinary registers once per loop iteration (seen in the generated code of a four-wave form).
-template <int NB, bool GATE_UP, int FMT, bool A16>
+// H16 (gate/up on fp16 rows): the fp16 h epilogue (GemmProblem::h16), a variant of its own so that
+// each variant's code holds one epilogue form.
+template <int NB, bool GATE_UP, int FMT, bool A16, bool H16 = false>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProblem p) {
   using F = WFmt<FMT>;
-  static_assert(!A16 || (GATE_UP && FMT == kFmtNvfp4), "fp16 rows: NVFP4 gate/up only");
+  static_assert(!A16 || FMT == kFmtNvfp4, "fp16 rows: NVFP4 only");
+  static_assert(!H16 || (GATE_UP && A16), "fp16 h: written by the gate/up GEMM on fp16 rows");
   using OpT = typename std::conditional<A16, f16x8, bf16x8>::type;
   auto w_op = [](const uint4& w, uint32_t sc, int j) -> OpT {
     if constexpr (A16) return w_operand16(w, sc, j);
@@ -767,6 +770,9 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
       const int src = (!t.extra && p.row_index) ? p.row_index[R] / p.row_divisor : R;
       s_aoff[tid] = (uint32_t)src * (uint32_t)p.K * 2u;
       if (A16) s_shift[0][tid] = p.row_shift[src];
+    } else if (A16 && !GATE_UP && tid < BM) {
+      // fp16 h (tiled): the power of two of each h row, in the output's row numbering
+      s_shift[0][tid] = p.row_shift[t.row0 + min(tid, t.rows - 1)];
     }
   }
   __syncthreads();
@@ -910,6 +916,12 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
         s_aoff[r] = (uint32_t)src * (uint32_t)a->K * 2u;
         if (A16)
           direct_load4(uniform(a->row_shift), 4u * (uint32_t)src, shift0 + (uint32_t)((par ^ 1) * BM * 4 + wave * 256));
+      } else if (A16 && !GATE_UP && wave < BM / 64) {
+        // fp16 h (tiled): the next tile's h-row powers of two
+        const int r = wave * 64 + lane_now();
+        const Tile nt = fetch(par ^ 1);
+        direct_load4(uniform(a->row_shift), 4u * (uint32_t)(nt.row0 + min(r, nt.rows - 1)),
+                     shift0 + (uint32_t)((par ^ 1) * BM * 4 + wave * 256));
       }
     }
   };
@@ -1126,6 +1138,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
     pe.out = a->out;
     pe.out_tiled = a->out_tiled;
     pe.a_gscale = a->a_gscale;
+    pe.h16 = H16 ? 1 : 0;
+    pe.hshift_out = a->hshift_out;
     // the expert's global scales by scalar loads (through the constant address space: they are not
     // written while the kernel runs), which leave the direct loads in flight alone
     float g0 = 1.f, g1 = 1.f;
@@ -1193,8 +1207,14 @@ moe_status_t launch_tall(const GemmProblem& p, hipStream_t stream) {
       if (cus <= 0) return MOE_ERR_HIP;
       grid = std::min(grid, (long long)std::max(kXcds, cus / kXcds * kXcds));
     }
-    if constexpr (GATE_UP && FMT == kFmtNvfp4) {
-      if (p.a16) {
+    if constexpr (FMT == kFmtNvfp4) {
+      // fp16 operand rows: the gate/up token rows, or h (down) when the gate/up launch wrote it as fp16
+      if (GATE_UP && p.a16 && p.h16 && p.hshift_out && p.out_tiled) {
+        hipLaunchKernelGGL((grouped_gemm_tall_lds_kernel<NB, GATE_UP, FMT, true, GATE_UP>), dim3((unsigned)grid),
+                           dim3(512), 0, stream, p);
+        return launch_status();
+      }
+      if (GATE_UP ? p.a16 != nullptr : (p.h16 && p.a16 && p.row_shift && p.a_tiled)) {
         hipLaunchKernelGGL((grouped_gemm_tall_lds_kernel<NB, GATE_UP, FMT, true>), dim3((unsigned)grid), dim3(512), 0,
                            stream, p);
         return launch_status();
@@ -1296,20 +1316,26 @@ bool grouped_gemm_uses_skinny_tiles(const GemmProblem& p) {
   return p.bank.format == kFmtNvfp4 && avg_rows(p) <= kSkinnyRows;
 }
 
-// The eight-wave NVFP4 gate/up path (launch_format) is the one that reads fp16 rows.
+// The eight-wave NVFP4 paths (launch_format) read fp16 rows: gate/up always, down when it is
+// handed fp16 h (GemmProblem::h16).
 bool grouped_gemm_takes_f16_rows(const GemmProblem& p) {
-  return p.stage == MOE_GEMM_GATE_UP && p.bank.format == kFmtNvfp4 && grouped_gemm_uses_tall_tiles(p) &&
-         p.N % 256 == 0;
+  if (p.bank.format != kFmtNvfp4 || !grouped_gemm_uses_tall_tiles(p)) return false;
+  return p.stage == MOE_GEMM_GATE_UP ? p.N % 256 == 0 : p.N % 512 == 0;
 }
 
 namespace {
-// One workgroup per row: the row's largest magnitude (NaN ignored), then the row times 2^shift in
-// fp16 (round to nearest even), shift = 14 - floor(log2(max)) so that the largest magnitude lands
+// One workgroup per row: the row's largest magnitude (NaN ignored), then the row times 2^xs in
+// fp16 (round to nearest even), xs = 14 - floor(log2(max)) so that the largest magnitude lands
 // in [2^14, 2^15): every bf16 element within 2^31 of it keeps all 8 significant bits (normal fp16
-// down to 2^-14, subnormal steps of 2^-24).  A row of zeros or with an infinity keeps shift 0.
+// down to 2^-14, subnormal steps of 2^-24).  A row of zeros or with an infinity keeps xs 0.  With
+// the weight-row norm bounds ng, nu (fp16 h path), the same pass sums the squares of the scaled
+// row and derives the power of two hs of the token's h rows (launch_act_to_f16); hs = 0 without
+// them, for a row of zeros and for a non-finite row.
 __global__ __launch_bounds__(256) void act_to_f16_kernel(const uint16_t* __restrict__ x, int H,
-                                                         uint16_t* __restrict__ x16, int32_t* __restrict__ shift) {
+                                                         uint16_t* __restrict__ x16, int32_t* __restrict__ shift,
+                                                         float ng, float nu) {
   __shared__ float wmax[4];
+  __shared__ float wss[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint16_t* row = x + (size_t)blockIdx.x * H;
   float m = 0.f;
@@ -1328,28 +1354,54 @@ __global__ __launch_bounds__(256) void act_to_f16_kernel(const uint16_t* __restr
   __syncthreads();
   m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   const int sh = (m > 0.f && m <= 3.4028235e38f) ? 14 - ilogbf(m) : 0;
-  if (tid == 0) shift[blockIdx.x] = sh;
   uint16_t* orow = x16 + (size_t)blockIdx.x * H;
+  // sum of squares of the scaled row (each square exact, below 2^30; the sum rounds in fp32)
+  float ss = 0.f;
   for (int h = tid * 8; h < H; h += 256 * 8) {
     const uint4 v = *reinterpret_cast<const uint4*>(row + h);
     const uint32_t q[4] = {v.x, v.y, v.z, v.w};
     uint32_t o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const _Float16 lo = (_Float16)ldexpf(__uint_as_float(q[i] << 16), sh);
-      const _Float16 hi = (_Float16)ldexpf(__uint_as_float(q[i] & 0xFFFF0000u), sh);
+      const float a = ldexpf(__uint_as_float(q[i] << 16), sh), b = ldexpf(__uint_as_float(q[i] & 0xFFFF0000u), sh);
+      ss += a * a + b * b;
+      const _Float16 lo = (_Float16)a;
+      const _Float16 hi = (_Float16)b;
       o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
     }
     *reinterpret_cast<uint4*>(orow + h) = uint4{o[0], o[1], o[2], o[3]};
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  if (lane == 0) wss[wave] = ss;
+  __syncthreads();
+  if (tid == 0) {
+    int hs = 0;
+    if (ng > 0.f && nu > 0.f) {
+      // ||x|| 2^sh, rounded up (1% covers the fp32 rounding of the sum and of the square root)
+      const float n16 = sqrtf((wss[0] + wss[1]) + (wss[2] + wss[3])) * 1.01f;
+      if (n16 > 0.f && n16 <= 3.4028235e38f && ng <= 3.4028235e38f && nu <= 3.4028235e38f) {
+        // |g| 2^sh <= n16 ng and |u| 2^sh <= n16 nu, taken apart into mantissas in [0.5, 1) and
+        // exponents so that nothing overflows; |silu(g)| = |g| sigmoid(g) <= |g| < 2^ea, |u| < 2^eb
+        int a, b, c;
+        const float fa = frexpf(n16, &a), fb = frexpf(ng, &b), fc = frexpf(nu, &c);
+        const int ea = ilogbf(fa * fb) + 1 + a + b - sh;
+        const int eb = ilogbf(fa * fc) + 1 + a + c - sh;
+        // |h| < 2^(ea + eb); below 2^13 after the shift.  The clamp keeps every finite bf16 h
+        // (below 2^128) within fp16 range
+        hs = min(max(13 - ea - eb, -120), 120);
+      }
+    }
+    shift[blockIdx.x] = (int32_t)(((uint32_t)sh & 0xFFFFu) | ((uint32_t)hs << 16));
+  }
 }
 }  // namespace
 
-moe_status_t launch_act_to_f16(const uint16_t* x, int32_t T, int32_t H, uint16_t* x16, int32_t* shift,
-                               hipStream_t stream) {
+moe_status_t launch_act_to_f16(const uint16_t* x, int32_t T, int32_t H, uint16_t* x16, int32_t* shift, float ng,
+                               float nu, hipStream_t stream) {
   if (T < 0 || H <= 0 || H % 8 != 0) return MOE_ERR_INVALID_ARGUMENT;
   if (T == 0) return MOE_OK;
-  hipLaunchKernelGGL(act_to_f16_kernel, dim3((unsigned)T), dim3(256), 0, stream, x, (int)H, x16, shift);
+  hipLaunchKernelGGL(act_to_f16_kernel, dim3((unsigned)T), dim3(256), 0, stream, x, (int)H, x16, shift, ng, nu);
   return launch_status();
 }
 

@@ -186,7 +186,76 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const In* __restrict__
   scales[g] = (uint8_t)(e + 127);
 }
 
+// Norm bound of the fp16 h path (weight preparation): one wave per 16-row block of one expert's
+// tiled w13 (gate rows, then up rows).  Lane l = 16q + n of the block's tile for K chunk c holds
+// row n's elements [128c + 32j + 8q, +8) in its dword j, with the E4M3 scale in byte j of the
+// tile's dword at 8n + 4(q >> 1) (the pack_tiles permutation).  Each row's squared Euclidean norm
+// of E2M1 value times E4M3 scale is summed in fp64 (every term exact), its square root times the
+// expert's gate or up global scale rounded up to fp32, and the largest over the block's rows folded
+// into bound[0] (gate) or bound[1] (up) by an atomic maximum on the bits (non-negative floats order
+// as their bit patterns; a NaN norm is ignored within the block, and a block of NaN norms leaves a
+// NaN bound, which switches the fp16 h path off).
+__global__ __launch_bounds__(256) void h16_bound_kernel(const uint8_t* __restrict__ w13,
+                                                        const uint8_t* __restrict__ s13,
+                                                        const float* __restrict__ gs, int E, int I, int H,
+                                                        float* __restrict__ bound) {
+  const int lane = threadIdx.x & 63;
+  const long long nblk = (long long)E * (2 * I / 16);
+  const long long blk = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blk >= nblk) return;
+  const int e = (int)(blk / (2 * I / 16)), nb = (int)(blk % (2 * I / 16));
+  const int nc = H / 128;
+  const uint8_t* wt = w13 + ((size_t)e * 2 * I + (size_t)nb * 16) * (size_t)(H / 2);
+  const uint8_t* st = s13 + ((size_t)e * 2 * I + (size_t)nb * 16) * (size_t)(H / 16);
+  const int q = lane >> 4, n = lane & 15;
+  double ss = 0.0;
+  for (int c = 0; c < nc; ++c) {
+    const uint4 v = *reinterpret_cast<const uint4*>(wt + (size_t)c * 1024 + 16 * lane);
+    const uint32_t sw = *reinterpret_cast<const uint32_t*>(st + (size_t)c * 128 + 8 * n + 4 * (q >> 1));
+    const uint32_t words[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 squared, times 4: 0, 1, 4, 9, 16, 36, 64, 144
+      int sq4 = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int m = (words[j] >> (4 * i)) & 7;
+        sq4 += m < 4 ? m * m : (m == 4 ? 16 : m == 5 ? 36 : m == 6 ? 64 : 144);
+      }
+      const float scf = j == 0   ? __builtin_amdgcn_cvt_f32_fp8((int)sw, 0)
+                        : j == 1 ? __builtin_amdgcn_cvt_f32_fp8((int)sw, 1)
+                        : j == 2 ? __builtin_amdgcn_cvt_f32_fp8((int)sw, 2)
+                                 : __builtin_amdgcn_cvt_f32_fp8((int)sw, 3);
+      const double sc = (double)scf;
+      ss += 0.25 * (double)sq4 * sc * sc;
+    }
+  }
+  ss += __shfl_xor(ss, 16);
+  ss += __shfl_xor(ss, 32);
+  const int up = nb * 16 >= I ? 1 : 0;
+  double r = sqrt(ss) * fabs((double)gs[2 * e + up]);
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) r = fmax(r, __shfl_xor(r, off));
+  if (lane == 0) {
+    float f = (float)r;
+    if ((double)f < r) f = nextafterf(f, __builtin_inff());
+    atomicMax(reinterpret_cast<unsigned int*>(bound) + up, __float_as_uint(f));
+  }
+}
+
 }  // namespace
+
+moe_status_t launch_h16_bound(const uint8_t* w13, const uint8_t* s13, const float* gs, int32_t E, int32_t I,
+                              int32_t H, float* bound, hipStream_t stream) {
+  if (E < 0 || I <= 0 || I % 16 != 0 || H <= 0 || H % 128 != 0) return MOE_ERR_INVALID_ARGUMENT;
+  const long long waves = (long long)E * (2 * I / 16);
+  if (waves == 0) return MOE_OK;
+  const long long blocks = (waves + 3) / 4;
+  if (blocks > 0x7FFFFFFFLL) return MOE_ERR_INVALID_ARGUMENT;
+  hipLaunchKernelGGL(h16_bound_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w13, s13, gs, (int)E, (int)I,
+                     (int)H, bound);
+  return launch_status();
+}
 
 moe_status_t launch_quantize_mx(const float* w, int32_t num_tensors, int32_t rows, int32_t cols, uint8_t* packed,
                                 uint8_t* scales, hipStream_t stream) {

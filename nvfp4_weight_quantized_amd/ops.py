@@ -8,7 +8,7 @@ from __future__ import annotations
 
 import ctypes
 import math
-from dataclasses import dataclass
+from dataclasses import dataclass, field
 from typing import Optional
 
 import numpy as np
@@ -60,6 +60,11 @@ class NvFp4Experts:
     the W4A4 tile layout, which makes a layer run the W4A4 path.  Shapes are those of
     the canonical tensors (include/moe_nvfp4.h); the bytes of each expert's tensors are permuted by
     ``pack_tiles``.  Use ``NvFp4Experts.from_canonical`` to build one from checkpoint-layout tensors.
+
+    An NVFP4 bank on the GPU also carries ``h16_bound``, the largest Euclidean norm of its dequantized
+    gate rows and of its up rows (``moe_nvfp4_h16_bound``), computed when the bank is made (or when
+    its weight tensors are replaced); the layer hands it to the forward, which then holds h as fp16.
+    After changing weight values in place, call ``refresh_h16_bound()``.
     """
     w13: torch.Tensor                    # uint8 [E, 2I, H/2]
     w13_scale: torch.Tensor              # uint8 [E, 2I, H/16] (nvfp4) or [E, 2I, H/32] (mxfp4)
@@ -68,6 +73,37 @@ class NvFp4Experts:
     w2_scale: torch.Tensor               # uint8 [E, H, I/16] or [E, H, I/32]
     w2_gscale: Optional[torch.Tensor]    # float32 [E] (nvfp4) or None
     fmt: str = "nvfp4"
+    h16_bound: tuple = field(default=(0.0, 0.0), init=False, compare=False, repr=False)
+    _h16_key: tuple = field(default=(), init=False, compare=False, repr=False)
+
+    def __post_init__(self):
+        self.refresh_h16_bound()
+
+    def _tensors_key(self):
+        return (id(self.w13), id(self.w13_scale), id(self.w13_gscale), self.fmt)
+
+    def refresh_h16_bound(self) -> tuple:
+        """(gate, up) weight-row norm bounds of an NVFP4 bank on the GPU, (0, 0) otherwise."""
+        self._h16_key = self._tensors_key()
+        self.h16_bound = (0.0, 0.0)
+        if self.fmt != "nvfp4" or not isinstance(self.w13, torch.Tensor) or not self.w13.is_cuda:
+            return self.h16_bound
+        try:
+            self.check()
+        except (ValueError, TypeError):
+            return self.h16_bound   # the layer's own check reports it
+        bound = torch.zeros(2, dtype=torch.float32, device=self.w13.device)
+        st = self.c_struct()
+        L.check("moe_nvfp4_h16_bound", L.lib().moe_nvfp4_h16_bound(ctypes.byref(st), _ptr(bound),
+                                                                   _stream(self.w13.device)))
+        self.h16_bound = tuple(float(v) for v in bound.cpu().tolist())
+        return self.h16_bound
+
+    def current_h16_bound(self) -> tuple:
+        """h16_bound, recomputed if the weight tensors were replaced since."""
+        if self._h16_key != self._tensors_key():
+            self.refresh_h16_bound()
+        return self.h16_bound
 
     @property
     def num_experts(self) -> int:
@@ -122,6 +158,8 @@ class NvFp4MoELayer:
     routed: NvFp4Experts
     shared: Optional[NvFp4Experts]
     top_k: int
+    # hold h as fp16 on the 128-row path (with the banks' weight-row norm bounds; NVFP4 only)
+    fp16_h: bool = True
 
     @property
     def hidden(self) -> int:
@@ -159,9 +197,10 @@ class NvFp4MoELayer:
 
     def _key(self):
         banks = [b for b in (self.routed, self.shared) if b is not None]
-        return (id(self.w_router), id(self.router_bias), self.top_k,
+        return (id(self.w_router), id(self.router_bias), self.top_k, self.fp16_h,
                 *[(id(t), b.fmt) for b in banks for t in (b.w13, b.w13_scale, b.w13_gscale, b.w2, b.w2_scale,
-                                                          b.w2_gscale)])
+                                                          b.w2_gscale)],
+                *[b.h16_bound for b in banks])
 
     def checked_struct(self) -> L.Layer:
         """check() + c_struct(), cached while the layer holds the same tensors."""
@@ -173,11 +212,23 @@ class NvFp4MoELayer:
             self.__dict__["_checked"] = cached
         return cached[1]
 
+    def h16_norm(self) -> tuple:
+        """The (gate, up) bounds the forward gets: the larger of the banks', (0, 0) when off."""
+        if not self.fp16_h:
+            return (0.0, 0.0)
+        banks = [b for b in (self.routed, self.shared) if b is not None]
+        bounds = [b.current_h16_bound() for b in banks]
+        if any(not (b[0] > 0.0 and b[1] > 0.0 and math.isfinite(b[0]) and math.isfinite(b[1])) for b in bounds):
+            return (0.0, 0.0)
+        return (max(b[0] for b in bounds), max(b[1] for b in bounds))
+
     def c_struct(self) -> L.Layer:
         empty = L.Experts()
+        norm = self.h16_norm()
         return L.Layer(self.hidden, self.num_experts, self.top_k, self.w_router.data_ptr(),
                        self.router_bias.data_ptr() if self.router_bias is not None else None,
-                       self.routed.c_struct(), self.shared.c_struct() if self.shared is not None else empty)
+                       self.routed.c_struct(), self.shared.c_struct() if self.shared is not None else empty,
+                       (ctypes.c_float * 2)(*norm))
 
     @classmethod
     def from_tensors(cls, tensors: dict, top_k: int, global_scale_convention: str = "modelopt",

@@ -95,6 +95,90 @@ def test_rows_of_widely_different_magnitude_on_128_row_tiles():
             parity.assert_close(got[t:t + 1], res["out"][t:t + 1], f"token {t}")
 
 
+def _row_norm_bounds(layer: omoe.Layer):
+    """Largest Euclidean norm of the dequantized gate rows and of the up rows over both banks
+    (float64, from the canonical bytes through the oracle's dequantization)."""
+    from oracle import nvfp4 as onv
+    g = u = 0.0
+    banks = [layer.routed] + ([layer.shared] if layer.shared is not None else [])
+    for bank in banks:
+        for e in range(len(bank)):
+            ew = bank[e]
+            i = ew.w13.shape[0] // 2
+            wg = onv.dequantize(ew.w13[:i], ew.w13_scale[:i], ew.w13_gscale[0])
+            wu = onv.dequantize(ew.w13[i:], ew.w13_scale[i:], ew.w13_gscale[1])
+            g = max(g, float(np.sqrt((wg * wg).sum(axis=1)).max()))
+            u = max(u, float(np.sqrt((wu * wu).sum(axis=1)).max()))
+    return g, u
+
+
+def test_fp16_h_bound_is_the_largest_weight_row_norm():
+    """moe_nvfp4_h16_bound: the largest gate-row and up-row norms of both banks, rounded up to fp32."""
+    rng = np.random.default_rng(31337)
+    layer = helpers.random_layer(rng, 512, 256, 8, 2, shared=True)
+    glayer = parity.to_gpu_layer(layer)
+    got = glayer.h16_norm()
+    ref = _row_norm_bounds(layer)
+    for a, b in zip(got, ref):
+        assert b <= a <= b * (1 + 2.0 ** -22), (got, ref)
+
+
+def _h16_layer(seed, T, H, I, E, k):
+    rng = np.random.default_rng(seed)
+    layer = helpers.random_layer(rng, H, I, E, k, shared=True)
+    return rng, layer, parity.to_gpu_layer(layer)
+
+
+def test_fp16_h_equals_bf16_h_on_rows_of_widely_different_magnitude():
+    """On 128-row tiles with both GEMMs on the eight-wave kernel, h travels as fp16 scaled per token
+    by a power of two chosen from the weight-row norm bounds.  Rows from 2^-40 to 2^20, a row
+    spanning 2^-30..1 and a row of zeros: the forward equals the one with bf16 h bitwise, and
+    every token matches the oracle."""
+    T, H, I, E, k = 300, 512, 256, 8, 2
+    rng, layer, glayer = _h16_layer(778, T, H, I, E, k)
+    assert glayer.h16_norm()[0] > 0
+    xf = rng.normal(0, 1, (T, H))
+    xf *= 2.0 ** rng.integers(-40, 21, T)[:, None]
+    xf[1] *= 2.0 ** rng.integers(-30, 1, H)
+    xf[2] = 0.0
+    x = helpers.bf16_bits(torch.from_numpy(xf.astype(np.float32)).to(torch.bfloat16))
+    xg = parity.bits_to_bf16(x)
+    out, aux = ops.forward(glayer, xg, return_aux=True)
+    glayer.fp16_h = False
+    out_bf = ops.forward(glayer, xg)
+    glayer.fp16_h = True
+    assert torch.equal(out, out_bf), "fp16 h and bf16 h differ"
+    ids = aux["topk_ids"].cpu().numpy()
+    res = parity.reference_for_selection(x, layer, ids)
+    got = parity.f64(out)
+    assert np.all(got[2] == 0.0)
+    for t in range(T):
+        if t != 2:
+            parity.assert_close(got[t:t + 1], res["out"][t:t + 1], f"token {t}")
+
+
+def test_fp16_h_bound_is_what_the_forward_uses():
+    """A bound 2^20 above the true norms is valid (no fp16 overflow) but leaves most of h below the
+    range it carries exactly: the output then moves off the bf16-h result, so the forward does take
+    h through fp16 with the layer's bounds; with the true bounds it is back to bitwise equal."""
+    T, H, I, E, k = 600, 1024, 256, 8, 2
+    rng, layer, glayer = _h16_layer(779, T, H, I, E, k)
+    xg = parity.bits_to_bf16(helpers.random_x(rng, T, H))
+    out = ops.forward(glayer, xg)
+    glayer.fp16_h = False
+    out_bf = ops.forward(glayer, xg)
+    glayer.fp16_h = True
+    assert torch.equal(out, out_bf)
+    true_bounds = (glayer.routed.h16_bound, glayer.shared.h16_bound)
+    for b in (glayer.routed, glayer.shared):
+        b.h16_bound = tuple(v * 2.0 ** 20 for v in b.h16_bound)
+    loose = ops.forward(glayer, xg)
+    glayer.routed.h16_bound, glayer.shared.h16_bound = true_bounds
+    assert torch.isfinite(loose.float()).all()
+    assert not torch.equal(loose, out_bf), "the forward ignored the layer's bounds"
+    assert torch.equal(ops.forward(glayer, xg), out_bf)
+
+
 def test_persistent_gemm_tiles_chain_and_steal():
     """More 128-row tiles than workgroups, down K at the six-chunk minimum for chaining, routing
     skewed so that the XCD windows hold very different work: the forward (tiles drawn from the
