@@ -123,6 +123,33 @@ def test_workspace_size_covers_intermediates():
     assert L.lib().moe_permute_workspace_size(4096, 8, 320) >= (4096 * 8 // 2048) * 320 * 4
 
 
+def test_h16_bound_validation_host_only():
+    """moe_nvfp4_h16_bound refuses, before any launch, a NULL bank or output, a non-NVFP4 bank, a bank
+    without its gate/up tensors, dimensions off the kernels' grid and a misaligned output; an empty
+    bank is a no-op."""
+    fn = L.lib().moe_nvfp4_h16_bound
+    out = ctypes.c_void_p(0x3000)
+    assert fn(None, out, None) == L.MOE_ERR_INVALID_ARGUMENT
+    assert fn(ctypes.byref(_fake_bank(8, 512, 256)), None, None) == L.MOE_ERR_INVALID_ARGUMENT
+    for fmt in (L.MOE_WEIGHT_MXFP4, L.MOE_WEIGHT_MXFP4_A4, 7):
+        assert fn(ctypes.byref(_fake_bank(8, 512, 256, fmt=fmt)), out, None) == L.MOE_ERR_INVALID_ARGUMENT
+    for h, i in ((500, 256), (512, 250), (0, 256), (512, 0)):
+        assert fn(ctypes.byref(_fake_bank(8, h, i)), out, None) == L.MOE_ERR_INVALID_ARGUMENT, (h, i)
+    for field in ("w13", "w13_scale", "w13_gscale"):
+        b = _fake_bank(8, 512, 256)
+        setattr(b, field, None)
+        assert fn(ctypes.byref(b), out, None) == L.MOE_ERR_INVALID_ARGUMENT, field
+    assert fn(ctypes.byref(_fake_bank(8, 512, 256)), ctypes.c_void_p(0x3002), None) == L.MOE_ERR_INVALID_ARGUMENT
+    assert fn(ctypes.byref(_fake_bank(0, 512, 256)), out, None) == L.MOE_OK
+
+
+def test_layer_struct_carries_the_fp16_h_bounds():
+    """h16_norm sits at the end of moe_nvfp4_layer_t; a zero-initialised struct keeps fp16 h off."""
+    lay = L.Layer()
+    assert list(lay.h16_norm) == [0.0, 0.0]
+    assert L.Layer.h16_norm.offset == L.Layer.shared.offset + ctypes.sizeof(L.Experts)
+
+
 def test_product_path_has_no_oracle_dependency():
     """The package never imports the oracle (the oracle is test infrastructure only)."""
     pkg = os.path.join(ROOT, "nvfp4_weight_quantized_amd")
