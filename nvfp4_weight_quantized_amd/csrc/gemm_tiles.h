@@ -2,6 +2,9 @@
 // expert groups, the weight fragments of a wave, and the bf16 epilogue with SiLU(gate)*up.
 #pragma once
 
+#include <cstddef>
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -156,10 +159,13 @@ __device__ __forceinline__ int32_t* epilogue_hshift_out(const P&) { return nullp
 // so a caller that never touched their accumulators need not keep them.
 // epilogue_at takes the weight global scales of the tile's expert (g0: gate or down, g1: up; 1
 // without) and the lane and wave indices from the caller.
-template <int MI, int NB, bool GATE_UP, int BN, int COLS_PER_WAVE, class P, int RBE = MI>
+template <int MI, int NB, bool GATE_UP, int BN, int COLS_PER_WAVE, class P, int RBE = MI, class RS = std::nullptr_t>
 __device__ __forceinline__ void epilogue_at(const P& p, float g0, float g1, const TileInfo& ti, int ntile,
-                                            const f32x4 (&acc)[MI][NB], int mtile, const int* rshift, IntC<RBE>,
+                                            const f32x4 (&acc)[MI][NB], int mtile, RS rshift, IntC<RBE>,
                                             int lane, int wave) {
+  // the row powers of two are there exactly when the caller passes a pointer (nullptr: none), so
+  // that their use is decided at compile time
+  constexpr bool kRS = !std::is_same<RS, std::nullptr_t>::value;
   const int q = lane >> 4, nl = lane & 15;
   const float da = epilogue_act_gscale(p);
   // output fragments per wave (16 columns each) and their first column
@@ -192,7 +198,7 @@ __device__ __forceinline__ void epilogue_at(const P& p, float g0, float g1, cons
     };
     return uint2{pair(a, b), pair(c, d)};
   };
-  const bool h16 = epilogue_h16(p) && rshift != nullptr;
+  const bool h16 = kRS && epilogue_h16(p);
   // address of column col (of this lane's row) in block i
   auto dst = [&](int i, int row, int col) -> uint16_t* {
     if (GATE_UP && p.out_tiled) {
@@ -211,7 +217,8 @@ __device__ __forceinline__ void epilogue_at(const P& p, float g0, float g1, cons
     uint2 v[NF];
     if (GATE_UP) {
       const float dg = g0 * da, du = g1 * da;
-      const int rs = rshift ? rshift[row] : 0;
+      int rs = 0;
+      if constexpr (kRS) rs = rshift[row];
       const int xs = (int)(int16_t)rs;
       const int hs = h16 ? rs >> 16 : 0;
 #pragma unroll
@@ -220,7 +227,7 @@ __device__ __forceinline__ void epilogue_at(const P& p, float g0, float g1, cons
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float g = acc[i][f][r] * dg, u = acc[i][f + NF][r] * du;
-          if (rshift) {
+          if constexpr (kRS) {
             g = ldexpf(g, -xs);
             u = ldexpf(u, hs - xs);
           }
@@ -231,7 +238,7 @@ __device__ __forceinline__ void epilogue_at(const P& p, float g0, float g1, cons
       if (h16 && ntile == 0 && wave == 0 && q == 0 && valid) epilogue_hshift_out(p)[ti.row0 + row] = hs;
     } else {
       const float dd = g0 * da;
-      if (rshift) {
+      if constexpr (kRS) {
         const int hs = rshift[row];
 #pragma unroll
         for (int f = 0; f < NF; ++f)
@@ -256,7 +263,7 @@ __device__ __forceinline__ void epilogue_at(const P& p, float g0, float g1, cons
 template <int MI, int NB, bool GATE_UP, int BN, int COLS_PER_WAVE, bool GSCALE, class P, int RBE = MI>
 __device__ __forceinline__ void epilogue(const P& p, const GemmBank& bank, const TileInfo& ti, int ntile,
                                          const f32x4 (&acc)[MI][NB], int mtile = 0,
-                                         const int* rshift = nullptr, IntC<RBE> = {}) {
+                                         std::nullptr_t rshift = nullptr, IntC<RBE> = {}) {
   const float* gs = GSCALE ? bank.gs + (size_t)ti.group * bank.gs_per_expert : nullptr;
   epilogue_at<MI, NB, GATE_UP, BN, COLS_PER_WAVE>(p, gs ? gs[0] : 1.f, (GATE_UP && gs) ? gs[1] : 1.f, ti, ntile, acc,
                                                   mtile, rshift, IntC<RBE>{}, (int)(threadIdx.x & 63),

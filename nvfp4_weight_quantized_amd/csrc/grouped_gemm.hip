@@ -1151,8 +1151,12 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_tall_lds_kernel(GemmProbl
       if (GATE_UP) g1 = gk[1];
     }
     const TileInfo ti{t.group, t.row0, t.rows, t.a_row0, t.extra};
-    epilogue_at<MI, NB, GATE_UP, BN, COLS_PER_WAVE>(pe, g0, g1, ti, t.ntile, acc, t.mtile,
-                                                    A16 ? s_shift[par] : nullptr, IntC<RB>{}, lane_now(), wave);
+    if constexpr (A16)
+      epilogue_at<MI, NB, GATE_UP, BN, COLS_PER_WAVE>(pe, g0, g1, ti, t.ntile, acc, t.mtile,
+                                                      (const int*)s_shift[par], IntC<RB>{}, lane_now(), wave);
+    else
+      epilogue_at<MI, NB, GATE_UP, BN, COLS_PER_WAVE>(pe, g0, g1, ti, t.ntile, acc, t.mtile, nullptr, IntC<RB>{},
+                                                      lane_now(), wave);
   };
   for (;;) {
     switch ((__builtin_amdgcn_readfirstlane(s_tile[par][3]) + 15) / 16) {
