@@ -18,7 +18,9 @@
 //    block scale and v_cvt_pk_bf16_f32 packs the result.  element * block scale has at most 6
 //    significant bits, so the bf16 operand is exact.  The eight-wave gate/up kernel can take the
 //    token rows as fp16 instead (each row scaled by a power of two, an exact re-encoding) and
-//    then builds fp16 weight operands with one packed fp16 multiply per two elements.
+//    then builds fp16 weight operands with one packed fp16 multiply per two elements; it can also
+//    write h as fp16 (each token's h rows scaled by a power of two from a bound on |h|), which the
+//    eight-wave down kernel then multiplies in fp16 as well.
 //  * The weights are the MFMA's first operand and the activations its second, so the 16x16
 //    accumulator block is (weight row, token row): lane l = 16q + n holds token row n and four
 //    consecutive output columns 4q..4q+3, stored as one 8-byte write.
@@ -70,7 +72,7 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& w, const bf16x8& x, const f3
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, x, acc, 0, 0, 0);
 }
 
-// fp16 operands (NVFP4 gate/up on fp16 activation rows; see grouped_gemm_tall_lds_kernel).
+// fp16 operands (NVFP4 on fp16 token rows or fp16 h; see grouped_gemm_tall_lds_kernel).
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ f32x4 mfma(const f16x8& w, const f16x8& x, const f32x4& acc) {
@@ -571,6 +573,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void grouped_gemm_tall_kerne
 //    returned), and the last two row blocks beside the reads of chunk c + 1's first fragments.
 //  * The 16-row blocks of the tile beyond the group's rows are neither computed nor stored (a
 //    template parameter counts the blocks with real rows; their accumulators are never live).
+//  * A16: fp16 operands, NVFP4 only -- gate/up on the token rows as fp16 (launch_act_to_f16), down
+//    on h as the gate/up launch wrote it in fp16.  Each tile's row powers of two enter LDS beside
+//    its rows (s_shift; for the next tile by direct loads, one tile ahead) and the epilogue takes
+//    them out of the sums exactly.
 //  * Accumulators stay in the ordinary registers (128 per lane at NB = 4): with 512 registers for a
 //    single wave per SIMD, the compiler keeps 16x16x32 accumulators in the accumulation registers but
 //    does not tie each MFMA's result to its accumulator input, and copies every accumulator through
