@@ -64,7 +64,7 @@ GemmBank bank_w2(const moe_nvfp4_experts_t& b) { return GemmBank{b.w2, b.w2_scal
 
 struct ForwardLayout {
   size_t logits, ids, w, counts, offsets, sorted_slot, slot_to_row, block_hist, x16, row_shift, h, h_shared, y,
-      ctr, xa, tiles, hshift;
+      ctr, xa, tiles, hshift, rpart;
   size_t total;
 };
 
@@ -115,6 +115,8 @@ ForwardLayout forward_layout(int32_t T, int32_t H, int32_t I, int32_t I_shared, 
   L.tiles = take(2 * moe::kTileCounterWords * 4);
   // the power of two of each h row when h is held as fp16 (tiled h only)
   L.hshift = take(tiled && !a4 ? (S + (size_t)T) * 4 : 0);
+  // partial router sums of a split router GEMM beyond the first (which goes to the logits)
+  L.rpart = take((size_t)(moe::router_k_splits(T, H, E, k) - 1) * T * E * 4);
   L.total = off;
   return L;
 }
@@ -338,19 +340,25 @@ moe_status_t moe_mxfp4_w4a4_validate_forward(const moe_nvfp4_layer_t* layer, int
 namespace {
 
 // S1-S3 of a forward pass: router logits, top-k, permutation.
+// rpart: room for the partial sums of a split router GEMM (moe::router_k_splits - 1 arrays of
+// [T][E] floats), or NULL for one pass.
 moe_status_t run_routing(const moe_nvfp4_layer_t* layer, const uint16_t* x, int32_t T, float* logits, int32_t* ids,
                          float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_to_row,
                          int32_t* block_hist, const std::function<moe_status_t(int)>& mark, hipStream_t stream,
-                         int32_t* zero = nullptr, int32_t n_zero = 0) {
+                         int32_t* zero = nullptr, int32_t n_zero = 0, float* rpart = nullptr) {
   const int32_t H = layer->hidden, E = layer->num_experts, k = layer->top_k;
-  moe_status_t st =
-      moe::launch_router_logits(x, layer->w_router, layer->router_bias, T, H, E, logits, stream, zero, n_zero);
+  const int32_t splits = rpart ? moe::router_k_splits(T, H, E, k) : 1;
+  moe_status_t st = moe::launch_router_logits(x, layer->w_router, layer->router_bias, T, H, E, logits, stream, zero,
+                                              n_zero, rpart, splits);
   if (st || (st = mark(1))) return st;
   if ((int64_t)T * k <= moe::kPermuteChunk) {
     // few tokens: top-k and permutation together in one workgroup
     st = moe::launch_topk_permute_small(logits, T, E, k, ids, w, counts, offsets, sorted_slot, slot_to_row, stream);
   } else {
-    st = moe::launch_route(nullptr, nullptr, nullptr, T, H, E, k, true, logits, ids, w, stream);
+    if (splits > 1)
+      st = moe::launch_topk_sum(logits, rpart, splits, layer->router_bias, T, E, k, ids, w, stream);
+    else
+      st = moe::launch_route(nullptr, nullptr, nullptr, T, H, E, k, true, logits, ids, w, stream);
     if (st) return st;
     st = moe::launch_permute(ids, T, k, E, counts, offsets, sorted_slot, slot_to_row, block_hist, stream);
   }
@@ -472,7 +480,7 @@ moe_status_t forward_impl(const moe_nvfp4_layer_t* layer, const uint16_t* x, int
   // the router launch clears the tile counters of the two GEMM launches
   int32_t* tile_ctr = at<int32_t>(workspace, L.tiles);
   st = run_routing(layer, x, T, logits, ids, w, counts, offsets, sorted_slot, slot_to_row, block_hist, mark, stream,
-                   tile_ctr, 2 * moe::kTileCounterWords);
+                   tile_ctr, 2 * moe::kTileCounterWords, at<float>(workspace, L.rpart));
   if (st) return st;
   gu.tile_ctr = tile_ctr;
   dn.tile_ctr = tile_ctr + moe::kTileCounterWords;

@@ -66,9 +66,19 @@ moe_status_t launch_topk_permute_small(const float* logits, int32_t T, int32_t E
 // T <= kRouterSmallTokens runs the one-pass few-token kernel, larger T the MFMA kernel; either
 // also clears `zero` [n_zero] (counters of the kernels that follow in the same stream).
 constexpr int kRouterSmallTokens = 32;
+// partial, splits (MFMA kernel only): the K range of each tile cut into `splits` runs on as many
+// workgroups; run 0 writes logits and run s partial + (s - 1) * T * E, all without the bias, and
+// launch_topk_sum adds them (splits = 1: one run, bias included, partial unused).
 moe_status_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, const float* bias, int32_t T,
                                   int32_t H, int32_t E, float* logits, hipStream_t stream, int32_t* zero = nullptr,
-                                  int32_t n_zero = 0);
+                                  int32_t n_zero = 0, float* partial = nullptr, int32_t splits = 1);
+// The forward's split count for the router GEMM (1 when it takes the few-token kernel or the
+// one-workgroup top-k + permutation, or when its tiles alone fill the GPU).
+int router_k_splits(int32_t T, int32_t H, int32_t E, int32_t k);
+// Top-k after a split router: logits = (partial sums in split order) + bias, written back, then the
+// selection of launch_route.
+moe_status_t launch_topk_sum(float* logits, const float* partial, int32_t splits, const float* bias, int32_t T,
+                             int32_t E, int32_t k, int32_t* ids, float* w, hipStream_t stream);
 moe_status_t launch_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int32_t T,
                           int32_t H, int32_t E, int32_t k, bool logits_given, float* logits,
                           int32_t* ids, float* w, hipStream_t stream);
