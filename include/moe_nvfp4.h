@@ -236,7 +236,8 @@ typedef struct {
 } moe_forward_aux_t;
 
 /* Workspace bytes moe_nvfp4_forward needs for T tokens (I_shared = 0: no shared expert).  It holds
- * the router logits, the selection, the permutation, x as fp16 rows with one power-of-two shift
+ * the router logits (and, for a router GEMM split along K, up to three more [T][E] fp32 arrays of
+ * partial sums), the selection, the permutation, x as fp16 rows with one power-of-two shift
  * per row ([T][H] fp16 + [T] int32; read by the NVFP4 gate/up GEMM on prefill shapes, an exact
  * re-encoding of the bf16 values), the intermediate h (row-major, or in the 128-row-tile fragment
  * order the prefill-shaped GEMMs exchange it in: up to (min(E, T*k) + T*k/128 + ceil(T/128)) * 128
