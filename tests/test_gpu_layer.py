@@ -55,6 +55,38 @@ def test_small_layer_end_to_end(case):
     assert torch.equal(out, out2), "two runs differ"
 
 
+# Shapes on the boundaries between the forward's paths (router kernel, router split along K, top-k
+# launch, permutation, 128-row tiles, fp16 token rows and fp16 h); every token checked.
+PATHS = [
+    # T, H, I, E, k, shared, bias, what the case sits on
+    (32, 512, 256, 8, 8, True, True, "few-token router (T = 32), one-workgroup top-k + permutation"),
+    (33, 512, 256, 8, 8, True, False, "MFMA router from T = 33, one-workgroup top-k + permutation"),
+    (256, 512, 256, 8, 8, True, True, "T*k = 2048: the last one-workgroup top-k + permutation, one router pass"),
+    (257, 512, 256, 8, 8, True, True, "T*k = 2056: split router (4 runs), multi-block permutation, fp16 h"),
+    (513, 256, 256, 8, 4, True, False, "split capped at H/128 = 2 runs; gate/up on fp16 rows, down on bf16 h (width 256)"),
+    (520, 128, 128, 16, 4, True, True, "H = 128: one router pass, top-k launch, four-wave 128-row tiles"),
+    (400, 384, 256, 100, 7, False, True, "E = 100, k = 7, 3 router runs (H = 384), no shared expert"),
+    (2049, 256, 128, 4, 1, True, False, "k = 1 past one permutation chunk, 2 router runs"),
+]
+
+
+@pytest.mark.parametrize("case", PATHS, ids=[f"T{c[0]}_H{c[1]}_I{c[2]}_E{c[3]}_k{c[4]}" for c in PATHS])
+def test_forward_path_boundaries(case):
+    T, H, I, E, k, shared, bias, _ = case
+    rng = np.random.default_rng(T * 7 + H + E)
+    layer = helpers.random_layer(rng, H, I, E, k, shared=shared, bias=bias)
+    x = helpers.random_x(rng, T, H)
+    glayer = parity.to_gpu_layer(layer)
+    xg = parity.bits_to_bf16(x)
+    out, aux = ops.forward(glayer, xg, return_aux=True)
+    parity.check_route(aux["logits"], aux["topk_ids"], aux["topk_w"], x, layer.w_router, layer.router_bias, k)
+    ids = aux["topk_ids"].cpu().numpy()
+    assert np.array_equal(aux["expert_counts"].cpu().numpy(), omoe.permute(ids, E)[0])
+    res = parity.reference_for_selection(x, layer, ids)
+    parity.assert_close(parity.f64(out), res["out"], "layer")
+    assert torch.equal(ops.forward(glayer, xg), out), "two runs differ"
+
+
 def test_skewed_routing_on_128_row_tiles():
     """A few experts take most rows and many take a handful: the XCD ranges of the 128-row GEMMs are
     cut by cost, so most tiles land on few XCDs' ranges; every token is checked."""
