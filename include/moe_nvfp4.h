@@ -204,6 +204,8 @@ moe_status_t moe_combine(const uint16_t* y_rows, const int32_t* slot_to_row, con
  * stage_events (host array of MOE_NUM_STAGE_EVENTS hipEvent_t handles, or NULL): when given,
  * event i is recorded on the stream at stage boundary i -- 0 before S1, 1 after S1, 2 after S2+S3,
  * 3 after S4, 4 after S5, 5 after S6 -- so callers can time each stage; NULL entries are skipped.
+ * Where S4's GEMM reads x as fp16 rows (NVFP4 on 128-row tiles), event 2 follows the pass that
+ * writes them, so that the S4 interval holds the GEMM launches alone.
  * The events are created and owned by the caller.
  * y_rows (device, bf16 [T*k + T_shared][H], T_shared = T with a shared expert, else 0): when given,
  * the expert outputs of S5 are written there instead of the workspace -- row r < T*k is the routed

@@ -339,7 +339,8 @@ moe_status_t moe_mxfp4_w4a4_validate_forward(const moe_nvfp4_layer_t* layer, int
 
 namespace {
 
-// S1-S3 of a forward pass: router logits, top-k, permutation.
+// S1-S3 of a forward pass: router logits, top-k, permutation (stage event 1 after S1; the caller
+// records event 2).
 // rpart: room for the partial sums of a split router GEMM (moe::router_k_splits - 1 arrays of
 // [T][E] floats), or NULL for one pass.
 moe_status_t run_routing(const moe_nvfp4_layer_t* layer, const uint16_t* x, int32_t T, float* logits, int32_t* ids,
@@ -362,8 +363,7 @@ moe_status_t run_routing(const moe_nvfp4_layer_t* layer, const uint16_t* x, int3
     if (st) return st;
     st = moe::launch_permute(ids, T, k, E, counts, offsets, sorted_slot, slot_to_row, block_hist, stream);
   }
-  if (st) return st;
-  return mark(2);
+  return st;
 }
 
 }  // namespace
@@ -489,6 +489,7 @@ moe_status_t forward_impl(const moe_nvfp4_layer_t* layer, const uint16_t* x, int
   // with d_x applied in their epilogues
   const uint16_t* xg = x;
   if (a4) {
+    if ((st = mark(2))) return st;
     uint16_t* xa = at<uint16_t>(workspace, L.xa);
     if ((st = moe::launch_quantize_act_nv(x, T, H, a4[0], nullptr, nullptr, xa, stream))) return st;
     xg = xa;
@@ -517,6 +518,10 @@ moe_status_t forward_impl(const moe_nvfp4_layer_t* layer, const uint16_t* x, int
     gu.a16 = x16;
     gu.row_shift = row_shift;
   }
+  // W4A16: event 2 after S3 and the fp16 row pass that prepares S4's operand rows, so that the S4
+  // interval is the GEMM launches alone (with W4A4 the activation quantizer, a step of that method,
+  // and the row pass on its output are in S4)
+  if (!a4 && (st = mark(2))) return st;
   if (h16) {
     int32_t* hshift = at<int32_t>(workspace, L.hshift);
     gu.h16 = 1;
@@ -791,7 +796,7 @@ moe_status_t moe_mxfp4_w4a4_forward(const moe_nvfp4_layer_t* layer, const uint16
   moe_status_t st = mark(0);
   if (st) return st;
   st = run_routing(layer, x, T, logits, ids, w, counts, offsets, sorted_slot, slot_to_row, block_hist, mark, stream);
-  if (st) return st;
+  if (st || (st = mark(2))) return st;
 
   // S4: x to MXFP4 once per token; routed rows gathered through sorted_slot, the shared expert in
   // the same launch when its width matches
