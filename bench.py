@@ -51,8 +51,8 @@ BYTES_PER_WEIGHT = {"nvfp4": 0.5 + 1 / 16, "mxfp4": 0.5 + 1 / 32, "mxfp4_a4": 0.
 _CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "nvfp4_weight_quantized_amd", "csrc")
 _GEMM_SRCS = [os.path.join(_CSRC, f) for f in ("grouped_gemm.hip", "gemm_tiles.h", "gemm_skinny.h")]
 _TRAFFIC = {  # workload: (code fingerprint of the GEMM sources, bytes read, bytes written) per gate/up launch
-    "decode": ("db0f1285a5e3e0575e20688041f99ea4a71d87476a05366ff23b507e737a9517", 432.49e6, 0.22e6),
-    "prefill": ("db0f1285a5e3e0575e20688041f99ea4a71d87476a05366ff23b507e737a9517", 2881.28e6, 113.99e6),
+    "decode": ("43f04cc0f3ee4e7e43eabb7761f144b6ccad315e393e345b5e2e5fca5504bfc9", 432.49e6, 0.22e6),
+    "prefill": ("43f04cc0f3ee4e7e43eabb7761f144b6ccad315e393e345b5e2e5fca5504bfc9", 2869.87e6, 113.99e6),
 }
 
 PREFILL_CONFIGS = ["prefill", "skewed", "long_prefill"]

@@ -72,8 +72,7 @@ __device__ __forceinline__ void combine_cols(const uint16_t* __restrict__ y, con
   uint32_t o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    o[i] = placed ? (uint32_t)f32_to_bf16(acc[2 * i]) | ((uint32_t)f32_to_bf16(acc[2 * i + 1]) << 16)
-                  : 0x7FC07FC0u;   // two bf16 quiet NaNs
+    o[i] = placed ? f32x2_to_bf16x2(acc[2 * i], acc[2 * i + 1]) : 0x7FC07FC0u;   // two bf16 quiet NaNs
   *reinterpret_cast<uint4*>(out + (size_t)t * H + h0) = uint4{o[0], o[1], o[2], o[3]};
 }
 

@@ -25,6 +25,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+// Two values to bf16 (round to nearest even) in one dword, lo in the low half: one
+// v_cvt_pk_bf16_f32 with both operands, the same rounding as f32_to_bf16 of each.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
 // 16 bytes per lane from global memory straight to LDS (global_load_lds_dwordx4): lane i's bytes
 // land at lds_addr + 16*i.  The global address is a wave-uniform base plus a 32-bit per-lane byte
 // offset; lds_addr must be wave-uniform (it is passed in M0).  Issued from inline assembly, so the

@@ -181,23 +181,24 @@ __device__ __forceinline__ void epilogue_at(const P& p, float g0, float g1, cons
   // chunks wait behind them (the memory counter counts stores).  An odd last fragment is stored
   // 8 bytes per lane as before.  The swap runs in every lane, rows past the tile's included.
   const int pc = 16 * (q & 1) + 8 * (q >> 1);
-  auto pack4 = [](float a, float b, float c, float d) {
-    return uint2{(uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16),
-                 (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16)};
-  };
+  auto pack4 = [](float a, float b, float c, float d) { return uint2{f32x2_to_bf16x2(a, b), f32x2_to_bf16x2(c, d)}; };
   // the bf16 rounding of each value, as fp16 (exact for every value of at least 2^-17 and below 2^16;
   // smaller ones round to nearest even on the fp16 subnormal grid): per pair one bf16 pair
   // conversion, the two halves back to fp32, one fp16 pair conversion (v_cvt_pk_f16_f32)
   auto pack4h = [](float a, float b, float c, float d) {
     auto pair = [](float x, float y) {
-      const uint32_t bb = (uint32_t)f32_to_bf16(x) | ((uint32_t)f32_to_bf16(y) << 16);
-      typedef float f32x2_t __attribute__((ext_vector_type(2)));
+      const uint32_t bb = f32x2_to_bf16x2(x, y);
       typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-      const f32x2_t v = {__uint_as_float(bb << 16), __uint_as_float(bb & 0xFFFF0000u)};
+      const f32x2 v = {__uint_as_float(bb << 16), __uint_as_float(bb & 0xFFFF0000u)};
       return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
     };
     return uint2{pair(a, b), pair(c, d)};
   };
+  // A row's power of two folded into a scale (one multiply per value instead of a multiply and an
+  // ldexp) gives the same roundings wherever the folded scale is a normal number (or the scale is 0):
+  // a product is then rounded once either way.  A wave takes the folded form for a row block only
+  // when that holds in all its lanes.
+  auto foldable = [](float folded, float scale) { return __builtin_isnormal(folded) || scale == 0.f; };
   const bool h16 = kRS && epilogue_h16(p);
   // address of column col (of this lane's row) in block i
   auto dst = [&](int i, int row, int col) -> uint16_t* {
@@ -221,29 +222,40 @@ __device__ __forceinline__ void epilogue_at(const P& p, float g0, float g1, cons
       if constexpr (kRS) rs = rshift[row];
       const int xs = (int)(int16_t)rs;
       const int hs = h16 ? rs >> 16 : 0;
+      auto store_h = [&](auto gate, auto up) {
 #pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        float h[4];
+        for (int f = 0; f < NF; ++f) {
+          float h[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float g = acc[i][f][r] * dg, u = acc[i][f + NF][r] * du;
-          if constexpr (kRS) {
-            g = ldexpf(g, -xs);
-            u = ldexpf(u, hs - xs);
-          }
-          h[r] = silu(g) * u;
+          for (int r = 0; r < 4; ++r) h[r] = silu(gate(acc[i][f][r])) * up(acc[i][f + NF][r]);
+          v[f] = h16 ? pack4h(h[0], h[1], h[2], h[3]) : pack4(h[0], h[1], h[2], h[3]);
         }
-        v[f] = h16 ? pack4h(h[0], h[1], h[2], h[3]) : pack4(h[0], h[1], h[2], h[3]);
+      };
+      if constexpr (kRS) {
+        const float dgr = ldexpf(dg, -xs), dur = ldexpf(du, hs - xs);
+        if (__builtin_amdgcn_ballot_w64(!(foldable(dgr, dg) && foldable(dur, du))) == 0)
+          store_h([&](float a) { return a * dgr; }, [&](float a) { return a * dur; });
+        else
+          store_h([&](float a) { return ldexpf(a * dg, -xs); }, [&](float a) { return ldexpf(a * du, hs - xs); });
+      } else {
+        store_h([&](float a) { return a * dg; }, [&](float a) { return a * du; });
       }
       if (h16 && ntile == 0 && wave == 0 && q == 0 && valid) epilogue_hshift_out(p)[ti.row0 + row] = hs;
     } else {
       const float dd = g0 * da;
       if constexpr (kRS) {
         const int hs = rshift[row];
+        const float ddr = ldexpf(dd, -hs);
+        if (__builtin_amdgcn_ballot_w64(!foldable(ddr, dd)) == 0) {
 #pragma unroll
-        for (int f = 0; f < NF; ++f)
-          v[f] = pack4(ldexpf(acc[i][f][0] * dd, -hs), ldexpf(acc[i][f][1] * dd, -hs), ldexpf(acc[i][f][2] * dd, -hs),
-                       ldexpf(acc[i][f][3] * dd, -hs));
+          for (int f = 0; f < NF; ++f)
+            v[f] = pack4(acc[i][f][0] * ddr, acc[i][f][1] * ddr, acc[i][f][2] * ddr, acc[i][f][3] * ddr);
+        } else {
+#pragma unroll
+          for (int f = 0; f < NF; ++f)
+            v[f] = pack4(ldexpf(acc[i][f][0] * dd, -hs), ldexpf(acc[i][f][1] * dd, -hs),
+                         ldexpf(acc[i][f][2] * dd, -hs), ldexpf(acc[i][f][3] * dd, -hs));
+        }
       } else {
 #pragma unroll
         for (int f = 0; f < NF; ++f)
