@@ -189,6 +189,40 @@ def test_fp16_h_equals_bf16_h_on_rows_of_widely_different_magnitude():
             parity.assert_close(got[t:t + 1], res["out"][t:t + 1], f"token {t}")
 
 
+def test_fp16_h_on_tiny_rows_that_take_the_unfolded_epilogues():
+    """Rows near 2^-55 and 2^-60 get h powers of two so large that the down epilogue cannot fold
+    them into the weight scale (the folded scale would be subnormal) and scales after the product
+    instead; for a row near 2^-100 the gate/up epilogue cannot fold the token's power of two either.
+    Such a row makes its whole 16-row block take the two-step form: the N(0,1) rows around them
+    equal the bf16-h forward bitwise; the tiny rows match the oracle (the bf16-h forward itself
+    loses bits there, its fp32 products of such h being subnormal); the 2^-100 row's output is 0,
+    the bf16 rounding of the oracle's."""
+    T, H, I, E, k = 300, 512, 256, 8, 2
+    rng, layer, glayer = _h16_layer(781, T, H, I, E, k)
+    xf = rng.normal(0, 1, (T, H))
+    tiny = {3: -55, 4: -60, 150: -55, 299: -60, 5: -100}
+    for t, e in tiny.items():
+        xf[t] *= 2.0 ** e
+    x = helpers.bf16_bits(torch.from_numpy(xf.astype(np.float32)).to(torch.bfloat16))
+    xg = parity.bits_to_bf16(x)
+    out, aux = ops.forward(glayer, xg, return_aux=True)
+    glayer.fp16_h = False
+    out_bf = ops.forward(glayer, xg)
+    glayer.fp16_h = True
+    others = [t for t in range(T) if t not in tiny]
+    assert torch.equal(out[others], out_bf[others]), "fp16 h and bf16 h differ on the N(0,1) rows"
+    ids = aux["topk_ids"].cpu().numpy()
+    res = parity.reference_for_selection(x, layer, ids)
+    got = parity.f64(out)
+    # below half the smallest bf16 subnormal (2^-133): its bf16 value is 0
+    assert np.abs(res["out"][5]).max() < 2.0 ** -134 and np.all(got[5] == 0.0)
+    for t in range(T):
+        if t != 5:
+            if t in tiny:
+                assert np.abs(res["out"][t]).max() > 2.0 ** -126, f"token {t} is not a normal bf16 output"
+            parity.assert_close(got[t:t + 1], res["out"][t:t + 1], f"token {t}")
+
+
 def test_fp16_h_bound_is_what_the_forward_uses():
     """A bound 2^20 above the true norms is valid (no fp16 overflow) but leaves most of h below the
     range it carries exactly: the output then moves off the bf16-h result, so the forward does take
