@@ -8,8 +8,9 @@
 // order in which atomics land; lanes of one wave holding the same expert are found with ballots.
 //
 // Small S (one workgroup): one launch does histogram, scan and scatter; for few tokens the top-k
-// selection (S2) runs in the same launch.  Large S: per-block histograms -> one scan workgroup ->
-// per-block stable scatter.
+// selection (S2) runs in the same launch.  Larger S: per-block histograms, then per-block stable
+// scatter, each scatter workgroup scanning the histograms itself (up to 16 blocks) or after one
+// scan workgroup (more blocks).
 // Source: the "Permute-Experts-Unpermute" stage of the modular fused MoE ("vLLM on the NVIDIA DGX
 // Spark: A Complete Technical Guide", section 7.1) and the token dispatch of the fused b12x MoE
 // (section 4).
@@ -141,6 +142,63 @@ __global__ __launch_bounds__(kPermuteThreads) void permute_scatter_kernel(
   if (s_begin < s_end) wave_stable_scatter(ids, s_begin, s_end, E, wave_hist[wave], sorted_slot, slot_to_row);
 }
 
+// Steps 2 and 3 in one launch for up to kScanInScatter blocks: every scatter workgroup reads all
+// the per-block histograms (nb * E values, from L2), forms the counts, their exclusive scan and its
+// own block's bases, then scatters as above; workgroup 0 writes counts and offsets.  One launch
+// fewer than scan then scatter, for S <= kScanInScatter * kPermuteChunk.
+constexpr int kScanInScatter = 16;
+__global__ __launch_bounds__(kPermuteThreads) void permute_scan_scatter_kernel(
+    const int32_t* __restrict__ ids, int S, int E, int nb, const int32_t* __restrict__ block_hist,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
+    int32_t* __restrict__ slot_to_row) {
+  __shared__ int wave_hist[kPermWaves][kPermMaxE];
+  __shared__ int offs[kPermMaxE];
+  __shared__ int before[kPermMaxE];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int b = blockIdx.x;
+  // per expert: the count over all blocks and the part of it in the blocks before this one
+  for (int e = tid; e < E; e += kPermuteThreads) {
+    int v[kScanInScatter];
+#pragma unroll
+    for (int i = 0; i < kScanInScatter; ++i) v[i] = i < nb ? block_hist[(size_t)i * E + e] : 0;
+    int total = 0, pre = 0;
+#pragma unroll
+    for (int i = 0; i < kScanInScatter; ++i) {
+      pre = i == b ? total : pre;
+      total += v[i];
+    }
+    offs[e] = total;
+    before[e] = pre;
+    if (b == 0) counts[e] = total;
+  }
+  for (int w = 0; w < kPermWaves; ++w)
+    for (int e = tid; e < E; e += kPermuteThreads) wave_hist[w][e] = 0;
+  __syncthreads();
+  const int blk0 = b * kPermuteChunk;
+  const int s_begin = blk0 + wave * kPermSlotsPerWave;
+  const int s_end = min(S, s_begin + kPermSlotsPerWave);
+  if (wave == 0) {
+    const int total = wave_exclusive_scan(offs, offs, E);
+    if (b == 0 && (tid & 63) == 0) offsets[E] = total;
+  }
+  for (int s = s_begin + (tid & 63); s < s_end; s += 64) {
+    const int e = ids[s];
+    if (e >= 0 && e < E) atomicAdd(&wave_hist[wave][e], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kPermuteThreads) {
+    if (b == 0) offsets[e] = offs[e];
+    int run = offs[e] + before[e];
+    for (int w = 0; w < kPermWaves; ++w) {
+      const int c = wave_hist[w][e];
+      wave_hist[w][e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  if (s_begin < s_end) wave_stable_scatter(ids, s_begin, s_end, E, wave_hist[wave], sorted_slot, slot_to_row);
+}
+
 }  // namespace
 
 moe_status_t launch_permute(const int32_t* ids, int32_t T, int32_t k, int32_t E, int32_t* counts,
@@ -155,6 +213,11 @@ moe_status_t launch_permute(const int32_t* ids, int32_t T, int32_t k, int32_t E,
   const int nb = permute_blocks(S);
   hipLaunchKernelGGL(permute_hist_kernel, dim3(nb), dim3(kPermuteThreads), 0, stream, ids, S, (int)E, block_hist);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
+  if (nb <= kScanInScatter) {
+    hipLaunchKernelGGL(permute_scan_scatter_kernel, dim3(nb), dim3(kPermuteThreads), 0, stream, ids, S, (int)E, nb,
+                       block_hist, counts, offsets, sorted_slot, slot_to_row);
+    return launch_status();
+  }
   hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, stream, block_hist, nb, (int)E, counts, offsets);
   if (launch_status() != MOE_OK) return MOE_ERR_HIP;
   hipLaunchKernelGGL(permute_scatter_kernel, dim3(nb), dim3(kPermuteThreads), 0, stream, ids, S, (int)E,
