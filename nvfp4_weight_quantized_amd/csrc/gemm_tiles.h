@@ -155,6 +155,8 @@ __device__ __forceinline__ int32_t* epilogue_hshift_out(const P&) { return nullp
 // scaling by 2^hs, hs = rshift[row] >> 16 (folded into u's scale: power-of-two scaling commutes with
 // the bf16 rounding), and the column-tile-0 workgroup records hs in p.hshift_out[row of h].  Down
 // (fp16 h): h row `row` was scaled by 2^rshift[row]; the sums are scaled back by 2^-rshift[row].
+// These powers of two enter the global scales (one multiply per value) wherever the scaled global
+// scale stays a normal number; otherwise the row block applies them after the product.
 // RBE (default MI): the 16-row blocks that can hold rows of the tile; blocks past it are not read,
 // so a caller that never touched their accumulators need not keep them.
 // epilogue_at takes the weight global scales of the tile's expert (g0: gate or down, g1: up; 1
